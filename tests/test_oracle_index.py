@@ -1,0 +1,202 @@
+"""Pins of the oracle's indexer score, Top-K, hierarchical pool and Reindex
+(CPU only).  Exact integer cases, an fp64 error bound, brute-force sorting,
+tie rules and the mode equivalences the CSA2 description implies."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def bf16(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16f(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_score_exact_on_integer_inputs():
+    # integers in [-3,3] and weights in {0, .5, 1}: every product, sum and
+    # weighted sum is exact in fp32, so the score is a hand-computable integer.
+    rng = np.random.default_rng(10)
+    for h_i, d_i in [(4, 64), (64, 128), (3, 5)]:
+        for _ in range(20):
+            q = rng.integers(-3, 4, (h_i, d_i))
+            k = rng.integers(-3, 4, d_i)
+            w = rng.choice([0.0, 0.5, 1.0], h_i)
+            exp = sum(w[h] * max(0, int(q[h] @ k)) for h in range(h_i))
+            got = oracle.index_score(bf16(q), w.astype(np.float32), bf16(k))
+            assert got == exp
+
+
+def test_score_within_rounding_bound_of_fp64():
+    rng = np.random.default_rng(11)
+    h_i, d_i = 64, 128
+    u = 2.0 ** -24
+    g = lambda n: n * u / (1 - n * u)
+    for _ in range(200):
+        q = bf16(rng.standard_normal((h_i, d_i)))
+        k = bf16(rng.standard_normal(d_i))
+        w = rng.uniform(0, 1, h_i).astype(np.float32)
+        qf, kf = bf16f(q).astype(np.float64), bf16f(k).astype(np.float64)
+        dots = qf @ kf
+        exact = float(np.sum(w.astype(np.float64) * np.maximum(dots, 0)))
+        absdots = np.abs(qf) @ np.abs(kf)
+        bound = float(np.sum(w * (g(d_i) * absdots))) + g(h_i) * float(np.sum(w * (np.maximum(dots, 0) + g(d_i) * absdots)))
+        got = oracle.index_score(q, w, k)
+        assert abs(got - exact) <= bound
+
+
+def _brute_topk(scores, k, pos=None):
+    n = len(scores)
+    pos = np.arange(n) if pos is None else np.asarray(pos)
+    order = np.lexsort((pos, -np.asarray(scores, np.float64)))
+    sel = np.sort(pos[order[:min(k, n)]])
+    return np.concatenate([sel, -np.ones(k - len(sel), np.int64)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 511, 512, 513, 4096])
+def test_topk_matches_full_sort(n):
+    rng = np.random.default_rng(n)
+    s = rng.standard_normal(n).astype(np.float32)
+    s[rng.integers(0, max(n, 1), n // 3)] = 0.25        # plenty of exact ties
+    got = oracle.topk(s, 512)
+    assert np.array_equal(got, _brute_topk(s, 512))
+    keep = min(512, n)
+    assert np.all(got[keep:] == -1) and np.all(np.diff(got[:keep]) > 0)
+    if 0 < keep < n:   # every kept score >= every dropped score
+        mask = np.zeros(n, bool)
+        mask[got[:keep]] = True
+        assert s[mask].min() >= s[~mask].max()
+
+
+def test_topk_ties_go_to_lower_position_and_minus_zero_equals_zero():
+    assert np.array_equal(oracle.topk(np.full(2000, 3.0, np.float32), 512), np.arange(512))
+    s = np.zeros(1000, np.float32)
+    s[::2] = -0.0
+    assert np.array_equal(oracle.topk(s, 512), np.arange(512))
+    # explicit positions: ties resolved by the position, not the list order
+    s = np.array([1, 1, 1, 2], np.float32)
+    pos = np.array([40, 10, 30, 20], np.int32)
+    assert list(oracle.topk(s, 2, pos)) == [10, 20]
+
+
+def _inputs(n_q, L, h_i=4, d_i=64, seed=0):
+    rng = np.random.default_rng(seed)
+    iq = bf16(rng.standard_normal((n_q, h_i, d_i)))
+    w = rng.uniform(0, 1, (n_q, h_i)).astype(np.float32)
+    ik = bf16(rng.standard_normal((n_q * L, d_i)))
+    seq_base = np.arange(n_q, dtype=np.int64) * L
+    return iq, w, np.arange(n_q, dtype=np.int32), np.full(n_q, L, np.int32), ik, seq_base
+
+
+def test_full_is_topk_of_scores_with_zero_keys_and_equal_keys():
+    iq, w, qs, nv, ik, sb = _inputs(1, 3000)
+    ik[:] = 0                                           # every score is +0
+    assert np.array_equal(oracle.index_topk(iq, w, qs, nv, ik, sb, 512)[0], np.arange(512))
+    ik[:] = bf16(np.ones(64))                           # every key equal
+    assert np.array_equal(oracle.index_topk(iq, w, qs, nv, ik, sb, 512)[0], np.arange(512))
+
+
+def test_full_short_context_selects_everything():
+    for L in (1, 7, 300, 512):
+        iq, w, qs, nv, ik, sb = _inputs(2, L, seed=L)
+        idx = oracle.index_topk(iq, w, qs, nv, ik, sb, 512)
+        ref = np.concatenate([np.arange(L), -np.ones(512 - L)]).astype(np.int32)
+        assert np.array_equal(idx[0], ref) and np.array_equal(idx[1], ref)
+
+
+def test_full_matches_brute_force_sort():
+    iq, w, qs, nv, ik, sb = _inputs(2, 2500, seed=3)
+    idx = oracle.index_topk(iq, w, qs, nv, ik, sb, 512)
+    for q in range(2):
+        sc = [oracle.index_score(iq[q], w[q], ik[sb[q] + t]) for t in range(2500)]
+        assert np.array_equal(idx[q], _brute_topk(sc, 512))
+
+
+def test_duplicated_blocks_prefer_lower_positions():
+    iq, w, qs, nv, ik, sb = _inputs(1, 2048, seed=4)
+    ik[1024:2048] = ik[0:1024]                          # second half repeats the first
+    idx = oracle.index_topk(iq, w, qs, nv, ik, sb, 512)[0]
+    # a copy in the second half can only be chosen together with its original
+    hi = idx[idx >= 1024]
+    assert np.all(np.isin(hi - 1024, idx))
+
+
+def test_pool_takes_every_block_when_few():
+    iq, w, qs, nv, ik, sb = _inputs(2, 1000, seed=5)
+    idx, pool = oracle.index_topk(iq, w, qs, nv, ik, sb, 512, block=8, keep_blocks=2048)
+    nb = (1000 + 7) // 8
+    ref = np.concatenate([np.arange(nb), -np.ones(2048 - nb)]).astype(np.int32)
+    assert np.array_equal(pool[0], ref) and np.array_equal(pool[1], ref)
+    # the pool covers the whole context, so Reindex with the Full layer's own
+    # query reproduces Full bit for bit
+    r = oracle.reindex_topk(iq, w, qs, nv, ik, sb, pool, 512, block=8)
+    assert np.array_equal(r, idx)
+
+
+def test_block_constant_keys_make_reindex_equal_full():
+    # every block of 8 holds one key repeated: the block mean is that key
+    # exactly, so a block scores as its members and the Top-512 tokens are the
+    # members of the Top-64 blocks, all inside a 128-block pool.
+    L, keep = 4096, 128
+    iq, w, qs, nv, ik, sb = _inputs(1, L, seed=6)
+    ik[:] = np.repeat(ik[::8], 8, axis=0)
+    idx, pool = oracle.index_topk(iq, w, qs, nv, ik, sb, 512, block=8, keep_blocks=keep)
+    blocks_of_idx = np.unique(idx // 8)
+    assert len(blocks_of_idx) == 64 and np.all(np.isin(blocks_of_idx, pool))
+    r = oracle.reindex_topk(iq, w, qs, nv, ik, sb, pool, 512, block=8)
+    assert np.array_equal(r, idx)
+    # block scores equal member scores: the pool is the Top-128 blocks by the
+    # score of their (shared) key
+    bsc = [oracle.index_score(iq[0], w[0], ik[8 * b]) for b in range(L // 8)]
+    assert np.array_equal(pool[0], _brute_topk(bsc, keep))
+
+
+def test_pool_block_mean_and_partial_last_block():
+    # hand-made keys: block 0 = keys 1..8 times e_0 (mean 4.5), a partial last
+    # block of 3 tokens (mean of 2, 4, 9 = 5).  With one head, q = e_0 and w = 1,
+    # the block score is the mean itself.
+    d_i = 64
+    L = 8 * 3 + 3
+    ik = np.zeros((L, d_i), np.float32)
+    ik[0:8, 0] = np.arange(1, 9)
+    ik[8:16, 0] = -1.0
+    ik[16:24, 0] = 0.5
+    ik[24:27, 0] = [2, 4, 9]
+    iq = np.zeros((1, 1, d_i), np.float32)
+    iq[0, 0, 0] = 1
+    _, pool = oracle.index_topk(bf16(iq), np.ones((1, 1), np.float32), np.zeros(1, np.int32),
+                                np.array([L], np.int32), bf16(ik), np.zeros(1, np.int64), 4,
+                                block=8, keep_blocks=2)
+    assert list(pool[0]) == [0, 3]     # scores 4.5, 0, 0.5, 5 -> blocks 3 and 0
+
+
+def test_block_score_below_member_mean_jensen():
+    # ReLU is convex and w >= 0, so a block's score (at the mean key) is at
+    # most the mean of its members' scores, up to bf16 rounding of the mean.
+    rng = np.random.default_rng(7)
+    h_i, d_i = 8, 64
+    for _ in range(50):
+        iq = bf16(rng.standard_normal((h_i, d_i)))
+        w = rng.uniform(0, 1, h_i).astype(np.float32)
+        keys = bf16(rng.standard_normal((8, d_i)))
+        member = np.mean([oracle.index_score(iq, w, keys[j]) for j in range(8)])
+        _, pool = None, None
+        kbar = bf16(bf16f(keys).sum(axis=0) / 8)
+        bs = oracle.index_score(iq, w, kbar)
+        slack = 2 ** -7 * float(np.sum(w * (np.abs(bf16f(iq)) @ np.abs(bf16f(kbar)))))
+        assert bs <= member + slack + 1e-4
+
+
+def test_reindex_uses_only_pool_positions_and_visibility():
+    iq, w, qs, nv, ik, sb = _inputs(1, 200, seed=8)
+    pool = np.array([[3, 7, 24, -1]], np.int32)          # block 24 = positions 192..199
+    nv = np.array([197], np.int32)                       # 195 is the last visible position
+    r = oracle.reindex_topk(iq, w, qs, nv, ik, sb, pool, 64, block=8)[0]
+    cand = list(range(24, 32)) + list(range(56, 64)) + list(range(192, 197))
+    assert np.array_equal(r, np.concatenate([cand, -np.ones(64 - len(cand))]).astype(np.int32))
+    r = oracle.reindex_topk(iq, w, qs, nv, ik, sb, pool, 5, block=8)[0]
+    sc = [oracle.index_score(iq[0], w[0], ik[p]) for p in cand]
+    assert np.array_equal(r, _brute_topk(sc, 5, cand))
