@@ -1,0 +1,179 @@
+/*
+ * csa2.h -- C ABI of the CSA2 decode hot path for AMD Instinct MI355X (gfx950).
+ *
+ * CSA2 (Compressed Sparse Attention 2) gives every attention layer one of
+ * three static modes.  A Full layer owns the main KV, projects an indexer key
+ * from it and picks a fresh Top-512 set of positions; a Reindex layer keeps
+ * the last Full layer's main KV and indexer keys but re-scores them with its
+ * own indexer query; a Reuse layer takes both the main KV and the latest
+ * Top-K list and skips the indexer.  Each layer keeps its own main query and
+ * sliding-window (128-token) KV.  The main KV is stored as E2M1 values with
+ * one E4M3 scale per 16 channels and no global scale.  In the decoder a
+ * hierarchical indexer lets the Full layer build a pool of at most 2048
+ * blocks of 8 positions that later Reindex layers score instead of the whole
+ * context.
+ *   Source: "DeepSeek AI выпустила DeepSeek-V4.1-Flash с контекстом в 1 млн
+ *   токенов, KV-кэшем FP4 и повторным использованием внимания между слоями"
+ *   (wire.sakhanda.co), sections "Сжатое разреженное внимание 2 (CSA2)",
+ *   "FP4 KV, ограниченное повторное проигрывание и другие расширения" and
+ *   "Каузальный энкодер-декодер"; also "DeepSeek-V4.1-Flash: Frontier Agents
+ *   on a Smaller Memory Budget" (tgviewer.app), the CSA2 bullet.
+ *
+ * A decode step of one layer calls, in this order:
+ *   Full:    csa2_quant_append (new rows) -> csa2_index_topk -> csa2_sparse_attn
+ *   Reindex: csa2_reindex_topk -> csa2_sparse_attn
+ *   Reuse:   csa2_sparse_attn with the idx of the group's Full/Reindex layer
+ *
+ * Conventions shared by every entry point:
+ *  - Every data pointer is DEVICE memory owned by the caller.  The library
+ *    never allocates, frees or synchronises; scratch space is the caller's
+ *    `ws` buffer of at least the size the matching *_ws_bytes function
+ *    returns (its content on entry is irrelevant; it is clobbered).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns; results are ready when the stream is.
+ *  - Host-side argument checks fail with a status and enqueue nothing.
+ *    Device-side data (positions, lengths, pool entries) is trusted to be in
+ *    range; kernels clamp what they can, but out-of-range values give
+ *    unspecified results.  NaN/Inf inputs are outside the contract.
+ *  - Positions in idx and pool lists are relative to the sequence:
+ *    0 <= p < nvis.  Row `seq_base[s] + p` addresses both the FP4 cache and
+ *    the indexer-key array for position p of sequence s.
+ *  - Outputs are written completely, including the -1 padding.
+ *  - No state is kept between calls; calls on different streams may overlap
+ *    if their outputs and workspaces are distinct.  No exception, abort or
+ *    print ever leaves the library.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_E_INVAL = 1,        /* null/unaligned pointer, negative or too large size */
+  CSA2_E_UNSUPPORTED = 2,  /* shape outside the compiled set (see each call)     */
+  CSA2_E_WORKSPACE = 3,    /* ws_bytes smaller than the *_ws_bytes result         */
+  CSA2_E_HIP = 4           /* a HIP launch failed; see csa2_last_hip_error()      */
+} csa2_status;
+
+typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1 } csa2_dtype;
+
+/* One main-KV entry: 512 channels quantised to E2M1 with one E4M3 (OCP FN,
+ * max 448) scale per 16 channels.  288 bytes:
+ *   [0, 256)   codes; byte j holds channel 2j in its low nibble and channel
+ *              2j+1 in its high nibble; nibble = sign bit (bit 3) | magnitude
+ *              code (0..7 = 0, .5, 1, 1.5, 2, 3, 4, 6)
+ *   [256, 288) scale of group g (channels 16g..16g+15) at byte 256+g
+ * The 512-channel width is this library's choice; the pages fix only the
+ * formats and the 16-channel grouping. */
+#define CSA2_KV_CH 512
+#define CSA2_KV_GROUP 16
+#define CSA2_KV_RECORD_BYTES 288
+
+/* ------------------------------------------------------------------------
+ * csa2_quant_append -- quantise rows into the FP4 main-KV cache (the write
+ * side of the FP4 cache format; a Full layer owns and writes the main KV).
+ *   x        [n_rows][512], fp32 (x_dtype = CSA2_F32) or bf16 bits (CSA2_BF16)
+ *   dst_row  [n_rows] int64 record index of each row in `cache`; rows with an
+ *            index outside [0, cache_rows) are skipped
+ *   cache    [cache_rows][288] bytes, written in place
+ * Per group: scale = E4M3 nearest to amax/6 (ties to even, saturating at
+ * 448); code = E2M1 nearest to x/scale (ties to even, saturating at 6), sign
+ * bit copied from x (so -0 gives 0x8); scale 0 gives zero magnitudes.
+ * Alignment: x 16 B, dst_row 8 B, cache 4 B. */
+csa2_status csa2_quant_append(const void* x, int x_dtype, int64_t n_rows,
+                              const int64_t* dst_row, uint8_t* cache, int64_t cache_rows,
+                              void* stream);
+
+/* ------------------------------------------------------------------------
+ * csa2_index_topk -- Full layer: indexer scan of every visible position,
+ * exact Top-K, and optionally the hierarchical block pool.
+ *   iq       [n_q][h_i][d_i] bf16 indexer query;  w [n_q][h_i] fp32 head weights
+ *   q_seq    [n_q] sequence of each query; q_nvis [n_q] visible positions
+ *            (0 <= q_nvis[i] <= max_nvis)
+ *   ik       indexer keys, [rows][d_i] bf16, one key per position shared by
+ *            all indexer heads; row = seq_base[q_seq[i]] + position
+ *   score(p) = sum_h w[h] * ReLU(q_h . k_p), defined to the bit as:
+ *            acc_h = fma chain over d ascending from +0 (fp32);
+ *            s = fma chain over h ascending of w[h]*max(acc_h,0) from +0
+ *   idx_out  [n_q][k]: the k positions with the largest scores (ties: lower
+ *            position first), in ascending position order, -1 padded when
+ *            q_nvis < k
+ *   block, keep_blocks, pool_out: if keep_blocks > 0, also the pool: blocks
+ *            of `block` positions (must be 8); block key = bf16(nearest-even)
+ *            of the fp32 mean of its visible keys (summed in ascending
+ *            position order, divided by their count); block score as above;
+ *            pool_out [n_q][keep_blocks] = the Top-keep_blocks block ids in
+ *            ascending order, -1 padded.  keep_blocks = 0: no pool (pool_out
+ *            may be NULL).
+ * The result is exact (bit-identical to the definition above) although the
+ * scan runs on MFMA: candidates within a proven rounding bound of the cut
+ * are re-scored with the exact fp32 chain before the final selection.
+ * Supported: 1 <= h_i <= 64, d_i in {64, 128}, 1 <= k <= 2048,
+ * 0 <= keep_blocks <= 4096, max_nvis < 2^31 - 16.  Alignment: iq, ik 16 B. */
+csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
+                            const int32_t* q_seq, const int32_t* q_nvis, int32_t max_nvis,
+                            const uint16_t* ik, const int64_t* seq_base,
+                            int k, int32_t* idx_out,
+                            int block, int keep_blocks, int32_t* pool_out,
+                            void* ws, size_t ws_bytes, void* stream);
+size_t csa2_index_topk_ws_bytes(int n_q, int32_t max_nvis, int h_i, int d_i, int k,
+                                int block, int keep_blocks);
+
+/* ------------------------------------------------------------------------
+ * csa2_reindex_topk -- Reindex layer: re-score the pool of the last Full
+ * layer (its indexer keys `ik`) with this layer's own iq/w, exact Top-K.
+ *   pool_blocks [n_q][keep_blocks] block ids as written by csa2_index_topk:
+ *            ascending, distinct, -1 padded at the end.  Candidates are the
+ *            positions block*8 .. block*8+7 that are < q_nvis.
+ *   Other arguments and the score definition as in csa2_index_topk.
+ *   idx_out  [n_q][k] ascending positions, -1 padded.
+ * Supported: as csa2_index_topk, block = 8, 1 <= keep_blocks <= 4096. */
+csa2_status csa2_reindex_topk(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
+                              const int32_t* q_seq, const int32_t* q_nvis,
+                              const uint16_t* ik, const int64_t* seq_base,
+                              const int32_t* pool_blocks, int block, int keep_blocks,
+                              int k, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+size_t csa2_reindex_topk_ws_bytes(int n_q, int h_i, int d_i, int k, int block, int keep_blocks);
+
+/* ------------------------------------------------------------------------
+ * csa2_sparse_attn -- gather + dequantise the selected FP4 entries and run
+ * one softmax over them merged with the layer's sliding-window rows
+ * (Full, Reindex and Reuse layers all use this call).
+ *   q        [n_q][h][512] fp32 (q_dtype = CSA2_F32) or bf16 bits (CSA2_BF16)
+ *   q_seq    [n_q]; cache [*][288] FP4 records; seq_base [n_seq] int64
+ *   idx      [n_q][k] selected positions; entries < 0 are skipped
+ *   swa      bf16 rows [*][512]; query i uses rows swa_row0[i] ..
+ *            swa_row0[i] + swa_len[i] - 1 (0 <= swa_len[i] <= w_max)
+ *   Each selected entry and each window row is one key whose vector is both
+ *   key and value (shared by all heads).  For head j:
+ *     z = softmax_scale * q_j . v,  out_j = sum softmax(z) v,
+ *     lse_j = log sum exp(z)   (out = 0, lse = -inf when no key is valid)
+ *   out [n_q][h][512] fp32; lse [n_q][h] fp32 or NULL.
+ * Accuracy: main-KV values are decoded exactly; products run on fp16 MFMA
+ * with fp32 accumulation (fp32 queries are split into two fp16 terms);
+ * bf16 queries and window rows must lie within the fp16 range (|x| < 65504).
+ * Supported: d = 512, h in {16, 32, 48, 64}, 0 <= k <= 2048, 0 <= w_max <= 1024.
+ * Alignment: q 16 B, swa 16 B, cache 4 B. */
+csa2_status csa2_sparse_attn(const void* q, int q_dtype, int n_q, int h, int d,
+                             const int32_t* q_seq, const uint8_t* cache, const int64_t* seq_base,
+                             const int32_t* idx, int k,
+                             const uint16_t* swa, const int64_t* swa_row0, const int32_t* swa_len,
+                             int w_max, float softmax_scale, float* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream);
+size_t csa2_sparse_attn_ws_bytes(int n_q, int h, int k, int w_max);
+
+/* ------------------------------------------------------------------------ */
+const char* csa2_status_string(csa2_status s);
+/* hipError_t of the last CSA2_E_HIP returned on the calling thread. */
+int csa2_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

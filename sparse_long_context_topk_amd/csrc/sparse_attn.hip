@@ -1,0 +1,395 @@
+// sparse_attn.hip -- CSA2 sparse attention over the selected FP4 main-KV
+// entries merged with the layer's sliding-window rows (gfx950).
+//
+// Every decode layer attends over the Top-K entries chosen by its group's
+// Full/Reindex layer (Reuse layers inherit that list) plus its own 128-row
+// sliding window; the main KV is E2M1 with one E4M3 scale per 16 channels.
+// Sources: "DeepSeek AI выпустила DeepSeek-V4.1-Flash с контекстом в 1 млн
+// токенов, KV-кэшем FP4 ..." (wire.sakhanda.co), sections "Каузальный
+// энкодер-декодер" (128-token window in every layer), "Сжатое разреженное
+// внимание 2 (CSA2)" (modes, own Q and window KV per layer) and "FP4 KV ..."
+// (the cache format).
+//
+// Work decomposition: one work-group per (query, split of the key slots);
+// slots [0, k) are the selected entries, [k, k + swa_len) the window rows.
+// Per 32-slot sub-tile the whole work-group decodes the keys once into LDS,
+// in two layouts (key-major for Q.K, channel-major for P.V), as fp16 -- an
+// E2M1 value times an E4M3 scale has at most 6 significant bits and lies in
+// [2^-10, 2688], so the decode is exact.  Each of the h/16 head waves then
+// runs v_mfma_f32_16x16x32_f16:
+//   S^T (32 keys x 16 heads) = K (32 x 512) . Q^T      (q in registers)
+//   O  (16 heads x 512)     += P (16 x 32) . V (32 x 512)
+// Computing S transposed leaves each lane with 8 key scores of one head, which
+// is exactly the A-operand layout P needs, so P never moves between lanes.
+// An online softmax (base-2 exponent, running max per head) carries across
+// sub-tiles; splits are merged by k_merge with their (max, sum) pairs.
+#include "csa2_device.h"
+
+namespace csa2 {
+namespace attn {
+
+constexpr int kThreads = 256;
+constexpr int kSub = 32;            // key slots per sub-tile
+constexpr int kKRow = 512 + 8;      // fp16 per key row in the key-major tile (16 B pad)
+constexpr int kVRow = kSub + 4;     // fp16 per channel row in the channel-major tile (8 B pad)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct Params {
+  const void* q;
+  int n_q, h;
+  const int32_t* q_seq;
+  const uint8_t* cache;
+  const int64_t* seq_base;
+  const int32_t* idx;
+  int k;
+  const uint16_t* swa;
+  const int64_t* swa_row0;
+  const int32_t* swa_len;
+  float scale_log2;
+  float* out;
+  float* lse;
+  int nsplit, sub_per_split, nsub;
+  float* part_o;   // [n_q][nsplit][h][512]
+  float* part_ml;  // [n_q][nsplit][h][2]
+};
+
+// 8 E2M1 codes (one little-endian dword, channel 2i in the low nibble of byte
+// i) times an fp16 scale -> 4 packed fp16 pairs.  Magnitudes come from a byte
+// table (the fp16 high byte of 0, .5, 1, 1.5, 2, 3, 4, 6; the low byte is 0),
+// the sign bit is moved to bit 15, then one packed fp16 multiply by the scale
+// (exact, see above).
+__device__ __forceinline__ void decode8(uint32_t c, _Float16 sc, uint32_t out[4]) {
+  const uint32_t lut_lo = 0x3E3C3800u, lut_hi = 0x46444240u;
+  uint32_t ev = __builtin_amdgcn_perm(lut_hi, lut_lo, c & 0x07070707u) | ((c << 4) & 0x80808080u);
+  uint32_t od = __builtin_amdgcn_perm(lut_hi, lut_lo, (c >> 4) & 0x07070707u) | (c & 0x80808080u);
+  const f16x2 s2 = {sc, sc};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // result bytes: 0, even byte i, 0, odd byte i  (selector 0x0C yields 0x00)
+    const uint32_t sel = 0x000C000Cu | ((uint32_t)i << 8) | ((uint32_t)(4 + i) << 24);
+    uint32_t pr = __builtin_amdgcn_perm(od, ev, sel);
+    f16x2 v = __builtin_bit_cast(f16x2, pr) * s2;
+    out[i] = __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <bool QF32>
+__global__ __launch_bounds__(kThreads) void k_attn(Params P) {
+  __shared__ __attribute__((aligned(16))) _Float16 s_k[kSub * kKRow];
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[512 * kVRow];
+  __shared__ uint32_t s_valid[kSub];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int qi = blockIdx.x, split = blockIdx.y;
+  const bool head_wave = 16 * wave < P.h;
+  const int head = 16 * wave + n;
+  const int64_t cbase = P.seq_base[P.q_seq[qi]];
+  const int k = P.k;
+  const int nswa = P.swa_len ? P.swa_len[qi] : 0;
+  const int64_t srow0 = nswa ? P.swa_row0[qi] : 0;
+
+  // Q^T as the B operand: lane (head n, group g) holds channels 32*ks + 8*g .. +7
+  f16x8 qb[16];
+  f16x8 ql[QF32 ? 16 : 1];
+  if (head_wave) {
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const size_t off = ((size_t)qi * P.h + head) * 512 + 32 * ks + 8 * g;
+      float x[8];
+      if (QF32) {
+        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(P.q) + off);
+        float4 a = src[0], b = src[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+      } else {
+        uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(P.q) + off);
+        const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = __uint_as_float(wd[j] << 16);
+          x[2 * j + 1] = __uint_as_float(wd[j] & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        _Float16 hi = (_Float16)x[j];
+        qb[ks][j] = hi;
+        if constexpr (QF32) ql[ks][j] = (_Float16)(x[j] - (float)hi);
+      }
+    }
+  }
+
+  f32x4 o[32];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  // decode assignment: thread -> keys 8*kq .. 8*kq+7, channels 8*cg .. 8*cg+7
+  const int kq = tid & 3, cg = tid >> 2;
+  const int sub0 = split * P.sub_per_split;
+  const int sub1 = min(sub0 + P.sub_per_split, P.nsub);
+
+  for (int sub = sub0; sub < sub1; ++sub) {
+    const int slot0 = sub * kSub;
+    uint32_t vals[8][4];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int slot = slot0 + 8 * kq + jj;
+      bool valid = false;
+      vals[jj][0] = vals[jj][1] = vals[jj][2] = vals[jj][3] = 0u;
+      if (slot < k) {
+        const int pos = P.idx[(size_t)qi * k + slot];
+        if (pos >= 0) {
+          valid = true;
+          const uint8_t* rec = P.cache + (size_t)(cbase + pos) * CSA2_KV_RECORD_BYTES;
+          const uint32_t codes = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
+          const _Float16 sc = (_Float16)e4m3_to_f32(rec[256 + (cg >> 1)]);
+          decode8(codes, sc, vals[jj]);
+        }
+      } else if (slot - k < nswa) {
+        valid = true;
+        const uint4 r = *reinterpret_cast<const uint4*>(P.swa + (size_t)(srow0 + slot - k) * 512 + 8 * cg);
+        const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          vals[jj][j] = pack_f16(__uint_as_float(wd[j] << 16), __uint_as_float(wd[j] & 0xFFFF0000u));
+      }
+      if (cg == 0) s_valid[8 * kq + jj] = valid ? 1u : 0u;
+      *reinterpret_cast<uint4*>(&s_k[(8 * kq + jj) * kKRow + 8 * cg]) =
+          make_uint4(vals[jj][0], vals[jj][1], vals[jj][2], vals[jj][3]);
+    }
+    // channel-major copy: row (channel 8*cg + c) gets keys 8*kq .. 8*kq+7
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int jp = 0; jp < 4; ++jp) {
+        const uint32_t a = vals[2 * jp][c >> 1], b = vals[2 * jp + 1][c >> 1];
+        // take the low (c even) or high (c odd) fp16 of each
+        pk[jp] = (c & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u) : __builtin_amdgcn_perm(b, a, 0x05040100u);
+      }
+      uint2* dst = reinterpret_cast<uint2*>(&s_v[(8 * cg + c) * kVRow + 8 * kq]);
+      dst[0] = make_uint2(pk[0], pk[1]);
+      dst[1] = make_uint2(pk[2], pk[3]);
+    }
+    __syncthreads();
+
+    if (head_wave) {
+      // ---- S^T = K Q^T : lane (head n, g) gets keys 16*kt + 4*g + i
+      f32x4 sacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        sacc[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const _Float16* krow = &s_k[(16 * kt + n) * kKRow + 8 * g];
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+          const f16x8 a = *reinterpret_cast<const f16x8*>(krow + 32 * ks);
+          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[ks], sacc[kt], 0, 0, 0);
+          if constexpr (QF32) sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[ks], sacc[kt], 0, 0, 0);
+        }
+      }
+      float z[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * kt + 4 * g + i;
+          const float v = s_valid[key] ? sacc[kt][i] * P.scale_log2 : -INFINITY;
+          z[4 * kt + i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run, mx);
+      float alpha, pv[8];
+      if (m_new == -INFINITY) {
+        alpha = 1.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = 0.0f;
+      } else {
+        alpha = exp2f(m_run - m_new);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = exp2f(z[j] - m_new);
+      }
+      float ps = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ps += pv[j];
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+      // rescale O rows (heads 4*g + i live in this lane's accumulators)
+      float a4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, kWave);
+#pragma unroll
+      for (int t = 0; t < 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[t][i] *= a4[i];
+      // P as the A operand: slots 0..3 = keys 4g+i, slots 4..7 = keys 16+4g+i
+      f16x8 pa;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pa[j] = (_Float16)pv[j];
+      // ---- O += P V
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
+        const _Float16* vrow = &s_v[(16 * t + n) * kVRow];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * g);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
+        const f16x8 b = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, b, o[t], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!head_wave) return;
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16, kWave);
+  l_tot += __shfl_xor(l_tot, 32, kWave);
+  // per-row (head 4*g + i) values for this lane's accumulators
+  float lrow[4], mrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lrow[i] = __shfl(l_tot, 4 * g + i, kWave);
+    mrow[i] = __shfl(m_run, 4 * g + i, kWave);
+  }
+  if (P.nsplit == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 16 * wave + 4 * g + i;
+      const float inv = lrow[i] > 0.0f ? 1.0f / lrow[i] : 0.0f;
+      float* dst = P.out + ((size_t)qi * P.h + hh) * 512 + n;
+#pragma unroll
+      for (int t = 0; t < 32; ++t) dst[16 * t] = o[t][i] * inv;
+    }
+    if (P.lse && g == 0)
+      P.lse[(size_t)qi * P.h + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 16 * wave + 4 * g + i;
+      float* dst = P.part_o + (((size_t)qi * P.nsplit + split) * P.h + hh) * 512 + n;
+#pragma unroll
+      for (int t = 0; t < 32; ++t) dst[16 * t] = o[t][i];
+    }
+    if (g == 0) {
+      float* ml = P.part_ml + (((size_t)qi * P.nsplit + split) * P.h + head) * 2;
+      ml[0] = m_run;
+      ml[1] = l_tot;
+    }
+  }
+}
+
+// Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+__global__ __launch_bounds__(kThreads) void k_merge(Params P) {
+  const int qi = blockIdx.x, hh = blockIdx.y;
+  float M = -INFINITY;
+  for (int s = 0; s < P.nsplit; ++s)
+    M = fmaxf(M, P.part_ml[(((size_t)qi * P.nsplit + s) * P.h + hh) * 2]);
+  float L = 0.0f, acc0 = 0.0f, acc1 = 0.0f;
+  const int c = threadIdx.x;
+  for (int s = 0; s < P.nsplit; ++s) {
+    const float* ml = P.part_ml + (((size_t)qi * P.nsplit + s) * P.h + hh) * 2;
+    const float wgt = (ml[0] == -INFINITY) ? 0.0f : exp2f(ml[0] - M);
+    L = fmaf(wgt, ml[1], L);
+    const float* po = P.part_o + (((size_t)qi * P.nsplit + s) * P.h + hh) * 512;
+    acc0 = fmaf(wgt, po[c], acc0);
+    acc1 = fmaf(wgt, po[c + 256], acc1);
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  float* dst = P.out + ((size_t)qi * P.h + hh) * 512;
+  dst[c] = acc0 * inv;
+  dst[c + 256] = acc1 * inv;
+  if (P.lse && c == 0) P.lse[(size_t)qi * P.h + hh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+}  // namespace attn
+}  // namespace csa2
+
+using namespace csa2;
+using namespace csa2::attn;
+
+namespace {
+
+thread_local int g_attn_hip_error = 0;
+
+struct Split {
+  int nsub, nsplit, per;
+};
+
+Split choose_split(int n_q, int k, int w_max) {
+  Split s;
+  const int nslots = k + w_max;
+  s.nsub = std::max(1, (nslots + kSub - 1) / kSub);
+  const int target = std::max(1, std::min(s.nsub, (512 + n_q - 1) / std::max(n_q, 1)));
+  s.per = (s.nsub + target - 1) / target;
+  s.nsplit = (s.nsub + s.per - 1) / s.per;
+  return s;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" int csa2_internal_last_hip_error_attn(void) { return g_attn_hip_error; }
+
+extern "C" size_t csa2_sparse_attn_ws_bytes(int n_q, int h, int k, int w_max) {
+  if (n_q <= 0 || h <= 0) return 0;
+  const Split s = choose_split(n_q, k, w_max);
+  if (s.nsplit == 1) return 256;
+  return align256((size_t)n_q * s.nsplit * h * 512 * sizeof(float)) +
+         align256((size_t)n_q * s.nsplit * h * 2 * sizeof(float));
+}
+
+extern "C" csa2_status csa2_sparse_attn(const void* q, int q_dtype, int n_q, int h, int d,
+                                        const int32_t* q_seq, const uint8_t* cache, const int64_t* seq_base,
+                                        const int32_t* idx, int k, const uint16_t* swa,
+                                        const int64_t* swa_row0, const int32_t* swa_len, int w_max,
+                                        float softmax_scale, float* out, float* lse, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  if (n_q < 0 || k < 0 || k > 2048 || w_max < 0 || w_max > 1024) return CSA2_E_INVAL;
+  if (q_dtype != CSA2_F32 && q_dtype != CSA2_BF16) return CSA2_E_INVAL;
+  if (d != CSA2_KV_CH || h < 16 || h > 64 || h % 16 != 0) return CSA2_E_UNSUPPORTED;
+  if (n_q == 0) return CSA2_OK;
+  if (!q || !q_seq || !seq_base || !out || !ws) return CSA2_E_INVAL;
+  if (k > 0 && (!idx || !cache)) return CSA2_E_INVAL;
+  if (w_max > 0 && (!swa || !swa_row0 || !swa_len)) return CSA2_E_INVAL;
+  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(swa) & 15) ||
+      (reinterpret_cast<uintptr_t>(cache) & 3) || (reinterpret_cast<uintptr_t>(ws) & 255))
+    return CSA2_E_INVAL;
+  if (ws_bytes < csa2_sparse_attn_ws_bytes(n_q, h, k, w_max)) return CSA2_E_WORKSPACE;
+  const Split s = choose_split(n_q, k, w_max);
+  Params P{};
+  P.q = q; P.n_q = n_q; P.h = h; P.q_seq = q_seq; P.cache = cache; P.seq_base = seq_base;
+  P.idx = idx; P.k = k; P.swa = swa; P.swa_row0 = swa_row0; P.swa_len = w_max > 0 ? swa_len : nullptr;
+  P.scale_log2 = softmax_scale * kLog2e;
+  P.out = out; P.lse = lse;
+  P.nsplit = s.nsplit; P.sub_per_split = s.per; P.nsub = s.nsub;
+  char* w = static_cast<char*>(ws);
+  P.part_o = reinterpret_cast<float*>(w);
+  P.part_ml = reinterpret_cast<float*>(w + align256((size_t)n_q * s.nsplit * h * 512 * sizeof(float)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(n_q, s.nsplit);
+  if (q_dtype == CSA2_F32) hipLaunchKernelGGL(k_attn<true>, grid, dim3(kThreads), 0, st, P);
+  else hipLaunchKernelGGL(k_attn<false>, grid, dim3(kThreads), 0, st, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_attn_hip_error = (int)e;
+    return CSA2_E_HIP;
+  }
+  if (s.nsplit > 1) {
+    hipLaunchKernelGGL(k_merge, dim3(n_q, h), dim3(kThreads), 0, st, P);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+      g_attn_hip_error = (int)e;
+      return CSA2_E_HIP;
+    }
+  }
+  return CSA2_OK;
+}

@@ -1,0 +1,158 @@
+"""csa2_index_topk / csa2_reindex_topk on the GPU: indices and pools bit-exact
+versus the oracle at ragged lengths, ties, pools and both indexer shapes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_long_context_topk_amd as csa2
+from gpu_common import bits, device, gpu, index_inputs, note, to_dev
+
+
+def _gpu_full(inp, k, keep_blocks=0, ws=None):
+    dev = device()
+    d = to_dev(inp, dev)
+    max_nvis = int(inp["nvis"].max()) if len(inp["nvis"]) else 0
+    r = csa2.index_topk(d["iq"], d["w"], d["q_seq"], d["nvis"], max_nvis, d["ik"], d["seq_base"], k=k,
+                        keep_blocks=keep_blocks, ws=ws)
+    torch.cuda.synchronize()
+    if keep_blocks:
+        return r[0].cpu().numpy(), r[1].cpu().numpy()
+    return r.cpu().numpy()
+
+
+def _ref_full(inp, k, keep_blocks=0):
+    return oracle.index_topk(bits(inp["iq"]), inp["w"].numpy(), inp["q_seq"].numpy(), inp["nvis"].numpy(),
+                             bits(inp["ik"]), inp["seq_base"].numpy(), k, block=8, keep_blocks=keep_blocks)
+
+
+EDGE_LENGTHS = [1, 7, 8, 9, 127, 128, 129, 511, 512, 513, 4096, 16383, 16384, 16385, 16391, 20000]
+
+
+@gpu
+@pytest.mark.parametrize("h_i,d_i", [(4, 64), (64, 128), (20, 128), (33, 64)])
+def test_full_ragged_lengths(h_i, d_i):
+    note(f"full ragged h_i={h_i} d_i={d_i}")
+    inp = index_inputs(EDGE_LENGTHS, h_i, d_i, seed=100 + h_i)
+    got = _gpu_full(inp, 512)
+    ref = _ref_full(inp, 512)
+    assert np.array_equal(got, ref)
+
+
+@gpu
+@pytest.mark.parametrize("k", [1, 64, 512, 2048])
+def test_full_k_values(k):
+    note(f"full k={k}")
+    inp = index_inputs([9000, 3000, 1], 64, 128, seed=7 + k)
+    assert np.array_equal(_gpu_full(inp, k), _ref_full(inp, k))
+
+
+@gpu
+@pytest.mark.parametrize("case", ["zero", "equal", "dup_blocks", "two_values"])
+def test_full_ties(case):
+    note(f"full ties {case}")
+
+    def kf(ik):
+        if case == "zero":
+            return torch.zeros_like(ik)
+        if case == "equal":
+            return ik[:1].expand_as(ik).contiguous()
+        if case == "dup_blocks":
+            ik = ik.clone()
+            ik[4096:8192] = ik[0:4096]
+            return ik
+        ik = ik.clone()
+        ik[::2] = ik[0]
+        ik[1::2] = ik[1]
+        return ik
+    inp = index_inputs([8192, 5000], 64, 128, seed=3, key_fn=kf)
+    assert np.array_equal(_gpu_full(inp, 512), _ref_full(inp, 512))
+
+
+@gpu
+@pytest.mark.parametrize("lengths,keep", [([20000, 16391, 300], 2048), ([4096, 1000, 8], 64),
+                                          ([16384, 16385], 2048), ([30000], 1024)])
+def test_full_with_pool(lengths, keep):
+    note(f"full+pool {lengths} keep={keep}")
+    inp = index_inputs(lengths, 64, 128, seed=11)
+    g_idx, g_pool = _gpu_full(inp, 512, keep)
+    r_idx, r_pool = _ref_full(inp, 512, keep)
+    assert np.array_equal(g_idx, r_idx)
+    assert np.array_equal(g_pool, r_pool)
+
+
+@gpu
+def test_pool_with_block_constant_keys():
+    note("pool block-constant keys")
+    inp = index_inputs([24000], 64, 128, seed=12, key_fn=lambda ik: ik[::8].repeat_interleave(8, 0)[:ik.shape[0]].contiguous())
+    g_idx, g_pool = _gpu_full(inp, 512, 512)
+    r_idx, r_pool = _ref_full(inp, 512, 512)
+    assert np.array_equal(g_idx, r_idx) and np.array_equal(g_pool, r_pool)
+
+
+@gpu
+@pytest.mark.parametrize("lengths,keep", [([20000, 16391, 300], 2048), ([40000, 9], 512)])
+def test_reindex(lengths, keep):
+    note(f"reindex {lengths} keep={keep}")
+    inp = index_inputs(lengths, 64, 128, seed=21)
+    _, r_pool = _ref_full(inp, 512, keep)
+    iq2 = torch.flip(inp["iq"], dims=[1]).contiguous()       # the Reindex layer's own query
+    dev = device()
+    d = to_dev(inp, dev)
+    got = csa2.reindex_topk(iq2.to(dev), d["w"], d["q_seq"], d["nvis"], d["ik"], d["seq_base"],
+                            torch.from_numpy(r_pool).to(dev), k=512)
+    torch.cuda.synchronize()
+    ref = oracle.reindex_topk(bits(iq2), inp["w"].numpy(), inp["q_seq"].numpy(), inp["nvis"].numpy(),
+                              bits(inp["ik"]), inp["seq_base"].numpy(), r_pool, 512, block=8)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+@gpu
+def test_reindex_with_full_query_equals_full_when_pool_covers_context():
+    note("reindex == full")
+    inp = index_inputs([16000, 7000], 64, 128, seed=22)
+    g_idx, g_pool = _gpu_full(inp, 512, 2048)
+    dev = device()
+    d = to_dev(inp, dev)
+    got = csa2.reindex_topk(d["iq"], d["w"], d["q_seq"], d["nvis"], d["ik"], d["seq_base"],
+                            torch.from_numpy(g_pool).to(dev), k=512)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), g_idx)
+
+
+@gpu
+def test_deterministic_and_workspace_reuse():
+    note("determinism")
+    inp = index_inputs([20000, 512, 70000], 64, 128, seed=5)
+    ws = csa2.Workspace()
+    a = _gpu_full(inp, 512, 2048, ws=ws)
+    small = index_inputs([600], 64, 128, seed=6)
+    _gpu_full(small, 512, 2048, ws=ws)
+    b = _gpu_full(inp, 512, 2048, ws=ws)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@gpu
+def test_mfma_scores_within_proven_bound():
+    """The scan's approximate scores (left in the workspace) never leave the
+    rounding bound the selection relies on."""
+    note("mfma bound")
+    L, h_i, d_i = 6000, 64, 128
+    inp = index_inputs([L], h_i, d_i, seed=9)
+    inp["ik"] = (inp["ik"].float() * torch.where(torch.arange(L)[:, None] % 97 == 0, 20.0, 1.0)).to(torch.bfloat16)
+    ws = csa2.Workspace()
+    _gpu_full(inp, 512, ws=ws)
+    approx = ws.buf[:L * 4].view(torch.float32).cpu().numpy().astype(np.float64)
+    iqb, ikb, w = bits(inp["iq"])[0], bits(inp["ik"]), inp["w"].numpy()[0]
+    exact = np.array([oracle.index_score(iqb, w, ikb[t]) for t in range(L)])
+    qf = inp["iq"][0].double().numpy()
+    kf = inp["ik"].double().numpy()
+    qw = float(np.sum(np.abs(w) * np.linalg.norm(qf, axis=1)))
+    u, u2 = 2.0 ** -24, 2.0 ** -23
+    gam = lambda n, uu: n * uu / (1 - n * uu)
+    gd, gm, gh = gam(d_i, u), gam(d_i + 2, u2), gam(66, u)
+    c = 2 * (gd + gm + gh * (2 + gd + gm))
+    bound = c * qw * np.linalg.norm(kf, axis=1)
+    ratio = np.abs(approx - exact) / bound
+    print(f"max |mfma - exact| / bound = {ratio.max():.3e}")
+    assert np.all(np.abs(approx - exact) <= bound)
