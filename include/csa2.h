@@ -105,12 +105,15 @@ csa2_status csa2_quant_append(const void* x, int x_dtype, int64_t n_rows,
  *            position first), in ascending position order, -1 padded when
  *            q_nvis < k
  *   block, keep_blocks, pool_out: if keep_blocks > 0, also the pool: blocks
- *            of `block` positions (must be 8); block key = bf16(nearest-even)
- *            of the fp32 mean of its visible keys (summed in ascending
- *            position order, divided by their count); block score as above;
+ *            of `block` positions (must be 8), scored as the indexer score of
+ *            the mean of the block's visible keys.  Through linearity its
+ *            per-head dot product is the mean of the members' per-head dot
+ *            products, defined to the bit as: members' fma-chain dots summed
+ *            in fp32 in ascending position from +0, divided by the member
+ *            count (IEEE), then ReLU and the head fma chain as above;
  *            pool_out [n_q][keep_blocks] = the Top-keep_blocks block ids in
- *            ascending order, -1 padded.  keep_blocks = 0: no pool (pool_out
- *            may be NULL).
+ *            ascending order (ties: lower id), -1 padded.  keep_blocks = 0:
+ *            no pool (pool_out may be NULL).
  * The result is exact (bit-identical to the definition above) although the
  * scan runs on MFMA: candidates within a proven rounding bound of the cut
  * are re-scored with the exact fp32 chain before the final selection.
@@ -167,6 +170,15 @@ csa2_status csa2_sparse_attn(const void* q, int q_dtype, int n_q, int h, int d,
                              int w_max, float softmax_scale, float* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
 size_t csa2_sparse_attn_ws_bytes(int n_q, int h, int k, int w_max);
+
+/* ------------------------------------------------------------------------
+ * csa2_record_scan_events -- measurement hook.  The next csa2_index_topk or
+ * csa2_reindex_topk call made on the calling thread records the hipEvent_t
+ * `start` right before and `stop` right after its indexer-scan kernel, on
+ * that call's stream, and then forgets both.  Either may be NULL.  Lets a
+ * caller time the dominant kernel with its own events while the whole step
+ * runs normally. */
+void csa2_record_scan_events(void* start, void* stop);
 
 /* ------------------------------------------------------------------------ */
 const char* csa2_status_string(csa2_status s);

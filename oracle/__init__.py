@@ -37,7 +37,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle with g++ (no GPU code involved)."""
     if force or not os.path.exists(LIB):
         tmp = LIB + ".tmp"
-        cmd = ["g++", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+        cmd = ["g++", "-O2", "-mfma", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
                "-std=c++17", "-shared", "-fPIC", "-Wall", "-o", tmp, SRC]
         subprocess.run(cmd, check=True)
         os.replace(tmp, LIB)

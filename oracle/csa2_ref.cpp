@@ -212,13 +212,18 @@ void csa2_ref_dequant_record(const uint8_t* rec, float* out512) {
  *   r_h = acc_h > 0 ? acc_h : +0
  *   s = +0;     for h ascending: s = fma(w_h, r_h, s)
  * ====================================================================== */
+/* One head's dot product q_h . k as the fp32 fma chain over d ascending. */
+static float head_dot(const uint16_t* qh, const uint16_t* key, int d_i) {
+  float acc = 0.0f;
+  for (int d = 0; d < d_i; ++d) acc = std::fma(bf16_to_float(qh[d]), bf16_to_float(key[d]), acc);
+  return acc;
+}
+
 float csa2_ref_index_score(const uint16_t* iq, const float* w, int h_i, int d_i,
                            const uint16_t* key) {
   float s = 0.0f;
   for (int h = 0; h < h_i; ++h) {
-    float acc = 0.0f;
-    for (int d = 0; d < d_i; ++d)
-      acc = std::fma(bf16_to_float(iq[h * d_i + d]), bf16_to_float(key[d]), acc);
+    float acc = head_dot(iq + (size_t)h * d_i, key, d_i);
     float r = (acc > 0.0f) ? acc : 0.0f;
     s = std::fma(w[h], r, s);
   }
@@ -251,10 +256,13 @@ void csa2_ref_topk(const float* scores, const int32_t* pos, int64_t n, int k, in
  * section, Full mode].  With keep_blocks > 0 it also forms the candidate pool
  * of the hierarchical indexer: positions grouped into blocks of `block`
  * (8 on the pages, at most 2048 blocks kept, so at most 16384 positions
- * [W1, CSA2 section]).  Reading for the block key (the pages give none): the
- * mean of the block's valid indexer keys, summed in fp32 in ascending
- * position order from +0, divided by the count (IEEE), rounded to bf16
- * nearest-even; the block score is the indexer score of that key; the kept
+ * [W1, CSA2 section]).  Reading (the pages give no block key): a block is
+ * scored as the indexer score of the mean of its visible members' keys, with
+ * the mean kept exact.  Because a dot product is linear in the key, the
+ * per-head dot product of the mean key is the mean of the members' per-head
+ * dot products; it is evaluated as the fp32 sum of the members' head_dot
+ * values in ascending position order from +0, divided by the member count
+ * (IEEE), then ReLU and the head fma chain exactly as for a token.  The kept
  * blocks are the Top-keep_blocks blocks under the same order as tokens
  * (score desc, block id asc), emitted ascending and padded with -1.
  * ====================================================================== */
@@ -279,16 +287,19 @@ int csa2_ref_index_topk(const uint16_t* iq, const float* w, int n_q, int h_i, in
     if (keep_blocks > 0) {
       int64_t nb = (nvis + block - 1) / block;
       std::vector<float> bs((size_t)nb);
-      std::vector<uint16_t> kbar((size_t)d_i);
       for (int64_t b = 0; b < nb; ++b) {
         int64_t t0 = b * block, t1 = std::min<int64_t>(nvis, t0 + block);
         float cnt = (float)(t1 - t0);
-        for (int d = 0; d < d_i; ++d) {
+        float s = 0.0f;
+        for (int h = 0; h < h_i; ++h) {
           float sum = 0.0f;
-          for (int64_t t = t0; t < t1; ++t) sum = sum + bf16_to_float(keys[(size_t)t * d_i + d]);
-          kbar[(size_t)d] = csa2_ref_bf16_bits(sum / cnt);
+          for (int64_t t = t0; t < t1; ++t)
+            sum = sum + head_dot(qv + (size_t)h * d_i, keys + (size_t)t * d_i, d_i);
+          float mean = sum / cnt;
+          float r = (mean > 0.0f) ? mean : 0.0f;
+          s = std::fma(wv[h], r, s);
         }
-        bs[(size_t)b] = csa2_ref_index_score(qv, wv, h_i, d_i, kbar.data());
+        bs[(size_t)b] = s;
       }
       csa2_ref_topk(bs.data(), nullptr, nb, keep_blocks, pool_out + (size_t)q * keep_blocks);
     }

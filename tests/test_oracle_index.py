@@ -137,21 +137,26 @@ def test_pool_takes_every_block_when_few():
 
 
 def test_block_constant_keys_make_reindex_equal_full():
-    # every block of 8 holds one key repeated: the block mean is that key
-    # exactly, so a block scores as its members and the Top-512 tokens are the
-    # members of the Top-64 blocks, all inside a 128-block pool.
+    # every block of 8 holds one key repeated, and keys, queries and weights are
+    # small integers / halves so every dot product, sum and mean is exact: a
+    # block then scores exactly as its members, the Top-512 tokens are the
+    # members of the Top-64 blocks, all inside a 128-block pool, and Reindex
+    # with the Full query reproduces Full.
     L, keep = 4096, 128
-    iq, w, qs, nv, ik, sb = _inputs(1, L, seed=6)
-    ik[:] = np.repeat(ik[::8], 8, axis=0)
+    rng = np.random.default_rng(6)
+    ik = bf16(np.repeat(rng.integers(-3, 4, (L // 8, 64)), 8, axis=0))
+    iq = bf16(rng.integers(-3, 4, (1, 4, 64)))
+    w = rng.choice([0.0, 0.5, 1.0], (1, 4)).astype(np.float32)
+    w[0, 0] = 1.0
+    qs, nv, sb = np.zeros(1, np.int32), np.array([L], np.int32), np.zeros(1, np.int64)
     idx, pool = oracle.index_topk(iq, w, qs, nv, ik, sb, 512, block=8, keep_blocks=keep)
-    blocks_of_idx = np.unique(idx // 8)
-    assert len(blocks_of_idx) == 64 and np.all(np.isin(blocks_of_idx, pool))
-    r = oracle.reindex_topk(iq, w, qs, nv, ik, sb, pool, 512, block=8)
-    assert np.array_equal(r, idx)
-    # block scores equal member scores: the pool is the Top-128 blocks by the
-    # score of their (shared) key
     bsc = [oracle.index_score(iq[0], w[0], ik[8 * b]) for b in range(L // 8)]
     assert np.array_equal(pool[0], _brute_topk(bsc, keep))
+    tsc = [oracle.index_score(iq[0], w[0], ik[t]) for t in range(L)]
+    assert np.array_equal(idx[0], _brute_topk(tsc, 512))
+    assert np.all(np.isin(idx[0] // 8, pool[0]))
+    r = oracle.reindex_topk(iq, w, qs, nv, ik, sb, pool, 512, block=8)
+    assert np.array_equal(r, idx)
 
 
 def test_pool_block_mean_and_partial_last_block():
@@ -174,20 +179,44 @@ def test_pool_block_mean_and_partial_last_block():
 
 
 def test_block_score_below_member_mean_jensen():
-    # ReLU is convex and w >= 0, so a block's score (at the mean key) is at
-    # most the mean of its members' scores, up to bf16 rounding of the mean.
+    # ReLU is convex and w >= 0, so a block's score (the score of its mean
+    # key) is at most the mean of its members' scores, up to fp32 rounding.
     rng = np.random.default_rng(7)
     h_i, d_i = 8, 64
     for _ in range(50):
-        iq = bf16(rng.standard_normal((h_i, d_i)))
-        w = rng.uniform(0, 1, h_i).astype(np.float32)
+        iq = bf16(rng.standard_normal((1, h_i, d_i)))
+        w = rng.uniform(0, 1, (1, h_i)).astype(np.float32)
         keys = bf16(rng.standard_normal((8, d_i)))
-        member = np.mean([oracle.index_score(iq, w, keys[j]) for j in range(8)])
-        _, pool = None, None
-        kbar = bf16(bf16f(keys).sum(axis=0) / 8)
-        bs = oracle.index_score(iq, w, kbar)
-        slack = 2 ** -7 * float(np.sum(w * (np.abs(bf16f(iq)) @ np.abs(bf16f(kbar)))))
-        assert bs <= member + slack + 1e-4
+        member = [oracle.index_score(iq[0], w[0], keys[j]) for j in range(8)]
+        _, pool = oracle.index_topk(iq, w, np.zeros(1, np.int32), np.array([8], np.int32), keys,
+                                    np.zeros(1, np.int64), 1, block=8, keep_blocks=1)
+        assert pool[0, 0] == 0
+        # the block score itself, by the exact-arithmetic definition, in fp64
+        qf, kf = bf16f(iq[0]).astype(np.float64), bf16f(keys).astype(np.float64)
+        bs = float(np.sum(w[0] * np.maximum(qf @ kf.mean(axis=0), 0)))
+        assert bs <= np.mean(member) + 1e-4
+
+
+def test_block_score_is_mean_of_member_dots():
+    # the oracle's block scores, read back through a pool of every block,
+    # against the same definition evaluated in fp64: equal to rounding error
+    rng = np.random.default_rng(17)
+    h_i, d_i, L = 16, 64, 8 * 40 + 5
+    iq = bf16(rng.standard_normal((1, h_i, d_i)))
+    w = rng.uniform(0, 1, (1, h_i)).astype(np.float32)
+    ik = bf16(rng.standard_normal((L, d_i)))
+    qf, kf = bf16f(iq[0]).astype(np.float64), bf16f(ik).astype(np.float64)
+    exact = []
+    for b in range(41):
+        blk = kf[8 * b:min(L, 8 * b + 8)]
+        exact.append(float(np.sum(w[0] * np.maximum(qf @ blk.mean(axis=0), 0))))
+    # order of the 41 blocks by the fp64 definition must match the oracle's
+    # Top-k for every k (no near-ties at this seed)
+    order = np.argsort(-np.array(exact), kind="stable")
+    for k in (1, 5, 20, 40):
+        _, pool = oracle.index_topk(iq, w, np.zeros(1, np.int32), np.array([L], np.int32), ik,
+                                    np.zeros(1, np.int64), 1, block=8, keep_blocks=k)
+        assert np.array_equal(pool[0], np.sort(order[:k]))
 
 
 def test_reindex_uses_only_pool_positions_and_visibility():
