@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""CSA2 decode-step benchmark on one MI355X.
+
+A step is one pass of the whole hot path over one batch: FP4 append of each
+sequence's new token, then every layer of the workload's schedule (Full:
+index scan + Top-512 (+ block pool); Reindex: pool re-scoring + Top-512;
+Reuse: nothing), each followed by its sparse attention over the selected FP4
+entries and its 128-row window.  Inputs are synthetic and seeded, resident in
+HBM before timing starts.  The default workload is the 1M-context Reindex
+group (batch 4, Full + Reindex layers).
+
+Prints one JSON line.  `value` is query-layers per second (one query attended
+in one layer, including that layer's index/reindex/append work).  `roofline`
+covers the dominant kernel, the indexer scan: algorithmic bytes per launch /
+its mean launch time (HIP events recorded around that kernel inside the timed
+steps).  `cpu_baseline` runs the plain CPU oracle on the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA2 decode attention queries·layers/sec at 1M ctx; achieved HBM GB/s vs peak"
+PEAK_HBM_GBPS = 8000.0
+SCAN_SRC = os.path.join(ROOT, "sparse_long_context_topk_amd", "csrc", "index_topk.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c5"])
+    p.add_argument("--cpu-baseline", default="auto", choices=["auto", "off"])
+    p.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the oracle sample (0: workload default)")
+    return p.parse_args()
+
+
+def build_state(wl, dev):
+    import torch
+
+    import csa2_inputs as gen
+    import sparse_long_context_topk_amd as csa2
+    from sparse_long_context_topk_amd.schedule import DecodeState, LayerInputs
+
+    rows = wl["rows"]
+    cache = torch.empty((rows, 288), dtype=torch.uint8, device=dev)
+    chunk = 1 << 20
+    for r0 in range(0, rows, chunk):
+        n = min(chunk, rows - r0)
+        x = gen.kv_rows(wl, r0, n, dev)
+        csa2.quant_append(x, torch.arange(r0, r0 + n, dtype=torch.int64, device=dev), cache)
+        del x
+    ik = gen.index_keys(wl, dev)
+    s = gen.seq_tensors(wl, dev)
+    st = DecodeState(cache=cache, ik=ik, seq_base=s["seq_base"], q_seq=s["q_seq"], q_nvis=s["q_nvis"],
+                     max_nvis=max(wl["lengths"]), k=wl["k"], keep_blocks=wl["keep_blocks"], w_max=wl["w"],
+                     softmax_scale=512 ** -0.5)
+    layers = [LayerInputs(**gen.layer_tensors(wl, i, dev)) for i in range(len(wl["layers"]))]
+    app_x, app_rows = gen.append_rows(wl, dev)
+    torch.cuda.synchronize()
+    return st, layers, app_x, app_rows
+
+
+def scan_bytes(wl):
+    """Algorithmic bytes of one Full-layer indexer-scan launch: every visible
+    key (d_i bf16) once, plus each query's indexer query and head weights."""
+    n_q, h_i, d_i = wl["n_q"], wl["h_i"], wl["d_i"]
+    return sum(wl["lengths"]) * d_i * 2 + n_q * (h_i * d_i * 2 + h_i * 4)
+
+
+def step_bytes(wl):
+    """Algorithmic bytes of one whole step (what the method must move)."""
+    n_q, h_i, d_i, h, k, W = wl["n_q"], wl["h_i"], wl["d_i"], wl["h"], wl["k"], wl["w"]
+    qb = 4 if wl["q_dtype"] == "f32" else 2
+    b = n_q * (1024 + 288)                                   # append: read a bf16 row, write a record
+    for mode in wl["layers"]:
+        if mode == "full":
+            b += scan_bytes(wl) + n_q * k * 4 + (n_q * wl["keep_blocks"] * 4)
+        elif mode == "reindex":
+            b += sum(min(L, 8 * wl["keep_blocks"]) for L in wl["lengths"]) * d_i * 2
+            b += n_q * (h_i * d_i * 2 + h_i * 4 + wl["keep_blocks"] * 4 + k * 4)
+        # attention: selected records, window rows, q in, out
+        b += sum(min(k, L) * 288 + min(W, L) * 1024 for L in wl["lengths"])
+        b += n_q * h * 512 * (qb + 4)
+    return b
+
+
+def traffic_from_profile(kernel_sha):
+    """HBM bytes per scan launch measured with rocprofv3 counters (committed
+    summary), if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "index_scan_c3_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != kernel_sha:
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(wl, st, layers, app_x, dev, nseq, gpu_results):
+    """Time the CPU oracle on the first `nseq` sequences of the same inputs."""
+    import numpy as np
+    import torch
+
+    import csa2_inputs as gen
+    import oracle
+    from oracle.step import decode_step as oracle_step
+
+    bits = gen.bf16_bits
+    sel = list(range(nseq))
+    lens = [wl["lengths"][i] for i in sel]
+    base = [int(wl["seq_base"][i]) for i in sel]
+    cbase = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    ik = np.concatenate([bits(st.ik[b:b + L]) for b, L in zip(base, lens)])
+
+    def raw_rows(crow):
+        # compact row -> (sequence, position) -> global row of the generator
+        s = np.searchsorted(cbase, crow, side="right") - 1
+        g = np.asarray(base)[s] + (crow - cbase[s])
+        x = gen.kv_rows_at(wl, g, dev)
+        return x.cpu().numpy() if x.dtype == torch.float32 else bits(x)
+
+    def host(t):
+        return t.cpu().numpy() if t.dtype != torch.bfloat16 else bits(t)
+
+    hl = []
+    for lay in layers:
+        d = dict(mode=lay.mode, q=host(lay.q[:nseq]), swa=bits(lay.swa), swa_row0=host(lay.swa_row0[:nseq]),
+                 swa_len=host(lay.swa_len[:nseq]))
+        if lay.iq is not None:
+            d["iq"], d["w"] = bits(lay.iq[:nseq]), host(lay.w[:nseq])
+        hl.append(d)
+    ax = host(app_x[:nseq])
+    threads = max(1, min(nseq, 16, os.cpu_count() or 1))
+    oracle.lib()
+    res, _, secs = oracle_step(hl, ik, cbase, np.arange(nseq, dtype=np.int32), np.array(lens, np.int32),
+                               wl["k"], wl["keep_blocks"], wl["block"], raw_rows, ax, st.softmax_scale,
+                               n_threads=threads)
+    # parity of the sample against the timed GPU step's outputs
+    idx_ok, err = True, 0.0
+    for (gidx, gout, _), (ridx, rout, _) in zip(gpu_results, res):
+        idx_ok &= bool(np.array_equal(gidx[:nseq].cpu().numpy(), ridx))
+        o = gout[:nseq].cpu().numpy()
+        den = np.abs(rout).max(axis=-1)
+        den[den == 0] = 1
+        err = max(err, float((np.abs(o - rout).max(axis=-1) / den).max()))
+    ql = nseq * len(wl["layers"])
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return ({"value": ql / secs, "unit": "query·layers/s", "cores": threads, "kind": "oracle",
+             "sample": f"{nseq} of {wl['n_q']} sequences (full contexts {sorted(set(lens))}), all "
+                       f"{len(wl['layers'])} layers of one step = {ql} query-layers in {secs:.2f} s",
+             "cpu": cpu_model},
+            {"idx_bitexact": idx_ok, "attn_max_normwise_err": err, "sequences": nseq})
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import csa2_inputs as gen
+    from sparse_long_context_topk_amd.schedule import decode_step
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = gen.workload(a.workload)
+    log(f"workload {wl['name']}: {wl['desc']}; building inputs")
+    t0 = time.time()
+    st, layers, app_x, app_rows = build_state(wl, dev)
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    def step(ev=None, keep=False):
+        return decode_step(st, layers, append_x=app_x, append_rows=app_rows, scan_events=ev, keep_outputs=keep)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+    K = a.steps
+    has_full = "full" in wl["layers"]
+    evs = []
+    for _ in range(K if has_full else 0):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        e1.record()
+        evs.append((e0, e1))
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(K):
+        step(evs[i] if has_full else None)
+    t_stop.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_stop) / K
+    log(f"timed {K} steps: {ms:.4f} ms/step")
+    ql_per_step = wl["n_q"] * len(wl["layers"])
+    value = ql_per_step / (ms * 1e-3)
+
+    roofline = None
+    if has_full:
+        scan_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / K
+        sb = scan_bytes(wl)
+        achieved = sb / (scan_ms * 1e-3) / 1e9
+        sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
+        traffic = traffic_from_profile(sha)
+        roofline = {"bound": "hbm", "kernel": "k_scan (indexer scan, Full layer)", "achieved": round(achieved, 1),
+                    "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                    "traffic": traffic, "algorithmic_bytes_per_launch": sb, "launch_ms": round(scan_ms, 5)}
+    sbytes = step_bytes(wl)
+
+    cpu = None
+    parity = None
+    if a.cpu_baseline == "auto":
+        nseq = a.cpu_seqs or {"c1": 1, "c2": 8, "c3": 4, "c5": 2}[a.workload]
+        log(f"cpu baseline: oracle on {nseq} sequence(s)")
+        gres, _ = step(keep=True)
+        torch.cuda.synchronize()
+        cpu, parity = cpu_baseline(wl, st, layers, app_x, dev, nseq, gres)
+        log(f"cpu baseline {cpu['value']:.3f} q.l/s; sample parity {parity}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "query·layers/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl['name']}: {wl['desc']}", "batch": wl["n_q"],
+                   "context": max(wl["lengths"]), "context_total": wl["rows"], "layers": wl["layers"],
+                   "query_layers_per_step": ql_per_step, "heads": wl["h"],
+                   "indexer": f"{wl['h_i']}x{wl['d_i']}", "top_k": wl["k"], "swa": wl["w"],
+                   "pool_blocks": wl["keep_blocks"], "parallelism": "none (1 GPU)"},
+        "step_hbm": {"algorithmic_bytes": sbytes, "GB/s": round(sbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac": round(sbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,7 @@ ROW_CHUNK = 1 << 16          # rows per generator chunk for large row-major tens
 
 
 def _sub_seed(seed: int, tag: str, chunk: int = 0) -> int:
-    return (int(seed) * 0x9E3779B1 + zlib.crc32(tag.encode()) * 0x85EBCA77 + chunk * 0xC2B2AE3D) & (
+    return (int(seed) * 0x9E3779B1 + zlib.crc32(tag.encode()) * 0x85EBCA77 + int(chunk) * 0xC2B2AE3D) & (
         (1 << 63) - 1)
 
 
@@ -80,3 +80,112 @@ def log_uniform_lengths(n, lo, hi, seed, tag="lengths"):
     u = uniform((n,), seed, tag).double()
     v = torch.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))
     return [int(min(hi, max(lo, math.floor(x)))) for x in v.tolist()]
+
+
+# ---------------------------------------------------------------------------
+# Decode workloads (shapes and distributions of the CSA2 configurations).
+# A workload is a plain dict; the tensors are drawn on demand.
+# ---------------------------------------------------------------------------
+def _decoder_layers():
+    return ["full", "reuse", "reuse", "reuse"] + ["reindex", "reuse", "reuse", "reuse"] * 4
+
+
+def workload(name: str, seed: int | None = None, length_div: int = 1) -> dict:
+    """Named decode workload.  length_div > 1 shrinks every context length
+    (for oracle-sized parity runs) and keeps everything else."""
+    base = {"k": 512, "w": 128, "outlier_p": 0.0, "block": 8}
+    if name == "c1":
+        wl = dict(base, desc="single Full layer, batch 1, context 4096, 16 heads fp32 query, "
+                             "indexer 4x64", lengths=[4096], h=16, q_dtype="f32", kv_dtype="f32",
+                  h_i=4, d_i=64, layers=["full"], keep_blocks=0, append=True)
+    elif name == "c2":
+        wl = dict(base, desc="decoder group 1 (Full + 3 Reuse), batch 8, context 131072",
+                  lengths=[131072] * 8, h=64, q_dtype="bf16", kv_dtype="bf16", h_i=64, d_i=128,
+                  layers=["full", "reuse", "reuse", "reuse"], keep_blocks=0, append=True)
+    elif name == "c3":
+        wl = dict(base, desc="Reindex group at 1M context, batch 4: Full + pool (2048 blocks of 8), "
+                             "then Reindex; 64 heads, FP4 512-ch KV, indexer 64x128, Top-512, SWA-128",
+                  lengths=[1 << 20] * 4, h=64, q_dtype="bf16", kv_dtype="bf16", h_i=64, d_i=128,
+                  layers=["full", "reindex"], keep_blocks=2048, append=True)
+    elif name == "c5":
+        s = 0xC5A20005 if seed is None else seed
+        wl = dict(base, desc="20-layer decoder schedule, 64 sequences, lengths log-uniform in "
+                             "[4096, 1048576]", lengths=log_uniform_lengths(64, 4096, 1 << 20, s),
+                  h=64, q_dtype="bf16", kv_dtype="bf16", h_i=64, d_i=128, layers=_decoder_layers(),
+                  keep_blocks=2048, append=True)
+    else:
+        raise ValueError(f"unknown workload {name}")
+    wl["name"] = name
+    wl["seed"] = (0xC5A20000 + int(name[1:])) if seed is None else seed
+    if length_div > 1:
+        wl["lengths"] = [max(1, L // length_div) for L in wl["lengths"]]
+        wl["name"] = f"{name}/{length_div}"
+    wl["n_q"] = len(wl["lengths"])
+    wl["rows"] = int(sum(wl["lengths"]))
+    wl["seq_base"] = [0] + [int(v) for v in np.cumsum(wl["lengths"])[:-1]]
+    return wl
+
+
+def _tdtype(s):
+    return torch.float32 if s == "f32" else torch.bfloat16
+
+
+def kv_rows(wl, row0, nrows, device="cpu"):
+    """Raw (unquantised) main-KV rows [row0, row0+nrows) of the whole batch."""
+    return normal_rows(wl["seed"], "main-kv", row0, nrows, 512, device=device, dtype=_tdtype(wl["kv_dtype"]),
+                       outlier_p=wl["outlier_p"])
+
+
+def index_keys(wl, device="cpu", row0=0, nrows=None):
+    nrows = wl["rows"] - row0 if nrows is None else nrows
+    return normal_rows(wl["seed"], "index-k", row0, nrows, wl["d_i"], device=device, dtype=torch.bfloat16,
+                       outlier_p=wl["outlier_p"])
+
+
+def seq_tensors(wl, device="cpu"):
+    n_q = wl["n_q"]
+    return dict(seq_base=torch.tensor(wl["seq_base"], dtype=torch.int64, device=device),
+                q_seq=torch.arange(n_q, dtype=torch.int32, device=device),
+                q_nvis=torch.tensor(wl["lengths"], dtype=torch.int32, device=device))
+
+
+def layer_tensors(wl, layer, device="cpu"):
+    """Layer `layer`'s own main query, window rows and (Full/Reindex) indexer query."""
+    n_q, h, W = wl["n_q"], wl["h"], wl["w"]
+    s, tag = wl["seed"], f"layer{layer}"
+    d = dict(mode=wl["layers"][layer],
+             q=normal((n_q, h, 512), s, tag + "-q", device=device, dtype=_tdtype(wl["q_dtype"]),
+                      outlier_p=wl["outlier_p"]),
+             swa=normal((n_q * W, 512), s, tag + "-swa", device=device, dtype=torch.bfloat16,
+                        outlier_p=wl["outlier_p"]),
+             swa_row0=torch.arange(n_q, dtype=torch.int64, device=device) * W,
+             swa_len=torch.tensor([min(W, L) for L in wl["lengths"]], dtype=torch.int32, device=device))
+    if d["mode"] in ("full", "reindex"):
+        d["iq"] = normal((n_q, wl["h_i"], wl["d_i"]), s, tag + "-iq", device=device, dtype=torch.bfloat16,
+                         outlier_p=wl["outlier_p"])
+        d["w"] = uniform((n_q, wl["h_i"]), s, tag + "-w", device=device)
+    return d
+
+
+def append_rows(wl, device="cpu"):
+    """The new token of every sequence (its last position): raw row and cache row."""
+    rows = [wl["seq_base"][i] + wl["lengths"][i] - 1 for i in range(wl["n_q"])]
+    x = torch.cat([kv_rows(wl, r, 1, device) for r in rows])
+    return x, torch.tensor(rows, dtype=torch.int64, device=device)
+
+
+def kv_rows_at(wl, rows, device="cpu"):
+    """Raw main-KV rows at arbitrary global row indices (sorted or not),
+    drawing each generator chunk once."""
+    rows = np.asarray(rows, dtype=np.int64)
+    out = torch.empty((len(rows), 512), dtype=_tdtype(wl["kv_dtype"]), device=device)
+    if len(rows) == 0:
+        return out
+    chunks = rows // ROW_CHUNK
+    for c in np.unique(chunks):
+        sel = np.nonzero(chunks == c)[0]
+        c0 = int(c) * ROW_CHUNK
+        n = min(ROW_CHUNK, wl["rows"] - c0)
+        blk = kv_rows(wl, c0, n, device)
+        out[torch.from_numpy(sel).to(device)] = blk[torch.from_numpy(rows[sel] - c0).to(device)]
+    return out

@@ -1,0 +1,58 @@
+"""One CSA2 decode step run by the oracle, layer by layer, on host arrays.
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU-baseline leg of the bench).
+It sequences the oracle calls in schedule order -- Full: index (+pool),
+Reindex: re-score the pool, Reuse: the group head's list -- and attends each
+layer with its own query and window rows, as CSA2 prescribes ("DeepSeek AI
+выпустила DeepSeek-V4.1-Flash ..." (wire.sakhanda.co), section "Сжатое
+разреженное внимание 2 (CSA2)").
+
+The FP4 records the attention reads are quantised here by the oracle from the
+raw rows (callers pass a function that draws raw rows from the seeded input
+generator), so no oracle input comes from the GPU path.
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+
+from . import index_topk, quantize_rows, reindex_topk, sparse_attn
+
+
+def decode_step(layers, ik, seq_base, q_seq, q_nvis, k, keep_blocks, block, raw_rows_fn, append_x,
+                scale, n_threads=0):
+    """layers: list of dicts of host arrays: mode, q (float32 or uint16 bf16 bits),
+    swa (uint16), swa_row0, swa_len and, for full/reindex, iq (uint16) and w.
+    raw_rows_fn(rows) -> raw main-KV rows (float32 or uint16) of global cache rows.
+    Returns (results, pool, seconds): results = [(idx, out, lse)] per layer and
+    the time spent inside the oracle's decode-step calls (input plumbing excluded)."""
+    secs = 0.0
+    t0 = time.perf_counter()
+    quantize_rows(append_x)                # a1: the new token of every sequence
+    secs += time.perf_counter() - t0
+    idx = pool = None
+    results = []
+    for lay in layers:
+        mode = lay["mode"]
+        t0 = time.perf_counter()
+        if mode == "full":
+            r = index_topk(lay["iq"], lay["w"], q_seq, q_nvis, ik, seq_base, k, block=block,
+                           keep_blocks=keep_blocks, n_threads=n_threads)
+            idx, pool = r if keep_blocks else (r, None)
+        elif mode == "reindex":
+            idx = reindex_topk(lay["iq"], lay["w"], q_seq, q_nvis, ik, seq_base, pool, k, block=block,
+                               n_threads=n_threads)
+        secs += time.perf_counter() - t0
+        # records of the selected entries, quantised by the oracle
+        rows = np.where(idx >= 0, seq_base[q_seq][:, None] + idx, -1)
+        uniq = np.unique(rows[rows >= 0])
+        recs = quantize_rows(raw_rows_fn(uniq)) if len(uniq) else np.zeros((1, 288), np.uint8)
+        cidx = np.where(rows >= 0, np.searchsorted(uniq, rows), -1).astype(np.int32)
+        zq = np.zeros(len(q_seq), np.int32)
+        t0 = time.perf_counter()
+        out, lse = sparse_attn(lay["q"], zq, recs, np.zeros(1, np.int64), cidx, lay["swa"], lay["swa_row0"],
+                               lay["swa_len"], scale, n_threads=n_threads)
+        secs += time.perf_counter() - t0
+        results.append((idx, out, lse))
+    return results, pool, secs

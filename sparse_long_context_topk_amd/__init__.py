@@ -67,6 +67,8 @@ def lib():
         L.csa2_status_string.argtypes = [i32]
         L.csa2_last_hip_error.restype = i32
         L.csa2_last_hip_error.argtypes = []
+        L.csa2_record_scan_events.restype = None
+        L.csa2_record_scan_events.argtypes = [vp, vp]
         _lib = L
     return _lib
 
@@ -118,6 +120,14 @@ def _ws(device, nbytes, ws):
         key = torch.device(device)
         ws = _default_ws.setdefault(key, Workspace())
     return ws.get(nbytes, device)
+
+
+def record_scan_events(start, stop) -> None:
+    """Have the next index/reindex call record these torch.cuda.Event objects
+    around its scan kernel (each event must have been recorded once already so
+    that its HIP handle exists)."""
+    lib().csa2_record_scan_events(ctypes.c_void_p(start.cuda_event) if start is not None else None,
+                                  ctypes.c_void_p(stop.cuda_event) if stop is not None else None)
 
 
 # ------------------------------------------------------------------ calls

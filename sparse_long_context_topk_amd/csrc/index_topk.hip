@@ -4,45 +4,53 @@
 // indexer score of every candidate position, score = sum_h w_h ReLU(q_h . k),
 // defined to the bit as an fp32 fma chain over d and then over h; the Top-K
 // positions by (score desc, position asc).  Full layers score every visible
-// position and may also build the hierarchical pool (blocks of 8, block key =
-// bf16 mean key, Top-keep_blocks blocks); Reindex layers score the positions
-// of a pool.  Sources: "DeepSeek AI выпустила DeepSeek-V4.1-Flash с
-// контекстом в 1 млн токенов, KV-кэшем FP4 ..." (wire.sakhanda.co), section
-// "Сжатое разреженное внимание 2 (CSA2)": the Full / Reindex / Reuse modes,
-// Top-512, and the pool of up to 2048 blocks of 8 positions.
+// position and may also build the hierarchical pool (blocks of 8 scored by
+// their mean key, Top-keep_blocks blocks); Reindex layers score the positions
+// of a pool.  Source: "DeepSeek AI выпустила DeepSeek-V4.1-Flash с контекстом
+// в 1 млн токенов, KV-кэшем FP4 ..." (wire.sakhanda.co), section "Сжатое
+// разреженное внимание 2 (CSA2)": the Full / Reindex / Reuse modes, Top-512,
+// and the pool of up to 2048 blocks of 8 positions.
 //
 // How (one pass over the keys at HBM speed, exact result):
 //  1. k_prologue  zeroes per-problem counters and histograms, and computes
 //                 QW = sum_h |w_h| ||q_h|| for the rounding bound.
-//  2. k_scan      streams the indexer keys once.  Scores come from bf16 MFMA
+//  2. k_scan      streams the indexer keys once, two 16-key groups ahead of
+//                 the math.  Scores come from bf16 MFMA
 //                 (v_mfma_f32_16x16x32_bf16: 16 heads x 16 positions x 32
-//                 dims per instruction, the query held in registers); each
-//                 work-group keeps a 4096-bin histogram of the top 12 bits of
-//                 the scores in LDS and the largest squared key norm.  With a
-//                 pool, block keys are averaged in LDS from the keys already
-//                 loaded and scored by MFMA as well, so the pool costs no
-//                 extra HBM traffic.  The last work-group of a query turns the
-//                 histogram into a threshold below which no Top-K member can
-//                 lie: T = (lowest value of the bin holding the K-th score) -
-//                 2*Delta, where Delta bounds |MFMA score - exact score| for
-//                 every key:  Delta = C * QW * max||k|| (Cauchy-Schwarz on
-//                 the dot-product rounding error, ReLU is 1-Lipschitz, plus
-//                 the head-sum rounding), C from the fp32 error constants with
-//                 a 2x safety factor.
+//                 dims, the query held in registers).  A block's per-head dot
+//                 product is the mean of its members' (linearity), so block
+//                 scores come from the same accumulators with a three-step DPP
+//                 butterfly: the pool costs no extra HBM traffic and no extra
+//                 MFMA.  Each work-group keeps a 4096-bin histogram of the top
+//                 12 bits of the scores and the largest squared key norm; the
+//                 last work-group of a query turns the histogram into a
+//                 threshold below which no Top-K member can lie:
+//                 T = (lowest value of the bin holding the K-th score) - 2*Delta,
+//                 where Delta bounds |MFMA score - exact score| for every key:
+//                 Delta = C * QW * max||k|| (Cauchy-Schwarz on the dot-product
+//                 rounding error, ReLU is 1-Lipschitz, plus the head-sum and
+//                 block-mean roundings), C from the fp32 error constants with a
+//                 2x safety factor.
 //  3. k_compact   keeps the candidates with approximate score >= T in
-//                 position order; its last work-group finds the exact K-th
-//                 approximate score a_K (radix select) and narrows the band
-//                 to a >= a_K - 2*Delta.  Every exact Top-K member is in this
-//                 band (it has exact score >= the K-th exact score >= a_K -
-//                 Delta, hence approximate score >= a_K - 2*Delta).
-//  4. k_rescore   recomputes the band's scores with the exact fp32 chain
-//                 (one lane per head, then one lane for the head sum); its
-//                 last work-group selects the Top-K by (score desc, position
-//                 asc) with a radix select on the exact scores and writes the
-//                 positions in ascending order.
+//                 position order; its last work-group finds the exact K-th and
+//                 (K+1)-th approximate scores a_K >= a_K1 (radix select) and
+//                 splits the band:  every exact Top-K member has approximate
+//                 score >= a_K - 2*Delta (it beats the K-th exact score, which
+//                 is >= a_K - Delta), and every member with approximate score
+//                 > a_K1 + 2*Delta is certainly in (its exact score exceeds
+//                 a_K1 + Delta, which only candidates with approximate score
+//                 above a_K1 -- at most K of them, itself included -- can
+//                 reach).  Only the members in between need exact scores.
+//  4. k_rescore   recomputes those scores with the exact fp32 chains (one lane
+//                 per head, then one lane for the head sum); its last
+//                 work-group selects the missing members by (exact score desc,
+//                 position asc) and writes the positions in ascending order.
 // Degenerate inputs (ties everywhere) only make the band large; the result
 // stays exact.
 #include "csa2_device.h"
+
+#include <algorithm>
+#include <cmath>
 
 namespace csa2 {
 namespace idx {
@@ -53,19 +61,23 @@ constexpr int kNBins = 4096;
 constexpr int kBinShift = 20;
 constexpr int kCmpChunk = 4096;
 constexpr int kCmpPerThread = kCmpChunk / kThreads;
-constexpr int kRescoreWGs = 32;
+constexpr int kMaxChunksLds = 2048;
+constexpr int kRescoreWGs = 64;
+constexpr int kMaxScanChunk = 4096;
+constexpr int kBandLds = 8192;       // band entries whose keys the last work-groups keep in LDS
+constexpr uint32_t kCertain = 0x80000000u;
 
 struct Meta {
   uint32_t scan_done, cmp_done, rs_done, maxk2;
   float qw, wabs, thr, delta;
-  int32_t nc, nband, nband2, pad0;
-  uint32_t pad[4];
+  int32_t nc, nband, nband2, nunc, nin;
+  uint32_t pad[3];
 };
 static_assert(sizeof(Meta) == 64, "Meta is one 64-byte line");
 
 struct Entry {
-  int32_t cand;
-  float s;
+  uint32_t cand;  // candidate index; top bit set = certainly selected
+  float s;        // approximate score, replaced by the exact one when rescored
 };
 
 struct Params {
@@ -87,29 +99,52 @@ struct Params {
   int scan_chunk;
   int64_t stride;          // slots per problem in scores / band arrays
   int nchunk_cmp;
-  float bound_c;
+  float bound_tok, bound_blk;
   float* scores;
   uint32_t* hist;
   Meta* meta;
   uint32_t* chunk_cnt;
   Entry* band_a;
   Entry* band_b;
+  uint32_t* unc;
 };
 
 // ---------------------------------------------------------------- helpers
-__device__ __forceinline__ float delta_of(const Meta& m, float bound_c, int d_i) {
-  float kn = sqrtf(__uint_as_float(m.maxk2));
-  return bound_c * m.qw * kn * (1.0f + 0.0009765625f) + m.wabs * (float)d_i * 7.8886e-31f;
-}
-
-// Band threshold below a value v: v - 2*Delta with room for the rounding of
-// this subtraction itself.
+// v - 2*Delta and v + 2*Delta with room for the rounding of these operations.
 __device__ __forceinline__ float band_below(float v, float delta) {
   return v - 2.0f * delta * (1.0f + 0.00390625f) - fabsf(v) * 9.5367431640625e-07f;
 }
+__device__ __forceinline__ float band_above(float v, float delta) {
+  return v + 2.0f * delta * (1.0f + 0.00390625f) + fabsf(v) * 9.5367431640625e-07f;
+}
 
-// Exclusive prefix sum over the work-group (256 threads); returns the
-// exclusive offset of this thread and writes the total to *total.
+__device__ __forceinline__ float dpp_f(float v, int ctrl) {
+  // the DPP control must be a constant: dispatch on the three patterns used
+  int x = __float_as_int(v);
+  int r;
+  if (ctrl == 0xB1) r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);        // quad xor 1
+  else if (ctrl == 0x4E) r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad xor 2
+  else r = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);                    // half-row mirror
+  return __int_as_float(r);
+}
+
+// Sum over the 8 lanes of each half row (lanes 8j..8j+7 of every 16).
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_f(v, 0xB1);
+  v += dpp_f(v, 0x4E);
+  v += dpp_f(v, 0x141);
+  return v;
+}
+
+// Sum over the 16 lanes of each row.
+__device__ __forceinline__ float sum16(float v) {
+  v = sum8(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row mirror
+  return v;
+}
+
+// Exclusive prefix sum over the work-group; returns this thread's offset and
+// writes the total.
 __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t x = v;
@@ -132,9 +167,9 @@ __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* s_tm
   return before + x - v;
 }
 
-// K-th largest of the sortable keys key_of(i), i < n (1 <= K <= n), by a
-// most-significant-digit radix select with 8-bit digits.  Returns the key and
-// in *ties the number of entries equal to it that belong to the Top-K.
+// K-th largest of the sortable keys key_of(i), i < n (1 <= K <= n): a
+// most-significant-digit radix select with 8-bit digits.  Returns the key; in
+// *ties the number of entries equal to it that belong to the Top-K.
 template <typename KeyOf>
 __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist /*256*/,
                                    uint32_t* s_tmp, uint32_t* ties) {
@@ -145,21 +180,20 @@ __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist 
     s_hist[tid] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += kThreads) {
-      uint32_t key = key_of(i);
+      const uint32_t key = key_of(i);
       if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    // suffix sums: S[d] = sum_{d' >= d} hist[d'] ; thread tid owns digit 255 - tid
-    uint32_t v = s_hist[255 - tid];
+    // thread tid owns digit 255 - tid; the exclusive scan counts larger digits
+    const uint32_t v = s_hist[255 - tid];
     uint32_t tot;
-    uint32_t excl = wg_exclusive_scan(v, s_tmp, &tot);  // sum over digits above
-    uint32_t incl = excl + v;
-    if (excl < remaining && incl >= remaining) {
+    const uint32_t excl = wg_exclusive_scan(v, s_tmp, &tot);
+    if (excl < remaining && excl + v >= remaining) {
       s_tmp[8] = 255u - tid;
       s_tmp[9] = excl;
     }
     __syncthreads();
-    uint32_t d = s_tmp[8];
+    const uint32_t d = s_tmp[8];
     remaining -= s_tmp[9];
     prefix |= d << shift;
     mask |= 255u << shift;
@@ -169,29 +203,57 @@ __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist 
   return prefix;
 }
 
-__device__ __forceinline__ int cand_pos(const Params& P, int q, int kind, int cand) {
+// Largest key_of(i) strictly below `below` (0 if none).
+template <typename KeyOf>
+__device__ uint32_t wg_max_below(int n, uint32_t below, KeyOf key_of, uint32_t* s_tmp) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const uint32_t key = key_of(i);
+    if (key < below && key > m) m = key;
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) s_tmp[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t r = 0;
+  for (int i = 0; i < kWaves; ++i) r = max(r, s_tmp[i]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int cand_pos(const Params& P, int q, int kind, uint32_t cand) {
+  cand &= ~kCertain;
   if (P.reindex) {
-    int b = P.pool_in[(size_t)q * P.keep_in + (cand >> 3)];
-    return b * 8 + (cand & 7);
+    const int b = P.pool_in[(size_t)q * P.keep_in + (cand >> 3)];
+    return b * 8 + (int)(cand & 7);
   }
   (void)kind;
-  return cand;
+  return (int)cand;
 }
 
 // ---------------------------------------------------------------- 1. prologue
+template <int D>
 __global__ __launch_bounds__(kThreads) void k_prologue(Params P) {
   const int p = blockIdx.x, q = p % P.n_q, kind = p / P.n_q;
-  uint32_t* h = P.hist + (size_t)p * kNBins;
-  for (int i = threadIdx.x; i < kNBins; i += kThreads) h[i] = 0;
+  uint4* h = reinterpret_cast<uint4*>(P.hist + (size_t)p * kNBins);
+  for (int i = threadIdx.x; i < kNBins / 4; i += kThreads) h[i] = make_uint4(0, 0, 0, 0);
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     float qn = 0.0f, wa = 0.0f;
     if (lane < P.h_i) {
-      const uint16_t* qh = P.iq + ((size_t)q * P.h_i + lane) * P.d_i;
+      const uint4* qh = reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + lane) * D);
+      uint4 v[D / 8];
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) v[i] = qh[i];
       float ss = 0.0f;
-      for (int d = 0; d < P.d_i; ++d) {
-        float v = bf16_to_f32(qh[d]);
-        ss = fmaf(v, v, ss);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = __uint_as_float(wd[j] << 16), hi = __uint_as_float(wd[j] & 0xFFFF0000u);
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+        }
       }
       wa = fabsf(P.w[(size_t)q * P.h_i + lane]);
       qn = wa * sqrtf(ss);
@@ -205,46 +267,49 @@ __global__ __launch_bounds__(kThreads) void k_prologue(Params P) {
       m.wabs = wa;
       m.thr = -INFINITY;
       m.delta = 0.0f;
-      int nvis = P.q_nvis[q];
+      const int nvis = P.q_nvis[q];
       m.nc = P.reindex ? 8 * P.keep_in : (kind == 0 ? nvis : (nvis + 7) / 8);
-      m.nband = m.nband2 = m.pad0 = 0;
-      for (int i = 0; i < 4; ++i) m.pad[i] = 0;
+      m.nband = m.nband2 = m.nunc = m.nin = 0;
+      m.pad[0] = m.pad[1] = m.pad[2] = 0;
       P.meta[p] = m;
     }
   }
 }
 
-// Threshold from the global histogram of problem p (run by one work-group).
-__device__ void wg_threshold(const Params& P, int p, int K, uint32_t* s_tmp) {
+// Threshold from the global histogram of problem p (one work-group).
+__device__ void wg_threshold(const Params& P, int p, int K, float kmax2, float bound, uint32_t* s_tmp) {
   const int tid = threadIdx.x;
   const uint32_t* h = P.hist + (size_t)p * kNBins;
-  constexpr int kPer = kNBins / kThreads;  // 16 bins per thread
-  // thread tid owns bins [kNBins - kPer*(tid+1), kNBins - kPer*tid): highest first
+  constexpr int kPer = kNBins / kThreads;  // 16 bins per thread, highest bins first
   const int b_hi = kNBins - kPer * tid - 1;
   uint32_t loc = 0;
+  uint32_t hv[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) loc += h[b_hi - j];
+  for (int j = 0; j < kPer; ++j) {
+    hv[j] = h[b_hi - j];
+    loc += hv[j];
+  }
   uint32_t tot;
-  uint32_t above = wg_exclusive_scan(loc, s_tmp, &tot);
+  const uint32_t above = wg_exclusive_scan(loc, s_tmp, &tot);
   const Meta m = P.meta[p];
-  const float delta = delta_of(m, P.bound_c, P.d_i);
-  if (tid == 0 && tot <= (uint32_t)K) {
-    P.meta[p].thr = -INFINITY;
+  const float delta = bound * m.qw * sqrtf(kmax2) * (1.0f + 0.0009765625f) + m.wabs * (float)P.d_i * 7.8886e-31f;
+  if (tid == 0) {
     P.meta[p].delta = delta;
+    if (tot <= (uint32_t)K) P.meta[p].thr = -INFINITY;
   }
   if (tot > (uint32_t)K && above < (uint32_t)K && above + loc >= (uint32_t)K) {
     uint32_t run = above;
     int bstar = b_hi;
+#pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      run += h[b_hi - j];
+      run += hv[j];
       if (run >= (uint32_t)K) {
         bstar = b_hi - j;
         break;
       }
     }
-    float t0 = unsortable((uint32_t)bstar << kBinShift);
+    const float t0 = unsortable((uint32_t)bstar << kBinShift);
     P.meta[p].thr = band_below(t0, delta);
-    P.meta[p].delta = delta;
   }
 }
 
@@ -252,19 +317,22 @@ __device__ void wg_threshold(const Params& P, int p, int K, uint32_t* s_tmp) {
 template <int D, int MT, bool POOL, bool INDIRECT>
 __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   constexpr int KS = D / 32;   // MFMA k-steps; also 16-byte loads per lane per key
-  constexpr int DPL = D / 4;   // key dims held by one lane (one quarter of the key)
-  constexpr int U4 = D / 8;    // 16-byte words per key row
+  constexpr int DPL = D / 4;   // key dims held by one lane (a quarter of the key)
+  constexpr int NBUF = 3;      // key groups in registers: two in flight, one in use
   __shared__ uint32_t s_hist[kNBins];
   __shared__ uint32_t s_hist_b[POOL ? kNBins : 1];
-  __shared__ uint4 s_stage[POOL ? kWaves * 16 * U4 : 1];
-  __shared__ uint4 s_bkey[POOL ? kWaves * 16 * U4 : 1];
+  __shared__ int32_t s_pool[INDIRECT ? 512 : 1];
+  // the chunk's scores stay in LDS until the end: the hot loop then issues
+  // only loads, and the results leave as one coalesced write
+  __shared__ float s_sc[kMaxScanChunk];
+  __shared__ float s_scb[POOL ? kMaxScanChunk / 8 : 1];
   __shared__ uint32_t s_tmp[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int q = blockIdx.y;
-  const int p = q;                 // token problem
-  const int pb = P.n_q + q;        // block problem (POOL)
+  const int p = q;             // token problem
+  const int pb = P.n_q + q;    // block problem (POOL)
   const int nvis = P.q_nvis[q];
   const int64_t base = P.seq_base[P.q_seq[q]];
   const int nc = INDIRECT ? 8 * P.keep_in : nvis;
@@ -275,10 +343,17 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     s_hist[i] = 0;
     if (POOL) s_hist_b[i] = 0;
   }
+  if constexpr (INDIRECT) {
+    // block ids of this chunk's pool slots (scan_chunk / 8 <= 512 of them)
+    for (int i = tid; i < P.scan_chunk / 8; i += kThreads) {
+      const int slot = c0 / 8 + i;
+      s_pool[i] = slot < P.keep_in ? P.pool_in[(size_t)q * P.keep_in + slot] : -1;
+    }
+  }
 
-  // query (A operand): lane (n, g) holds head 16*mt + n, dims g*DPL + 8*ks .. +7
-  bf16x8 qa[MT][KS];
-  float wr[MT][4];
+  // Q^T as the MFMA B operand: lane (n, g) holds head 16*mt + n, dims g*DPL + 8*ks .. +7
+  bf16x8 qb[MT][KS];
+  float wr[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int head = 16 * mt + n;
@@ -287,199 +362,192 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (head < P.h_i)
         v = *reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + head) * D + g * DPL + 8 * ks);
-      qa[mt][ks] = __builtin_bit_cast(bf16x8, v);
+      qb[mt][ks] = __builtin_bit_cast(bf16x8, v);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = 16 * mt + 4 * g + i;
-      wr[mt][i] = hh < P.h_i ? P.w[(size_t)q * P.h_i + hh] : 0.0f;
-    }
+    wr[mt] = head < P.h_i ? P.w[(size_t)q * P.h_i + head] : 0.0f;
   }
   __syncthreads();
 
-  float mk2 = 0.0f, mk2b = 0.0f;
+  float mk2 = 0.0f;
   float* sc = P.scores + (size_t)p * P.stride;
   float* scb = P.scores + (size_t)pb * P.stride;
   const int nslots = min(P.scan_chunk, max(nc - c0, 0));
   const int ngroups = (nslots + 15) >> 4;
-  int batch_slot = 0;   // POOL: groups collected in the current block batch
-  int batch_first = 0;  // POOL: loop index of the batch's first group
+  const int my_groups = ngroups > wave ? (ngroups - wave + kWaves - 1) / kWaves : 0;
 
-  auto score_tile = [&](const uint4* kb, f32x4* acc) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 b = __builtin_bit_cast(bf16x8, kb[ks]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][ks], b, acc[mt], 0, 0, 0);
-    }
-    float part = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part = fmaf(wr[mt][i], fmaxf(acc[mt][i], 0.0f), part);
-    part += __shfl_xor(part, 16, kWave);
-    part += __shfl_xor(part, 32, kWave);
-    return part;
-  };
-  auto norm2 = [&](const uint4* kb) {
-    float k2 = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t wds[4] = {kb[ks].x, kb[ks].y, kb[ks].z, kb[ks].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float lo = __uint_as_float(wds[j] << 16), hi = __uint_as_float(wds[j] & 0xFFFF0000u);
-        k2 = fmaf(lo, lo, k2);
-        k2 = fmaf(hi, hi, k2);
-      }
-    }
-    k2 += __shfl_xor(k2, 16, kWave);
-    k2 += __shfl_xor(k2, 32, kWave);
-    return k2;
-  };
-
-  // Block batch: 8 groups -> 16 block keys in s_bkey[wave], scored by one MFMA tile.
-  auto flush_blocks = [&](int nfill) {
-    if constexpr (POOL) {
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      // slot n = (group t = n/2 of the batch, block j = n%2)
-      const int t = n >> 1, j = n & 1;
-      const int gi = wave + kWaves * (batch_first + t);
-      const int blk = (c0 >> 3) + 2 * gi + j;
-      const bool valid = t < nfill && blk < nblk;
-      uint4 kb[KS];
-      const uint4* row = s_bkey + (wave * 16 + n) * U4 + g * KS;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kb[ks] = row[ks];
-      f32x4 acc[MT];
-      float a = score_tile(kb, acc);
-      float k2 = norm2(kb);
-      if (valid) {
-        if (g == 0) {
-          scb[blk] = a;
-          atomicAdd(&s_hist_b[sortable(a) >> kBinShift], 1u);
-        }
-        mk2b = fmaxf(mk2b, k2);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-    }
-  };
-
-  for (int it = 0;; ++it) {
-    const int gi = wave + kWaves * it;
-    if (gi >= ngroups) break;
-    const int cand = c0 + 16 * gi + n;
-    bool valid;
+  // Row of the key that lane (n, g) loads for local group `it` (the wave's
+  // it-th group), clamped to a visible row so that every load is in bounds
+  // and unconditional; `valid` says whether the key counts.
+  auto key_row = [&](int it, bool& valid) -> int64_t {
+    const int cand = c0 + 16 * (wave + kWaves * it) + n;
     int pos;
     if (INDIRECT) {
-      const int b = cand < nc ? P.pool_in[(size_t)q * P.keep_in + (cand >> 3)] : -1;
+      const int b = cand < nc ? s_pool[(cand - c0) >> 3] : -1;
       pos = b * 8 + (cand & 7);
       valid = b >= 0 && pos < nvis;
     } else {
       pos = cand;
       valid = cand < nc;
     }
+    return base + (valid ? pos : 0);
+  };
+  auto load = [&](int it, uint4* kb) {
+    bool v;
+    const uint4* src = reinterpret_cast<const uint4*>(P.ik + (size_t)key_row(min(it, my_groups - 1), v) * D + g * DPL);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kb[ks] = src[ks];
+  };
+
+  auto process = [&](int it, const uint4* kin) {
+    const int gi = wave + kWaves * it;
+    bool valid;
+    key_row(it, valid);
+    // zero the keys that do not count with a mask (straight-line code: a
+    // select here would become a branch and stall the load pipeline)
+    const uint32_t vm = valid ? 0xFFFFFFFFu : 0u;
     uint4 kb[KS];
-    const uint4* src = reinterpret_cast<const uint4*>(P.ik + (size_t)(base + (valid ? pos : 0)) * D + g * DPL);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kb[ks] = valid ? src[ks] : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks)
+      kb[ks] = make_uint4(kin[ks].x & vm, kin[ks].y & vm, kin[ks].z & vm, kin[ks].w & vm);
+    // S (16 keys x 16 heads per tile) = K . Q^T ; lane (n, g) gets keys 4g+i, head 16*mt+n
     f32x4 acc[MT];
-    float a = score_tile(kb, acc);
-    float k2 = norm2(kb);
-    if (g == 0 && cand < nc) {
-      sc[cand] = valid ? a : -INFINITY;
-      if (valid) atomicAdd(&s_hist[sortable(a) >> kBinShift], 1u);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, kb[ks]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[mt][ks], acc[mt], 0, 0, 0);
     }
-    if (valid) mk2 = fmaxf(mk2, k2);
-
+    // token scores of keys 4g..4g+3: this lane's MT heads, then the 16 lanes of the row
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) v = fmaf(wr[mt], fmaxf(acc[mt][i], 0.0f), v);
+      s[i] = sum16(v);
+    }
+    // squared key norm of key n (an upper bound is all the error bound needs)
+    float k2 = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t wd[4] = {kb[ks].x, kb[ks].y, kb[ks].z, kb[ks].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2 x = __builtin_bit_cast(bf16x2, wd[j]);
+        k2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, k2, false);
+      }
+    }
+    mk2 = fmaxf(mk2, k2);   // invalid keys were zeroed
+    // every lane stores one score: lanes n, n+4, n+8, n+12 write the same value
+    const int i0 = n & 3;
+    const int cand = c0 + 16 * gi + 4 * g + i0;
+    bool cvalid;
+    {
+      const float si = i0 == 0 ? s[0] : i0 == 1 ? s[1] : i0 == 2 ? s[2] : s[3];
+      if (INDIRECT) {
+        const int b = cand < nc ? s_pool[(cand - c0) >> 3] : -1;
+        cvalid = b >= 0 && b * 8 + (cand & 7) < nvis;
+      } else {
+        cvalid = cand < nc;
+      }
+      s_sc[cand - c0] = cvalid ? si : -INFINITY;
+      if (n < 4 && cvalid) atomicAdd(&s_hist[sortable(si) >> kBinShift], 1u);
+    }
     if constexpr (POOL) {
-      // stage the 16 keys (natural dim order) and average each block of 8
-      uint4* st = s_stage + (wave * 16 + n) * U4 + g * KS;
+      // block j = g/2 holds keys 8j..8j+7 = rows 4g+i of lane groups g and g^1
+      const int blk = ((c0 + 16 * gi) >> 3) + (g >> 1);
+      const int nb = min(max(nvis - 8 * blk, 0), 8);
+      const float inv = nb == 8 ? 0.125f : __builtin_amdgcn_rcpf((float)max(nb, 1));
+      float v = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) st[ks] = kb[ks];
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      const int j = lane >> 5;                 // block of the group
-      const int first = c0 + 16 * gi + 8 * j;  // its first position
-      const int nb = min(max(nvis - first, 0), 8);
-      const float inv_cnt = (float)nb;
-      const uint16_t* stage16 = reinterpret_cast<const uint16_t*>(s_stage + wave * 16 * U4);
-      uint16_t* bk16 = reinterpret_cast<uint16_t*>(s_bkey + (wave * 16 + 2 * batch_slot + j) * U4);
-      constexpr int DPB = D / 32;  // dims per lane for the block mean
-#pragma unroll
-      for (int e = 0; e < DPB; ++e) {
-        const int d = (lane & 31) * DPB + e;
-        float s = 0.0f;
-        for (int t = 0; t < nb; ++t) s = s + bf16_to_f32(stage16[(8 * j + t) * D + d]);
-        uint32_t kbar = nb ? f32_to_bf16_rne(__fdiv_rn(s, inv_cnt)) : 0u;
-        bk16[d] = (uint16_t)kbar;
+      for (int mt = 0; mt < MT; ++mt) {
+        float bsum = (acc[mt][0] + acc[mt][1]) + (acc[mt][2] + acc[mt][3]);
+        bsum += __shfl_xor(bsum, 16, kWave);
+        v = fmaf(wr[mt], fmaxf(bsum * inv, 0.0f), v);
       }
-      ++batch_slot;
-      if (batch_slot == 8) {
-        flush_blocks(8);
-        batch_slot = 0;
-        batch_first = it + 1;
+      const float bs = sum16(v);
+      // lanes of both lane groups of the block write the same value
+      s_scb[blk - (c0 >> 3)] = blk < nblk ? bs : -INFINITY;
+      if (lane == 0 || lane == 32) {
+        if (blk < nblk) atomicAdd(&s_hist_b[sortable(bs) >> kBinShift], 1u);
       }
     }
-  }
-  if constexpr (POOL) {
-    if (batch_slot > 0) flush_blocks(batch_slot);
-  }
+  };
 
-  // ---- publish histograms and key norms
+  // Software pipeline over this wave's groups with NBUF-1 groups in flight.
+  // The steady state is straight-line code (every load and store issued
+  // unconditionally), so the compiler waits only for the group it is about
+  // to use; the tail has no loads left to issue.
+  uint4 buf[NBUF][KS];
+  if (my_groups > 0) {
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b) {
+      load(b, buf[b]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  int it = 0;
+  for (; it + NBUF <= my_groups; it += NBUF) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      load(it + b + NBUF - 1, buf[(b + NBUF - 1) % NBUF]);
+      // keep the loads in issue order (vmcnt retires in order: a group loaded
+      // later must not be scheduled ahead of the one needed next)
+      __builtin_amdgcn_sched_barrier(0);
+      process(it + b, buf[b]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NBUF - 1; ++b)
+    if (it + b < my_groups) process(it + b, buf[b]);
+
+  // ---- publish scores, histograms and the key-norm maximum
   __syncthreads();
+  for (int i = tid; i < nslots; i += kThreads) sc[c0 + i] = s_sc[i];
+  if constexpr (POOL) {
+    const int nbs = min((nslots + 7) >> 3, max(nblk - (c0 >> 3), 0));
+    for (int i = tid; i < nbs; i += kThreads) scb[(c0 >> 3) + i] = s_scb[i];
+  }
   {
     uint32_t* gh = P.hist + (size_t)p * kNBins;
     for (int i = tid; i < kNBins; i += kThreads) {
-      uint32_t c = s_hist[i];
+      const uint32_t c = s_hist[i];
       if (c) atomicAdd(&gh[i], c);
       if (POOL) {
-        uint32_t cb = s_hist_b[i];
+        const uint32_t cb = s_hist_b[i];
         if (cb) atomicAdd(&P.hist[(size_t)pb * kNBins + i], cb);
       }
     }
     mk2 = wave_max(mk2);
-    mk2b = wave_max(mk2b);
-    if (lane == 0) {
-      s_tmp[wave] = __float_as_uint(mk2);
-      s_tmp[4 + wave] = __float_as_uint(mk2b);
-    }
+    if (lane == 0) s_tmp[wave] = __float_as_uint(mk2);
     __syncthreads();
     if (tid == 0) {
-      uint32_t m0 = 0, m1 = 0;
-      for (int i = 0; i < kWaves; ++i) {
-        m0 = max(m0, s_tmp[i]);
-        m1 = max(m1, s_tmp[4 + i]);
-      }
+      uint32_t m0 = 0;
+      for (int i = 0; i < kWaves; ++i) m0 = max(m0, s_tmp[i]);
       if (m0) atomicMax(&P.meta[p].maxk2, m0);
-      if (POOL && m1) atomicMax(&P.meta[pb].maxk2, m1);
     }
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t prev = atomic_inc_acq_rel(&P.meta[p].scan_done);
-    s_tmp[12] = (prev == gridDim.x - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!s_tmp[12]) return;
-  __threadfence();
-  wg_threshold(P, p, P.k, s_tmp);
-  if (POOL) {
-    __syncthreads();
-    wg_threshold(P, pb, P.keep_blocks, s_tmp);
   }
 }
 
-// ---------------------------------------------------------------- 3. compaction
+// ---------------------------------------------------------------- 3. threshold
+// One work-group per problem turns the scan's histogram into the band
+// threshold (kernel boundaries make the scan's histograms visible).
+__global__ __launch_bounds__(kThreads) void k_thresh(Params P) {
+  __shared__ uint32_t s_tmp[16];
+  const int p = blockIdx.x, q = p % P.n_q, kind = p / P.n_q;
+  // the token problem's scan holds the key-norm maximum; blocks use it too
+  const float kmax2 = __uint_as_float(P.meta[q].maxk2);
+  if (kind == 1) wg_threshold(P, p, P.keep_blocks, kmax2, P.bound_blk, s_tmp);
+  else wg_threshold(P, p, P.k, kmax2, P.bound_tok, s_tmp);
+}
+
+// ---------------------------------------------------------------- 4. compaction
 __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
   __shared__ uint32_t s_tmp[16];
-  __shared__ uint32_t s_hist[256];
   const int tid = threadIdx.x;
   const int p = blockIdx.y, chunk = blockIdx.x;
   const float thr = P.meta[p].thr;
@@ -493,7 +561,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
     const float4* s4 = reinterpret_cast<const float4*>(sc + my0);
 #pragma unroll
     for (int j = 0; j < kCmpPerThread / 4; ++j) {
-      float4 t = s4[j];
+      const float4 t = s4[j];
       v[4 * j] = t.x;
       v[4 * j + 1] = t.y;
       v[4 * j + 2] = t.z;
@@ -501,7 +569,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
     }
 #pragma unroll
     for (int j = 0; j < kCmpPerThread; ++j) {
-      bool keep = (my0 + j < nc) && v[j] != -INFINITY && v[j] >= thr;
+      const bool keep = (my0 + j < nc) && v[j] != -INFINITY && v[j] >= thr;
       flags |= (keep ? 1u : 0u) << j;
     }
   }
@@ -510,172 +578,285 @@ __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
   Entry* dst = P.band_a + (size_t)p * P.stride + c0;
 #pragma unroll
   for (int j = 0; j < kCmpPerThread; ++j)
-    if (flags & (1u << j)) dst[off++] = Entry{my0 + j, v[j]};
+    if (flags & (1u << j)) dst[off++] = Entry{(uint32_t)(my0 + j), v[j]};
   if (tid == 0) P.chunk_cnt[(size_t)p * P.nchunk_cmp + chunk] = total;
+}
 
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t prev = atomic_inc_acq_rel(&P.meta[p].cmp_done);
-    s_tmp[12] = (prev == gridDim.x - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!s_tmp[12]) return;
-  __threadfence();
-
-  // ---- last work-group: gather the band in position order
-  const int nch = gridDim.x;
+// ---------------------------------------------------------------- 5. band
+// One work-group per problem: gathers the chunks' survivors in position
+// order, finds a_K and a_K1 and splits the band into certain and uncertain
+// members.
+__global__ __launch_bounds__(kThreads) void k_band(Params P) {
+  __shared__ uint32_t s_tmp[16];
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_off[kMaxChunksLds + 1];
+  __shared__ uint32_t s_key[kBandLds];
+  const int tid = threadIdx.x;
+  const int p = blockIdx.x;
+  const int nch = P.nchunk_cmp;
   uint32_t* cnt = P.chunk_cnt + (size_t)p * P.nchunk_cmp;
+  const bool lds_off = nch <= kMaxChunksLds;
   uint32_t carry = 0;
   for (int t0 = 0; t0 < nch; t0 += kThreads) {
     const int c = t0 + tid;
-    uint32_t cv = c < nch ? cnt[c] : 0u;
+    const uint32_t cv = c < nch ? cnt[c] : 0u;
     uint32_t tt;
-    uint32_t ex = wg_exclusive_scan(cv, s_tmp, &tt);
-    if (c < nch) cnt[c] = carry + ex;   // now the exclusive offset
+    const uint32_t ex = wg_exclusive_scan(cv, s_tmp, &tt);
+    if (c < nch) {
+      if (lds_off) s_off[c] = carry + ex;
+      else cnt[c] = carry + ex;
+    }
     carry += tt;
-    __syncthreads();
   }
+  if (lds_off && tid == 0) s_off[nch] = carry;
   __threadfence_block();
   __syncthreads();
   const uint32_t nband = carry;
-  Entry* ba = P.band_a + (size_t)p * P.stride;
-  Entry* bb = P.band_b + (size_t)p * P.stride;
-  for (int c = tid; c < nch; c += kThreads) {
-    const uint32_t o = cnt[c];
-    const uint32_t e = (c + 1 < nch) ? cnt[c + 1] : nband;
-    const Entry* src = ba + (size_t)c * kCmpChunk;
-    for (uint32_t i = 0; i < e - o; ++i) bb[o + i] = src[i];
+  const Entry* __restrict__ ba = P.band_a + (size_t)p * P.stride;
+  Entry* __restrict__ bb = P.band_b + (size_t)p * P.stride;
+  if (lds_off) {
+    // flat copy: output j comes from the chunk whose offset range holds it
+    for (uint32_t j0 = 0; j0 < nband; j0 += 4 * kThreads) {
+      Entry e[4];
+      uint32_t jj[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        jj[u] = j0 + u * kThreads + tid;
+        if (jj[u] < nband) {
+          int lo = 0, hi = nch - 1;  // largest c with s_off[c] <= j
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= jj[u]) lo = mid;
+            else hi = mid - 1;
+          }
+          e[u] = ba[(size_t)lo * kCmpChunk + (jj[u] - s_off[lo])];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (jj[u] < nband) bb[jj[u]] = e[u];
+    }
+  } else {
+    for (int c = tid; c < nch; c += kThreads) {
+      const uint32_t o = cnt[c];
+      const uint32_t e = (c + 1 < nch) ? cnt[c + 1] : nband;
+      for (uint32_t i = 0; i < e - o; ++i) bb[o + i] = ba[(size_t)c * kCmpChunk + i];
+    }
   }
   __threadfence_block();
   __syncthreads();
 
   const int kind = p / P.n_q;
   const int K = (kind == 1) ? P.keep_blocks : P.k;
-  uint32_t n2 = 0;
+  Entry* __restrict__ b2 = P.band_a + (size_t)p * P.stride;   // the chunk staging area is free now
+  uint32_t* __restrict__ unc = P.unc + (size_t)p * P.stride;
+  const bool in_lds = nband <= (uint32_t)kBandLds;
+  if (in_lds)
+    for (uint32_t i = tid; i < nband; i += kThreads) s_key[i] = sortable(bb[i].s);
+  __syncthreads();
+  auto key = [&](int i) { return in_lds ? s_key[i] : sortable(bb[i].s); };
+  uint32_t n2 = 0, nu = 0;
   if (nband > (uint32_t)K) {
+    const float delta = P.meta[p].delta;
     uint32_t ties;
-    uint32_t kth = wg_kth_largest((int)nband, K, [&](int i) { return sortable(bb[i].s); }, s_hist,
-                                  s_tmp, &ties);
-    const float thr2 = band_below(unsortable(kth), P.meta[p].delta);
-    // order-preserving compaction bb -> ba of entries >= thr2
-    for (uint32_t t0 = 0; t0 < nband; t0 += kThreads) {
-      const uint32_t i = t0 + tid;
-      Entry e = i < nband ? bb[i] : Entry{0, 0.0f};
-      const uint32_t keep = (i < nband && e.s >= thr2) ? 1u : 0u;
-      uint32_t tt;
-      uint32_t ex = wg_exclusive_scan(keep, s_tmp, &tt);
-      if (keep) ba[n2 + ex] = e;
-      n2 += tt;
+    const uint32_t kth = wg_kth_largest((int)nband, K, key, s_hist, s_tmp, &ties);
+    // (K+1)-th largest: kth again if more entries equal it than the Top-K takes
+    uint32_t eq = 0;
+    for (uint32_t i = tid; i < nband; i += kThreads) eq += key(i) == kth ? 1u : 0u;
+    uint32_t eq_tot;
+    wg_exclusive_scan(eq, s_tmp, &eq_tot);
+    const uint32_t k1 = (eq_tot > ties) ? kth : wg_max_below((int)nband, kth, key, s_tmp);
+    // keep >= a_K - 2 Delta; certain > a_K1 + 2 Delta (compared as sortable keys)
+    const uint32_t keep_key = sortable(band_below(unsortable(kth), delta));
+    const uint32_t in_key = (k1 == 0) ? 0xFFFFFFFFu : sortable(band_above(unsortable(k1), delta));
+    // contiguous range per thread: count, scan, then write in order
+    const uint32_t per = (nband + kThreads - 1) / kThreads;
+    const uint32_t i0 = min(nband, tid * per), i1 = min(nband, i0 + per);
+    uint32_t ck = 0, cu = 0;
+    for (uint32_t i = i0; i < i1; ++i) {
+      const uint32_t kk = key(i);
+      ck += kk >= keep_key ? 1u : 0u;
+      cu += (kk >= keep_key && kk <= in_key) ? 1u : 0u;
     }
+    uint32_t tk, tu;
+    uint32_t ok = wg_exclusive_scan(ck, s_tmp, &tk);
+    uint32_t ou = wg_exclusive_scan(cu, s_tmp, &tu);
+    for (uint32_t i = i0; i < i1; ++i) {
+      const uint32_t kk = key(i);
+      if (kk >= keep_key) {
+        Entry e = bb[i];
+        if (kk > in_key) e.cand |= kCertain;
+        else unc[ou++] = ok;
+        b2[ok++] = e;
+      }
+    }
+    n2 = tk;
+    nu = tu;
   } else {
-    for (uint32_t i = tid; i < nband; i += kThreads) ba[i] = bb[i];
+    for (uint32_t i = tid; i < nband; i += kThreads) {
+      Entry e = bb[i];
+      e.cand |= kCertain;
+      b2[i] = e;
+    }
     n2 = nband;
   }
   if (tid == 0) {
     P.meta[p].nband = (int)nband;
     P.meta[p].nband2 = (int)n2;
+    P.meta[p].nunc = (int)nu;
+    P.meta[p].nin = (int)(n2 - nu);
   }
 }
 
-// ---------------------------------------------------------------- 4. rescoring
+// ---------------------------------------------------------------- 6. rescoring
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
   constexpr int DW = D / 2;  // packed bf16 pairs per head row
-  __shared__ float s_key[kWaves][D];
+  __shared__ float s_key[kWaves][8][D];
   __shared__ float s_r[kWaves][64];
   __shared__ float s_w[64];
-  __shared__ uint32_t s_tmp[16];
-  __shared__ uint32_t s_hist[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int p = blockIdx.y, q = p % P.n_q, kind = p / P.n_q;
   const int nvis = P.q_nvis[q];
   const int64_t base = P.seq_base[P.q_seq[q]];
-  const int n2 = P.meta[p].nband2;
-  Entry* ba = P.band_a + (size_t)p * P.stride;
+  const int nu = P.meta[p].nunc;
+  Entry* b2 = P.band_a + (size_t)p * P.stride;
+  const uint32_t* unc = P.unc + (size_t)p * P.stride;
 
   if (tid < 64) s_w[tid] = tid < P.h_i ? P.w[(size_t)q * P.h_i + tid] : 0.0f;
   uint32_t qrow[DW];
   {
     const int hh = lane < P.h_i ? lane : 0;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(P.iq + ((size_t)q * P.h_i + hh) * D);
+    const uint4* src = reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + hh) * D);
 #pragma unroll
-    for (int i = 0; i < DW; ++i) qrow[i] = src[i];
+    for (int i = 0; i < DW / 4; ++i) {
+      const uint4 v = src[i];
+      qrow[4 * i] = v.x;
+      qrow[4 * i + 1] = v.y;
+      qrow[4 * i + 2] = v.z;
+      qrow[4 * i + 3] = v.w;
+    }
   }
   __syncthreads();
 
-  const int stride_w = gridDim.x * kWaves;
-  for (int j = blockIdx.x * kWaves + wave; j < n2; j += stride_w) {
-    const int cand = ba[j].cand;
-    if (kind == 1) {
-      // block key: sequential fp32 sum of the visible keys, / count, bf16 nearest-even
-      const int first = cand * 8;
-      const int nb = min(nvis - first, 8);
-      for (int d = lane; d < D; d += 64) {
-        float s = 0.0f;
-        for (int t = 0; t < nb; ++t) s = s + bf16_to_f32(P.ik[(size_t)(base + first + t) * D + d]);
-        s_key[wave][d] = bf16_to_f32(f32_to_bf16_rne(__fdiv_rn(s, (float)nb)));
-      }
-    } else {
-      const int pos = cand_pos(P, q, kind, cand);
-      for (int d = lane; d < D; d += 64) s_key[wave][d] = bf16_to_f32(P.ik[(size_t)(base + pos) * D + d]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
+  auto head_dot = [&](const float* key) {
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < DW; ++i) {
-      acc = fmaf(__uint_as_float(qrow[i] << 16), s_key[wave][2 * i], acc);
-      acc = fmaf(__uint_as_float(qrow[i] & 0xFFFF0000u), s_key[wave][2 * i + 1], acc);
+      acc = fmaf(__uint_as_float(qrow[i] << 16), key[2 * i], acc);
+      acc = fmaf(__uint_as_float(qrow[i] & 0xFFFF0000u), key[2 * i + 1], acc);
     }
-    s_r[wave][lane] = acc > 0.0f ? acc : 0.0f;
+    return acc;
+  };
+
+  const int stride_w = gridDim.x * kWaves;
+  for (int j = blockIdx.x * kWaves + wave; j < nu; j += stride_w) {
+    const uint32_t slot = unc[j];
+    const uint32_t cand = b2[slot].cand & ~kCertain;
+    int first, nmem;
+    if (kind == 1) {
+      first = (int)cand * 8;
+      nmem = min(nvis - first, 8);
+    } else {
+      first = cand_pos(P, q, kind, cand);
+      nmem = 1;
+    }
+    // members' keys -> LDS (fp32)
+    for (int e = lane; e < nmem * (D / 2); e += 64) {
+      const int t = e / (D / 2), d2 = e % (D / 2);
+      const uint32_t wv = reinterpret_cast<const uint32_t*>(P.ik + (size_t)(base + first + t) * D)[d2];
+      s_key[wave][t][2 * d2] = __uint_as_float(wv << 16);
+      s_key[wave][t][2 * d2 + 1] = __uint_as_float(wv & 0xFFFF0000u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    float r;
+    if (kind == 1) {
+      float sum = 0.0f;
+      for (int t = 0; t < nmem; ++t) sum = sum + head_dot(s_key[wave][t]);
+      const float mean = __fdiv_rn(sum, (float)nmem);
+      r = mean > 0.0f ? mean : 0.0f;
+    } else {
+      const float acc = head_dot(s_key[wave][0]);
+      r = acc > 0.0f ? acc : 0.0f;
+    }
+    s_r[wave][lane] = r;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     __builtin_amdgcn_wave_barrier();
     if (lane == 0) {
       float s = 0.0f;
       for (int h = 0; h < P.h_i; ++h) s = fmaf(s_w[h], s_r[wave][h], s);
-      ba[j].s = s;
+      b2[slot].s = s;
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     __builtin_amdgcn_wave_barrier();
   }
 
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t prev = atomic_inc_acq_rel(&P.meta[p].rs_done);
-    s_tmp[12] = (prev == gridDim.x - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!s_tmp[12]) return;
-  __threadfence();
+}
 
-  // ---- last work-group: exact Top-K of the band, ascending positions
+// ---------------------------------------------------------------- 7. final
+// One work-group per problem: the certain members plus the best rescored
+// ones, written as ascending positions and padded with -1.
+__global__ __launch_bounds__(kThreads) void k_final(Params P) {
+  __shared__ uint32_t s_tmp[16];
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_ukey[kBandLds];
+  const int tid = threadIdx.x;
+  const int p = blockIdx.x, q = p % P.n_q, kind = p / P.n_q;
+  const int nu = P.meta[p].nunc;
+  const Entry* b2 = P.band_a + (size_t)p * P.stride;
+  const uint32_t* unc = P.unc + (size_t)p * P.stride;
   const int K = (kind == 1) ? P.keep_blocks : P.k;
   int32_t* out = (kind == 1) ? P.pool_out + (size_t)q * P.keep_blocks : P.idx_out + (size_t)q * P.k;
+  const int n2 = P.meta[p].nband2;
+  const int need = K - P.meta[p].nin;
+  const bool take_none = need <= 0;
+  const bool take_all = !take_none && nu <= need;
+  const bool in_lds = nu <= kBandLds;
+  if (in_lds)
+    for (int i = tid; i < nu; i += kThreads) s_ukey[i] = sortable(b2[unc[i]].s);
+  __syncthreads();
   uint32_t kth = 0, ties = 0;
-  const bool all = n2 <= K;
-  if (!all) kth = wg_kth_largest(n2, K, [&](int i) { return sortable(ba[i].s); }, s_hist, s_tmp, &ties);
-  uint32_t nsel = 0, nties = 0;
-  for (int t0 = 0; t0 < n2; t0 += kThreads) {
-    const int i = t0 + tid;
-    uint32_t key = 0;
-    int cand = 0;
-    if (i < n2) {
-      key = sortable(ba[i].s);
-      cand = ba[i].cand;
+  if (!take_all && !take_none)
+    kth = wg_kth_largest(nu, need, [&](int i) { return in_lds ? s_ukey[i] : sortable(b2[unc[i]].s); },
+                         s_hist, s_tmp, &ties);
+  // contiguous range per thread of the (position-ordered) band.  Pass 1 counts
+  // the entries tied at the cut, pass 2 the kept ones, pass 3 writes; the tie
+  // rank of an entry is its rank among tied entries in position order, so the
+  // lower positions win the ties.
+  const int per = (n2 + kThreads - 1) / kThreads;
+  const int i0 = min(n2, tid * per), i1 = min(n2, i0 + per);
+  const bool cut = !take_all && !take_none;
+  auto decide = [&](const Entry& e, uint32_t& rank) {
+    if (e.cand & kCertain) return true;
+    if (take_none) return false;
+    if (take_all) return true;
+    const uint32_t key = sortable(e.s);
+    if (key > kth) return true;
+    if (key == kth) return rank++ < ties;
+    return false;
+  };
+  uint32_t nt = 0;
+  if (cut)
+    for (int i = i0; i < i1; ++i) {
+      const Entry e = b2[i];
+      nt += (!(e.cand & kCertain) && sortable(e.s) == kth) ? 1u : 0u;
     }
-    const uint32_t is_tie = (!all && i < n2 && key == kth) ? 1u : 0u;
-    uint32_t tt;
-    const uint32_t tie_rank = nties + wg_exclusive_scan(is_tie, s_tmp, &tt);
-    nties += tt;
-    const uint32_t keep = (i < n2 && (all || key > kth || (is_tie && tie_rank < ties))) ? 1u : 0u;
-    uint32_t kt;
-    const uint32_t ex = wg_exclusive_scan(keep, s_tmp, &kt);
-    if (keep) out[nsel + ex] = (kind == 1) ? cand : cand_pos(P, q, kind, cand);
-    nsel += kt;
+  uint32_t tot_t;
+  const uint32_t tie_base = wg_exclusive_scan(nt, s_tmp, &tot_t);
+  uint32_t cnt = 0, rank = tie_base;
+  for (int i = i0; i < i1; ++i) cnt += decide(b2[i], rank) ? 1u : 0u;
+  uint32_t tot;
+  uint32_t o = wg_exclusive_scan(cnt, s_tmp, &tot);
+  rank = tie_base;
+  for (int i = i0; i < i1; ++i) {
+    const Entry e = b2[i];
+    if (decide(e, rank)) {
+      const uint32_t cand = e.cand & ~kCertain;
+      out[o++] = (kind == 1) ? (int)cand : cand_pos(P, q, kind, cand);
+    }
   }
-  for (int i = (int)nsel + tid; i < K; i += kThreads) out[i] = -1;
+  for (int i = (int)tot + tid; i < K; i += kThreads) out[i] = -1;
 }
 
 }  // namespace idx
@@ -690,11 +871,13 @@ using namespace csa2::idx;
 namespace {
 
 thread_local int g_last_hip_error = 0;
+thread_local hipEvent_t g_scan_ev_start = nullptr;
+thread_local hipEvent_t g_scan_ev_stop = nullptr;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t scores, hist, meta, chunk_cnt, band_a, band_b, total;
+  size_t scores, hist, meta, chunk_cnt, band_a, band_b, unc, total;
 };
 
 Layout make_layout(int nprob, int64_t stride, int nchunk_cmp) {
@@ -712,6 +895,8 @@ Layout make_layout(int nprob, int64_t stride, int nchunk_cmp) {
   o = align256(o + (size_t)nprob * stride * sizeof(Entry));
   L.band_b = o;
   o = align256(o + (size_t)nprob * stride * sizeof(Entry));
+  L.unc = o;
+  o = align256(o + (size_t)nprob * stride * sizeof(uint32_t));
   L.total = o;
   return L;
 }
@@ -720,18 +905,20 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 double gamma_n(double n, double u) { return n * u / (1.0 - n * u); }
 
-// Delta = C * QW * max||k||: C covers the fp32 fma chain of the exact score
-// (unit roundoff 2^-24) and any MFMA accumulation order or truncation (2^-23),
-// for the d_i-term dot products and the head sum, doubled for safety.
-float bound_constant(int h_i, int d_i) {
+// Delta = C * QW * max||k||.  C covers the exact score's fp32 fma chain (unit
+// roundoff 2^-24) and any MFMA accumulation order or truncation (2^-23) of the
+// d_i-term dot products, the head sum, and for blocks the 8-term member sums
+// and the division by the member count; doubled for safety.
+float bound_constant(int d_i, bool block) {
   const double u = std::ldexp(1.0, -24), u2 = std::ldexp(1.0, -23);
-  const double gd = gamma_n(d_i, u), gm = gamma_n(d_i + 2, u2);
-  const double gh = gamma_n(std::max(h_i, 66), u);
-  return (float)(2.0 * (gd + gm + gh * (2.0 + gd + gm)));
+  double e = gamma_n(d_i, u) + gamma_n(d_i + 2, u2);
+  if (block) e += 2.0 * gamma_n(8, u) + 8.0 * u;
+  const double gh = gamma_n(66, u);
+  return (float)(2.0 * (e + gh * (2.0 + e)));
 }
 
 bool launch_ok() {
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return false;
@@ -741,19 +928,18 @@ bool launch_ok() {
 
 template <int D>
 void launch_scan(const Params& P, int mt, bool pool, bool indirect, dim3 grid, hipStream_t s) {
-#define CSA2_SCAN(MTV)                                                                   \
-  if (mt == MTV) {                                                                       \
-    if (indirect) hipLaunchKernelGGL((k_scan<D, MTV, false, true>), grid, dim3(kThreads), 0, s, P);  \
-    else if (pool) hipLaunchKernelGGL((k_scan<D, MTV, true, false>), grid, dim3(kThreads), 0, s, P); \
-    else hipLaunchKernelGGL((k_scan<D, MTV, false, false>), grid, dim3(kThreads), 0, s, P);         \
-    return;                                                                              \
+#define CSA2_SCAN(MTV)                                                                                      \
+  if (mt == MTV) {                                                                                          \
+    if (indirect) hipLaunchKernelGGL((k_scan<D, MTV, false, true>), grid, dim3(kThreads), 0, s, P);        \
+    else if (pool) hipLaunchKernelGGL((k_scan<D, MTV, true, false>), grid, dim3(kThreads), 0, s, P);       \
+    else hipLaunchKernelGGL((k_scan<D, MTV, false, false>), grid, dim3(kThreads), 0, s, P);                \
+    return;                                                                                                 \
   }
   CSA2_SCAN(1) CSA2_SCAN(2) CSA2_SCAN(3) CSA2_SCAN(4)
 #undef CSA2_SCAN
 }
 
-csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes, hipStream_t s,
-                         size_t need) {
+csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes, hipStream_t s, size_t need) {
   if (ws_bytes < need) return CSA2_E_WORKSPACE;
   const Layout L = make_layout(P.nprob, P.stride, P.nchunk_cmp);
   char* w = static_cast<char*>(ws);
@@ -763,21 +949,34 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   P.chunk_cnt = reinterpret_cast<uint32_t*>(w + L.chunk_cnt);
   P.band_a = reinterpret_cast<Entry*>(w + L.band_a);
   P.band_b = reinterpret_cast<Entry*>(w + L.band_b);
-  P.bound_c = bound_constant(P.h_i, P.d_i);
+  P.unc = reinterpret_cast<uint32_t*>(w + L.unc);
+  P.bound_tok = bound_constant(P.d_i, false);
+  P.bound_blk = bound_constant(P.d_i, true);
 
   const int mt = (P.h_i + 15) / 16;
   const bool pool = !P.reindex && P.keep_blocks > 0;
-  hipLaunchKernelGGL(k_prologue, dim3(P.nprob), dim3(kThreads), 0, s, P);
+  if (P.d_i == 128) hipLaunchKernelGGL(k_prologue<128>, dim3(P.nprob), dim3(kThreads), 0, s, P);
+  else hipLaunchKernelGGL(k_prologue<64>, dim3(P.nprob), dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
   const int nx = (int)std::max<int64_t>(1, (max_slots + P.scan_chunk - 1) / P.scan_chunk);
   const dim3 gscan(nx, P.n_q);
+  hipEvent_t ev0 = g_scan_ev_start, ev1 = g_scan_ev_stop;
+  g_scan_ev_start = g_scan_ev_stop = nullptr;
+  if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return CSA2_E_HIP;
   if (P.d_i == 128) launch_scan<128>(P, mt, pool, P.reindex, gscan, s);
   else launch_scan<64>(P, mt, pool, P.reindex, gscan, s);
   if (!launch_ok()) return CSA2_E_HIP;
+  if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return CSA2_E_HIP;
+  hipLaunchKernelGGL(k_thresh, dim3(P.nprob), dim3(kThreads), 0, s, P);
+  if (!launch_ok()) return CSA2_E_HIP;
   hipLaunchKernelGGL(k_compact, dim3(P.nchunk_cmp, P.nprob), dim3(kThreads), 0, s, P);
+  if (!launch_ok()) return CSA2_E_HIP;
+  hipLaunchKernelGGL(k_band, dim3(P.nprob), dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
   if (P.d_i == 128) hipLaunchKernelGGL(k_rescore<128>, dim3(kRescoreWGs, P.nprob), dim3(kThreads), 0, s, P);
   else hipLaunchKernelGGL(k_rescore<64>, dim3(kRescoreWGs, P.nprob), dim3(kThreads), 0, s, P);
+  if (!launch_ok()) return CSA2_E_HIP;
+  hipLaunchKernelGGL(k_final, dim3(P.nprob), dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
   return CSA2_OK;
 }
@@ -790,8 +989,13 @@ bool shape_ok(int h_i, int d_i) { return h_i >= 1 && h_i <= 64 && (d_i == 64 || 
 
 extern "C" int csa2_internal_last_hip_error_index(void) { return g_last_hip_error; }
 
-extern "C" size_t csa2_index_topk_ws_bytes(int n_q, int32_t max_nvis, int h_i, int d_i, int k,
-                                           int block, int keep_blocks) {
+extern "C" void csa2_record_scan_events(void* start, void* stop) {
+  g_scan_ev_start = static_cast<hipEvent_t>(start);
+  g_scan_ev_stop = static_cast<hipEvent_t>(stop);
+}
+
+extern "C" size_t csa2_index_topk_ws_bytes(int n_q, int32_t max_nvis, int h_i, int d_i, int k, int block,
+                                           int keep_blocks) {
   (void)h_i; (void)d_i; (void)k; (void)block;
   if (n_q <= 0) return 0;
   const int nprob = n_q * (keep_blocks > 0 ? 2 : 1);
@@ -808,9 +1012,9 @@ extern "C" size_t csa2_reindex_topk_ws_bytes(int n_q, int h_i, int d_i, int k, i
 
 extern "C" csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
                                        const int32_t* q_seq, const int32_t* q_nvis, int32_t max_nvis,
-                                       const uint16_t* ik, const int64_t* seq_base, int k,
-                                       int32_t* idx_out, int block, int keep_blocks, int32_t* pool_out,
-                                       void* ws, size_t ws_bytes, void* stream) {
+                                       const uint16_t* ik, const int64_t* seq_base, int k, int32_t* idx_out,
+                                       int block, int keep_blocks, int32_t* pool_out, void* ws, size_t ws_bytes,
+                                       void* stream) {
   if (n_q < 0 || max_nvis < 0 || max_nvis > 0x7FFFFFF0 || k < 1 || k > 2048 || keep_blocks < 0 ||
       keep_blocks > 4096)
     return CSA2_E_INVAL;
@@ -837,14 +1041,13 @@ extern "C" csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n
 extern "C" csa2_status csa2_reindex_topk(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
                                          const int32_t* q_seq, const int32_t* q_nvis, const uint16_t* ik,
                                          const int64_t* seq_base, const int32_t* pool_blocks, int block,
-                                         int keep_blocks, int k, int32_t* idx_out, void* ws,
-                                         size_t ws_bytes, void* stream) {
+                                         int keep_blocks, int k, int32_t* idx_out, void* ws, size_t ws_bytes,
+                                         void* stream) {
   if (n_q < 0 || k < 1 || k > 2048 || keep_blocks < 1 || keep_blocks > 4096) return CSA2_E_INVAL;
   if (!shape_ok(h_i, d_i)) return CSA2_E_UNSUPPORTED;
   if (block != 8) return CSA2_E_UNSUPPORTED;
   if (n_q == 0) return CSA2_OK;
-  if (!iq || !w || !q_seq || !q_nvis || !ik || !seq_base || !pool_blocks || !idx_out || !ws)
-    return CSA2_E_INVAL;
+  if (!iq || !w || !q_seq || !q_nvis || !ik || !seq_base || !pool_blocks || !idx_out || !ws) return CSA2_E_INVAL;
   if (!aligned(iq, 16) || !aligned(ik, 16) || !aligned(w, 4) || !aligned(ws, 256)) return CSA2_E_INVAL;
   Params P{};
   P.iq = iq; P.w = w; P.n_q = n_q; P.h_i = h_i; P.d_i = d_i;
@@ -853,7 +1056,7 @@ extern "C" csa2_status csa2_reindex_topk(const uint16_t* iq, const float* w, int
   P.idx_out = idx_out; P.pool_out = nullptr;
   P.nprob = n_q;
   P.reindex = 1;
-  P.scan_chunk = 512;
+  P.scan_chunk = 256;
   const int64_t slots = 8LL * keep_blocks;
   P.stride = round_up(slots, kCmpChunk);
   P.nchunk_cmp = (int)(P.stride / kCmpChunk);

@@ -1,0 +1,96 @@
+"""Static per-layer CSA2 schedules and a decode-step driver.
+
+Every CSA2 layer has a fixed mode: Full (own main KV, fresh Top-512),
+Reindex (re-scores the last Full layer's keys with its own indexer query) or
+Reuse (takes the group head's Top-K list, no indexer).  The decoder's 20
+layers form 5 groups of 4: Full + 3 Reuse, then 4 x (Reindex + 3 Reuse); the
+encoder's CSA2 layers form groups of 1 Full + 5 Reuse.  Source: "DeepSeek AI
+выпустила DeepSeek-V4.1-Flash с контекстом в 1 млн токенов, KV-кэшем FP4 ..."
+(wire.sakhanda.co), section "Сжатое разреженное внимание 2 (CSA2)".
+
+The driver only sequences the C-ABI calls of one decode step; all arithmetic
+runs in libcsa2.so.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import index_topk, quant_append, reindex_topk, sparse_attn, Workspace
+
+FULL, REINDEX, REUSE = "full", "reindex", "reuse"
+
+
+def decoder_schedule() -> list[str]:
+    """The 20 decoder layers: [Full, Reuse x3] + 4 x [Reindex, Reuse x3]."""
+    return [FULL, REUSE, REUSE, REUSE] + [REINDEX, REUSE, REUSE, REUSE] * 4
+
+
+def encoder_group() -> list[str]:
+    """One encoder group: 1 Full + 5 Reuse."""
+    return [FULL] + [REUSE] * 5
+
+
+@dataclass
+class LayerInputs:
+    """Per-layer tensors: each layer owns its main query and its window rows;
+    Full/Reindex layers also own an indexer query and head weights."""
+    mode: str
+    q: torch.Tensor                       # [n_q, h, 512] fp32 | bf16
+    swa: torch.Tensor                     # [rows, 512] bf16
+    swa_row0: torch.Tensor                # [n_q] int64
+    swa_len: torch.Tensor                 # [n_q] int32
+    iq: torch.Tensor | None = None        # [n_q, h_i, d_i] bf16
+    w: torch.Tensor | None = None         # [n_q, h_i] f32
+
+
+@dataclass
+class DecodeState:
+    """Shared tensors of one decode batch: the FP4 main KV and the indexer keys
+    written by the Full layer, and the per-query sequence bookkeeping."""
+    cache: torch.Tensor                   # [rows, 288] uint8
+    ik: torch.Tensor                      # [rows, d_i] bf16
+    seq_base: torch.Tensor                # [n_seq] int64
+    q_seq: torch.Tensor                   # [n_q] int32
+    q_nvis: torch.Tensor                  # [n_q] int32
+    max_nvis: int
+    k: int = 512
+    keep_blocks: int = 2048               # pool size built by the Full layer (0: none)
+    w_max: int = 128
+    softmax_scale: float = 512 ** -0.5
+    ws_index: Workspace = field(default_factory=Workspace)
+    ws_attn: Workspace = field(default_factory=Workspace)
+
+
+def decode_step(st: DecodeState, layers: list[LayerInputs], append_x=None, append_rows=None,
+                scan_events=None, keep_outputs=True):
+    """Run one decode step over `layers`.  append_x/append_rows: new main-KV
+    rows quantised into the cache before the Full layer indexes.  Returns a
+    list of (idx, out, lse) per layer (idx shared by a group's Reuse layers)."""
+    from . import record_scan_events
+    if append_x is not None:
+        quant_append(append_x, append_rows, st.cache)
+    results = []
+    idx = pool = None
+    for lay in layers:
+        if lay.mode == FULL:
+            if scan_events is not None:
+                record_scan_events(*scan_events)
+            r = index_topk(lay.iq, lay.w, st.q_seq, st.q_nvis, st.max_nvis, st.ik, st.seq_base, k=st.k,
+                           keep_blocks=st.keep_blocks, ws=st.ws_index)
+            idx, pool = (r if st.keep_blocks else (r, None))
+        elif lay.mode == REINDEX:
+            if pool is None:
+                raise ValueError("a Reindex layer needs a preceding Full layer that built a pool")
+            idx = reindex_topk(lay.iq, lay.w, st.q_seq, st.q_nvis, st.ik, st.seq_base, pool, k=st.k,
+                               ws=st.ws_index)
+        elif lay.mode != REUSE:
+            raise ValueError(f"unknown layer mode {lay.mode}")
+        if idx is None:
+            raise ValueError("a Reuse layer needs a preceding Full or Reindex layer")
+        out, lse = sparse_attn(lay.q, st.q_seq, st.cache, st.seq_base, idx, lay.swa, lay.swa_row0,
+                               lay.swa_len, st.w_max, st.softmax_scale, ws=st.ws_attn)
+        if keep_outputs:
+            results.append((idx, out, lse))
+    return results, pool
