@@ -118,7 +118,7 @@ csa2_status csa2_quant_append(const void* x, int x_dtype, int64_t n_rows,
  * scan runs on MFMA: candidates within a proven rounding bound of the cut
  * are re-scored with the exact fp32 chain before the final selection.
  * Supported: 1 <= h_i <= 64, d_i in {64, 128}, 1 <= k <= 2048,
- * 0 <= keep_blocks <= 4096, max_nvis < 2^31 - 16.  Alignment: iq, ik 16 B. */
+ * 0 <= keep_blocks <= 4096, max_nvis <= 2^25 (32M positions).  Alignment: iq, ik 16 B. */
 csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
                             const int32_t* q_seq, const int32_t* q_nvis, int32_t max_nvis,
                             const uint16_t* ik, const int64_t* seq_base,

@@ -59,6 +59,12 @@ __device__ __forceinline__ T wave_max(T v) {
   return v;
 }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  return v;
+}
+
 // Agent-scope acquire/release counter used by the "last work-group of a
 // problem finishes the job" pattern.
 __device__ __forceinline__ uint32_t atomic_inc_acq_rel(uint32_t* p) {

@@ -61,17 +61,24 @@ constexpr int kNBins = 4096;
 constexpr int kBinShift = 20;
 constexpr int kCmpChunk = 4096;
 constexpr int kCmpPerThread = kCmpChunk / kThreads;
-constexpr int kMaxChunksLds = 2048;
+constexpr int kMaxChunksLds = 8192;   // compaction chunks per problem (max_nvis <= 2^25)
 constexpr int kRescoreWGs = 64;
 constexpr int kMaxScanChunk = 4096;
-constexpr int kBandLds = 8192;       // band entries whose keys the last work-groups keep in LDS
+constexpr int kBandLds = 12288;      // band entries the final kernel keeps in LDS (96 KiB)
+constexpr int kUncLds = 4096;        // uncertain members whose keys the final kernel keeps in LDS
 constexpr uint32_t kCertain = 0x80000000u;
+constexpr uint32_t kAll = 0xFFFFFFFFu;
 
 struct Meta {
-  uint32_t scan_done, cmp_done, rs_done, maxk2;
-  float qw, wabs, thr, delta;
-  int32_t nc, nband, nband2, nunc, nin;
-  uint32_t pad[3];
+  uint32_t maxk2;   // scan (token problem): largest squared key norm, float bits
+  uint32_t bin;     // coarse bin holding the K-th score; kAll: every candidate is kept
+  uint32_t above;   // valid candidates in coarse bins above `bin`
+  uint32_t total;   // valid candidates
+  float qw, wabs, delta;
+  float keep_thr;   // band: approximate score >= keep_thr
+  float in_thr;     // certainly selected: approximate score > in_thr
+  int32_t nc;       // candidate slots
+  uint32_t pad[6];
 };
 static_assert(sizeof(Meta) == 64, "Meta is one 64-byte line");
 
@@ -101,12 +108,13 @@ struct Params {
   int nchunk_cmp;
   float bound_tok, bound_blk;
   float* scores;
-  uint32_t* hist;
+  uint32_t* hist;       // [nprob][kNBins] coarse histogram (top 12 bits of the key)
+  uint32_t* hist2;      // [nprob][kNBins] fine histogram inside the coarse bin `bin`
   Meta* meta;
-  uint32_t* chunk_cnt;
-  Entry* band_a;
-  Entry* band_b;
-  uint32_t* unc;
+  uint32_t* chunk_cnt;  // [nprob][nchunk_cmp] band members per chunk
+  uint32_t* chunk_unc;  // [nprob][nchunk_cmp] uncertain members per chunk
+  Entry* band;          // [nprob][stride] band members, chunk c at c*kCmpChunk, in position order
+  uint2* unc;           // [nprob][stride] uncertain members: {chunk-local index, candidate}
 };
 
 // ---------------------------------------------------------------- helpers
@@ -168,20 +176,48 @@ __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* s_tm
 }
 
 // K-th largest of the sortable keys key_of(i), i < n (1 <= K <= n): a
-// most-significant-digit radix select with 8-bit digits.  Returns the key; in
+// most-significant-digit radix select with 8-bit digits.  Band keys share
+// their leading bits, so the digits start at the highest bit where the
+// smallest and largest key differ: the first histogram then spreads over many
+// bins instead of piling every LDS atomic onto one.  Returns the key; in
 // *ties the number of entries equal to it that belong to the Top-K.
 template <typename KeyOf>
 __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist /*256*/,
                                    uint32_t* s_tmp, uint32_t* ties) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int i = tid; i < n; i += kThreads) {
+    const uint32_t key = key_of(i);
+    lo = min(lo, key);
+    hi = max(hi, key);
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max(hi);
+  if ((tid & 63) == 0) {
+    s_tmp[tid >> 6] = lo;
+    s_tmp[4 + (tid >> 6)] = hi;
+  }
+  __syncthreads();
+  lo = min(min(s_tmp[0], s_tmp[1]), min(s_tmp[2], s_tmp[3]));
+  hi = max(max(s_tmp[4], s_tmp[5]), max(s_tmp[6], s_tmp[7]));
+  __syncthreads();
+  if (lo == hi) {
+    *ties = (uint32_t)K;
+    return lo;
+  }
+  const int top = 31 - __clz(lo ^ hi);          // highest differing bit
+  uint32_t mask = top == 31 ? 0u : (0xFFFFFFFFu << (top + 1));
+  uint32_t prefix = lo & mask;
   uint32_t remaining = (uint32_t)K;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int shift = top - 7;; shift -= 8) {
+    const int sh = shift < 0 ? 0 : shift;
+    const int width = shift < 0 ? 8 + shift : 8;   // last digit may be narrower
+    const uint32_t dmask = (1u << width) - 1u;
     s_hist[tid] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += kThreads) {
       const uint32_t key = key_of(i);
-      if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+      if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
     }
     __syncthreads();
     // thread tid owns digit 255 - tid; the exclusive scan counts larger digits
@@ -195,29 +231,13 @@ __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist 
     __syncthreads();
     const uint32_t d = s_tmp[8];
     remaining -= s_tmp[9];
-    prefix |= d << shift;
-    mask |= 255u << shift;
+    prefix |= d << sh;
+    mask |= dmask << sh;
     __syncthreads();
+    if (sh == 0) break;
   }
   *ties = remaining;
   return prefix;
-}
-
-// Largest key_of(i) strictly below `below` (0 if none).
-template <typename KeyOf>
-__device__ uint32_t wg_max_below(int n, uint32_t below, KeyOf key_of, uint32_t* s_tmp) {
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    const uint32_t key = key_of(i);
-    if (key < below && key > m) m = key;
-  }
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) s_tmp[threadIdx.x >> 6] = m;
-  __syncthreads();
-  uint32_t r = 0;
-  for (int i = 0; i < kWaves; ++i) r = max(r, s_tmp[i]);
-  __syncthreads();
-  return r;
 }
 
 __device__ __forceinline__ int cand_pos(const Params& P, int q, int kind, uint32_t cand) {
@@ -235,7 +255,11 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void k_prologue(Params P) {
   const int p = blockIdx.x, q = p % P.n_q, kind = p / P.n_q;
   uint4* h = reinterpret_cast<uint4*>(P.hist + (size_t)p * kNBins);
-  for (int i = threadIdx.x; i < kNBins / 4; i += kThreads) h[i] = make_uint4(0, 0, 0, 0);
+  uint4* h2 = reinterpret_cast<uint4*>(P.hist2 + (size_t)p * kNBins);
+  for (int i = threadIdx.x; i < kNBins / 4; i += kThreads) {
+    h[i] = make_uint4(0, 0, 0, 0);
+    h2[i] = make_uint4(0, 0, 0, 0);
+  }
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     float qn = 0.0f, wa = 0.0f;
@@ -262,22 +286,24 @@ __global__ __launch_bounds__(kThreads) void k_prologue(Params P) {
     wa = wave_sum(wa);
     if (lane == 0) {
       Meta m;
-      m.scan_done = m.cmp_done = m.rs_done = m.maxk2 = 0;
+      m.maxk2 = 0;
+      m.bin = kAll;
+      m.above = m.total = 0;
       m.qw = qn * (1.0f + 0.0009765625f);
       m.wabs = wa;
-      m.thr = -INFINITY;
       m.delta = 0.0f;
+      m.keep_thr = m.in_thr = -INFINITY;
       const int nvis = P.q_nvis[q];
       m.nc = P.reindex ? 8 * P.keep_in : (kind == 0 ? nvis : (nvis + 7) / 8);
-      m.nband = m.nband2 = m.nunc = m.nin = 0;
-      m.pad[0] = m.pad[1] = m.pad[2] = 0;
+      for (int i = 0; i < 6; ++i) m.pad[i] = 0;
       P.meta[p] = m;
     }
   }
 }
 
-// Threshold from the global histogram of problem p (one work-group).
-__device__ void wg_threshold(const Params& P, int p, int K, float kmax2, float bound, uint32_t* s_tmp) {
+// Coarse step of the threshold (one work-group): the bin of the coarse
+// histogram that holds the K-th score, and how many candidates lie above it.
+__device__ void wg_coarse_bin(const Params& P, int p, int K, float kmax2, float bound, uint32_t* s_tmp) {
   const int tid = threadIdx.x;
   const uint32_t* h = P.hist + (size_t)p * kNBins;
   constexpr int kPer = kNBins / kThreads;  // 16 bins per thread, highest bins first
@@ -295,21 +321,20 @@ __device__ void wg_threshold(const Params& P, int p, int K, float kmax2, float b
   const float delta = bound * m.qw * sqrtf(kmax2) * (1.0f + 0.0009765625f) + m.wabs * (float)P.d_i * 7.8886e-31f;
   if (tid == 0) {
     P.meta[p].delta = delta;
-    if (tot <= (uint32_t)K) P.meta[p].thr = -INFINITY;
+    P.meta[p].total = tot;
+    if (tot <= (uint32_t)K) P.meta[p].bin = kAll;
   }
   if (tot > (uint32_t)K && above < (uint32_t)K && above + loc >= (uint32_t)K) {
     uint32_t run = above;
-    int bstar = b_hi;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      run += hv[j];
-      if (run >= (uint32_t)K) {
-        bstar = b_hi - j;
+      if (run + hv[j] >= (uint32_t)K) {
+        P.meta[p].bin = (uint32_t)(b_hi - j);
+        P.meta[p].above = run;
         break;
       }
+      run += hv[j];
     }
-    const float t0 = unsortable((uint32_t)bstar << kBinShift);
-    P.meta[p].thr = band_below(t0, delta);
   }
 }
 
@@ -533,197 +558,200 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   }
 }
 
-// ---------------------------------------------------------------- 3. threshold
-// One work-group per problem turns the scan's histogram into the band
-// threshold (kernel boundaries make the scan's histograms visible).
+// ---------------------------------------------------------------- 3. coarse threshold
+// One work-group per problem (kernel boundaries make the scan's histograms
+// visible).  The token problem's scan holds the key-norm maximum; blocks use
+// it too.
 __global__ __launch_bounds__(kThreads) void k_thresh(Params P) {
   __shared__ uint32_t s_tmp[16];
   const int p = blockIdx.x, q = p % P.n_q, kind = p / P.n_q;
-  // the token problem's scan holds the key-norm maximum; blocks use it too
   const float kmax2 = __uint_as_float(P.meta[q].maxk2);
-  if (kind == 1) wg_threshold(P, p, P.keep_blocks, kmax2, P.bound_blk, s_tmp);
-  else wg_threshold(P, p, P.k, kmax2, P.bound_tok, s_tmp);
+  if (kind == 1) wg_coarse_bin(P, p, P.keep_blocks, kmax2, P.bound_blk, s_tmp);
+  else wg_coarse_bin(P, p, P.k, kmax2, P.bound_tok, s_tmp);
 }
 
-// ---------------------------------------------------------------- 4. compaction
+// 16 consecutive scores of one compaction chunk per thread.
+__device__ __forceinline__ int load16(const Params& P, int p, int nc, int my0, float* v) {
+  if (my0 >= nc) return 0;
+  const float4* s4 = reinterpret_cast<const float4*>(P.scores + (size_t)p * P.stride + my0);
+#pragma unroll
+  for (int j = 0; j < kCmpPerThread / 4; ++j) {
+    const float4 t = s4[j];
+    v[4 * j] = t.x;
+    v[4 * j + 1] = t.y;
+    v[4 * j + 2] = t.z;
+    v[4 * j + 3] = t.w;
+  }
+  return min(kCmpPerThread, nc - my0);
+}
+
+// ---------------------------------------------------------------- 4. fine histogram
+// Histogram of bits 19..8 of the keys that fall into the coarse bin: the K-th
+// score is then located to 2^-15 of its value.
+__global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
+  __shared__ uint32_t s_h[kNBins];
+  const int tid = threadIdx.x;
+  const int p = blockIdx.y, chunk = blockIdx.x;
+  const uint32_t bin = P.meta[p].bin;
+  if (bin == kAll) return;
+  const int nc = P.meta[p].nc;
+  const int my0 = chunk * kCmpChunk + tid * kCmpPerThread;
+  if (chunk * kCmpChunk >= nc) return;
+  for (int i = tid; i < kNBins; i += kThreads) s_h[i] = 0;
+  __syncthreads();
+  float v[kCmpPerThread];
+  const int m = load16(P, p, nc, my0, v);
+#pragma unroll
+  for (int j = 0; j < kCmpPerThread; ++j) {
+    if (j < m && v[j] != -INFINITY) {
+      const uint32_t key = sortable(v[j]);
+      if ((key >> kBinShift) == bin) atomicAdd(&s_h[(key >> 8) & (kNBins - 1)], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = P.hist2 + (size_t)p * kNBins;
+  for (int i = tid; i < kNBins; i += kThreads) {
+    const uint32_t c = s_h[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+// ---------------------------------------------------------------- 5. band thresholds
+// With the fine bin [L, U] that holds the K-th approximate score a_K (so
+// L <= a_K and U >= a_K >= a_K1): keep a >= L - 2 Delta (every exact Top-K
+// member), certain a > U + 2 Delta.
+__global__ __launch_bounds__(kThreads) void k_thresh2(Params P) {
+  __shared__ uint32_t s_tmp[16];
+  const int tid = threadIdx.x;
+  const int p = blockIdx.x, kind = p / P.n_q;
+  const int K = (kind == 1) ? P.keep_blocks : P.k;
+  const Meta m = P.meta[p];
+  if (m.bin == kAll) {
+    if (tid == 0) {
+      P.meta[p].keep_thr = -INFINITY;
+      P.meta[p].in_thr = -INFINITY;
+    }
+    return;
+  }
+  const uint32_t need = (uint32_t)K - m.above;   // >= 1
+  const uint32_t* h = P.hist2 + (size_t)p * kNBins;
+  constexpr int kPer = kNBins / kThreads;
+  const int f_hi = kNBins - kPer * tid - 1;
+  uint32_t loc = 0;
+  uint32_t hv[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    hv[j] = h[f_hi - j];
+    loc += hv[j];
+  }
+  uint32_t tot;
+  const uint32_t above = wg_exclusive_scan(loc, s_tmp, &tot);
+  if (above < need && above + loc >= need) {
+    uint32_t run = above;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (run + hv[j] >= need) {
+        const uint32_t lo_key = (m.bin << kBinShift) | ((uint32_t)(f_hi - j) << 8);
+        P.meta[p].keep_thr = band_below(unsortable(lo_key), m.delta);
+        P.meta[p].in_thr = band_above(unsortable(lo_key + 255u), m.delta);
+        break;
+      }
+      run += hv[j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 6. compaction
+// Band members of one chunk, in position order, flagged certain or not; the
+// uncertain ones are also listed (chunk-local index) for the rescoring.
 __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
   __shared__ uint32_t s_tmp[16];
   const int tid = threadIdx.x;
   const int p = blockIdx.y, chunk = blockIdx.x;
-  const float thr = P.meta[p].thr;
+  const float keep_thr = P.meta[p].keep_thr, in_thr = P.meta[p].in_thr;
   const int nc = P.meta[p].nc;
   const int c0 = chunk * kCmpChunk;
   const int my0 = c0 + tid * kCmpPerThread;
-  const float* sc = P.scores + (size_t)p * P.stride;
   float v[kCmpPerThread];
-  uint32_t flags = 0;
-  if (my0 < nc) {
-    const float4* s4 = reinterpret_cast<const float4*>(sc + my0);
+  const int m = load16(P, p, nc, my0, v);
+  uint32_t keep = 0, cert = 0;
 #pragma unroll
-    for (int j = 0; j < kCmpPerThread / 4; ++j) {
-      const float4 t = s4[j];
-      v[4 * j] = t.x;
-      v[4 * j + 1] = t.y;
-      v[4 * j + 2] = t.z;
-      v[4 * j + 3] = t.w;
-    }
+  for (int j = 0; j < kCmpPerThread; ++j) {
+    const bool k_ = j < m && v[j] != -INFINITY && v[j] >= keep_thr;
+    keep |= (k_ ? 1u : 0u) << j;
+    cert |= ((k_ && v[j] > in_thr) ? 1u : 0u) << j;
+  }
+  uint32_t total, utotal;
+  uint32_t off = wg_exclusive_scan(__popc(keep), s_tmp, &total);
+  uint32_t uoff = wg_exclusive_scan(__popc(keep & ~cert), s_tmp, &utotal);
+  Entry* dst = P.band + (size_t)p * P.stride + c0;
+  uint2* udst = P.unc + (size_t)p * P.stride + c0;
 #pragma unroll
-    for (int j = 0; j < kCmpPerThread; ++j) {
-      const bool keep = (my0 + j < nc) && v[j] != -INFINITY && v[j] >= thr;
-      flags |= (keep ? 1u : 0u) << j;
+  for (int j = 0; j < kCmpPerThread; ++j) {
+    if (keep & (1u << j)) {
+      const bool c_ = (cert >> j) & 1u;
+      dst[off] = Entry{(uint32_t)(my0 + j) | (c_ ? kCertain : 0u), v[j]};
+      if (!c_) udst[uoff++] = make_uint2(off, (uint32_t)(my0 + j));
+      ++off;
     }
   }
-  uint32_t total;
-  uint32_t off = wg_exclusive_scan(__popc(flags), s_tmp, &total);
-  Entry* dst = P.band_a + (size_t)p * P.stride + c0;
-#pragma unroll
-  for (int j = 0; j < kCmpPerThread; ++j)
-    if (flags & (1u << j)) dst[off++] = Entry{(uint32_t)(my0 + j), v[j]};
-  if (tid == 0) P.chunk_cnt[(size_t)p * P.nchunk_cmp + chunk] = total;
+  if (tid == 0) {
+    P.chunk_cnt[(size_t)p * P.nchunk_cmp + chunk] = total;
+    P.chunk_unc[(size_t)p * P.nchunk_cmp + chunk] = utotal;
+  }
 }
 
-// ---------------------------------------------------------------- 5. band
-// One work-group per problem: gathers the chunks' survivors in position
-// order, finds a_K and a_K1 and splits the band into certain and uncertain
-// members.
-__global__ __launch_bounds__(kThreads) void k_band(Params P) {
-  __shared__ uint32_t s_tmp[16];
-  __shared__ uint32_t s_hist[256];
-  __shared__ uint32_t s_off[kMaxChunksLds + 1];
-  __shared__ uint32_t s_key[kBandLds];
-  const int tid = threadIdx.x;
-  const int p = blockIdx.x;
-  const int nch = P.nchunk_cmp;
-  uint32_t* cnt = P.chunk_cnt + (size_t)p * P.nchunk_cmp;
-  const bool lds_off = nch <= kMaxChunksLds;
+// Exclusive prefix of a problem's per-chunk counts into LDS (s[0..nch]).
+__device__ __forceinline__ void chunk_prefix(const uint32_t* cnt, int nch, uint32_t* s, uint32_t* s_tmp) {
   uint32_t carry = 0;
   for (int t0 = 0; t0 < nch; t0 += kThreads) {
-    const int c = t0 + tid;
+    const int c = t0 + threadIdx.x;
     const uint32_t cv = c < nch ? cnt[c] : 0u;
     uint32_t tt;
     const uint32_t ex = wg_exclusive_scan(cv, s_tmp, &tt);
-    if (c < nch) {
-      if (lds_off) s_off[c] = carry + ex;
-      else cnt[c] = carry + ex;
-    }
+    if (c < nch) s[c] = carry + ex;
     carry += tt;
   }
-  if (lds_off && tid == 0) s_off[nch] = carry;
-  __threadfence_block();
+  if (threadIdx.x == 0) s[nch] = carry;
   __syncthreads();
-  const uint32_t nband = carry;
-  const Entry* __restrict__ ba = P.band_a + (size_t)p * P.stride;
-  Entry* __restrict__ bb = P.band_b + (size_t)p * P.stride;
-  if (lds_off) {
-    // flat copy: output j comes from the chunk whose offset range holds it
-    for (uint32_t j0 = 0; j0 < nband; j0 += 4 * kThreads) {
-      Entry e[4];
-      uint32_t jj[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        jj[u] = j0 + u * kThreads + tid;
-        if (jj[u] < nband) {
-          int lo = 0, hi = nch - 1;  // largest c with s_off[c] <= j
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_off[mid] <= jj[u]) lo = mid;
-            else hi = mid - 1;
-          }
-          e[u] = ba[(size_t)lo * kCmpChunk + (jj[u] - s_off[lo])];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (jj[u] < nband) bb[jj[u]] = e[u];
-    }
-  } else {
-    for (int c = tid; c < nch; c += kThreads) {
-      const uint32_t o = cnt[c];
-      const uint32_t e = (c + 1 < nch) ? cnt[c + 1] : nband;
-      for (uint32_t i = 0; i < e - o; ++i) bb[o + i] = ba[(size_t)c * kCmpChunk + i];
-    }
-  }
-  __threadfence_block();
-  __syncthreads();
-
-  const int kind = p / P.n_q;
-  const int K = (kind == 1) ? P.keep_blocks : P.k;
-  Entry* __restrict__ b2 = P.band_a + (size_t)p * P.stride;   // the chunk staging area is free now
-  uint32_t* __restrict__ unc = P.unc + (size_t)p * P.stride;
-  const bool in_lds = nband <= (uint32_t)kBandLds;
-  if (in_lds)
-    for (uint32_t i = tid; i < nband; i += kThreads) s_key[i] = sortable(bb[i].s);
-  __syncthreads();
-  auto key = [&](int i) { return in_lds ? s_key[i] : sortable(bb[i].s); };
-  uint32_t n2 = 0, nu = 0;
-  if (nband > (uint32_t)K) {
-    const float delta = P.meta[p].delta;
-    uint32_t ties;
-    const uint32_t kth = wg_kth_largest((int)nband, K, key, s_hist, s_tmp, &ties);
-    // (K+1)-th largest: kth again if more entries equal it than the Top-K takes
-    uint32_t eq = 0;
-    for (uint32_t i = tid; i < nband; i += kThreads) eq += key(i) == kth ? 1u : 0u;
-    uint32_t eq_tot;
-    wg_exclusive_scan(eq, s_tmp, &eq_tot);
-    const uint32_t k1 = (eq_tot > ties) ? kth : wg_max_below((int)nband, kth, key, s_tmp);
-    // keep >= a_K - 2 Delta; certain > a_K1 + 2 Delta (compared as sortable keys)
-    const uint32_t keep_key = sortable(band_below(unsortable(kth), delta));
-    const uint32_t in_key = (k1 == 0) ? 0xFFFFFFFFu : sortable(band_above(unsortable(k1), delta));
-    // contiguous range per thread: count, scan, then write in order
-    const uint32_t per = (nband + kThreads - 1) / kThreads;
-    const uint32_t i0 = min(nband, tid * per), i1 = min(nband, i0 + per);
-    uint32_t ck = 0, cu = 0;
-    for (uint32_t i = i0; i < i1; ++i) {
-      const uint32_t kk = key(i);
-      ck += kk >= keep_key ? 1u : 0u;
-      cu += (kk >= keep_key && kk <= in_key) ? 1u : 0u;
-    }
-    uint32_t tk, tu;
-    uint32_t ok = wg_exclusive_scan(ck, s_tmp, &tk);
-    uint32_t ou = wg_exclusive_scan(cu, s_tmp, &tu);
-    for (uint32_t i = i0; i < i1; ++i) {
-      const uint32_t kk = key(i);
-      if (kk >= keep_key) {
-        Entry e = bb[i];
-        if (kk > in_key) e.cand |= kCertain;
-        else unc[ou++] = ok;
-        b2[ok++] = e;
-      }
-    }
-    n2 = tk;
-    nu = tu;
-  } else {
-    for (uint32_t i = tid; i < nband; i += kThreads) {
-      Entry e = bb[i];
-      e.cand |= kCertain;
-      b2[i] = e;
-    }
-    n2 = nband;
-  }
-  if (tid == 0) {
-    P.meta[p].nband = (int)nband;
-    P.meta[p].nband2 = (int)n2;
-    P.meta[p].nunc = (int)nu;
-    P.meta[p].nin = (int)(n2 - nu);
-  }
 }
 
-// ---------------------------------------------------------------- 6. rescoring
+// Largest c in [0, nch) with s[c] <= j.
+__device__ __forceinline__ int chunk_of(const uint32_t* s, int nch, uint32_t j) {
+  int lo = 0, hi = nch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s[mid] <= j) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------- 7. rescoring
+// Exact scores of the uncertain band members, one member per wave, one lane
+// per head.  The member keys are wave-uniform: each lane loads a slice of
+// them into registers and the values reach every lane through readlane, so
+// the fp32 chains (eight per block, run interleaved) wait on no memory.  The
+// head sum is the ordered fma chain over the lanes' ReLU'd dots.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
-  constexpr int DW = D / 2;  // packed bf16 pairs per head row
-  __shared__ float s_key[kWaves][8][D];
-  __shared__ float s_r[kWaves][64];
-  __shared__ float s_w[64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int DW = D / 2;            // packed bf16 pairs per key row
+  constexpr int KPER = 8 * DW / 64;    // key dwords of 8 members per lane
+  __shared__ uint32_t s_tmp[16];
+  __shared__ uint32_t s_uoff[kMaxChunksLds + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int p = blockIdx.y, q = p % P.n_q, kind = p / P.n_q;
   const int nvis = P.q_nvis[q];
   const int64_t base = P.seq_base[P.q_seq[q]];
-  const int nu = P.meta[p].nunc;
-  Entry* b2 = P.band_a + (size_t)p * P.stride;
-  const uint32_t* unc = P.unc + (size_t)p * P.stride;
+  const int nch = P.nchunk_cmp;
+  Entry* band = P.band + (size_t)p * P.stride;
+  const uint2* unc = P.unc + (size_t)p * P.stride;
 
-  if (tid < 64) s_w[tid] = tid < P.h_i ? P.w[(size_t)q * P.h_i + tid] : 0.0f;
+  chunk_prefix(P.chunk_unc + (size_t)p * nch, nch, s_uoff, s_tmp);
+  const int nu = (int)s_uoff[nch];
+  if (blockIdx.x * kWaves >= nu) return;
+  const float wl = lane < P.h_i ? P.w[(size_t)q * P.h_i + lane] : 0.0f;
   uint32_t qrow[DW];
   {
     const int hh = lane < P.h_i ? lane : 0;
@@ -737,22 +765,12 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
       qrow[4 * i + 3] = v.w;
     }
   }
-  __syncthreads();
-
-  auto head_dot = [&](const float* key) {
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < DW; ++i) {
-      acc = fmaf(__uint_as_float(qrow[i] << 16), key[2 * i], acc);
-      acc = fmaf(__uint_as_float(qrow[i] & 0xFFFF0000u), key[2 * i + 1], acc);
-    }
-    return acc;
-  };
 
   const int stride_w = gridDim.x * kWaves;
   for (int j = blockIdx.x * kWaves + wave; j < nu; j += stride_w) {
-    const uint32_t slot = unc[j];
-    const uint32_t cand = b2[slot].cand & ~kCertain;
+    const int c = chunk_of(s_uoff, nch, (uint32_t)j);
+    const uint2 u = unc[(size_t)c * kCmpChunk + (j - s_uoff[c])];
+    const uint32_t cand = __builtin_amdgcn_readfirstlane(u.y);
     int first, nmem;
     if (kind == 1) {
       first = (int)cand * 8;
@@ -761,98 +779,187 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
       first = cand_pos(P, q, kind, cand);
       nmem = 1;
     }
-    // members' keys -> LDS (fp32)
-    for (int e = lane; e < nmem * (D / 2); e += 64) {
-      const int t = e / (D / 2), d2 = e % (D / 2);
-      const uint32_t wv = reinterpret_cast<const uint32_t*>(P.ik + (size_t)(base + first + t) * D)[d2];
-      s_key[wave][t][2 * d2] = __uint_as_float(wv << 16);
-      s_key[wave][t][2 * d2 + 1] = __uint_as_float(wv & 0xFFFF0000u);
+    // dword e of the 8-member key block (member e / DW, dword e % DW) sits in
+    // lane e % 64, register e / 64; members past nmem read as zero
+    uint32_t wv[KPER];
+#pragma unroll
+    for (int k = 0; k < KPER; ++k) {
+      const int e = lane + 64 * k, t = e / DW, d2 = e % DW;
+      wv[k] = t < nmem ? reinterpret_cast<const uint32_t*>(P.ik + (size_t)(base + first + t) * D)[d2] : 0u;
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
+    auto kdw = [&](int t, int d2) -> uint32_t {
+      const int e = t * DW + d2;
+      return (uint32_t)__builtin_amdgcn_readlane((int)wv[e / 64], e % 64);
+    };
     float r;
     if (kind == 1) {
+      float a[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) a[t] = 0.0f;
+#pragma unroll
+      for (int d2 = 0; d2 < DW; ++d2) {
+        const float qlo = __uint_as_float(qrow[d2] << 16), qhi = __uint_as_float(qrow[d2] & 0xFFFF0000u);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t kw = kdw(t, d2);
+          a[t] = fmaf(qlo, __uint_as_float(kw << 16), a[t]);
+          a[t] = fmaf(qhi, __uint_as_float(kw & 0xFFFF0000u), a[t]);
+        }
+      }
       float sum = 0.0f;
-      for (int t = 0; t < nmem; ++t) sum = sum + head_dot(s_key[wave][t]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (t < nmem) sum = sum + a[t];
       const float mean = __fdiv_rn(sum, (float)nmem);
       r = mean > 0.0f ? mean : 0.0f;
     } else {
-      const float acc = head_dot(s_key[wave][0]);
+      float acc = 0.0f;
+#pragma unroll
+      for (int d2 = 0; d2 < DW; ++d2) {
+        const uint32_t kw = kdw(0, d2);
+        acc = fmaf(__uint_as_float(qrow[d2] << 16), __uint_as_float(kw << 16), acc);
+        acc = fmaf(__uint_as_float(qrow[d2] & 0xFFFF0000u), __uint_as_float(kw & 0xFFFF0000u), acc);
+      }
       r = acc > 0.0f ? acc : 0.0f;
     }
-    s_r[wave][lane] = r;
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    if (lane == 0) {
-      float s = 0.0f;
-      for (int h = 0; h < P.h_i; ++h) s = fmaf(s_w[h], s_r[wave][h], s);
-      b2[slot].s = s;
+    // ordered head sum: s = fma(w_h, r_h, s) for h ascending, values read across lanes
+    float sc = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 64; ++h) {
+      if (h < P.h_i) {
+        const float wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), h));
+        const float rh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), h));
+        sc = fmaf(wh, rh, sc);
+      }
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
+    if (lane == 0) band[(size_t)c * kCmpChunk + u.x].s = sc;
   }
-
 }
 
-// ---------------------------------------------------------------- 7. final
+// ---------------------------------------------------------------- 8. final
 // One work-group per problem: the certain members plus the best rescored
-// ones, written as ascending positions and padded with -1.
+// ones (exact score desc, position asc), written as ascending positions and
+// padded with -1.  The band is read in position order through the chunk
+// prefix; bands up to kBandLds entries are staged in LDS first.
 __global__ __launch_bounds__(kThreads) void k_final(Params P) {
   __shared__ uint32_t s_tmp[16];
   __shared__ uint32_t s_hist[256];
-  __shared__ uint32_t s_ukey[kBandLds];
+  __shared__ uint32_t s_off[kMaxChunksLds + 1];
+  __shared__ uint32_t s_key[kBandLds];
+  __shared__ uint32_t s_cand[kBandLds];
+  __shared__ uint32_t s_ukey[kUncLds];
   const int tid = threadIdx.x;
   const int p = blockIdx.x, q = p % P.n_q, kind = p / P.n_q;
-  const int nu = P.meta[p].nunc;
-  const Entry* b2 = P.band_a + (size_t)p * P.stride;
-  const uint32_t* unc = P.unc + (size_t)p * P.stride;
+  const int nch = P.nchunk_cmp;
+  const Entry* band = P.band + (size_t)p * P.stride;
   const int K = (kind == 1) ? P.keep_blocks : P.k;
   int32_t* out = (kind == 1) ? P.pool_out + (size_t)q * P.keep_blocks : P.idx_out + (size_t)q * P.k;
-  const int n2 = P.meta[p].nband2;
-  const int need = K - P.meta[p].nin;
-  const bool take_none = need <= 0;
-  const bool take_all = !take_none && nu <= need;
-  const bool in_lds = nu <= kBandLds;
-  if (in_lds)
-    for (int i = tid; i < nu; i += kThreads) s_ukey[i] = sortable(b2[unc[i]].s);
-  __syncthreads();
-  uint32_t kth = 0, ties = 0;
-  if (!take_all && !take_none)
-    kth = wg_kth_largest(nu, need, [&](int i) { return in_lds ? s_ukey[i] : sortable(b2[unc[i]].s); },
-                         s_hist, s_tmp, &ties);
-  // contiguous range per thread of the (position-ordered) band.  Pass 1 counts
-  // the entries tied at the cut, pass 2 the kept ones, pass 3 writes; the tie
-  // rank of an entry is its rank among tied entries in position order, so the
-  // lower positions win the ties.
+
+  chunk_prefix(P.chunk_cnt + (size_t)p * nch, nch, s_off, s_tmp);
+  const int n2 = (int)s_off[nch];
+  // per-thread contiguous segment of the position-ordered band
   const int per = (n2 + kThreads - 1) / kThreads;
   const int i0 = min(n2, tid * per), i1 = min(n2, i0 + per);
+  const bool in_lds = n2 <= kBandLds;
+  auto entry_at = [&](int i) {
+    const int c = chunk_of(s_off, nch, (uint32_t)i);
+    return band[(size_t)c * kCmpChunk + (i - s_off[c])];
+  };
+  if (in_lds) {
+    // strided batches of U independent loads (addresses from the chunk prefix)
+    constexpr int U = 8;
+    int steps = 0;
+    while ((1 << steps) < nch) ++steps;
+    for (int b0 = 0; b0 < n2; b0 += U * kThreads) {
+      // U binary searches in lock step: each step's LDS reads issue together
+      int lo[U], hi[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        lo[u] = 0;
+        hi[u] = nch - 1;
+      }
+      for (int st = 0; st < steps; ++st) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t i = (uint32_t)(b0 + u * kThreads + tid);
+          const int mid = (lo[u] + hi[u] + 1) >> 1;
+          if (lo[u] < hi[u]) {
+            if (s_off[mid] <= i) lo[u] = mid;
+            else hi[u] = mid - 1;
+          }
+        }
+      }
+      Entry e[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = b0 + u * kThreads + tid;
+        if (i < n2) e[u] = band[(size_t)lo[u] * kCmpChunk + (i - s_off[lo[u]])];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = b0 + u * kThreads + tid;
+        if (i < n2) {
+          s_key[i] = sortable(e[u].s);
+          s_cand[i] = e[u].cand;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  auto key = [&](int i) { return in_lds ? s_key[i] : sortable(entry_at(i).s); };
+  auto cand_of = [&](int i) { return in_lds ? s_cand[i] : entry_at(i).cand; };
+
+  // uncertain members in position order: count per segment, scan, collect keys
+  uint32_t cu = 0;
+  for (int i = i0; i < i1; ++i) cu += (cand_of(i) & kCertain) ? 0u : 1u;
+  uint32_t nu;
+  uint32_t uo = wg_exclusive_scan(cu, s_tmp, &nu);
+  const int nin = n2 - (int)nu;
+  const int need = K - nin;
+  const bool take_none = need <= 0;
+  const bool take_all = !take_none && (int)nu <= need;
   const bool cut = !take_all && !take_none;
-  auto decide = [&](const Entry& e, uint32_t& rank) {
-    if (e.cand & kCertain) return true;
+  const bool u_lds = (int)nu <= kUncLds;
+  if (cut && u_lds)
+    for (int i = i0; i < i1; ++i)
+      if (!(cand_of(i) & kCertain)) s_ukey[uo++] = key(i);
+  __syncthreads();
+  uint32_t kth = 0, ties = 0;
+  if (cut) {
+    if (u_lds) {
+      kth = wg_kth_largest((int)nu, need, [&](int i) { return s_ukey[i]; }, s_hist, s_tmp, &ties);
+    } else {
+      // degenerate: many uncertain members; select over the band, certain ones count as ineligible
+      kth = wg_kth_largest(n2, need, [&](int i) { return (cand_of(i) & kCertain) ? 0u : key(i); },
+                           s_hist, s_tmp, &ties);
+    }
+  }
+  // pass 1 counts the entries tied at the cut, pass 2 the kept ones, pass 3
+  // writes; a tied entry's rank among tied entries follows position order, so
+  // the lower positions win the ties.
+  auto decide = [&](int i, uint32_t& rank) {
+    const uint32_t c = cand_of(i);
+    if (c & kCertain) return true;
     if (take_none) return false;
     if (take_all) return true;
-    const uint32_t key = sortable(e.s);
-    if (key > kth) return true;
-    if (key == kth) return rank++ < ties;
+    const uint32_t kk = key(i);
+    if (kk > kth) return true;
+    if (kk == kth) return rank++ < ties;
     return false;
   };
   uint32_t nt = 0;
   if (cut)
-    for (int i = i0; i < i1; ++i) {
-      const Entry e = b2[i];
-      nt += (!(e.cand & kCertain) && sortable(e.s) == kth) ? 1u : 0u;
-    }
+    for (int i = i0; i < i1; ++i) nt += (!(cand_of(i) & kCertain) && key(i) == kth) ? 1u : 0u;
   uint32_t tot_t;
   const uint32_t tie_base = wg_exclusive_scan(nt, s_tmp, &tot_t);
   uint32_t cnt = 0, rank = tie_base;
-  for (int i = i0; i < i1; ++i) cnt += decide(b2[i], rank) ? 1u : 0u;
+  for (int i = i0; i < i1; ++i) cnt += decide(i, rank) ? 1u : 0u;
   uint32_t tot;
   uint32_t o = wg_exclusive_scan(cnt, s_tmp, &tot);
   rank = tie_base;
   for (int i = i0; i < i1; ++i) {
-    const Entry e = b2[i];
-    if (decide(e, rank)) {
-      const uint32_t cand = e.cand & ~kCertain;
+    if (decide(i, rank)) {
+      const uint32_t cand = cand_of(i) & ~kCertain;
       out[o++] = (kind == 1) ? (int)cand : cand_pos(P, q, kind, cand);
     }
   }
@@ -877,7 +984,7 @@ thread_local hipEvent_t g_scan_ev_stop = nullptr;
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t scores, hist, meta, chunk_cnt, band_a, band_b, unc, total;
+  size_t scores, hist, hist2, meta, chunk_cnt, chunk_unc, band, unc, total;
 };
 
 Layout make_layout(int nprob, int64_t stride, int nchunk_cmp) {
@@ -887,16 +994,18 @@ Layout make_layout(int nprob, int64_t stride, int nchunk_cmp) {
   o = align256(o + (size_t)nprob * stride * sizeof(float));
   L.hist = o;
   o = align256(o + (size_t)nprob * kNBins * sizeof(uint32_t));
+  L.hist2 = o;
+  o = align256(o + (size_t)nprob * kNBins * sizeof(uint32_t));
   L.meta = o;
   o = align256(o + (size_t)nprob * sizeof(Meta));
   L.chunk_cnt = o;
   o = align256(o + (size_t)nprob * nchunk_cmp * sizeof(uint32_t));
-  L.band_a = o;
-  o = align256(o + (size_t)nprob * stride * sizeof(Entry));
-  L.band_b = o;
+  L.chunk_unc = o;
+  o = align256(o + (size_t)nprob * nchunk_cmp * sizeof(uint32_t));
+  L.band = o;
   o = align256(o + (size_t)nprob * stride * sizeof(Entry));
   L.unc = o;
-  o = align256(o + (size_t)nprob * stride * sizeof(uint32_t));
+  o = align256(o + (size_t)nprob * stride * sizeof(uint2));
   L.total = o;
   return L;
 }
@@ -945,11 +1054,12 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   char* w = static_cast<char*>(ws);
   P.scores = reinterpret_cast<float*>(w + L.scores);
   P.hist = reinterpret_cast<uint32_t*>(w + L.hist);
+  P.hist2 = reinterpret_cast<uint32_t*>(w + L.hist2);
   P.meta = reinterpret_cast<Meta*>(w + L.meta);
   P.chunk_cnt = reinterpret_cast<uint32_t*>(w + L.chunk_cnt);
-  P.band_a = reinterpret_cast<Entry*>(w + L.band_a);
-  P.band_b = reinterpret_cast<Entry*>(w + L.band_b);
-  P.unc = reinterpret_cast<uint32_t*>(w + L.unc);
+  P.chunk_unc = reinterpret_cast<uint32_t*>(w + L.chunk_unc);
+  P.band = reinterpret_cast<Entry*>(w + L.band);
+  P.unc = reinterpret_cast<uint2*>(w + L.unc);
   P.bound_tok = bound_constant(P.d_i, false);
   P.bound_blk = bound_constant(P.d_i, true);
 
@@ -969,9 +1079,11 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return CSA2_E_HIP;
   hipLaunchKernelGGL(k_thresh, dim3(P.nprob), dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
-  hipLaunchKernelGGL(k_compact, dim3(P.nchunk_cmp, P.nprob), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(k_finehist, dim3(P.nchunk_cmp, P.nprob), dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
-  hipLaunchKernelGGL(k_band, dim3(P.nprob), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(k_thresh2, dim3(P.nprob), dim3(kThreads), 0, s, P);
+  if (!launch_ok()) return CSA2_E_HIP;
+  hipLaunchKernelGGL(k_compact, dim3(P.nchunk_cmp, P.nprob), dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
   if (P.d_i == 128) hipLaunchKernelGGL(k_rescore<128>, dim3(kRescoreWGs, P.nprob), dim3(kThreads), 0, s, P);
   else hipLaunchKernelGGL(k_rescore<64>, dim3(kRescoreWGs, P.nprob), dim3(kThreads), 0, s, P);
@@ -1015,9 +1127,9 @@ extern "C" csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n
                                        const uint16_t* ik, const int64_t* seq_base, int k, int32_t* idx_out,
                                        int block, int keep_blocks, int32_t* pool_out, void* ws, size_t ws_bytes,
                                        void* stream) {
-  if (n_q < 0 || max_nvis < 0 || max_nvis > 0x7FFFFFF0 || k < 1 || k > 2048 || keep_blocks < 0 ||
-      keep_blocks > 4096)
+  if (n_q < 0 || max_nvis < 0 || k < 1 || k > 2048 || keep_blocks < 0 || keep_blocks > 4096)
     return CSA2_E_INVAL;
+  if ((int64_t)max_nvis > (int64_t)kMaxChunksLds * kCmpChunk) return CSA2_E_UNSUPPORTED;
   if (!shape_ok(h_i, d_i)) return CSA2_E_UNSUPPORTED;
   if (keep_blocks > 0 && block != 8) return CSA2_E_UNSUPPORTED;
   if (n_q == 0) return CSA2_OK;

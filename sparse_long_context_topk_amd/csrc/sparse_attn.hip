@@ -323,11 +323,16 @@ struct Split {
   int nsub, nsplit, per;
 };
 
+#ifndef CSA2_ATTN_WG_TARGET
+#define CSA2_ATTN_WG_TARGET 256   // aim for about this many work-groups per call
+#endif
+
 Split choose_split(int n_q, int k, int w_max) {
   Split s;
   const int nslots = k + w_max;
   s.nsub = std::max(1, (nslots + kSub - 1) / kSub);
-  const int target = std::max(1, std::min(s.nsub, (512 + n_q - 1) / std::max(n_q, 1)));
+  const int target =
+      std::max(1, std::min(s.nsub, (CSA2_ATTN_WG_TARGET + n_q - 1) / std::max(n_q, 1)));
   s.per = (s.nsub + target - 1) / target;
   s.nsplit = (s.nsub + s.per - 1) / s.per;
   return s;

@@ -70,6 +70,17 @@ def test_full_ties(case):
 
 
 @gpu
+def test_full_ties_larger_than_lds_band():
+    """All keys equal over 20000 positions: every candidate is in the band and
+    uncertain, which takes the final selection's global-memory path."""
+    note("full ties 20000 equal")
+    inp = index_inputs([20000, 13000], 64, 128, seed=4, key_fn=lambda ik: ik[:1].expand_as(ik).contiguous())
+    g_idx, g_pool = _gpu_full(inp, 512, 2048)
+    r_idx, r_pool = _ref_full(inp, 512, 2048)
+    assert np.array_equal(g_idx, r_idx) and np.array_equal(g_pool, r_pool)
+
+
+@gpu
 @pytest.mark.parametrize("lengths,keep", [([20000, 16391, 300], 2048), ([4096, 1000, 8], 64),
                                           ([16384, 16385], 2048), ([30000], 1024)])
 def test_full_with_pool(lengths, keep):
