@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c5"])
     p.add_argument("--cpu-baseline", default="auto", choices=["auto", "off"])
     p.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the oracle sample (0: workload default)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="run only a plain device-to-device copy of MIB MiB, 5 times (scales HBM byte counters)")
     return p.parse_args()
 
 
@@ -176,6 +178,21 @@ def cpu_baseline(wl, st, layers, app_x, dev, nseq, gpu_results):
             {"idx_bitexact": idx_ok, "attn_max_normwise_err": err, "sequences": nseq})
 
 
+def copy_calibration(mib, dev):
+    """A copy of known size: each launch reads and writes exactly `mib` MiB,
+    so a profiler's HBM byte counters for it give the counters' scale."""
+    import torch
+
+    n = mib << 20
+    src = torch.full((n,), 7, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -189,6 +206,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration, dev)
+        return
     wl = gen.workload(a.workload)
     log(f"workload {wl['name']}: {wl['desc']}; building inputs")
     t0 = time.time()

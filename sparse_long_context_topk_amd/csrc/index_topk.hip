@@ -12,44 +12,47 @@
 // and the pool of up to 2048 blocks of 8 positions.
 //
 // How (one pass over the keys at HBM speed, exact result):
-//  1. k_prologue  zeroes per-problem counters and histograms, and computes
-//                 QW = sum_h |w_h| ||q_h|| for the rounding bound.
-//  2. k_scan      streams the indexer keys once, two 16-key groups ahead of
-//                 the math.  Scores come from bf16 MFMA
-//                 (v_mfma_f32_16x16x32_bf16: 16 heads x 16 positions x 32
-//                 dims, the query held in registers).  A block's per-head dot
-//                 product is the mean of its members' (linearity), so block
-//                 scores come from the same accumulators with a three-step DPP
-//                 butterfly: the pool costs no extra HBM traffic and no extra
-//                 MFMA.  Each work-group keeps a 4096-bin histogram of the top
-//                 12 bits of the scores and the largest squared key norm; the
-//                 last work-group of a query turns the histogram into a
-//                 threshold below which no Top-K member can lie:
-//                 T = (lowest value of the bin holding the K-th score) - 2*Delta,
-//                 where Delta bounds |MFMA score - exact score| for every key:
-//                 Delta = C * QW * max||k|| (Cauchy-Schwarz on the dot-product
-//                 rounding error, ReLU is 1-Lipschitz, plus the head-sum and
-//                 block-mean roundings), C from the fp32 error constants with a
-//                 2x safety factor.
-//  3. k_compact   keeps the candidates with approximate score >= T in
-//                 position order; its last work-group finds the exact K-th and
-//                 (K+1)-th approximate scores a_K >= a_K1 (radix select) and
-//                 splits the band:  every exact Top-K member has approximate
-//                 score >= a_K - 2*Delta (it beats the K-th exact score, which
-//                 is >= a_K - Delta), and every member with approximate score
-//                 > a_K1 + 2*Delta is certainly in (its exact score exceeds
-//                 a_K1 + Delta, which only candidates with approximate score
-//                 above a_K1 -- at most K of them, itself included -- can
-//                 reach).  Only the members in between need exact scores.
-//  4. k_rescore   recomputes those scores with the exact fp32 chains (one lane
-//                 per head, then one lane for the head sum); its last
-//                 work-group selects the missing members by (exact score desc,
-//                 position asc) and writes the positions in ascending order.
+//  1. k_prologue   zeroes the problem's histograms and Meta, and computes
+//                  QW = sum_h |w_h| ||q_h|| for the rounding bound.
+//  2. k_scan       streams the indexer keys once, two 16-key groups ahead of
+//                  the math.  Scores come from bf16 MFMA
+//                  (v_mfma_f32_16x16x32_bf16, S^T = K Q^T: 16 positions x 16
+//                  heads x 32 dims, the query held in registers).  A block's
+//                  per-head dot product is the mean of its members'
+//                  (linearity), so block scores come from the same accumulators
+//                  with a DPP butterfly: the pool costs no extra HBM traffic and
+//                  no extra MFMA.  Work-groups add into a 4096-bin histogram of
+//                  the top 12 bits of the scores' sortable keys and track the
+//                  largest squared key norm.
+//  3. k_finehist   every work-group finds the coarse bin holding the K-th
+//                  score, then histograms bits 19..8 of the keys in that bin:
+//                  the K-th approximate score a_K is located in a fine bin
+//                  [L, U].
+//  4. k_compact    every work-group derives the band from the fine histogram
+//                  and the rounding bound Delta = C * QW * max||k||
+//                  (Cauchy-Schwarz on the dot-product rounding, ReLU is
+//                  1-Lipschitz, plus the head-sum and block-mean roundings; C
+//                  from the fp32 error constants with a 2x margin):
+//                  every exact Top-K member has approximate score >= L - 2 Delta
+//                  (it is >= the K-th exact score >= a_K - Delta); a member with
+//                  approximate score > U + 2 Delta is certainly in (only members
+//                  above a_K1 <= U can reach its exact score).  The band is
+//                  written per chunk in position order, certain members flagged,
+//                  the uncertain ones listed.
+//  5. k_rescore    recomputes the uncertain members' scores with the exact fp32
+//                  chains (one lane per head; a block runs its eight member
+//                  chains and divides their sum by the member count).
+//  6. k_final      one work-group per problem: the certain members plus the
+//                  best uncertain ones by (exact score desc, position asc) --
+//                  pairwise ranks of (score, index) composites, or a radix
+//                  select when the uncertain set is large -- written as
+//                  ascending positions, -1 padded.
 // Degenerate inputs (ties everywhere) only make the band large; the result
 // stays exact.
 #include "csa2_device.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <cmath>
 
 namespace csa2 {
@@ -62,10 +65,11 @@ constexpr int kBinShift = 20;
 constexpr int kCmpChunk = 4096;
 constexpr int kCmpPerThread = kCmpChunk / kThreads;
 constexpr int kMaxChunksLds = 8192;   // compaction chunks per problem (max_nvis <= 2^25)
-constexpr int kRescoreWGs = 64;
+constexpr int kRescoreWGs = 128;
 constexpr int kMaxScanChunk = 4096;
 constexpr int kBandLds = 12288;      // band entries the final kernel keeps in LDS (96 KiB)
 constexpr int kUncLds = 4096;        // uncertain members whose keys the final kernel keeps in LDS
+constexpr int kRankMax = 1024;       // uncertain members the final kernel ranks pairwise
 constexpr uint32_t kCertain = 0x80000000u;
 constexpr uint32_t kAll = 0xFFFFFFFFu;
 
@@ -301,13 +305,18 @@ __global__ __launch_bounds__(kThreads) void k_prologue(Params P) {
   }
 }
 
-// Coarse step of the threshold (one work-group): the bin of the coarse
-// histogram that holds the K-th score, and how many candidates lie above it.
-__device__ void wg_coarse_bin(const Params& P, int p, int K, float kmax2, float bound, uint32_t* s_tmp) {
+// Coarse step of the threshold: the bin of the coarse histogram that holds
+// the K-th score (kAll when at most K candidates exist), computed by every
+// work-group that needs it; the publishing one also records it, with the
+// rounding bound Delta and the count above the bin, in the problem's Meta.
+__device__ uint32_t wg_coarse_bin(const Params& P, int p, bool publish, uint32_t* s_tmp /*>= 12*/) {
   const int tid = threadIdx.x;
+  const int q = p % P.n_q, kind = p / P.n_q;
+  const int K = kind == 1 ? P.keep_blocks : P.k;
   const uint32_t* h = P.hist + (size_t)p * kNBins;
   constexpr int kPer = kNBins / kThreads;  // 16 bins per thread, highest bins first
   const int b_hi = kNBins - kPer * tid - 1;
+  if (tid == 0) s_tmp[10] = kAll;          // ordered before its readers by the scan's barriers
   uint32_t loc = 0;
   uint32_t hv[kPer];
 #pragma unroll
@@ -317,25 +326,33 @@ __device__ void wg_coarse_bin(const Params& P, int p, int K, float kmax2, float 
   }
   uint32_t tot;
   const uint32_t above = wg_exclusive_scan(loc, s_tmp, &tot);
-  const Meta m = P.meta[p];
-  const float delta = bound * m.qw * sqrtf(kmax2) * (1.0f + 0.0009765625f) + m.wabs * (float)P.d_i * 7.8886e-31f;
-  if (tid == 0) {
-    P.meta[p].delta = delta;
+  if (publish && tid == 0) {
+    // the token problem's scan holds the key-norm maximum; blocks use it too
+    const float kmax2 = __uint_as_float(P.meta[q].maxk2);
+    const Meta m = P.meta[p];
+    const float bound = kind == 1 ? P.bound_blk : P.bound_tok;
+    P.meta[p].delta = bound * m.qw * sqrtf(kmax2) * (1.0f + 0.0009765625f) + m.wabs * (float)P.d_i * 7.8886e-31f;
     P.meta[p].total = tot;
-    if (tot <= (uint32_t)K) P.meta[p].bin = kAll;
   }
   if (tot > (uint32_t)K && above < (uint32_t)K && above + loc >= (uint32_t)K) {
     uint32_t run = above;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       if (run + hv[j] >= (uint32_t)K) {
-        P.meta[p].bin = (uint32_t)(b_hi - j);
-        P.meta[p].above = run;
+        s_tmp[10] = (uint32_t)(b_hi - j);
+        if (publish) {
+          P.meta[p].bin = (uint32_t)(b_hi - j);
+          P.meta[p].above = run;
+        }
         break;
       }
       run += hv[j];
     }
   }
+  __syncthreads();
+  const uint32_t bin = s_tmp[10];
+  __syncthreads();
+  return bin;
 }
 
 // ---------------------------------------------------------------- 2. scan
@@ -558,18 +575,6 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   }
 }
 
-// ---------------------------------------------------------------- 3. coarse threshold
-// One work-group per problem (kernel boundaries make the scan's histograms
-// visible).  The token problem's scan holds the key-norm maximum; blocks use
-// it too.
-__global__ __launch_bounds__(kThreads) void k_thresh(Params P) {
-  __shared__ uint32_t s_tmp[16];
-  const int p = blockIdx.x, q = p % P.n_q, kind = p / P.n_q;
-  const float kmax2 = __uint_as_float(P.meta[q].maxk2);
-  if (kind == 1) wg_coarse_bin(P, p, P.keep_blocks, kmax2, P.bound_blk, s_tmp);
-  else wg_coarse_bin(P, p, P.k, kmax2, P.bound_tok, s_tmp);
-}
-
 // 16 consecutive scores of one compaction chunk per thread.
 __device__ __forceinline__ int load16(const Params& P, int p, int nc, int my0, float* v) {
   if (my0 >= nc) return 0;
@@ -585,18 +590,21 @@ __device__ __forceinline__ int load16(const Params& P, int p, int nc, int my0, f
   return min(kCmpPerThread, nc - my0);
 }
 
-// ---------------------------------------------------------------- 4. fine histogram
+// ---------------------------------------------------------------- 3. fine histogram
 // Histogram of bits 19..8 of the keys that fall into the coarse bin: the K-th
-// score is then located to 2^-15 of its value.
+// score is then located to 2^-15 of its value.  Every work-group first finds
+// the coarse bin itself (kernel boundaries make the scan's histograms
+// visible); chunk 0 publishes it.
 __global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
   __shared__ uint32_t s_h[kNBins];
+  __shared__ uint32_t s_tmp[16];
   const int tid = threadIdx.x;
   const int p = blockIdx.y, chunk = blockIdx.x;
-  const uint32_t bin = P.meta[p].bin;
-  if (bin == kAll) return;
   const int nc = P.meta[p].nc;
+  if (chunk > 0 && chunk * kCmpChunk >= nc) return;
+  const uint32_t bin = wg_coarse_bin(P, p, chunk == 0, s_tmp);
+  if (bin == kAll || chunk * kCmpChunk >= nc) return;
   const int my0 = chunk * kCmpChunk + tid * kCmpPerThread;
-  if (chunk * kCmpChunk >= nc) return;
   for (int i = tid; i < kNBins; i += kThreads) s_h[i] = 0;
   __syncthreads();
   float v[kCmpPerThread];
@@ -616,27 +624,27 @@ __global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
   }
 }
 
-// ---------------------------------------------------------------- 5. band thresholds
-// With the fine bin [L, U] that holds the K-th approximate score a_K (so
-// L <= a_K and U >= a_K >= a_K1): keep a >= L - 2 Delta (every exact Top-K
-// member), certain a > U + 2 Delta.
-__global__ __launch_bounds__(kThreads) void k_thresh2(Params P) {
-  __shared__ uint32_t s_tmp[16];
+// Band thresholds, computed by every compaction work-group from the fine
+// histogram: with the fine bin [L, U] that holds the K-th approximate score
+// a_K (so L <= a_K and U >= a_K >= a_K1), keep a >= L - 2 Delta (every exact
+// Top-K member) and call a > U + 2 Delta certain.  No bin (at most K
+// candidates): keep everything, all certain.
+__device__ void wg_band_thresholds(const Params& P, int p, bool publish, uint32_t* s_tmp /*>= 16*/,
+                                   float* keep_thr, float* in_thr) {
   const int tid = threadIdx.x;
-  const int p = blockIdx.x, kind = p / P.n_q;
+  const int kind = p / P.n_q;
   const int K = (kind == 1) ? P.keep_blocks : P.k;
   const Meta m = P.meta[p];
   if (m.bin == kAll) {
-    if (tid == 0) {
-      P.meta[p].keep_thr = -INFINITY;
-      P.meta[p].in_thr = -INFINITY;
-    }
+    *keep_thr = *in_thr = -INFINITY;
+    if (publish && tid == 0) P.meta[p].keep_thr = P.meta[p].in_thr = -INFINITY;
     return;
   }
   const uint32_t need = (uint32_t)K - m.above;   // >= 1
   const uint32_t* h = P.hist2 + (size_t)p * kNBins;
   constexpr int kPer = kNBins / kThreads;
   const int f_hi = kNBins - kPer * tid - 1;
+  if (tid == 0) s_tmp[12] = s_tmp[13] = __float_as_uint(-INFINITY);   // ordered by the scan's barriers
   uint32_t loc = 0;
   uint32_t hv[kPer];
 #pragma unroll
@@ -652,25 +660,36 @@ __global__ __launch_bounds__(kThreads) void k_thresh2(Params P) {
     for (int j = 0; j < kPer; ++j) {
       if (run + hv[j] >= need) {
         const uint32_t lo_key = (m.bin << kBinShift) | ((uint32_t)(f_hi - j) << 8);
-        P.meta[p].keep_thr = band_below(unsortable(lo_key), m.delta);
-        P.meta[p].in_thr = band_above(unsortable(lo_key + 255u), m.delta);
+        const float kt = band_below(unsortable(lo_key), m.delta);
+        const float it = band_above(unsortable(lo_key + 255u), m.delta);
+        s_tmp[12] = __float_as_uint(kt);
+        s_tmp[13] = __float_as_uint(it);
+        if (publish) {
+          P.meta[p].keep_thr = kt;
+          P.meta[p].in_thr = it;
+        }
         break;
       }
       run += hv[j];
     }
   }
+  __syncthreads();
+  *keep_thr = __uint_as_float(s_tmp[12]);
+  *in_thr = __uint_as_float(s_tmp[13]);
+  __syncthreads();
 }
 
-// ---------------------------------------------------------------- 6. compaction
+// ---------------------------------------------------------------- 4. compaction
 // Band members of one chunk, in position order, flagged certain or not; the
 // uncertain ones are also listed (chunk-local index) for the rescoring.
 __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
   __shared__ uint32_t s_tmp[16];
   const int tid = threadIdx.x;
   const int p = blockIdx.y, chunk = blockIdx.x;
-  const float keep_thr = P.meta[p].keep_thr, in_thr = P.meta[p].in_thr;
   const int nc = P.meta[p].nc;
   const int c0 = chunk * kCmpChunk;
+  float keep_thr = -INFINITY, in_thr = -INFINITY;
+  if (chunk == 0 || c0 < nc) wg_band_thresholds(P, p, chunk == 0, s_tmp, &keep_thr, &in_thr);
   const int my0 = c0 + tid * kCmpPerThread;
   float v[kCmpPerThread];
   const int m = load16(P, p, nc, my0, v);
@@ -727,18 +746,23 @@ __device__ __forceinline__ int chunk_of(const uint32_t* s, int nch, uint32_t j) 
   return lo;
 }
 
-// ---------------------------------------------------------------- 7. rescoring
+// ---------------------------------------------------------------- 5. rescoring
 // Exact scores of the uncertain band members, one member per wave, one lane
-// per head.  The member keys are wave-uniform: each lane loads a slice of
-// them into registers and the values reach every lane through readlane, so
-// the fp32 chains (eight per block, run interleaved) wait on no memory.  The
-// head sum is the ordered fma chain over the lanes' ReLU'd dots.
+// per head.  The lane's query row is held in registers; the member keys
+// (wave-uniform) are converted to fp32 once into the wave's LDS slot and read
+// back as broadcast 16-byte reads, four chain steps per read, the next four
+// dimensions of all eight members loading while the current ones are used.
+// The next member's keys are loaded while the current one is scored.  A block
+// runs its eight member chains interleaved.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
   constexpr int DW = D / 2;            // packed bf16 pairs per key row
   constexpr int KPER = 8 * DW / 64;    // key dwords of 8 members per lane
   __shared__ uint32_t s_tmp[16];
   __shared__ uint32_t s_uoff[kMaxChunksLds + 1];
+  __shared__ __attribute__((aligned(16))) float s_kf[kWaves][8][D];
+  __shared__ __attribute__((aligned(16))) float s_w[kWave];
+  __shared__ __attribute__((aligned(16))) float s_r[kWaves][kWave];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int p = blockIdx.y, q = p % P.n_q, kind = p / P.n_q;
@@ -748,11 +772,11 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
   Entry* band = P.band + (size_t)p * P.stride;
   const uint2* unc = P.unc + (size_t)p * P.stride;
 
-  chunk_prefix(P.chunk_unc + (size_t)p * nch, nch, s_uoff, s_tmp);
+  if (tid < kWave) s_w[tid] = tid < P.h_i ? P.w[(size_t)q * P.h_i + tid] : 0.0f;
+  chunk_prefix(P.chunk_unc + (size_t)p * nch, nch, s_uoff, s_tmp);   // ends with a barrier
   const int nu = (int)s_uoff[nch];
   if (blockIdx.x * kWaves >= nu) return;
-  const float wl = lane < P.h_i ? P.w[(size_t)q * P.h_i + lane] : 0.0f;
-  uint32_t qrow[DW];
+  uint32_t qrow[DW];   // the lane's query row, packed bf16 pairs
   {
     const int hh = lane < P.h_i ? lane : 0;
     const uint4* src = reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + hh) * D);
@@ -765,78 +789,139 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
       qrow[4 * i + 3] = v.w;
     }
   }
+  auto qv = [&](int d) {   // query element d as fp32
+    return (d & 1) ? __uint_as_float(qrow[d >> 1] & 0xFFFF0000u) : __uint_as_float(qrow[d >> 1] << 16);
+  };
+  float* kf = &s_kf[wave][0][0];
 
-  const int stride_w = gridDim.x * kWaves;
-  for (int j = blockIdx.x * kWaves + wave; j < nu; j += stride_w) {
+  // Ordered head sum s = fma(w_h, r_h, s), h ascending, from LDS (every lane
+  // runs the same chain on broadcast reads).  Entries h >= h_i hold w = 0 and
+  // a finite r, so fma(0, r, s) returns s exactly: running all 64 equals the
+  // chain over h < h_i.
+  auto head_sum = [&](float r) {
+    s_r[wave][lane] = r;   // wave-private row: LDS keeps the wave's order
+    float sc = 0.0f;
+#pragma unroll 2
+    for (int h4 = 0; h4 < 16; ++h4) {   // partial unroll: few reads in flight, few VGPRs
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(&s_w[4 * h4]);
+      const f32x4 rv = *reinterpret_cast<const f32x4*>(&s_r[wave][4 * h4]);
+      sc = fmaf(wv.x, rv.x, sc);
+      sc = fmaf(wv.y, rv.y, sc);
+      sc = fmaf(wv.z, rv.z, sc);
+      sc = fmaf(wv.w, rv.w, sc);
+    }
+    return sc;
+  };
+
+  // candidate j of this problem: its band slot, first member and member count
+  struct Cand {
+    uint32_t slot;
+    int first, nmem;
+  };
+  auto locate = [&](int j) {
     const int c = chunk_of(s_uoff, nch, (uint32_t)j);
     const uint2 u = unc[(size_t)c * kCmpChunk + (j - s_uoff[c])];
     const uint32_t cand = __builtin_amdgcn_readfirstlane(u.y);
-    int first, nmem;
+    Cand r;
+    r.slot = (uint32_t)c * kCmpChunk + __builtin_amdgcn_readfirstlane(u.x);
     if (kind == 1) {
-      first = (int)cand * 8;
-      nmem = min(nvis - first, 8);
+      r.first = (int)cand * 8;
+      r.nmem = min(nvis - r.first, 8);
     } else {
-      first = cand_pos(P, q, kind, cand);
-      nmem = 1;
+      r.first = cand_pos(P, q, kind, cand);
+      r.nmem = 1;
     }
-    // dword e of the 8-member key block (member e / DW, dword e % DW) sits in
-    // lane e % 64, register e / 64; members past nmem read as zero
-    uint32_t wv[KPER];
+    return r;
+  };
+  // dword e of the 8-member key block (member e / DW, dword e % DW) goes to
+  // lane e % 64, register e / 64; rows past the member count read member 0
+  auto load_keys = [&](const Cand& c, uint32_t* wv) {
 #pragma unroll
     for (int k = 0; k < KPER; ++k) {
       const int e = lane + 64 * k, t = e / DW, d2 = e % DW;
-      wv[k] = t < nmem ? reinterpret_cast<const uint32_t*>(P.ik + (size_t)(base + first + t) * D)[d2] : 0u;
+      const int tt = t < c.nmem ? t : 0;
+      wv[k] = reinterpret_cast<const uint32_t*>(P.ik + (size_t)(base + c.first + tt) * D)[d2];
     }
-    auto kdw = [&](int t, int d2) -> uint32_t {
-      const int e = t * DW + d2;
-      return (uint32_t)__builtin_amdgcn_readlane((int)wv[e / 64], e % 64);
-    };
+  };
+  auto stage_keys = [&](const Cand& c, const uint32_t* wv) {
+#pragma unroll
+    for (int k = 0; k < KPER; ++k) {
+      const int e = lane + 64 * k, t = e / DW, d2 = e % DW;
+      const uint32_t x = t < c.nmem ? wv[k] : 0u;
+      *reinterpret_cast<f32x2*>(&kf[t * D + 2 * d2]) = f32x2{__uint_as_float(x << 16), __uint_as_float(x & 0xFFFF0000u)};
+    }
+  };
+
+  const int stride_w = gridDim.x * kWaves;
+  int j = blockIdx.x * kWaves + wave;
+  if (j >= nu) return;
+  Cand cur = locate(j);
+  uint32_t wv[KPER];
+  load_keys(cur, wv);
+  for (;;) {
+    stage_keys(cur, wv);
+    const int jn = j + stride_w;
+    const bool more = jn < nu;
+    Cand nxt = cur;
+    if (more) {
+      nxt = locate(jn);
+      load_keys(nxt, wv);   // in flight while the chains below run
+    }
     float r;
     if (kind == 1) {
       float a[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) a[t] = 0.0f;
+      f32x4 kb[2][8];
 #pragma unroll
-      for (int d2 = 0; d2 < DW; ++d2) {
-        const float qlo = __uint_as_float(qrow[d2] << 16), qhi = __uint_as_float(qrow[d2] & 0xFFFF0000u);
+      for (int t = 0; t < 8; ++t) kb[0][t] = *reinterpret_cast<const f32x4*>(&kf[t * D]);
+#pragma unroll
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        if (d4 + 1 < D / 4) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) kb[(d4 + 1) & 1][t] = *reinterpret_cast<const f32x4*>(&kf[t * D + 4 * d4 + 4]);
+        }
+        const float q0 = qv(4 * d4), q1 = qv(4 * d4 + 1), q2 = qv(4 * d4 + 2), q3 = qv(4 * d4 + 3);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const uint32_t kw = kdw(t, d2);
-          a[t] = fmaf(qlo, __uint_as_float(kw << 16), a[t]);
-          a[t] = fmaf(qhi, __uint_as_float(kw & 0xFFFF0000u), a[t]);
+          const f32x4 k4 = kb[d4 & 1][t];
+          a[t] = fmaf(q0, k4.x, a[t]);
+          a[t] = fmaf(q1, k4.y, a[t]);
+          a[t] = fmaf(q2, k4.z, a[t]);
+          a[t] = fmaf(q3, k4.w, a[t]);
         }
       }
       float sum = 0.0f;
 #pragma unroll
       for (int t = 0; t < 8; ++t)
-        if (t < nmem) sum = sum + a[t];
-      const float mean = __fdiv_rn(sum, (float)nmem);
+        if (t < cur.nmem) sum = sum + a[t];
+      const float mean = __fdiv_rn(sum, (float)cur.nmem);
       r = mean > 0.0f ? mean : 0.0f;
     } else {
       float acc = 0.0f;
 #pragma unroll
-      for (int d2 = 0; d2 < DW; ++d2) {
-        const uint32_t kw = kdw(0, d2);
-        acc = fmaf(__uint_as_float(qrow[d2] << 16), __uint_as_float(kw << 16), acc);
-        acc = fmaf(__uint_as_float(qrow[d2] & 0xFFFF0000u), __uint_as_float(kw & 0xFFFF0000u), acc);
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&kf[4 * d4]);
+        acc = fmaf(qv(4 * d4), k4.x, acc);
+        acc = fmaf(qv(4 * d4 + 1), k4.y, acc);
+        acc = fmaf(qv(4 * d4 + 2), k4.z, acc);
+        acc = fmaf(qv(4 * d4 + 3), k4.w, acc);
       }
       r = acc > 0.0f ? acc : 0.0f;
     }
-    // ordered head sum: s = fma(w_h, r_h, s) for h ascending, values read across lanes
-    float sc = 0.0f;
+    const float sc = head_sum(r);
+    if (lane == 0) band[cur.slot].s = sc;
+    if (!more) break;
+    // the prefetched words become visible only here, so their wait stays
+    // below the chains
 #pragma unroll
-    for (int h = 0; h < 64; ++h) {
-      if (h < P.h_i) {
-        const float wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), h));
-        const float rh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), h));
-        sc = fmaf(wh, rh, sc);
-      }
-    }
-    if (lane == 0) band[(size_t)c * kCmpChunk + u.x].s = sc;
+    for (int k = 0; k < KPER; ++k) asm volatile("" : "+v"(wv[k]));
+    cur = nxt;
+    j = jn;
   }
 }
 
-// ---------------------------------------------------------------- 8. final
+// ---------------------------------------------------------------- 6. final
 // One work-group per problem: the certain members plus the best rescored
 // ones (exact score desc, position asc), written as ascending positions and
 // padded with -1.  The band is read in position order through the chunk
@@ -847,7 +932,11 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
   __shared__ uint32_t s_off[kMaxChunksLds + 1];
   __shared__ uint32_t s_key[kBandLds];
   __shared__ uint32_t s_cand[kBandLds];
-  __shared__ uint32_t s_ukey[kUncLds];
+  // the radix path keys the uncertain members, the pairwise path ranks
+  // (key, index) composites: the two never coexist
+  __shared__ __attribute__((aligned(16))) uint32_t s_ukey[kUncLds];
+  uint64_t* s_ucomp = reinterpret_cast<uint64_t*>(s_ukey);
+  __shared__ uint8_t s_usel[kRankMax];
   const int tid = threadIdx.x;
   const int p = blockIdx.x, q = p % P.n_q, kind = p / P.n_q;
   const int nch = P.nchunk_cmp;
@@ -865,40 +954,25 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
     const int c = chunk_of(s_off, nch, (uint32_t)i);
     return band[(size_t)c * kCmpChunk + (i - s_off[c])];
   };
-  if (in_lds) {
-    // strided batches of U independent loads (addresses from the chunk prefix)
-    constexpr int U = 8;
-    int steps = 0;
-    while ((1 << steps) < nch) ++steps;
-    for (int b0 = 0; b0 < n2; b0 += U * kThreads) {
-      // U binary searches in lock step: each step's LDS reads issue together
-      int lo[U], hi[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        lo[u] = 0;
-        hi[u] = nch - 1;
-      }
-      for (int st = 0; st < steps; ++st) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint32_t i = (uint32_t)(b0 + u * kThreads + tid);
-          const int mid = (lo[u] + hi[u] + 1) >> 1;
-          if (lo[u] < hi[u]) {
-            if (s_off[mid] <= i) lo[u] = mid;
-            else hi[u] = mid - 1;
-          }
-        }
-      }
+  if (in_lds && i0 < i1) {
+    // this thread's segment: one search for its first chunk, then a forward
+    // walk; batches of U loads are in flight together
+    constexpr int U = 16;
+    int c = chunk_of(s_off, nch, (uint32_t)i0);
+    for (int b0 = i0; b0 < i1; b0 += U) {
       Entry e[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = b0 + u * kThreads + tid;
-        if (i < n2) e[u] = band[(size_t)lo[u] * kCmpChunk + (i - s_off[lo[u]])];
+        const int i = b0 + u;
+        if (i < i1) {
+          while (s_off[c + 1] <= (uint32_t)i) ++c;
+          e[u] = band[(size_t)c * kCmpChunk + (i - s_off[c])];
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = b0 + u * kThreads + tid;
-        if (i < n2) {
+        const int i = b0 + u;
+        if (i < i1) {
           s_key[i] = sortable(e[u].s);
           s_cand[i] = e[u].cand;
         }
@@ -913,19 +987,61 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
   uint32_t cu = 0;
   for (int i = i0; i < i1; ++i) cu += (cand_of(i) & kCertain) ? 0u : 1u;
   uint32_t nu;
-  uint32_t uo = wg_exclusive_scan(cu, s_tmp, &nu);
+  const uint32_t u_first = wg_exclusive_scan(cu, s_tmp, &nu);
   const int nin = n2 - (int)nu;
   const int need = K - nin;
   const bool take_none = need <= 0;
   const bool take_all = !take_none && (int)nu <= need;
   const bool cut = !take_all && !take_none;
-  const bool u_lds = (int)nu <= kUncLds;
-  if (cut && u_lds)
+  const bool u_lds = (int)nu <= kUncLds - 4;
+  // up to kRankMax uncertain members: rank each against all (larger exact
+  // score first, then lower position, i.e. lower index in this list)
+  const bool pairwise = cut && (int)nu <= kRankMax;
+  if (cut && u_lds) {
+    uint32_t uo = u_first;
     for (int i = i0; i < i1; ++i)
-      if (!(cand_of(i) & kCertain)) s_ukey[uo++] = key(i);
+      if (!(cand_of(i) & kCertain)) {
+        if (pairwise) s_ucomp[uo] = ((uint64_t)key(i) << 32) | (uint64_t)(0xFFFFFFFFu - uo);
+        else s_ukey[uo] = key(i);
+        ++uo;
+      }
+    if (pairwise && tid < 4) s_ucomp[nu + tid] = 0;   // padding: below every member
+  }
   __syncthreads();
   uint32_t kth = 0, ties = 0;
-  if (cut) {
+  if (pairwise) {
+    // composite (key, complement of the list index): a larger composite is a
+    // larger exact score, or an equal one at a lower position; all distinct.
+    // Each thread ranks up to four members (tid + 256 m) in one sweep.
+    const int nu4 = ((int)nu + 3) & ~3;
+    const int mm = ((int)nu + kThreads - 1) / kThreads;   // 1..4
+    uint64_t ci[4];
+    uint32_t r[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i = tid + kThreads * m;
+      ci[m] = i < (int)nu ? s_ucomp[i] : ~0ull;   // absent: nothing ranks above it
+    }
+    auto sweep = [&](auto M) {
+      constexpr int kM = decltype(M)::value;
+      for (int j = 0; j < nu4; j += 4) {
+        const uint64_t c0 = s_ucomp[j], c1 = s_ucomp[j + 1], c2 = s_ucomp[j + 2], c3 = s_ucomp[j + 3];
+#pragma unroll
+        for (int m = 0; m < kM; ++m)
+          r[m] += (c0 > ci[m] ? 1u : 0u) + (c1 > ci[m] ? 1u : 0u) + (c2 > ci[m] ? 1u : 0u) + (c3 > ci[m] ? 1u : 0u);
+      }
+    };
+    if (mm == 1) sweep(std::integral_constant<int, 1>{});
+    else if (mm == 2) sweep(std::integral_constant<int, 2>{});
+    else if (mm == 3) sweep(std::integral_constant<int, 3>{});
+    else sweep(std::integral_constant<int, 4>{});
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i = tid + kThreads * m;
+      if (i < (int)nu) s_usel[i] = r[m] < (uint32_t)need ? 1 : 0;
+    }
+    __syncthreads();
+  } else if (cut) {
     if (u_lds) {
       kth = wg_kth_largest((int)nu, need, [&](int i) { return s_ukey[i]; }, s_hist, s_tmp, &ties);
     } else {
@@ -934,31 +1050,34 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
                            s_hist, s_tmp, &ties);
     }
   }
-  // pass 1 counts the entries tied at the cut, pass 2 the kept ones, pass 3
-  // writes; a tied entry's rank among tied entries follows position order, so
-  // the lower positions win the ties.
-  auto decide = [&](int i, uint32_t& rank) {
+  // Radix-select path: pass 1 counts the entries tied at the cut, pass 2 the
+  // kept ones, pass 3 writes; a tied entry's rank among tied entries follows
+  // position order, so the lower positions win the ties.
+  auto decide = [&](int i, uint32_t& u, uint32_t& rank) {
     const uint32_t c = cand_of(i);
     if (c & kCertain) return true;
+    const uint32_t ui = u++;
     if (take_none) return false;
     if (take_all) return true;
+    if (pairwise) return s_usel[ui] != 0;
     const uint32_t kk = key(i);
     if (kk > kth) return true;
     if (kk == kth) return rank++ < ties;
     return false;
   };
   uint32_t nt = 0;
-  if (cut)
+  if (cut && !pairwise)
     for (int i = i0; i < i1; ++i) nt += (!(cand_of(i) & kCertain) && key(i) == kth) ? 1u : 0u;
   uint32_t tot_t;
   const uint32_t tie_base = wg_exclusive_scan(nt, s_tmp, &tot_t);
-  uint32_t cnt = 0, rank = tie_base;
-  for (int i = i0; i < i1; ++i) cnt += decide(i, rank) ? 1u : 0u;
+  uint32_t cnt = 0, rank = tie_base, u = u_first;
+  for (int i = i0; i < i1; ++i) cnt += decide(i, u, rank) ? 1u : 0u;
   uint32_t tot;
   uint32_t o = wg_exclusive_scan(cnt, s_tmp, &tot);
   rank = tie_base;
+  u = u_first;
   for (int i = i0; i < i1; ++i) {
-    if (decide(i, rank)) {
+    if (decide(i, u, rank)) {
       const uint32_t cand = cand_of(i) & ~kCertain;
       out[o++] = (kind == 1) ? (int)cand : cand_pos(P, q, kind, cand);
     }
@@ -1077,11 +1196,7 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   else launch_scan<64>(P, mt, pool, P.reindex, gscan, s);
   if (!launch_ok()) return CSA2_E_HIP;
   if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return CSA2_E_HIP;
-  hipLaunchKernelGGL(k_thresh, dim3(P.nprob), dim3(kThreads), 0, s, P);
-  if (!launch_ok()) return CSA2_E_HIP;
   hipLaunchKernelGGL(k_finehist, dim3(P.nchunk_cmp, P.nprob), dim3(kThreads), 0, s, P);
-  if (!launch_ok()) return CSA2_E_HIP;
-  hipLaunchKernelGGL(k_thresh2, dim3(P.nprob), dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
   hipLaunchKernelGGL(k_compact, dim3(P.nchunk_cmp, P.nprob), dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;

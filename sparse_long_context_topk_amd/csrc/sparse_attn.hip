@@ -12,6 +12,10 @@
 //
 // Work decomposition: one work-group per (query, split of the key slots);
 // slots [0, k) are the selected entries, [k, k + swa_len) the window rows.
+// A split is a run of 32-slot sub-tiles.  The split's slot positions are
+// staged in LDS first; then, double-buffered, the loads of sub-tile s+1 are
+// in flight while the MFMA work of sub-tile s runs, and are decoded into the
+// other LDS buffer after it.
 // Per 32-slot sub-tile the whole work-group decodes the keys once into LDS,
 // in two layouts (key-major for Q.K, channel-major for P.V), as fp16 -- an
 // E2M1 value times an E4M3 scale has at most 6 significant bits and lies in
@@ -34,6 +38,8 @@ constexpr int kKRow = 512 + 8;      // fp16 per key row in the key-major tile (1
 constexpr int kVRow = kSub + 4;     // fp16 per channel row in the channel-major tile (8 B pad)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxSlotsWG = 3072;   // key slots one work-group stages: k <= 2048 plus a window <= 1024
+constexpr int kMaxSplit = 64;       // splits per query (one wave merges their weights)
 
 struct Params {
   const void* q;
@@ -79,11 +85,24 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Raw words of one thread's share of a sub-tile (8 key slots x 8 channels),
+// loaded one sub-tile ahead of the MFMA work and decoded after it.
+struct Stage {
+  uint32_t w[8][4];   // selected entry: codes dword, scale dword; window row: 8 bf16
+  uint32_t valid;   // bit jj: slot 8*kq + jj holds a key
+};
+
+// Slot classes of a sub-tile: all selected entries, all window rows, or both.
+__device__ __forceinline__ int sub_kind(int slot0, int k) {
+  return slot0 + kSub <= k ? 0 : (slot0 >= k ? 1 : 2);
+}
+
 template <bool QF32>
 __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
-  __shared__ __attribute__((aligned(16))) _Float16 s_k[kSub * kKRow];
-  __shared__ __attribute__((aligned(16))) _Float16 s_v[512 * kVRow];
-  __shared__ uint32_t s_valid[kSub];
+  __shared__ __attribute__((aligned(16))) _Float16 s_k[2][kSub * kKRow];
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[2][512 * kVRow];
+  __shared__ uint32_t s_valid[2][kSub];
+  __shared__ int32_t s_pos[kMaxSlotsWG];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -94,6 +113,14 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
   const int k = P.k;
   const int nswa = P.swa_len ? P.swa_len[qi] : 0;
   const int64_t srow0 = nswa ? P.swa_row0[qi] : 0;
+  const int sub0 = split * P.sub_per_split;
+  const int sub1 = min(sub0 + P.sub_per_split, P.nsub);
+  const int slot_lo = sub0 * kSub;
+  const int sel_hi = min(sub1 * kSub, k);
+  // fallback address for slots without a key: any readable bytes (the query)
+  const uint8_t* fb = static_cast<const uint8_t*>(P.q);
+
+  for (int i = slot_lo + tid; i < sel_hi; i += kThreads) s_pos[i - slot_lo] = P.idx[(size_t)qi * k + i];
 
   // Q^T as the B operand: lane (head n, group g) holds channels 32*ks + 8*g .. +7
   f16x8 qb[16];
@@ -124,69 +151,125 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
       }
     }
   }
+  __syncthreads();   // s_pos
+
+  // decode assignment: thread -> key slots 8*kq .. 8*kq+7, channels 8*cg .. 8*cg+7
+  const int kq = tid & 3, cg = tid >> 2;
+  Stage st;
+
+  // Global loads of a sub-tile, one loader per slot class.  Addresses of
+  // empty slots point at the fallback bytes, so no load is conditional.
+  auto load_sel = [&](int sub) {      // all 32 slots are selected entries
+    const int i0 = sub * kSub + 8 * kq - slot_lo;   // multiple of 8: two 16-byte LDS reads
+    const int4 pa = *reinterpret_cast<const int4*>(&s_pos[i0]);
+    const int4 pb = *reinterpret_cast<const int4*>(&s_pos[i0 + 4]);
+    const int pos[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    st.valid = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const uint8_t* rec = pos[jj] >= 0 ? P.cache + (size_t)(cbase + pos[jj]) * CSA2_KV_RECORD_BYTES : fb;
+      st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
+      st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * (cg >> 3));
+      st.valid |= (pos[jj] >= 0 ? 1u : 0u) << jj;
+    }
+  };
+  auto load_win = [&](int sub) {      // all 32 slots are window rows (or past the window)
+    const int r0 = sub * kSub + 8 * kq - k;
+    st.valid = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const bool ok = r0 + jj < nswa;
+      const uint16_t* src =
+          ok ? P.swa + (size_t)(srow0 + r0 + jj) * 512 + 8 * cg : reinterpret_cast<const uint16_t*>(fb) + 8 * cg;
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
+      st.valid |= (ok ? 1u : 0u) << jj;
+    }
+  };
+  auto load_mixed = [&](int sub) {    // the one sub-tile that straddles slot k
+    const int slot0 = sub * kSub + 8 * kq;
+    st.valid = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int slot = slot0 + jj;
+      st.w[jj][0] = st.w[jj][1] = st.w[jj][2] = st.w[jj][3] = 0u;
+      if (slot < k) {
+        const int pos = s_pos[slot - slot_lo];
+        if (pos >= 0) {
+          const uint8_t* rec = P.cache + (size_t)(cbase + pos) * CSA2_KV_RECORD_BYTES;
+          st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
+          st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * (cg >> 3));
+          st.valid |= 1u << jj;
+        }
+      } else if (slot - k < nswa) {
+        const uint4 v = *reinterpret_cast<const uint4*>(P.swa + (size_t)(srow0 + slot - k) * 512 + 8 * cg);
+        st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
+        st.valid |= 1u << jj;
+      }
+    }
+  };
+  auto load_stage = [&](int sub) {
+    const int kind = sub_kind(sub * kSub, k);
+    if (kind == 0) load_sel(sub);
+    else if (kind == 1) load_win(sub);
+    else load_mixed(sub);
+  };
+
+  // Decode the loaded words to fp16 and write both LDS layouts of buffer b.
+  auto store_stage = [&](int sub, int b) {
+    const int slot0 = sub * kSub;
+    const int sc_shift = 8 * ((cg >> 1) & 3);   // this thread's scale byte in the loaded scale dword
+    uint32_t vals[8][4];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const bool is_sel = slot0 + 8 * kq + jj < k;
+      const uint32_t keep = (st.valid >> jj) & 1u ? 0xFFFFFFFFu : 0u;
+      uint32_t dv[4], sv[4];
+      decode8(st.w[jj][0], (_Float16)e4m3_to_f32((st.w[jj][1] >> sc_shift) & 0xFFu), dv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sv[j] = pack_f16(__uint_as_float(st.w[jj][j] << 16), __uint_as_float(st.w[jj][j] & 0xFFFF0000u));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vals[jj][j] = (is_sel ? dv[j] : sv[j]) & keep;
+      if (cg == 0) s_valid[b][8 * kq + jj] = keep & 1u;
+      *reinterpret_cast<uint4*>(&s_k[b][(8 * kq + jj) * kKRow + 8 * cg]) =
+          make_uint4(vals[jj][0], vals[jj][1], vals[jj][2], vals[jj][3]);
+    }
+    // channel-major copy: row (channel 8*cg + c) gets key slots 8*kq .. 8*kq+7
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int jp = 0; jp < 4; ++jp) {
+        const uint32_t a = vals[2 * jp][c >> 1], bb = vals[2 * jp + 1][c >> 1];
+        // take the low (c even) or high (c odd) fp16 of each
+        pk[jp] = (c & 1) ? __builtin_amdgcn_perm(bb, a, 0x07060302u) : __builtin_amdgcn_perm(bb, a, 0x05040100u);
+      }
+      uint2* dst = reinterpret_cast<uint2*>(&s_v[b][(8 * cg + c) * kVRow + 8 * kq]);
+      dst[0] = make_uint2(pk[0], pk[1]);
+      dst[1] = make_uint2(pk[2], pk[3]);
+    }
+  };
 
   f32x4 o[32];
 #pragma unroll
   for (int t = 0; t < 32; ++t) o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // decode assignment: thread -> keys 8*kq .. 8*kq+7, channels 8*cg .. 8*cg+7
-  const int kq = tid & 3, cg = tid >> 2;
-  const int sub0 = split * P.sub_per_split;
-  const int sub1 = min(sub0 + P.sub_per_split, P.nsub);
+  if (sub0 < sub1) {
+    load_stage(sub0);
+    store_stage(sub0, 0);
+  }
+  __syncthreads();
 
-  for (int sub = sub0; sub < sub1; ++sub) {
-    const int slot0 = sub * kSub;
-    uint32_t vals[8][4];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int slot = slot0 + 8 * kq + jj;
-      bool valid = false;
-      vals[jj][0] = vals[jj][1] = vals[jj][2] = vals[jj][3] = 0u;
-      if (slot < k) {
-        const int pos = P.idx[(size_t)qi * k + slot];
-        if (pos >= 0) {
-          valid = true;
-          const uint8_t* rec = P.cache + (size_t)(cbase + pos) * CSA2_KV_RECORD_BYTES;
-          const uint32_t codes = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
-          const _Float16 sc = (_Float16)e4m3_to_f32(rec[256 + (cg >> 1)]);
-          decode8(codes, sc, vals[jj]);
-        }
-      } else if (slot - k < nswa) {
-        valid = true;
-        const uint4 r = *reinterpret_cast<const uint4*>(P.swa + (size_t)(srow0 + slot - k) * 512 + 8 * cg);
-        const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vals[jj][j] = pack_f16(__uint_as_float(wd[j] << 16), __uint_as_float(wd[j] & 0xFFFF0000u));
-      }
-      if (cg == 0) s_valid[8 * kq + jj] = valid ? 1u : 0u;
-      *reinterpret_cast<uint4*>(&s_k[(8 * kq + jj) * kKRow + 8 * cg]) =
-          make_uint4(vals[jj][0], vals[jj][1], vals[jj][2], vals[jj][3]);
-    }
-    // channel-major copy: row (channel 8*cg + c) gets keys 8*kq .. 8*kq+7
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int jp = 0; jp < 4; ++jp) {
-        const uint32_t a = vals[2 * jp][c >> 1], b = vals[2 * jp + 1][c >> 1];
-        // take the low (c even) or high (c odd) fp16 of each
-        pk[jp] = (c & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u) : __builtin_amdgcn_perm(b, a, 0x05040100u);
-      }
-      uint2* dst = reinterpret_cast<uint2*>(&s_v[(8 * cg + c) * kVRow + 8 * kq]);
-      dst[0] = make_uint2(pk[0], pk[1]);
-      dst[1] = make_uint2(pk[2], pk[3]);
-    }
-    __syncthreads();
-
+  auto compute = [&](int b) {
     if (head_wave) {
       // ---- S^T = K Q^T : lane (head n, g) gets keys 16*kt + 4*g + i
       f32x4 sacc[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         sacc[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        const _Float16* krow = &s_k[(16 * kt + n) * kKRow + 8 * g];
+        const _Float16* krow = &s_k[b][(16 * kt + n) * kKRow + 8 * g];
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
           const f16x8 a = *reinterpret_cast<const f16x8*>(krow + 32 * ks);
@@ -201,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = 16 * kt + 4 * g + i;
-          const float v = s_valid[key] ? sacc[kt][i] * P.scale_log2 : -INFINITY;
+          const float v = s_valid[b][key] ? sacc[kt][i] * P.scale_log2 : -INFINITY;
           z[4 * kt + i] = v;
           mx = fmaxf(mx, v);
         }
@@ -223,14 +306,17 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
       for (int j = 0; j < 8; ++j) ps += pv[j];
       l_run = l_run * alpha + ps;
       m_run = m_new;
-      // rescale O rows (heads 4*g + i live in this lane's accumulators)
-      float a4[4];
+      // rescale O rows (heads 4*g + i live in this lane's accumulators); a
+      // wave whose maxima did not move skips it
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+        float a4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, kWave);
+        for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, kWave);
 #pragma unroll
-      for (int t = 0; t < 32; ++t)
+        for (int t = 0; t < 32; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[t][i] *= a4[i];
+          for (int i = 0; i < 4; ++i) o[t][i] *= a4[i];
+      }
       // P as the A operand: slots 0..3 = keys 4g+i, slots 4..7 = keys 16+4g+i
       f16x8 pa;
 #pragma unroll
@@ -238,13 +324,32 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
       // ---- O += P V
 #pragma unroll
       for (int t = 0; t < 32; ++t) {
-        const _Float16* vrow = &s_v[(16 * t + n) * kVRow];
+        const _Float16* vrow = &s_v[b][(16 * t + n) * kVRow];
         const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * g);
         const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
-        const f16x8 b = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, b, o[t], 0, 0, 0);
+        const f16x8 bv = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, o[t], 0, 0, 0);
       }
     }
+  };
+
+  // Selected-entry sub-tiles (all but the last few) are prefetched: their
+  // loads stay in flight during this sub-tile's MFMA work.  Window and
+  // straddling sub-tiles load after it.
+  for (int sub = sub0; sub < sub1; ++sub) {
+    const int b = (sub - sub0) & 1;
+    const int kind = sub + 1 < sub1 ? sub_kind((sub + 1) * kSub, k) : 3;
+    if (kind == 0) load_sel(sub + 1);
+    compute(b);
+    if (kind == 0) {
+      // the loaded words become visible to the decode only here, so the
+      // compiler cannot hoist the decode (and its wait) above the MFMA work
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) asm volatile("" : "+v"(st.w[jj][0]), "+v"(st.w[jj][1]));
+    }
+    if (kind == 1) load_win(sub + 1);
+    else if (kind == 2) load_mixed(sub + 1);
+    if (kind != 3) store_stage(sub + 1, b ^ 1);   // the other buffer: last read before the previous barrier
     __syncthreads();
   }
 
@@ -253,12 +358,9 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
   l_tot += __shfl_xor(l_tot, 16, kWave);
   l_tot += __shfl_xor(l_tot, 32, kWave);
   // per-row (head 4*g + i) values for this lane's accumulators
-  float lrow[4], mrow[4];
+  float lrow[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lrow[i] = __shfl(l_tot, 4 * g + i, kWave);
-    mrow[i] = __shfl(m_run, 4 * g + i, kWave);
-  }
+  for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l_tot, 4 * g + i, kWave);
   if (P.nsplit == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -287,26 +389,59 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One work-group per (query, head); the first wave turns the (m_s, l_s) pairs
+// into weights, then every thread sums two channels over the splits with all
+// loads of a batch of splits in flight.
 __global__ __launch_bounds__(kThreads) void k_merge(Params P) {
-  const int qi = blockIdx.x, hh = blockIdx.y;
-  float M = -INFINITY;
-  for (int s = 0; s < P.nsplit; ++s)
-    M = fmaxf(M, P.part_ml[(((size_t)qi * P.nsplit + s) * P.h + hh) * 2]);
-  float L = 0.0f, acc0 = 0.0f, acc1 = 0.0f;
-  const int c = threadIdx.x;
-  for (int s = 0; s < P.nsplit; ++s) {
-    const float* ml = P.part_ml + (((size_t)qi * P.nsplit + s) * P.h + hh) * 2;
-    const float wgt = (ml[0] == -INFINITY) ? 0.0f : exp2f(ml[0] - M);
-    L = fmaf(wgt, ml[1], L);
-    const float* po = P.part_o + (((size_t)qi * P.nsplit + s) * P.h + hh) * 512;
-    acc0 = fmaf(wgt, po[c], acc0);
-    acc1 = fmaf(wgt, po[c + 256], acc1);
+  __shared__ float s_w[kMaxSplit];
+  __shared__ float s_ml[2];
+  const int qi = blockIdx.x, hh = blockIdx.y, c = threadIdx.x;
+  const int ns = P.nsplit;
+  const size_t row0 = (size_t)qi * ns * P.h + hh;   // row of split 0; split s adds s * h
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    float m = -INFINITY, l = 0.0f;
+    if (s < ns) {
+      const float2 v = *reinterpret_cast<const float2*>(P.part_ml + (row0 + (size_t)s * P.h) * 2);
+      m = v.x;
+      l = v.y;
+    }
+    const float M = wave_max(m);
+    const float w = (s < ns && m != -INFINITY) ? exp2f(m - M) : 0.0f;
+    const float L = wave_sum(w * l);
+    if (s < ns) s_w[s] = w;
+    if (s == 0) {
+      s_ml[0] = M;
+      s_ml[1] = L;
+    }
   }
+  __syncthreads();
+  const float* po = P.part_o + row0 * 512;
+  const size_t so = (size_t)P.h * 512;
+  float acc0 = 0.0f, acc1 = 0.0f;
+  constexpr int U = 8;
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    float x0[U], x1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + u, ns - 1);
+      x0[u] = po[s * so + c];
+      x1[u] = po[s * so + c + 256];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < ns) {
+        acc0 = fmaf(s_w[s0 + u], x0[u], acc0);
+        acc1 = fmaf(s_w[s0 + u], x1[u], acc1);
+      }
+    }
+  }
+  const float L = s_ml[1];
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   float* dst = P.out + ((size_t)qi * P.h + hh) * 512;
   dst[c] = acc0 * inv;
   dst[c + 256] = acc1 * inv;
-  if (P.lse && c == 0) P.lse[(size_t)qi * P.h + hh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  if (P.lse && c == 0) P.lse[(size_t)qi * P.h + hh] = L > 0.0f ? (s_ml[0] + log2f(L)) * kLn2 : -INFINITY;
 }
 
 }  // namespace attn
@@ -331,8 +466,8 @@ Split choose_split(int n_q, int k, int w_max) {
   Split s;
   const int nslots = k + w_max;
   s.nsub = std::max(1, (nslots + kSub - 1) / kSub);
-  const int target =
-      std::max(1, std::min(s.nsub, (CSA2_ATTN_WG_TARGET + n_q - 1) / std::max(n_q, 1)));
+  const int target = std::max(
+      1, std::min({s.nsub, kMaxSplit, (CSA2_ATTN_WG_TARGET + n_q - 1) / std::max(n_q, 1)}));
   s.per = (s.nsub + target - 1) / target;
   s.nsplit = (s.nsub + s.per - 1) / s.per;
   return s;
