@@ -66,7 +66,13 @@ constexpr int kCmpChunk = 4096;
 constexpr int kCmpPerThread = kCmpChunk / kThreads;
 constexpr int kMaxChunksLds = 8192;   // compaction chunks per problem (max_nvis <= 2^25)
 constexpr int kRescoreWGs = 128;
-constexpr int kMaxScanChunk = 4096;
+#ifndef CSA2_SCAN_NBUF
+#define CSA2_SCAN_NBUF 3
+#endif
+#ifndef CSA2_SCAN_CHUNK
+#define CSA2_SCAN_CHUNK 8192
+#endif
+constexpr int kMaxScanChunk = CSA2_SCAN_CHUNK;   // keys per scan work-group (Full layers)
 constexpr int kBandLds = 12288;      // band entries the final kernel keeps in LDS (96 KiB)
 constexpr int kUncLds = 4096;        // uncertain members whose keys the final kernel keeps in LDS
 constexpr int kRankMax = 1024;       // uncertain members the final kernel ranks pairwise
@@ -359,8 +365,7 @@ __device__ uint32_t wg_coarse_bin(const Params& P, int p, bool publish, uint32_t
 template <int D, int MT, bool POOL, bool INDIRECT>
 __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   constexpr int KS = D / 32;   // MFMA k-steps; also 16-byte loads per lane per key
-  constexpr int DPL = D / 4;   // key dims held by one lane (a quarter of the key)
-  constexpr int NBUF = 3;      // key groups in registers: two in flight, one in use
+  constexpr int NBUF = CSA2_SCAN_NBUF;   // key groups in registers: NBUF-1 in flight, one in use
   __shared__ uint32_t s_hist[kNBins];
   __shared__ uint32_t s_hist_b[POOL ? kNBins : 1];
   __shared__ int32_t s_pool[INDIRECT ? 512 : 1];
@@ -393,7 +398,9 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     }
   }
 
-  // Q^T as the MFMA B operand: lane (n, g) holds head 16*mt + n, dims g*DPL + 8*ks .. +7
+  // Q^T as the MFMA B operand: lane (n, g) holds head 16*mt + n, dims 32*ks + 8*g .. +7
+  // (the natural k-layout: for each k-step the four lane groups cover 64
+  // contiguous bytes of a row, so every key load instruction reads whole lines)
   bf16x8 qb[MT][KS];
   float wr[MT];
 #pragma unroll
@@ -403,12 +410,17 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (head < P.h_i)
-        v = *reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + head) * D + g * DPL + 8 * ks);
+        v = *reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + head) * D + 32 * ks + 8 * g);
       qb[mt][ks] = __builtin_bit_cast(bf16x8, v);
     }
     wr[mt] = head < P.h_i ? P.w[(size_t)q * P.h_i + head] : 0.0f;
   }
-  __syncthreads();
+  // LDS-only barrier: orders the histogram clear and the pool ids before any
+  // wave uses them, without waiting for the query loads still in flight (the
+  // first key loads below then overlap them)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
   float mk2 = 0.0f;
   float* sc = P.scores + (size_t)p * P.stride;
@@ -435,9 +447,9 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   };
   auto load = [&](int it, uint4* kb) {
     bool v;
-    const uint4* src = reinterpret_cast<const uint4*>(P.ik + (size_t)key_row(min(it, my_groups - 1), v) * D + g * DPL);
+    const uint4* src = reinterpret_cast<const uint4*>(P.ik + (size_t)key_row(min(it, my_groups - 1), v) * D + 8 * g);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kb[ks] = src[ks];
+    for (int ks = 0; ks < KS; ++ks) kb[ks] = src[4 * ks];
   };
 
   auto process = [&](int it, const uint4* kin) {
@@ -1258,7 +1270,7 @@ extern "C" csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n
   P.idx_out = idx_out; P.pool_out = pool_out;
   P.nprob = n_q * (keep_blocks > 0 ? 2 : 1);
   P.reindex = 0;
-  P.scan_chunk = 4096;
+  P.scan_chunk = kMaxScanChunk;
   P.stride = round_up(std::max<int64_t>(max_nvis, 1), kCmpChunk);
   P.nchunk_cmp = (int)(P.stride / kCmpChunk);
   const size_t need = csa2_index_topk_ws_bytes(n_q, max_nvis, h_i, d_i, k, block, keep_blocks);
