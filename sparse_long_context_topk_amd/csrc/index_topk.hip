@@ -125,6 +125,7 @@ struct Params {
   uint32_t* chunk_unc;  // [nprob][nchunk_cmp] uncertain members per chunk
   Entry* band;          // [nprob][stride] band members, chunk c at c*kCmpChunk, in position order
   uint2* unc;           // [nprob][stride] uncertain members: {chunk-local index, candidate}
+  float* kpart;         // Reindex scan: [n_q][scan work-groups] largest squared key norm of each
 };
 
 // ---------------------------------------------------------------- helpers
@@ -366,7 +367,9 @@ template <int D, int MT, bool POOL, bool INDIRECT>
 __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   constexpr int KS = D / 32;   // MFMA k-steps; also 16-byte loads per lane per key
   constexpr int NBUF = CSA2_SCAN_NBUF;   // key groups in registers: NBUF-1 in flight, one in use
-  __shared__ uint32_t s_hist[kNBins];
+  // the Reindex variant keeps no histograms: its selection runs in one
+  // work-group per query that sees every score
+  __shared__ uint32_t s_hist[INDIRECT ? 1 : kNBins];
   __shared__ uint32_t s_hist_b[POOL ? kNBins : 1];
   __shared__ int32_t s_pool[INDIRECT ? 512 : 1];
   // the chunk's scores stay in LDS until the end: the hot loop then issues
@@ -386,9 +389,11 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   const int nblk = (nvis + 7) >> 3;
   const int c0 = blockIdx.x * P.scan_chunk;
 
-  for (int i = tid; i < kNBins; i += kThreads) {
-    s_hist[i] = 0;
-    if (POOL) s_hist_b[i] = 0;
+  if constexpr (!INDIRECT) {
+    for (int i = tid; i < kNBins; i += kThreads) {
+      s_hist[i] = 0;
+      if (POOL) s_hist_b[i] = 0;
+    }
   }
   if constexpr (INDIRECT) {
     // block ids of this chunk's pool slots (scan_chunk / 8 <= 512 of them)
@@ -508,7 +513,9 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
         cvalid = cand < nc;
       }
       s_sc[cand - c0] = cvalid ? si : -INFINITY;
-      if (n < 4 && cvalid) atomicAdd(&s_hist[sortable(si) >> kBinShift], 1u);
+      if constexpr (!INDIRECT) {
+        if (n < 4 && cvalid) atomicAdd(&s_hist[sortable(si) >> kBinShift], 1u);
+      }
     }
     if constexpr (POOL) {
       // block j = g/2 holds keys 8j..8j+7 = rows 4g+i of lane groups g and g^1
@@ -566,7 +573,16 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     const int nbs = min((nslots + 7) >> 3, max(nblk - (c0 >> 3), 0));
     for (int i = tid; i < nbs; i += kThreads) scb[(c0 >> 3) + i] = s_scb[i];
   }
-  {
+  if constexpr (INDIRECT) {
+    mk2 = wave_max(mk2);
+    if (lane == 0) s_tmp[wave] = __float_as_uint(mk2);
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t m0 = 0;
+      for (int i = 0; i < kWaves; ++i) m0 = max(m0, s_tmp[i]);
+      P.kpart[(size_t)q * gridDim.x + blockIdx.x] = __uint_as_float(m0);
+    }
+  } else {
     uint32_t* gh = P.hist + (size_t)p * kNBins;
     for (int i = tid; i < kNBins; i += kThreads) {
       const uint32_t c = s_hist[i];
@@ -1097,6 +1113,417 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
   for (int i = (int)tot + tid; i < K; i += kThreads) out[i] = -1;
 }
 
+// ---------------------------------------------------------------- 7. small problems
+// A problem with at most kSmallMax candidates (a Reindex layer's pool) is
+// selected by one work-group per query that holds every approximate score:
+// thread t owns the contiguous slots [32 t, 32 t + 32), keys in registers.  A
+// radix select gives the K-th approximate score a_K exactly, and a_K1 (the
+// (K+1)-th) from its tie count; every exact Top-K member has approximate score
+// >= a_K - 2 Delta and a member above a_K1 + 2 Delta is certainly in (at most K
+// members have approximate score > a_K1, and only they can reach its exact
+// score).  The members in between are rescored with the exact fp32 chains
+// (one wave per member, one lane per head); among them the final choice is by
+// (exact score desc, position asc).  Slots are in position order (pool blocks
+// ascending), so a prefix sum over the threads' segments places the output.
+constexpr int kSmallMax = 16384;
+constexpr int kSmallThreads = 512;
+constexpr int kSmallWaves = kSmallThreads / kWave;
+constexpr int kSmallPer = kSmallMax / kSmallThreads;   // slots per thread
+
+// Exclusive prefix sum over the 512-thread work-group (s_tmp: >= 8 entries).
+__device__ __forceinline__ uint32_t wg8_exclusive_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_tmp[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kSmallWaves; ++i) {
+    const uint32_t t = s_tmp[i];
+    if (i < wave) before += t;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+// K-th largest of the register keys for which elig(key) holds (1 <= K <=
+// their count): most-significant-digit radix select, 8-bit digits starting at
+// the highest bit where the smallest and largest eligible key differ; one
+// 256-bin histogram per wave.  *ties = how many keys equal to the result
+// belong to the Top-K, *eq = how many eligible keys equal it.
+//
+// With stop_bits > 0 the search may end once at most stop_bits low bits are
+// undetermined: the result r then satisfies r <= K-th largest <= r | *span
+// (*span = the undetermined low-bit mask; 0 when exact), and *ties / *eq are
+// not meaningful.
+template <typename Elig>
+__device__ uint32_t small_kth(const uint32_t key[kSmallPer], Elig elig, int K, uint32_t* s_h /*8*256*/,
+                              uint32_t* s_tmp /*>= 24*/, uint32_t* ties, uint32_t* eq, int stop_bits = 0,
+                              uint32_t* span = nullptr) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u, c = 0;
+#pragma unroll
+  for (int j = 0; j < kSmallPer; ++j) {
+    const bool e = elig(key[j]);
+    lo = e ? min(lo, key[j]) : lo;
+    hi = e ? max(hi, key[j]) : hi;
+    c += e ? 1u : 0u;
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max(hi);
+  if (lane == 0) {
+    s_tmp[wave] = lo;
+    s_tmp[8 + wave] = hi;
+  }
+  __syncthreads();
+  lo = 0xFFFFFFFFu;
+  hi = 0u;
+#pragma unroll
+  for (int i = 0; i < kSmallWaves; ++i) {
+    lo = min(lo, s_tmp[i]);
+    hi = max(hi, s_tmp[8 + i]);
+  }
+  __syncthreads();
+  if (span) *span = 0u;
+  if (lo == hi) {
+    uint32_t tot;
+    (void)wg8_exclusive_scan(c, s_tmp, &tot);
+    *ties = (uint32_t)K;
+    *eq = tot;
+    return lo;
+  }
+  const int top = 31 - __clz(lo ^ hi);
+  uint32_t mask = top == 31 ? 0u : (0xFFFFFFFFu << (top + 1));
+  uint32_t prefix = lo & mask;
+  uint32_t remaining = (uint32_t)K;
+  uint32_t cnt_digit = 0;
+  for (int shift = top - 7;; shift -= 8) {
+    const int sh = shift < 0 ? 0 : shift;
+    const int width = shift < 0 ? 8 + shift : 8;
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int i = tid; i < kSmallWaves * 256; i += kSmallThreads) s_h[i] = 0;
+    __syncthreads();
+    uint32_t* h = s_h + wave * 256;
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j)
+      if (elig(key[j]) && (key[j] & mask) == prefix) atomicAdd(&h[(key[j] >> sh) & dmask], 1u);
+    __syncthreads();
+    // thread tid < 256 owns digit 255 - tid; the exclusive scan counts larger digits
+    uint32_t v = 0;
+    const int dg = 255 - tid;
+    if (tid < 256) {
+#pragma unroll
+      for (int w = 0; w < kSmallWaves; ++w) v += s_h[w * 256 + dg];
+    }
+    uint32_t tot;
+    const uint32_t excl = wg8_exclusive_scan(v, s_tmp, &tot);
+    if (tid < 256 && excl < remaining && excl + v >= remaining) {
+      s_tmp[16] = (uint32_t)dg;
+      s_tmp[17] = excl;
+      s_tmp[18] = v;
+    }
+    __syncthreads();
+    const uint32_t d = s_tmp[16];
+    remaining -= s_tmp[17];
+    cnt_digit = s_tmp[18];
+    prefix |= d << sh;
+    mask |= dmask << sh;
+    __syncthreads();
+    if (sh == 0) break;
+    if (sh <= stop_bits) {
+      *span = (1u << sh) - 1u;
+      return prefix;
+    }
+  }
+  *ties = remaining;
+  *eq = cnt_digit;   // the last digit's bucket holds exactly the keys equal to the result
+  return prefix;
+}
+
+// Slot states in the key registers: 0 = no candidate or out of the band,
+// kSure = certainly selected, anything else = a key to be ranked.
+constexpr uint32_t kSure = 0xFFFFFFFFu;   // above every finite score's sortable key
+
+template <int D>
+__global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
+  constexpr int DW = D / 2;
+  __shared__ uint32_t s_key[kSmallMax];      // exact keys of rescored slots
+  __shared__ int32_t s_pool[kSmallMax / 8];
+  __shared__ uint16_t s_ul[kSmallMax];       // uncertain slots
+  __shared__ uint32_t s_h[kSmallWaves * 256];
+  __shared__ uint32_t s_tmp[32];
+  __shared__ float s_par[4];
+  __shared__ float s_qn[kWave];
+  __shared__ __attribute__((aligned(16))) float s_w[kWave];
+  __shared__ __attribute__((aligned(16))) float s_r[kSmallWaves][2][kWave];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = blockIdx.x;
+  const int K = P.k;
+  const int nc = 8 * P.keep_in;
+  const int64_t base = P.seq_base[P.q_seq[q]];
+  const float* sc = P.scores + (size_t)q * P.stride;
+  int32_t* out = P.idx_out + (size_t)q * K;
+  const int s0 = tid * kSmallPer;   // this thread's first slot
+
+  // every load of the prologue is issued before any of them is used; indices
+  // are clamped so that no load is conditional
+  constexpr int kSeg = D / 8;               // query dims per thread: eight threads per head
+  const int h = tid >> 3, part = tid & 7;
+  const int nwg = (nc + P.scan_chunk - 1) / P.scan_chunk;   // <= 64
+  float4 raw[kSmallPer / 4];
+#pragma unroll
+  for (int j4 = 0; j4 < kSmallPer / 4; ++j4)
+    raw[j4] = *reinterpret_cast<const float4*>(sc + min(s0 + 4 * j4, nc - 4));   // nc is a multiple of 8
+  int32_t praw[kSmallMax / 8 / kSmallThreads];
+#pragma unroll
+  for (int k = 0; k < kSmallMax / 8 / kSmallThreads; ++k)
+    praw[k] = P.pool_in[(size_t)q * P.keep_in + min(tid + kSmallThreads * k, P.keep_in - 1)];
+  uint4 qseg[kSeg / 8];
+  {
+    const uint4* qh = reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + min(h, P.h_i - 1)) * D + part * kSeg);
+#pragma unroll
+    for (int i = 0; i < kSeg / 8; ++i) qseg[i] = qh[i];
+  }
+  const float wraw = P.w[(size_t)q * P.h_i + min(tid & 63, P.h_i - 1)];
+  const float kraw = P.kpart[(size_t)q * nwg + min(tid & 63, nwg - 1)];
+
+  // approximate scores -> sortable keys in registers (0: no candidate)
+  uint32_t key[kSmallPer];
+#pragma unroll
+  for (int j4 = 0; j4 < kSmallPer / 4; ++j4) {
+    const bool in = s0 + 4 * j4 < nc;
+    const float vv[4] = {raw[j4].x, raw[j4].y, raw[j4].z, raw[j4].w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) key[4 * j4 + u] = (in && vv[u] != -INFINITY) ? sortable(vv[u]) : 0u;
+  }
+  uint32_t nv_loc = 0;
+#pragma unroll
+  for (int j = 0; j < kSmallPer; ++j) nv_loc += key[j] != 0u ? 1u : 0u;
+#pragma unroll
+  for (int k = 0; k < kSmallMax / 8 / kSmallThreads; ++k)
+    if (tid + kSmallThreads * k < nc / 8) s_pool[tid + kSmallThreads * k] = praw[k];
+  if (tid < kWave) s_w[tid] = tid < P.h_i ? wraw : 0.0f;
+  // rounding bound Delta = C * QW * max||k|| (as the multi-kernel path)
+  {
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kSeg / 8; ++i) {
+      const uint32_t wd[4] = {qseg[i].x, qseg[i].y, qseg[i].z, qseg[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = __uint_as_float(wd[j] << 16), hi = __uint_as_float(wd[j] & 0xFFFF0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+    }
+    ss += __shfl_xor(ss, 1, kWave);
+    ss += __shfl_xor(ss, 2, kWave);
+    ss += __shfl_xor(ss, 4, kWave);
+    if (part == 0) s_qn[h] = h < P.h_i ? sqrtf(ss) : 0.0f;   // times |w_h| below
+    if (wave == 0) {
+      const float mk = wave_max(lane < nwg ? kraw : 0.0f);
+      if (lane == 0) s_par[1] = mk;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const float qn = wave_sum(fabsf(s_w[lane]) * s_qn[lane]);
+    const float wa = wave_sum(fabsf(s_w[lane]));
+    if (lane == 0)
+      s_par[0] = P.bound_tok * (qn * (1.0f + 0.0009765625f)) * sqrtf(s_par[1]) * (1.0f + 0.0009765625f) +
+                 wa * (float)P.d_i * 7.8886e-31f;
+  }
+  uint32_t nv;
+  (void)wg8_exclusive_scan(nv_loc, s_tmp, &nv);   // its barriers publish s_pool, s_w, s_par
+  const float delta = s_par[0];
+
+  // classify into the key registers: kSure, 0 (out), or the approximate key
+  // of an uncertain member
+  auto is_real = [](uint32_t k) { return k != 0u && k != kSure; };
+  if ((int)nv > K) {
+    // bracket the K-th approximate score: L <= a_K and U >= a_K >= a_K1 (the
+    // last 8 bits of the key, 2^-15 of the value, are left open)
+    uint32_t ties, eq, span;
+    const uint32_t kL = small_kth(key, is_real, K, s_h, s_tmp, &ties, &eq, 8, &span);
+    const uint32_t kK = kL, kK1 = kL | span;
+    const float keep_thr = band_below(unsortable(kK), delta);    // L - 2 Delta
+    const float in_thr = band_above(unsortable(kK1), delta);     // U + 2 Delta
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j) {
+      const float v = unsortable(key[j]);
+      key[j] = key[j] == 0u || !(v >= keep_thr) ? 0u : (v > in_thr ? kSure : key[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j) key[j] = key[j] != 0u ? kSure : 0u;
+  }
+  // uncertain list (any order: exact keys go back to their slots)
+  uint32_t cu = 0;
+#pragma unroll
+  for (int j = 0; j < kSmallPer; ++j) cu += is_real(key[j]) ? 1u : 0u;
+  uint32_t nu;
+  uint32_t uo = wg8_exclusive_scan(cu, s_tmp, &nu);
+#pragma unroll
+  for (int j = 0; j < kSmallPer; ++j)
+    if (is_real(key[j])) s_ul[uo++] = (uint16_t)(s0 + j);
+  __syncthreads();
+
+  // exact scores of the uncertain members: one wave per member, lane = head;
+  // the key row reaches the lanes through readlane, the next row loads meanwhile
+  if (nu > 0) {
+    uint32_t qrow[DW];   // the lane's query row, packed bf16 pairs
+    {
+      const int hh = lane < P.h_i ? lane : 0;
+      const uint4* src = reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + hh) * D);
+#pragma unroll
+      for (int i = 0; i < DW / 4; ++i) {
+        const uint4 v = src[i];
+        qrow[4 * i] = v.x;
+        qrow[4 * i + 1] = v.y;
+        qrow[4 * i + 2] = v.z;
+        qrow[4 * i + 3] = v.w;
+      }
+    }
+    auto load_row = [&](int j) -> uint32_t {
+      const int slot = s_ul[min(j, (int)nu - 1)];
+      const int64_t row = base + (int64_t)s_pool[slot >> 3] * 8 + (slot & 7);
+      const int l = lane < DW ? lane : 0;
+      return reinterpret_cast<const uint32_t*>(P.ik + (size_t)row * D)[l];
+    };
+    // wave w scores members 2w + 16 r and 2w + 1 + 16 r, chains interleaved
+    constexpr int kStep = 2 * kSmallWaves;
+    int j = 2 * wave;
+    uint32_t kw0 = 0, kw1 = 0;
+    if (j < (int)nu) {
+      kw0 = load_row(j);
+      kw1 = load_row(j + 1);
+    }
+    for (; j < (int)nu; j += kStep) {
+      const uint32_t c0 = kw0, c1 = kw1;
+      if (j + kStep < (int)nu) {   // in flight during the chains
+        kw0 = load_row(j + kStep);
+        kw1 = load_row(j + kStep + 1);
+      }
+      float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+      for (int d2 = 0; d2 < DW; ++d2) {
+        const uint32_t x0 = (uint32_t)__builtin_amdgcn_readlane((int)c0, d2);
+        const uint32_t x1 = (uint32_t)__builtin_amdgcn_readlane((int)c1, d2);
+        const float ql = __uint_as_float(qrow[d2] << 16), qh = __uint_as_float(qrow[d2] & 0xFFFF0000u);
+        a0 = fmaf(ql, __uint_as_float(x0 << 16), a0);
+        a1 = fmaf(ql, __uint_as_float(x1 << 16), a1);
+        a0 = fmaf(qh, __uint_as_float(x0 & 0xFFFF0000u), a0);
+        a1 = fmaf(qh, __uint_as_float(x1 & 0xFFFF0000u), a1);
+      }
+      // ordered head sums s = fma(w_h, r_h, s), h ascending; entries h >= h_i
+      // hold w = 0 and a finite r, which leave s unchanged
+      s_r[wave][0][lane] = a0 > 0.0f ? a0 : 0.0f;
+      s_r[wave][1][lane] = a1 > 0.0f ? a1 : 0.0f;
+      float s0v = 0.0f, s1v = 0.0f;
+#pragma unroll 2
+      for (int h4 = 0; h4 < 16; ++h4) {
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(&s_w[4 * h4]);
+        const f32x4 r0 = *reinterpret_cast<const f32x4*>(&s_r[wave][0][4 * h4]);
+        const f32x4 r1 = *reinterpret_cast<const f32x4*>(&s_r[wave][1][4 * h4]);
+        s0v = fmaf(wv.x, r0.x, s0v);
+        s1v = fmaf(wv.x, r1.x, s1v);
+        s0v = fmaf(wv.y, r0.y, s0v);
+        s1v = fmaf(wv.y, r1.y, s1v);
+        s0v = fmaf(wv.z, r0.z, s0v);
+        s1v = fmaf(wv.z, r1.z, s1v);
+        s0v = fmaf(wv.w, r0.w, s0v);
+        s1v = fmaf(wv.w, r1.w, s1v);
+      }
+      if (lane == 0) {
+        s_key[s_ul[j]] = sortable(s0v);
+        if (j + 1 < (int)nu) s_key[s_ul[j + 1]] = sortable(s1v);
+      }
+      // the next rows become visible only here, so their wait stays below the chains
+      asm volatile("" : "+v"(kw0), "+v"(kw1));
+    }
+  }
+  __syncthreads();
+
+  // final choice: every certain member plus the best `need` uncertain ones,
+  // by (exact score desc, position asc); afterwards every slot is kSure or 0
+  uint32_t ci = 0;
+#pragma unroll
+  for (int j = 0; j < kSmallPer; ++j) ci += key[j] == kSure ? 1u : 0u;
+  uint32_t nin;
+  (void)wg8_exclusive_scan(ci, s_tmp, &nin);
+  const int need = K - (int)nin;
+  if ((int)nu <= need || need <= 0) {
+    const uint32_t to = need > 0 ? kSure : 0u;
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j) key[j] = is_real(key[j]) ? to : key[j];
+  } else if ((int)nu <= kWave) {
+    // one wave ranks (exact key, complement of slot) composites pairwise and
+    // marks each uncertain slot in s_key (kSure = chosen, 0 = not)
+    if (wave == 0) {
+      uint32_t slot = 0;
+      uint64_t comp = 0;
+      if (lane < (int)nu) {
+        slot = s_ul[lane];
+        comp = ((uint64_t)s_key[slot] << 32) | (uint64_t)(0xFFFFFFFFu - slot);
+      }
+      uint32_t r = 0;
+      for (int jj = 0; jj < (int)nu; ++jj) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)comp, jj);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(comp >> 32), jj);
+        r += ((((uint64_t)hi << 32) | lo) > comp) ? 1u : 0u;
+      }
+      if (lane < (int)nu) s_key[slot] = r < (uint32_t)need ? kSure : 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j)
+      if (is_real(key[j])) key[j] = s_key[s0 + j];
+  } else {
+    // many uncertain members: radix select on their exact keys, ties at the
+    // cut to the lower slots
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j)
+      if (is_real(key[j])) key[j] = max(min(s_key[s0 + j], kSure - 1u), 1u);   // stay real
+    uint32_t ties, eq;
+    const uint32_t kth = small_kth(key, is_real, need, s_h, s_tmp, &ties, &eq);
+    uint32_t tl = 0;
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j) tl += (is_real(key[j]) && key[j] == kth) ? 1u : 0u;
+    uint32_t ttot;
+    uint32_t tr = wg8_exclusive_scan(tl, s_tmp, &ttot);   // tied slots before this segment
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j) {
+      const uint32_t k = key[j];
+      if (is_real(k)) {
+        const bool tie = k == kth;
+        key[j] = (k > kth || (tie && tr < ties)) ? kSure : 0u;
+        tr += tie ? 1u : 0u;
+      }
+    }
+  }
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kSmallPer; ++j) cnt += key[j] == kSure ? 1u : 0u;
+  uint32_t tot;
+  uint32_t o = wg8_exclusive_scan(cnt, s_tmp, &tot);
+#pragma unroll
+  for (int j = 0; j < kSmallPer; ++j) {
+    if (key[j] == kSure) {
+      const int slot = s0 + j;
+      out[o++] = s_pool[slot >> 3] * 8 + (slot & 7);
+    }
+  }
+  for (int i = (int)tot + tid; i < K; i += kSmallThreads) out[i] = -1;
+}
+
 }  // namespace idx
 }  // namespace csa2
 
@@ -1115,7 +1542,7 @@ thread_local hipEvent_t g_scan_ev_stop = nullptr;
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t scores, hist, hist2, meta, chunk_cnt, chunk_unc, band, unc, total;
+  size_t scores, hist, hist2, meta, chunk_cnt, chunk_unc, band, unc, kpart, total;
 };
 
 Layout make_layout(int nprob, int64_t stride, int nchunk_cmp) {
@@ -1137,6 +1564,8 @@ Layout make_layout(int nprob, int64_t stride, int nchunk_cmp) {
   o = align256(o + (size_t)nprob * stride * sizeof(Entry));
   L.unc = o;
   o = align256(o + (size_t)nprob * stride * sizeof(uint2));
+  L.kpart = o;   // one float per Reindex scan work-group (256 slots each)
+  o = align256(o + (size_t)nprob * (size_t)(stride / 256) * sizeof(float));
   L.total = o;
   return L;
 }
@@ -1191,11 +1620,27 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   P.chunk_unc = reinterpret_cast<uint32_t*>(w + L.chunk_unc);
   P.band = reinterpret_cast<Entry*>(w + L.band);
   P.unc = reinterpret_cast<uint2*>(w + L.unc);
+  P.kpart = reinterpret_cast<float*>(w + L.kpart);
   P.bound_tok = bound_constant(P.d_i, false);
   P.bound_blk = bound_constant(P.d_i, true);
 
   const int mt = (P.h_i + 15) / 16;
   const bool pool = !P.reindex && P.keep_blocks > 0;
+  if (P.reindex && 8 * P.keep_in <= kSmallMax) {
+    // small problem: the scan, then one work-group per query selects in LDS
+    const int nx = (int)std::max<int64_t>(1, (max_slots + P.scan_chunk - 1) / P.scan_chunk);
+    hipEvent_t ev0 = g_scan_ev_start, ev1 = g_scan_ev_stop;
+    g_scan_ev_start = g_scan_ev_stop = nullptr;
+    if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return CSA2_E_HIP;
+    if (P.d_i == 128) launch_scan<128>(P, mt, false, true, dim3(nx, P.n_q), s);
+    else launch_scan<64>(P, mt, false, true, dim3(nx, P.n_q), s);
+    if (!launch_ok()) return CSA2_E_HIP;
+    if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return CSA2_E_HIP;
+    if (P.d_i == 128) hipLaunchKernelGGL(k_select_small<128>, dim3(P.n_q), dim3(kSmallThreads), 0, s, P);
+    else hipLaunchKernelGGL(k_select_small<64>, dim3(P.n_q), dim3(kSmallThreads), 0, s, P);
+    if (!launch_ok()) return CSA2_E_HIP;
+    return CSA2_OK;
+  }
   if (P.d_i == 128) hipLaunchKernelGGL(k_prologue<128>, dim3(P.nprob), dim3(kThreads), 0, s, P);
   else hipLaunchKernelGGL(k_prologue<64>, dim3(P.nprob), dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
