@@ -363,13 +363,16 @@ __device__ uint32_t wg_coarse_bin(const Params& P, int p, bool publish, uint32_t
 }
 
 // ---------------------------------------------------------------- 2. scan
-template <int D, int MT, bool POOL, bool INDIRECT>
+// POOL: also score the 8-position blocks (Full layers building a pool).
+// INDIRECT: candidates are the slots of a pool (Reindex layers).
+// HIST: build the coarse score histograms (and the key-norm maximum) that the
+// multi-kernel selection uses; without it the scan records each work-group's
+// key-norm maximum for the single-work-group selection.
+template <int D, int MT, bool POOL, bool INDIRECT, bool HIST>
 __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   constexpr int KS = D / 32;   // MFMA k-steps; also 16-byte loads per lane per key
   constexpr int NBUF = CSA2_SCAN_NBUF;   // key groups in registers: NBUF-1 in flight, one in use
-  // the Reindex variant keeps no histograms: its selection runs in one
-  // work-group per query that sees every score
-  __shared__ uint32_t s_hist[INDIRECT ? 1 : kNBins];
+  __shared__ uint32_t s_hist[HIST ? kNBins : 1];
   __shared__ uint32_t s_hist_b[POOL ? kNBins : 1];
   __shared__ int32_t s_pool[INDIRECT ? 512 : 1];
   // the chunk's scores stay in LDS until the end: the hot loop then issues
@@ -389,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   const int nblk = (nvis + 7) >> 3;
   const int c0 = blockIdx.x * P.scan_chunk;
 
-  if constexpr (!INDIRECT) {
+  if constexpr (HIST) {
     for (int i = tid; i < kNBins; i += kThreads) {
       s_hist[i] = 0;
       if (POOL) s_hist_b[i] = 0;
@@ -513,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
         cvalid = cand < nc;
       }
       s_sc[cand - c0] = cvalid ? si : -INFINITY;
-      if constexpr (!INDIRECT) {
+      if constexpr (HIST) {
         if (n < 4 && cvalid) atomicAdd(&s_hist[sortable(si) >> kBinShift], 1u);
       }
     }
@@ -573,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     const int nbs = min((nslots + 7) >> 3, max(nblk - (c0 >> 3), 0));
     for (int i = tid; i < nbs; i += kThreads) scb[(c0 >> 3) + i] = s_scb[i];
   }
-  if constexpr (INDIRECT) {
+  if constexpr (!HIST) {
     mk2 = wave_max(mk2);
     if (lane == 0) s_tmp[wave] = __float_as_uint(mk2);
     __syncthreads();
@@ -1596,13 +1599,14 @@ bool launch_ok() {
 }
 
 template <int D>
-void launch_scan(const Params& P, int mt, bool pool, bool indirect, dim3 grid, hipStream_t s) {
-#define CSA2_SCAN(MTV)                                                                                      \
-  if (mt == MTV) {                                                                                          \
-    if (indirect) hipLaunchKernelGGL((k_scan<D, MTV, false, true>), grid, dim3(kThreads), 0, s, P);        \
-    else if (pool) hipLaunchKernelGGL((k_scan<D, MTV, true, false>), grid, dim3(kThreads), 0, s, P);       \
-    else hipLaunchKernelGGL((k_scan<D, MTV, false, false>), grid, dim3(kThreads), 0, s, P);                \
-    return;                                                                                                 \
+void launch_scan(const Params& P, int mt, bool pool, bool indirect, bool hist, dim3 grid, hipStream_t s) {
+#define CSA2_SCAN(MTV)                                                                                       \
+  if (mt == MTV) {                                                                                           \
+    if (indirect && hist) hipLaunchKernelGGL((k_scan<D, MTV, false, true, true>), grid, dim3(kThreads), 0, s, P); \
+    else if (indirect) hipLaunchKernelGGL((k_scan<D, MTV, false, true, false>), grid, dim3(kThreads), 0, s, P);  \
+    else if (pool) hipLaunchKernelGGL((k_scan<D, MTV, true, false, true>), grid, dim3(kThreads), 0, s, P);       \
+    else hipLaunchKernelGGL((k_scan<D, MTV, false, false, true>), grid, dim3(kThreads), 0, s, P);                \
+    return;                                                                                                  \
   }
   CSA2_SCAN(1) CSA2_SCAN(2) CSA2_SCAN(3) CSA2_SCAN(4)
 #undef CSA2_SCAN
@@ -1632,8 +1636,8 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
     hipEvent_t ev0 = g_scan_ev_start, ev1 = g_scan_ev_stop;
     g_scan_ev_start = g_scan_ev_stop = nullptr;
     if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return CSA2_E_HIP;
-    if (P.d_i == 128) launch_scan<128>(P, mt, false, true, dim3(nx, P.n_q), s);
-    else launch_scan<64>(P, mt, false, true, dim3(nx, P.n_q), s);
+    if (P.d_i == 128) launch_scan<128>(P, mt, false, true, false, dim3(nx, P.n_q), s);
+    else launch_scan<64>(P, mt, false, true, false, dim3(nx, P.n_q), s);
     if (!launch_ok()) return CSA2_E_HIP;
     if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return CSA2_E_HIP;
     if (P.d_i == 128) hipLaunchKernelGGL(k_select_small<128>, dim3(P.n_q), dim3(kSmallThreads), 0, s, P);
@@ -1649,8 +1653,8 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   hipEvent_t ev0 = g_scan_ev_start, ev1 = g_scan_ev_stop;
   g_scan_ev_start = g_scan_ev_stop = nullptr;
   if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return CSA2_E_HIP;
-  if (P.d_i == 128) launch_scan<128>(P, mt, pool, P.reindex, gscan, s);
-  else launch_scan<64>(P, mt, pool, P.reindex, gscan, s);
+  if (P.d_i == 128) launch_scan<128>(P, mt, pool, P.reindex, true, gscan, s);
+  else launch_scan<64>(P, mt, pool, P.reindex, true, gscan, s);
   if (!launch_ok()) return CSA2_E_HIP;
   if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return CSA2_E_HIP;
   hipLaunchKernelGGL(k_finehist, dim3(P.nchunk_cmp, P.nprob), dim3(kThreads), 0, s, P);

@@ -102,7 +102,8 @@ def test_pool_with_block_constant_keys():
 
 
 @gpu
-@pytest.mark.parametrize("lengths,keep", [([20000, 16391, 300], 2048), ([40000, 9], 512)])
+@pytest.mark.parametrize("lengths,keep", [([20000, 16391, 300], 2048), ([40000, 9], 512),
+                                          ([40000, 33000, 700], 4096)])   # 32,768 slots: the multi-kernel path
 def test_reindex(lengths, keep):
     note(f"reindex {lengths} keep={keep}")
     inp = index_inputs(lengths, 64, 128, seed=21)
