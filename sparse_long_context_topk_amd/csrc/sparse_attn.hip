@@ -265,17 +265,36 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
   auto compute = [&](int b) {
     if (head_wave) {
       // ---- S^T = K Q^T : lane (head n, g) gets keys 16*kt + 4*g + i
-      f32x4 sacc[2];
+      // the two key tiles' chains interleaved (independent accumulators); each
+      // k-step's fragments are read one k-step ahead of their MFMAs
+      f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+      const _Float16* krow0 = &s_k[b][n * kKRow + 8 * g];
+      const _Float16* krow1 = &s_k[b][(16 + n) * kKRow + 8 * g];
+      f16x8 n0 = *reinterpret_cast<const f16x8*>(krow0);
+      f16x8 n1 = *reinterpret_cast<const f16x8*>(krow1);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        sacc[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        const _Float16* krow = &s_k[b][(16 * kt + n) * kKRow + 8 * g];
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-          const f16x8 a = *reinterpret_cast<const f16x8*>(krow + 32 * ks);
-          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[ks], sacc[kt], 0, 0, 0);
-          if constexpr (QF32) sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[ks], sacc[kt], 0, 0, 0);
+      for (int ks = 0; ks < 16; ++ks) {
+        const f16x8 a0 = n0, a1 = n1;
+        if (ks + 1 < 16) {
+          n0 = *reinterpret_cast<const f16x8*>(krow0 + 32 * (ks + 1));
+          n1 = *reinterpret_cast<const f16x8*>(krow1 + 32 * (ks + 1));
         }
+        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[ks], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[ks], sacc[1], 0, 0, 0);
+        if constexpr (QF32) {
+          sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, ql[ks], sacc[0], 0, 0, 0);
+          sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, ql[ks], sacc[1], 0, 0, 0);
+        }
+      }
+      {
+        constexpr int kM = QF32 ? 4 : 2;   // MFMAs per k-step
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int r = 0; r < 15; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);
       }
       float z[8];
       float mx = -INFINITY;
@@ -305,10 +324,12 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) ps += pv[j];
       l_run = l_run * alpha + ps;
-      m_run = m_new;
       // rescale O rows (heads 4*g + i live in this lane's accumulators); a
-      // wave whose maxima did not move skips it
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+      // wave whose maxima did not move, or whose O is still zero (no key seen
+      // yet), skips it
+      const bool rescale = alpha != 1.0f && m_run != -INFINITY;
+      m_run = m_new;
+      if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
         float a4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, kWave);
@@ -321,15 +342,27 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
       f16x8 pa;
 #pragma unroll
       for (int j = 0; j < 8; ++j) pa[j] = (_Float16)pv[j];
-      // ---- O += P V
-#pragma unroll
-      for (int t = 0; t < 32; ++t) {
+      // ---- O += P V  (each V fragment read one MFMA ahead)
+      auto vfrag = [&](int t) {
         const _Float16* vrow = &s_v[b][(16 * t + n) * kVRow];
         const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * g);
         const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
-        const f16x8 bv = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        return __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      };
+      f16x8 nv = vfrag(0);
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
+        const f16x8 bv = nv;
+        if (t + 1 < 32) nv = vfrag(t + 1);
         o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, o[t], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int r = 0; r < 30; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
   };
 
@@ -389,15 +422,28 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One work-group per (query, head); the first wave turns the (m_s, l_s) pairs
-// into weights, then every thread sums two channels over the splits with all
-// loads of a batch of splits in flight.
+// One work-group per (query, head); every thread sums two channels over the
+// splits (ascending), its first 32 splits' values loading while the first
+// wave turns the (m_s, l_s) pairs into weights.
 __global__ __launch_bounds__(kThreads) void k_merge(Params P) {
   __shared__ float s_w[kMaxSplit];
   __shared__ float s_ml[2];
   const int qi = blockIdx.x, hh = blockIdx.y, c = threadIdx.x;
   const int ns = P.nsplit;
   const size_t row0 = (size_t)qi * ns * P.h + hh;   // row of split 0; split s adds s * h
+  const float* po = P.part_o + row0 * 512;
+  const size_t so = (size_t)P.h * 512;
+  // the first kBatch splits' partials load while the weights are formed
+  constexpr int kBatch = 32;
+  float x0[kBatch], x1[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    x0[u] = x1[u] = 0.0f;
+    if (u < ns) {   // uniform
+      x0[u] = po[u * so + c];
+      x1[u] = po[u * so + c + 256];
+    }
+  }
   if (threadIdx.x < 64) {
     const int s = threadIdx.x;
     float m = -INFINITY, l = 0.0f;
@@ -416,25 +462,17 @@ __global__ __launch_bounds__(kThreads) void k_merge(Params P) {
     }
   }
   __syncthreads();
-  const float* po = P.part_o + row0 * 512;
-  const size_t so = (size_t)P.h * 512;
   float acc0 = 0.0f, acc1 = 0.0f;
-  constexpr int U = 8;
-  for (int s0 = 0; s0 < ns; s0 += U) {
-    float x0[U], x1[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = min(s0 + u, ns - 1);
-      x0[u] = po[s * so + c];
-      x1[u] = po[s * so + c + 256];
+  for (int u = 0; u < kBatch; ++u) {
+    if (u < ns) {
+      acc0 = fmaf(s_w[u], x0[u], acc0);
+      acc1 = fmaf(s_w[u], x1[u], acc1);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (s0 + u < ns) {
-        acc0 = fmaf(s_w[s0 + u], x0[u], acc0);
-        acc1 = fmaf(s_w[s0 + u], x1[u], acc1);
-      }
-    }
+  }
+  for (int s = kBatch; s < ns; ++s) {
+    acc0 = fmaf(s_w[s], po[s * so + c], acc0);
+    acc1 = fmaf(s_w[s], po[s * so + c + 256], acc1);
   }
   const float L = s_ml[1];
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
