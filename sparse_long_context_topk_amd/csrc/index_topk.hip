@@ -14,8 +14,10 @@
 // How (one pass over the keys at HBM speed, exact result):
 //  1. k_prologue   zeroes the problem's histograms and Meta, and computes
 //                  QW = sum_h |w_h| ||q_h|| for the rounding bound.
-//  2. k_scan       streams the indexer keys once, two 16-key groups ahead of
-//                  the math.  Scores come from bf16 MFMA
+//  2. k_scan       streams the indexer keys once (8192 keys per work-group,
+//                  NBUF - 1 groups of 16 keys per wave in flight ahead of the
+//                  math, scores staged in LDS and written once at the end).
+//                  Scores come from bf16 MFMA
 //                  (v_mfma_f32_16x16x32_bf16, S^T = K Q^T: 16 positions x 16
 //                  heads x 32 dims, the query held in registers).  A block's
 //                  per-head dot product is the mean of its members'
@@ -49,6 +51,9 @@
 //                  ascending positions, -1 padded.
 // Degenerate inputs (ties everywhere) only make the band large; the result
 // stays exact.
+// A Reindex pool of at most 16,384 slots skips steps 1 and 3-6: its scan keeps
+// each work-group's key-norm maximum instead of histograms, and one work-group
+// per query (section 7) selects from the scores it holds in registers.
 #include "csa2_device.h"
 
 #include <algorithm>
