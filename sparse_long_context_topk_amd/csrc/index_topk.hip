@@ -70,7 +70,7 @@ constexpr int kBinShift = 20;
 constexpr int kCmpChunk = 4096;
 constexpr int kCmpPerThread = kCmpChunk / kThreads;
 constexpr int kMaxChunksLds = 8192;   // compaction chunks per problem (max_nvis <= 2^25)
-constexpr int kRescoreWGs = 128;
+constexpr int kRescoreWGs = 512;   // rescoring work-groups per launch (all queries)
 #ifndef CSA2_SCAN_NBUF
 #define CSA2_SCAN_NBUF 3
 #endif
@@ -121,6 +121,7 @@ struct Params {
   int scan_chunk;
   int64_t stride;          // slots per problem in scores / band arrays
   int nchunk_cmp;
+  int rs_tok;              // rescoring work-groups per query given to the token problem (the rest: blocks)
   float bound_tok, bound_blk;
   float* scores;
   uint32_t* hist;       // [nprob][kNBins] coarse histogram (top 12 bits of the key)
@@ -167,9 +168,11 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
-// Exclusive prefix sum over the work-group; returns this thread's offset and
-// writes the total.
+// Exclusive prefix sum over the NT-thread work-group (s_tmp: >= NT / 64
+// entries); returns this thread's offset and writes the total.
+template <int NT = kThreads>
 __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
+  constexpr int NW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -181,7 +184,7 @@ __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* s_tm
   __syncthreads();
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     uint32_t t = s_tmp[i];
     if (i < wave) before += t;
     all += t;
@@ -196,13 +199,15 @@ __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* s_tm
 // their leading bits, so the digits start at the highest bit where the
 // smallest and largest key differ: the first histogram then spreads over many
 // bins instead of piling every LDS atomic onto one.  Returns the key; in
-// *ties the number of entries equal to it that belong to the Top-K.
-template <typename KeyOf>
+// *ties the number of entries equal to it that belong to the Top-K.  NT >= 256
+// threads; s_tmp holds >= 2 NT / 64 + 2 entries.
+template <int NT = kThreads, typename KeyOf>
 __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist /*256*/,
                                    uint32_t* s_tmp, uint32_t* ties) {
+  constexpr int NW = NT / kWave;
   const int tid = threadIdx.x;
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int i = tid; i < n; i += kThreads) {
+  for (int i = tid; i < n; i += NT) {
     const uint32_t key = key_of(i);
     lo = min(lo, key);
     hi = max(hi, key);
@@ -211,11 +216,16 @@ __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist 
   hi = wave_max(hi);
   if ((tid & 63) == 0) {
     s_tmp[tid >> 6] = lo;
-    s_tmp[4 + (tid >> 6)] = hi;
+    s_tmp[NW + (tid >> 6)] = hi;
   }
   __syncthreads();
-  lo = min(min(s_tmp[0], s_tmp[1]), min(s_tmp[2], s_tmp[3]));
-  hi = max(max(s_tmp[4], s_tmp[5]), max(s_tmp[6], s_tmp[7]));
+  lo = s_tmp[0];
+  hi = s_tmp[NW];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    lo = min(lo, s_tmp[i]);
+    hi = max(hi, s_tmp[NW + i]);
+  }
   __syncthreads();
   if (lo == hi) {
     *ties = (uint32_t)K;
@@ -229,24 +239,24 @@ __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist 
     const int sh = shift < 0 ? 0 : shift;
     const int width = shift < 0 ? 8 + shift : 8;   // last digit may be narrower
     const uint32_t dmask = (1u << width) - 1u;
-    s_hist[tid] = 0;
+    if (tid < 256) s_hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
+    for (int i = tid; i < n; i += NT) {
       const uint32_t key = key_of(i);
       if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
     }
     __syncthreads();
-    // thread tid owns digit 255 - tid; the exclusive scan counts larger digits
-    const uint32_t v = s_hist[255 - tid];
+    // thread tid < 256 owns digit 255 - tid; the exclusive scan counts larger digits
+    const uint32_t v = tid < 256 ? s_hist[255 - tid] : 0u;
     uint32_t tot;
-    const uint32_t excl = wg_exclusive_scan(v, s_tmp, &tot);
+    const uint32_t excl = wg_exclusive_scan<NT>(v, s_tmp, &tot);
     if (excl < remaining && excl + v >= remaining) {
-      s_tmp[8] = 255u - tid;
-      s_tmp[9] = excl;
+      s_tmp[2 * NW] = 255u - tid;
+      s_tmp[2 * NW + 1] = excl;
     }
     __syncthreads();
-    const uint32_t d = s_tmp[8];
-    remaining -= s_tmp[9];
+    const uint32_t d = s_tmp[2 * NW];
+    remaining -= s_tmp[2 * NW + 1];
     prefix |= d << sh;
     mask |= dmask << sh;
     __syncthreads();
@@ -757,13 +767,14 @@ __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
 }
 
 // Exclusive prefix of a problem's per-chunk counts into LDS (s[0..nch]).
+template <int NT = kThreads>
 __device__ __forceinline__ void chunk_prefix(const uint32_t* cnt, int nch, uint32_t* s, uint32_t* s_tmp) {
   uint32_t carry = 0;
-  for (int t0 = 0; t0 < nch; t0 += kThreads) {
+  for (int t0 = 0; t0 < nch; t0 += NT) {
     const int c = t0 + threadIdx.x;
     const uint32_t cv = c < nch ? cnt[c] : 0u;
     uint32_t tt;
-    const uint32_t ex = wg_exclusive_scan(cv, s_tmp, &tt);
+    const uint32_t ex = wg_exclusive_scan<NT>(cv, s_tmp, &tt);
     if (c < nch) s[c] = carry + ex;
     carry += tt;
   }
@@ -801,7 +812,12 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
   __shared__ __attribute__((aligned(16))) float s_r[kWaves][kWave];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int p = blockIdx.y, q = p % P.n_q, kind = p / P.n_q;
+  // work-groups [0, rs_tok) of a query serve its token (or Reindex) problem,
+  // the rest its block problem
+  const int q = blockIdx.y, kind = (int)blockIdx.x < P.rs_tok ? 0 : 1;
+  const int p = kind * P.n_q + q;
+  const int wg = kind ? (int)blockIdx.x - P.rs_tok : (int)blockIdx.x;
+  const int nwg = kind ? (int)gridDim.x - P.rs_tok : P.rs_tok;
   const int nvis = P.q_nvis[q];
   const int64_t base = P.seq_base[P.q_seq[q]];
   const int nch = P.nchunk_cmp;
@@ -811,7 +827,7 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
   if (tid < kWave) s_w[tid] = tid < P.h_i ? P.w[(size_t)q * P.h_i + tid] : 0.0f;
   chunk_prefix(P.chunk_unc + (size_t)p * nch, nch, s_uoff, s_tmp);   // ends with a barrier
   const int nu = (int)s_uoff[nch];
-  if (blockIdx.x * kWaves >= nu) return;
+  if (wg * kWaves >= nu) return;
   uint32_t qrow[DW];   // the lane's query row, packed bf16 pairs
   {
     const int hh = lane < P.h_i ? lane : 0;
@@ -888,8 +904,8 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
     }
   };
 
-  const int stride_w = gridDim.x * kWaves;
-  int j = blockIdx.x * kWaves + wave;
+  const int stride_w = nwg * kWaves;
+  int j = wg * kWaves + wave;
   if (j >= nu) return;
   Cand cur = locate(j);
   uint32_t wv[KPER];
@@ -961,9 +977,13 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
 // One work-group per problem: the certain members plus the best rescored
 // ones (exact score desc, position asc), written as ascending positions and
 // padded with -1.  The band is read in position order through the chunk
-// prefix; bands up to kBandLds entries are staged in LDS first.
-__global__ __launch_bounds__(kThreads) void k_final(Params P) {
-  __shared__ uint32_t s_tmp[16];
+// prefix; bands up to kBandLds entries are staged in LDS first.  1024 threads:
+// only a few problems run, so each gets a whole CU.
+constexpr int kFinalThreads = 1024;
+
+__global__ __launch_bounds__(kFinalThreads) void k_final(Params P) {
+  constexpr int NT = kFinalThreads;
+  __shared__ uint32_t s_tmp[2 * NT / kWave + 2];
   __shared__ uint32_t s_hist[256];
   __shared__ uint32_t s_off[kMaxChunksLds + 1];
   __shared__ uint32_t s_key[kBandLds];
@@ -972,7 +992,7 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
   // (key, index) composites: the two never coexist
   __shared__ __attribute__((aligned(16))) uint32_t s_ukey[kUncLds];
   uint64_t* s_ucomp = reinterpret_cast<uint64_t*>(s_ukey);
-  __shared__ uint8_t s_usel[kRankMax];
+  __shared__ uint32_t s_rank[kRankMax];
   const int tid = threadIdx.x;
   const int p = blockIdx.x, q = p % P.n_q, kind = p / P.n_q;
   const int nch = P.nchunk_cmp;
@@ -980,10 +1000,10 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
   const int K = (kind == 1) ? P.keep_blocks : P.k;
   int32_t* out = (kind == 1) ? P.pool_out + (size_t)q * P.keep_blocks : P.idx_out + (size_t)q * P.k;
 
-  chunk_prefix(P.chunk_cnt + (size_t)p * nch, nch, s_off, s_tmp);
+  chunk_prefix<NT>(P.chunk_cnt + (size_t)p * nch, nch, s_off, s_tmp);
   const int n2 = (int)s_off[nch];
   // per-thread contiguous segment of the position-ordered band
-  const int per = (n2 + kThreads - 1) / kThreads;
+  const int per = (n2 + NT - 1) / NT;
   const int i0 = min(n2, tid * per), i1 = min(n2, i0 + per);
   const bool in_lds = n2 <= kBandLds;
   auto entry_at = [&](int i) {
@@ -993,7 +1013,7 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
   if (in_lds && i0 < i1) {
     // this thread's segment: one search for its first chunk, then a forward
     // walk; batches of U loads are in flight together
-    constexpr int U = 16;
+    constexpr int U = 12;
     int c = chunk_of(s_off, nch, (uint32_t)i0);
     for (int b0 = i0; b0 < i1; b0 += U) {
       Entry e[U];
@@ -1023,7 +1043,7 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
   uint32_t cu = 0;
   for (int i = i0; i < i1; ++i) cu += (cand_of(i) & kCertain) ? 0u : 1u;
   uint32_t nu;
-  const uint32_t u_first = wg_exclusive_scan(cu, s_tmp, &nu);
+  const uint32_t u_first = wg_exclusive_scan<NT>(cu, s_tmp, &nu);
   const int nin = n2 - (int)nu;
   const int need = K - nin;
   const bool take_none = need <= 0;
@@ -1043,47 +1063,38 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
       }
     if (pairwise && tid < 4) s_ucomp[nu + tid] = 0;   // padding: below every member
   }
+  if (pairwise)
+    for (int i = tid; i < (int)nu; i += NT) s_rank[i] = 0;
   __syncthreads();
   uint32_t kth = 0, ties = 0;
   if (pairwise) {
     // composite (key, complement of the list index): a larger composite is a
     // larger exact score, or an equal one at a lower position; all distinct.
-    // Each thread ranks up to four members (tid + 256 m) in one sweep.
-    const int nu4 = ((int)nu + 3) & ~3;
-    const int mm = ((int)nu + kThreads - 1) / kThreads;   // 1..4
-    uint64_t ci[4];
-    uint32_t r[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int i = tid + kThreads * m;
-      ci[m] = i < (int)nu ? s_ucomp[i] : ~0ull;   // absent: nothing ranks above it
-    }
-    auto sweep = [&](auto M) {
-      constexpr int kM = decltype(M)::value;
-      for (int j = 0; j < nu4; j += 4) {
+    // The list is cut into R slices of four-entry groups and thread t counts
+    // the composites above member t % nu in slice t / nu, so that about all
+    // NT threads share the nu * nu comparisons.
+    const int ng = ((int)nu + 3) >> 2;                  // four-entry groups
+    const int R = max(1, min(NT / (int)nu, ng));        // slices
+    const int gps = (ng + R - 1) / R;                   // groups per slice
+    if (tid < R * (int)nu) {
+      const int i = tid % (int)nu, sl = tid / (int)nu;
+      const uint64_t ci = s_ucomp[i];
+      const int j0 = 4 * sl * gps, j1 = min(4 * ng, j0 + 4 * gps);
+      uint32_t r = 0;
+      for (int j = j0; j < j1; j += 4) {
         const uint64_t c0 = s_ucomp[j], c1 = s_ucomp[j + 1], c2 = s_ucomp[j + 2], c3 = s_ucomp[j + 3];
-#pragma unroll
-        for (int m = 0; m < kM; ++m)
-          r[m] += (c0 > ci[m] ? 1u : 0u) + (c1 > ci[m] ? 1u : 0u) + (c2 > ci[m] ? 1u : 0u) + (c3 > ci[m] ? 1u : 0u);
+        r += (c0 > ci ? 1u : 0u) + (c1 > ci ? 1u : 0u) + (c2 > ci ? 1u : 0u) + (c3 > ci ? 1u : 0u);
       }
-    };
-    if (mm == 1) sweep(std::integral_constant<int, 1>{});
-    else if (mm == 2) sweep(std::integral_constant<int, 2>{});
-    else if (mm == 3) sweep(std::integral_constant<int, 3>{});
-    else sweep(std::integral_constant<int, 4>{});
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int i = tid + kThreads * m;
-      if (i < (int)nu) s_usel[i] = r[m] < (uint32_t)need ? 1 : 0;
+      if (r) atomicAdd(&s_rank[i], r);
     }
     __syncthreads();
   } else if (cut) {
     if (u_lds) {
-      kth = wg_kth_largest((int)nu, need, [&](int i) { return s_ukey[i]; }, s_hist, s_tmp, &ties);
+      kth = wg_kth_largest<NT>((int)nu, need, [&](int i) { return s_ukey[i]; }, s_hist, s_tmp, &ties);
     } else {
       // degenerate: many uncertain members; select over the band, certain ones count as ineligible
-      kth = wg_kth_largest(n2, need, [&](int i) { return (cand_of(i) & kCertain) ? 0u : key(i); },
-                           s_hist, s_tmp, &ties);
+      kth = wg_kth_largest<NT>(n2, need, [&](int i) { return (cand_of(i) & kCertain) ? 0u : key(i); },
+                               s_hist, s_tmp, &ties);
     }
   }
   // Radix-select path: pass 1 counts the entries tied at the cut, pass 2 the
@@ -1095,7 +1106,7 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
     const uint32_t ui = u++;
     if (take_none) return false;
     if (take_all) return true;
-    if (pairwise) return s_usel[ui] != 0;
+    if (pairwise) return s_rank[ui] < (uint32_t)need;
     const uint32_t kk = key(i);
     if (kk > kth) return true;
     if (kk == kth) return rank++ < ties;
@@ -1105,11 +1116,11 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
   if (cut && !pairwise)
     for (int i = i0; i < i1; ++i) nt += (!(cand_of(i) & kCertain) && key(i) == kth) ? 1u : 0u;
   uint32_t tot_t;
-  const uint32_t tie_base = wg_exclusive_scan(nt, s_tmp, &tot_t);
+  const uint32_t tie_base = wg_exclusive_scan<NT>(nt, s_tmp, &tot_t);
   uint32_t cnt = 0, rank = tie_base, u = u_first;
   for (int i = i0; i < i1; ++i) cnt += decide(i, u, rank) ? 1u : 0u;
   uint32_t tot;
-  uint32_t o = wg_exclusive_scan(cnt, s_tmp, &tot);
+  uint32_t o = wg_exclusive_scan<NT>(cnt, s_tmp, &tot);
   rank = tie_base;
   u = u_first;
   for (int i = i0; i < i1; ++i) {
@@ -1118,7 +1129,7 @@ __global__ __launch_bounds__(kThreads) void k_final(Params P) {
       out[o++] = (kind == 1) ? (int)cand : cand_pos(P, q, kind, cand);
     }
   }
-  for (int i = (int)tot + tid; i < K; i += kThreads) out[i] = -1;
+  for (int i = (int)tot + tid; i < K; i += NT) out[i] = -1;
 }
 
 // ---------------------------------------------------------------- 7. small problems
@@ -1666,10 +1677,17 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   if (!launch_ok()) return CSA2_E_HIP;
   hipLaunchKernelGGL(k_compact, dim3(P.nchunk_cmp, P.nprob), dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
-  if (P.d_i == 128) hipLaunchKernelGGL(k_rescore<128>, dim3(kRescoreWGs, P.nprob), dim3(kThreads), 0, s, P);
-  else hipLaunchKernelGGL(k_rescore<64>, dim3(kRescoreWGs, P.nprob), dim3(kThreads), 0, s, P);
+  // One resident round (two work-groups per CU at this kernel's register
+  // use): about kRescoreWGs work-groups in all, a query's share split 1:7
+  // between its token and block problems (blocks have about ten times more
+  // undecided members, each eight chains).  Every wave strides over its
+  // problem's members, so any split stays correct.
+  const int per_q = std::min(128, std::max(pool ? 8 : 4, kRescoreWGs / P.n_q));
+  P.rs_tok = pool ? std::max(1, per_q / 8) : per_q;
+  if (P.d_i == 128) hipLaunchKernelGGL(k_rescore<128>, dim3(per_q, P.n_q), dim3(kThreads), 0, s, P);
+  else hipLaunchKernelGGL(k_rescore<64>, dim3(per_q, P.n_q), dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
-  hipLaunchKernelGGL(k_final, dim3(P.nprob), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(k_final, dim3(P.nprob), dim3(kFinalThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
   return CSA2_OK;
 }
