@@ -66,6 +66,57 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return v;
 }
 
+// Work-group barrier that orders LDS only: unlike __syncthreads it does not
+// wait for the thread's global loads in flight, which keep overlapping the
+// steps after the barrier.  For code whose threads exchange data through LDS
+// alone.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Cross-lane steps through DPP (row-local moves and row broadcasts of the
+// gfx9 wave), which stay in the vector ALU instead of the LDS crossbar that
+// shuffles use.  dpp0 reads 0 where a lane has no source.
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWMASK, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  x += dpp0<0x111>(x);        // row_shr:1
+  x += dpp0<0x112>(x);        // row_shr:2
+  x += dpp0<0x114>(x);        // row_shr:4
+  x += dpp0<0x118>(x);        // row_shr:8
+  x += dpp0<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp0<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// Wave-wide reductions (result in every lane): within each row of 16 lanes
+// by quad and mirror moves, then across the four rows by readlane.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp0<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = op(v, dpp0<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = op(v, dpp0<0x141>(v));   // row_half_mirror
+  v = op(v, dpp0<0x140>(v));   // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(a, b), op(c, d));
+}
+__device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+}
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+}
+__device__ __forceinline__ uint32_t wave_sum_dpp(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t x, uint32_t y) { return x + y; });
+}
+
 // Agent-scope acquire/release counter used by the "last work-group of a
 // problem finishes the job" pattern.
 __device__ __forceinline__ uint32_t atomic_inc_acq_rel(uint32_t* p) {

@@ -181,7 +181,7 @@ __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* s_tm
     if (lane >= o) x += y;
   }
   if (lane == 63) s_tmp[wave] = x;
-  __syncthreads();
+  lds_barrier();
   uint32_t before = 0, all = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
@@ -189,7 +189,7 @@ __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* s_tm
     if (i < wave) before += t;
     all += t;
   }
-  __syncthreads();
+  lds_barrier();
   *total = all;
   return before + x - v;
 }
@@ -218,7 +218,7 @@ __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist 
     s_tmp[tid >> 6] = lo;
     s_tmp[NW + (tid >> 6)] = hi;
   }
-  __syncthreads();
+  lds_barrier();
   lo = s_tmp[0];
   hi = s_tmp[NW];
 #pragma unroll
@@ -226,7 +226,7 @@ __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist 
     lo = min(lo, s_tmp[i]);
     hi = max(hi, s_tmp[NW + i]);
   }
-  __syncthreads();
+  lds_barrier();
   if (lo == hi) {
     *ties = (uint32_t)K;
     return lo;
@@ -240,12 +240,12 @@ __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist 
     const int width = shift < 0 ? 8 + shift : 8;   // last digit may be narrower
     const uint32_t dmask = (1u << width) - 1u;
     if (tid < 256) s_hist[tid] = 0;
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < n; i += NT) {
       const uint32_t key = key_of(i);
       if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> sh) & dmask], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     // thread tid < 256 owns digit 255 - tid; the exclusive scan counts larger digits
     const uint32_t v = tid < 256 ? s_hist[255 - tid] : 0u;
     uint32_t tot;
@@ -254,12 +254,12 @@ __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist 
       s_tmp[2 * NW] = 255u - tid;
       s_tmp[2 * NW + 1] = excl;
     }
-    __syncthreads();
+    lds_barrier();
     const uint32_t d = s_tmp[2 * NW];
     remaining -= s_tmp[2 * NW + 1];
     prefix |= d << sh;
     mask |= dmask << sh;
-    __syncthreads();
+    lds_barrier();
     if (sh == 0) break;
   }
   *ties = remaining;
@@ -371,9 +371,9 @@ __device__ uint32_t wg_coarse_bin(const Params& P, int p, bool publish, uint32_t
       run += hv[j];
     }
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t bin = s_tmp[10];
-  __syncthreads();
+  lds_barrier();
   return bin;
 }
 
@@ -441,9 +441,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   // LDS-only barrier: orders the histogram clear and the pool ids before any
   // wave uses them, without waiting for the query loads still in flight (the
   // first key loads below then overlap them)
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  lds_barrier();
 
   float mk2 = 0.0f;
   float* sc = P.scores + (size_t)p * P.stride;
@@ -585,7 +583,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     if (it + b < my_groups) process(it + b, buf[b]);
 
   // ---- publish scores, histograms and the key-norm maximum
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < nslots; i += kThreads) sc[c0 + i] = s_sc[i];
   if constexpr (POOL) {
     const int nbs = min((nslots + 7) >> 3, max(nblk - (c0 >> 3), 0));
@@ -594,7 +592,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   if constexpr (!HIST) {
     mk2 = wave_max(mk2);
     if (lane == 0) s_tmp[wave] = __float_as_uint(mk2);
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
       uint32_t m0 = 0;
       for (int i = 0; i < kWaves; ++i) m0 = max(m0, s_tmp[i]);
@@ -612,7 +610,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     }
     mk2 = wave_max(mk2);
     if (lane == 0) s_tmp[wave] = __float_as_uint(mk2);
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
       uint32_t m0 = 0;
       for (int i = 0; i < kWaves; ++i) m0 = max(m0, s_tmp[i]);
@@ -652,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
   if (bin == kAll || chunk * kCmpChunk >= nc) return;
   const int my0 = chunk * kCmpChunk + tid * kCmpPerThread;
   for (int i = tid; i < kNBins; i += kThreads) s_h[i] = 0;
-  __syncthreads();
+  lds_barrier();
   float v[kCmpPerThread];
   const int m = load16(P, p, nc, my0, v);
 #pragma unroll
@@ -662,7 +660,7 @@ __global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
       if ((key >> kBinShift) == bin) atomicAdd(&s_h[(key >> 8) & (kNBins - 1)], 1u);
     }
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t* gh = P.hist2 + (size_t)p * kNBins;
   for (int i = tid; i < kNBins; i += kThreads) {
     const uint32_t c = s_h[i];
@@ -719,10 +717,10 @@ __device__ void wg_band_thresholds(const Params& P, int p, bool publish, uint32_
       run += hv[j];
     }
   }
-  __syncthreads();
+  lds_barrier();
   *keep_thr = __uint_as_float(s_tmp[12]);
   *in_thr = __uint_as_float(s_tmp[13]);
-  __syncthreads();
+  lds_barrier();
 }
 
 // ---------------------------------------------------------------- 4. compaction
@@ -779,7 +777,7 @@ __device__ __forceinline__ void chunk_prefix(const uint32_t* cnt, int nch, uint3
     carry += tt;
   }
   if (threadIdx.x == 0) s[nch] = carry;
-  __syncthreads();
+  lds_barrier();
 }
 
 // Largest c in [0, nch) with s[c] <= j.
@@ -1035,7 +1033,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_final(Params P) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   auto key = [&](int i) { return in_lds ? s_key[i] : sortable(entry_at(i).s); };
   auto cand_of = [&](int i) { return in_lds ? s_cand[i] : entry_at(i).cand; };
 
@@ -1065,7 +1063,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_final(Params P) {
   }
   if (pairwise)
     for (int i = tid; i < (int)nu; i += NT) s_rank[i] = 0;
-  __syncthreads();
+  lds_barrier();
   uint32_t kth = 0, ties = 0;
   if (pairwise) {
     // composite (key, complement of the list index): a larger composite is a
@@ -1087,7 +1085,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_final(Params P) {
       }
       if (r) atomicAdd(&s_rank[i], r);
     }
-    __syncthreads();
+    lds_barrier();
   } else if (cut) {
     if (u_lds) {
       kth = wg_kth_largest<NT>((int)nu, need, [&](int i) { return s_ukey[i]; }, s_hist, s_tmp, &ties);
@@ -1152,14 +1150,9 @@ constexpr int kSmallPer = kSmallMax / kSmallThreads;   // slots per thread
 // Exclusive prefix sum over the 512-thread work-group (s_tmp: >= 8 entries).
 __device__ __forceinline__ uint32_t wg8_exclusive_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan_u32(v);
   if (lane == 63) s_tmp[wave] = x;
-  __syncthreads();
+  lds_barrier();
   uint32_t before = 0, all = 0;
 #pragma unroll
   for (int i = 0; i < kSmallWaves; ++i) {
@@ -1167,7 +1160,7 @@ __device__ __forceinline__ uint32_t wg8_exclusive_scan(uint32_t v, uint32_t* s_t
     if (i < wave) before += t;
     all += t;
   }
-  __syncthreads();
+  lds_barrier();
   *total = all;
   return before + x - v;
 }
@@ -1201,7 +1194,7 @@ __device__ uint32_t small_kth(const uint32_t key[kSmallPer], Elig elig, int K, u
     s_tmp[wave] = lo;
     s_tmp[8 + wave] = hi;
   }
-  __syncthreads();
+  lds_barrier();
   lo = 0xFFFFFFFFu;
   hi = 0u;
 #pragma unroll
@@ -1209,7 +1202,7 @@ __device__ uint32_t small_kth(const uint32_t key[kSmallPer], Elig elig, int K, u
     lo = min(lo, s_tmp[i]);
     hi = max(hi, s_tmp[8 + i]);
   }
-  __syncthreads();
+  lds_barrier();
   if (span) *span = 0u;
   if (lo == hi) {
     uint32_t tot;
@@ -1228,12 +1221,12 @@ __device__ uint32_t small_kth(const uint32_t key[kSmallPer], Elig elig, int K, u
     const int width = shift < 0 ? 8 + shift : 8;
     const uint32_t dmask = (1u << width) - 1u;
     for (int i = tid; i < kSmallWaves * 256; i += kSmallThreads) s_h[i] = 0;
-    __syncthreads();
+    lds_barrier();
     uint32_t* h = s_h + wave * 256;
 #pragma unroll
     for (int j = 0; j < kSmallPer; ++j)
       if (elig(key[j]) && (key[j] & mask) == prefix) atomicAdd(&h[(key[j] >> sh) & dmask], 1u);
-    __syncthreads();
+    lds_barrier();
     // thread tid < 256 owns digit 255 - tid; the exclusive scan counts larger digits
     uint32_t v = 0;
     const int dg = 255 - tid;
@@ -1248,13 +1241,13 @@ __device__ uint32_t small_kth(const uint32_t key[kSmallPer], Elig elig, int K, u
       s_tmp[17] = excl;
       s_tmp[18] = v;
     }
-    __syncthreads();
+    lds_barrier();
     const uint32_t d = s_tmp[16];
     remaining -= s_tmp[17];
     cnt_digit = s_tmp[18];
     prefix |= d << sh;
     mask |= dmask << sh;
-    __syncthreads();
+    lds_barrier();
     if (sh == 0) break;
     if (sh <= stop_bits) {
       *span = (1u << sh) - 1u;
@@ -1270,23 +1263,36 @@ __device__ uint32_t small_kth(const uint32_t key[kSmallPer], Elig elig, int K, u
 // kSure = certainly selected, anything else = a key to be ranked.
 constexpr uint32_t kSure = 0xFFFFFFFFu;   // above every finite score's sortable key
 
+constexpr int kPend = 4096;      // keys near the K-th that the fast path keeps in LDS
+constexpr int kPairMax = 256;    // pending keys ranked pairwise (larger lists: radix select)
+constexpr int kRsMembers = 4;    // uncertain members one wave rescores at a time
+
 template <int D>
 __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
-  constexpr int DW = D / 2;
-  __shared__ uint32_t s_key[kSmallMax];      // exact keys of rescored slots
+  // One buffer, two layouts: the general path's per-slot arrays, or the fast
+  // path's list of pending keys (those near the K-th approximate score)
+  __shared__ __attribute__((aligned(16))) uint32_t s_big[kSmallMax + kSmallMax / 2];
+  uint32_t* s_key = s_big;                                                   // general: exact keys by slot
+  uint16_t* s_ul = reinterpret_cast<uint16_t*>(s_big + kSmallMax);           // general: uncertain slots
+  uint32_t* s_pk = s_big;                                                    // fast: pending keys (exact once rescored)
+  uint16_t* s_ps = reinterpret_cast<uint16_t*>(s_big + kPend);               // fast: pending slots
+  uint16_t* s_pu = reinterpret_cast<uint16_t*>(s_big + kPend + kPend / 2);   // fast: uncertain pending indices
+  uint8_t* s_pst = reinterpret_cast<uint8_t*>(s_big + 2 * kPend);            // fast: pending states
+  __shared__ __attribute__((aligned(16))) float s_kf[kSmallWaves][kRsMembers][D];   // member keys being rescored
+  __shared__ __attribute__((aligned(16))) float s_r[kSmallWaves][kRsMembers][kWave];
   __shared__ int32_t s_pool[kSmallMax / 8];
-  __shared__ uint16_t s_ul[kSmallMax];       // uncertain slots
   __shared__ uint32_t s_h[kSmallWaves * 256];
+  __shared__ uint32_t s_selw[kSmallThreads];   // fast path: chosen pending slots, one word per thread
   __shared__ uint32_t s_tmp[32];
   __shared__ float s_par[4];
   __shared__ float s_qn[kWave];
   __shared__ __attribute__((aligned(16))) float s_w[kWave];
-  __shared__ __attribute__((aligned(16))) float s_r[kSmallWaves][2][kWave];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = blockIdx.x;
   const int K = P.k;
   const int nc = 8 * P.keep_in;
+  s_selw[tid] = 0;
   const int64_t base = P.seq_base[P.q_seq[q]];
   const float* sc = P.scores + (size_t)q * P.stride;
   int32_t* out = P.idx_out + (size_t)q * K;
@@ -1314,18 +1320,32 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
   const float wraw = P.w[(size_t)q * P.h_i + min(tid & 63, P.h_i - 1)];
   const float kraw = P.kpart[(size_t)q * nwg + min(tid & 63, nwg - 1)];
 
-  // approximate scores -> sortable keys in registers (0: no candidate)
+  // approximate scores -> sortable keys in registers (0: no candidate); the
+  // smallest and largest key and their count
   uint32_t key[kSmallPer];
+  uint32_t klo = 0xFFFFFFFFu, khi = 0u, nv_loc = 0;
 #pragma unroll
   for (int j4 = 0; j4 < kSmallPer / 4; ++j4) {
     const bool in = s0 + 4 * j4 < nc;
     const float vv[4] = {raw[j4].x, raw[j4].y, raw[j4].z, raw[j4].w};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) key[4 * j4 + u] = (in && vv[u] != -INFINITY) ? sortable(vv[u]) : 0u;
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = in && vv[u] != -INFINITY;
+      const uint32_t k = ok ? sortable(vv[u]) : 0u;
+      key[4 * j4 + u] = k;
+      klo = ok ? min(klo, k) : klo;
+      khi = max(khi, k);
+      nv_loc += ok ? 1u : 0u;
+    }
   }
-  uint32_t nv_loc = 0;
-#pragma unroll
-  for (int j = 0; j < kSmallPer; ++j) nv_loc += key[j] != 0u ? 1u : 0u;
+  klo = wave_min_dpp(klo);
+  khi = wave_max_dpp(khi);
+  nv_loc = wave_sum_dpp(nv_loc);
+  if (lane == 0) {
+    s_tmp[wave] = klo;
+    s_tmp[8 + wave] = khi;
+    s_tmp[16 + wave] = nv_loc;
+  }
 #pragma unroll
   for (int k = 0; k < kSmallMax / 8 / kSmallThreads; ++k)
     if (tid + kSmallThreads * k < nc / 8) s_pool[tid + kSmallThreads * k] = praw[k];
@@ -1343,16 +1363,17 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
         ss = fmaf(hi, hi, ss);
       }
     }
-    ss += __shfl_xor(ss, 1, kWave);
-    ss += __shfl_xor(ss, 2, kWave);
-    ss += __shfl_xor(ss, 4, kWave);
+    // sum over the eight threads of a head (lanes 8j .. 8j + 7)
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0xB1, 0xF, 0xF, false));
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x4E, 0xF, 0xF, false));
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x141, 0xF, 0xF, false));
     if (part == 0) s_qn[h] = h < P.h_i ? sqrtf(ss) : 0.0f;   // times |w_h| below
     if (wave == 0) {
-      const float mk = wave_max(lane < nwg ? kraw : 0.0f);
-      if (lane == 0) s_par[1] = mk;
+      const uint32_t mk = wave_max_dpp(lane < nwg ? __float_as_uint(kraw) : 0u);   // non-negative floats order as integers
+      if (lane == 0) s_par[1] = __uint_as_float(mk);
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) {
     const float qn = wave_sum(fabsf(s_w[lane]) * s_qn[lane]);
     const float wa = wave_sum(fabsf(s_w[lane]));
@@ -1360,185 +1381,327 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
       s_par[0] = P.bound_tok * (qn * (1.0f + 0.0009765625f)) * sqrtf(s_par[1]) * (1.0f + 0.0009765625f) +
                  wa * (float)P.d_i * 7.8886e-31f;
   }
-  uint32_t nv;
-  (void)wg8_exclusive_scan(nv_loc, s_tmp, &nv);   // its barriers publish s_pool, s_w, s_par
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u, nv = 0;
+#pragma unroll
+  for (int i = 0; i < kSmallWaves; ++i) {
+    lo = min(lo, s_tmp[i]);
+    hi = max(hi, s_tmp[8 + i]);
+    nv += s_tmp[16 + i];
+  }
+  lds_barrier();   // publishes s_par; s_tmp is free again
   const float delta = s_par[0];
 
-  // classify into the key registers: kSure, 0 (out), or the approximate key
-  // of an uncertain member
   auto is_real = [](uint32_t k) { return k != 0u && k != kSure; };
-  if ((int)nv > K) {
-    // bracket the K-th approximate score: L <= a_K and U >= a_K >= a_K1 (the
-    // last 8 bits of the key, 2^-15 of the value, are left open)
-    uint32_t ties, eq, span;
-    const uint32_t kL = small_kth(key, is_real, K, s_h, s_tmp, &ties, &eq, 8, &span);
-    const uint32_t kK = kL, kK1 = kL | span;
-    const float keep_thr = band_below(unsortable(kK), delta);    // L - 2 Delta
-    const float in_thr = band_above(unsortable(kK1), delta);     // U + 2 Delta
+  uint32_t sel = 0;   // bit j: slot s0 + j is selected
+  // ---- fast path: a linear histogram of the values, then only the keys near
+  // the K-th (a short list in LDS) are examined further
+  const float vlo = unsortable(lo), vhi = unsortable(hi);
+  const float rng = vhi - vlo;
+  const bool linear = (int)nv > K && lo != hi && rng >= 1e-30f && rng <= 3.0e38f;
+  bool fast = false;
+  int np = 0, n_cert = 0, p_first = 0;
+  uint32_t pend = 0;   // bit j: slot s0 + j is pending
+  if (linear) {
+    const float scale = 256.0f / rng;
+    // bin of a key: monotone in the value (each rounding step is monotone)
+    auto lbin = [vlo, scale](uint32_t k) { return (uint32_t)fminf((unsortable(k) - vlo) * scale, 255.0f); };
+    for (int i = tid; i < kSmallWaves * 256; i += kSmallThreads) s_h[i] = 0;
+    lds_barrier();
+    uint32_t* hw = s_h + wave * 256;
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j)
+      if (key[j] != 0u) atomicAdd(&hw[lbin(key[j])], 1u);
+    lds_barrier();
+    // thread tid < 256 owns bin 255 - tid; the exclusive scan counts higher bins
+    uint32_t v = 0;
+    const int dg = 255 - tid;
+    if (tid < 256) {
+#pragma unroll
+      for (int w = 0; w < kSmallWaves; ++w) v += s_h[w * 256 + dg];
+    }
+    uint32_t tot;
+    const uint32_t excl = wg8_exclusive_scan(v, s_tmp, &tot);
+    if (tid < 256 && excl < (uint32_t)K && excl + v >= (uint32_t)K) s_tmp[24] = (uint32_t)dg;
+    lds_barrier();
+    const uint32_t bk = s_tmp[24];
+    // [e_lo, e_hi] holds every value of bin bk (the bin's edges widened by far
+    // more than the rounding of the bin computation), so e_lo <= a_K <= e_hi:
+    // a key below band_below(e_lo) is out, one above band_above(e_hi) is
+    // certainly in, whatever a_K is inside the bin; the rest is pending.  The
+    // comparisons run on the sortable keys, which order as the values do.
+    const float wdt = rng * 0.00390625f;
+    const float slack = (fabsf(vlo) + fabsf(vhi)) * 6.103515625e-05f + wdt * 0.0078125f;
+    const float e_lo = bk == 0 ? vlo : vlo + (float)bk * wdt - slack;
+    const float e_hi = bk == 255 ? vhi : vlo + (float)(bk + 1) * wdt + slack;
+    const uint32_t k_keep0 = sortable(band_below(e_lo, delta)), k_in0 = sortable(band_above(e_hi, delta));
+    uint32_t cert = 0;
 #pragma unroll
     for (int j = 0; j < kSmallPer; ++j) {
-      const float v = unsortable(key[j]);
-      key[j] = key[j] == 0u || !(v >= keep_thr) ? 0u : (v > in_thr ? kSure : key[j]);
+      const uint32_t k = key[j];   // 0 (no candidate) is below every finite threshold's key
+      cert |= (k > k_in0 ? 1u : 0u) << j;
+      pend |= (k >= k_keep0 && k <= k_in0 ? 1u : 0u) << j;
     }
+    uint32_t all;
+    const uint32_t before = wg8_exclusive_scan(__popc(pend) | ((uint32_t)__popc(cert) << 16), s_tmp, &all);
+    np = (int)(all & 0xFFFFu);
+    n_cert = (int)(all >> 16);
+    p_first = (int)(before & 0xFFFFu);
+    fast = np <= kPend;
+    if (fast) {
+      sel = cert;
+      int po = p_first;
+#pragma unroll
+      for (int j = 0; j < kSmallPer; ++j) {
+        if ((pend >> j) & 1u) {
+          s_pk[po] = key[j];
+          s_ps[po] = (uint16_t)(s0 + j);
+          ++po;
+        }
+      }
+    }
+  }
+
+  // the query row of head `lane` for the rescoring (packed bf16 pairs): its
+  // loads overlap the selection steps below
+  constexpr int DW = D / 2;
+  uint32_t qrow[DW];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + min(lane, P.h_i - 1)) * D);
+#pragma unroll
+    for (int i = 0; i < DW / 4; ++i) {
+      const uint4 v = src[i];
+      qrow[4 * i] = v.x;
+      qrow[4 * i + 1] = v.y;
+      qrow[4 * i + 2] = v.z;
+      qrow[4 * i + 3] = v.w;
+    }
+  }
+
+  int nu = 0, need = 0;
+  if (fast) {
+    if (np <= kPairMax && tid < 8) s_pk[np + tid] = 0u;   // padding for four-wide reads (0: below every key)
+    lds_barrier();
+    // a_K exactly: the (K - n_cert)-th largest pending key (keys above the
+    // pending range are above a_K, keys below it below, and a_K is pending)
+    const int kp = K - n_cert;
+    uint32_t kK;
+    if (np <= kPairMax) {
+      // pairwise: entry i holds it when (#keys > key_i) < kp <= (#keys >= key_i).
+      // Threads t = i + npr * sl count slice sl of the list for entry i; the
+      // counts gather in s_h (greater: [0, 256), greater or equal: [256, 512))
+      const int npr = (np + 63) & ~63;                 // entries rounded to whole waves
+      const int R = kSmallThreads / npr;               // slices: 2 .. 8
+      const int per = ((np + R - 1) / R + 3) & ~3;     // list entries per slice, four-aligned
+      if (tid < 512) s_h[tid] = 0;
+      lds_barrier();
+      const int i = tid % npr, sl = tid / npr;
+      if (i < np && sl < R) {
+        const uint32_t ki = s_pk[i];
+        uint32_t gt = 0, ge = 0;
+        const int j0 = sl * per, j1 = min(np, j0 + per);
+        for (int j = j0; j < j1; j += 4) {   // entries past np read the zero padding
+          const uint4 k4 = *reinterpret_cast<const uint4*>(&s_pk[j]);
+          gt += (k4.x > ki ? 1u : 0u) + (k4.y > ki ? 1u : 0u) + (k4.z > ki ? 1u : 0u) + (k4.w > ki ? 1u : 0u);
+          ge += (k4.x >= ki ? 1u : 0u) + (k4.y >= ki ? 1u : 0u) + (k4.z >= ki ? 1u : 0u) + (k4.w >= ki ? 1u : 0u);
+        }
+        if (gt) atomicAdd(&s_h[i], gt);
+        if (ge) atomicAdd(&s_h[256 + i], ge);
+      }
+      lds_barrier();
+      if (tid < np && s_h[tid] < (uint32_t)kp && (uint32_t)kp <= s_h[256 + tid]) s_tmp[24] = s_pk[tid];   // one key
+      lds_barrier();
+      kK = s_tmp[24];
+    } else {
+      uint32_t ties;
+      kK = wg_kth_largest<kSmallThreads>(np, kp, [&](int i) { return s_pk[i]; }, s_h, s_tmp, &ties);
+    }
+    // classify the pending keys against the exact bracket [a_K, a_K]; the
+    // uncertain ones are listed in pending (= slot) order
+    const uint32_t k_keep1 = sortable(band_below(unsortable(kK), delta));
+    const uint32_t k_in1 = sortable(band_above(unsortable(kK), delta));
+    const int ppt = (np + kSmallThreads - 1) / kSmallThreads;
+    const int i0 = min(np, tid * ppt), i1 = min(np, i0 + ppt);
+    uint32_t c2 = 0;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t k = s_pk[i];
+      const uint8_t st = k < k_keep1 ? 0 : (k > k_in1 ? 1 : 2);
+      s_pst[i] = st;
+      c2 += st == 1 ? 0x10000u : (st == 2 ? 1u : 0u);
+    }
+    uint32_t all;
+    uint32_t uo = wg8_exclusive_scan(c2, s_tmp, &all) & 0xFFFFu;
+    nu = (int)(all & 0xFFFFu);
+    need = K - (n_cert + (int)(all >> 16));
+    for (int i = i0; i < i1; ++i)
+      if (s_pst[i] == 2) s_pu[uo++] = (uint16_t)i;
+    lds_barrier();
   } else {
+    // ---- general path: bracket the K-th approximate score by a radix select
+    // over all register keys (L <= a_K and U >= a_K >= a_K1, the last 8 bits of
+    // the key -- 2^-15 of the value -- left open)
+    if ((int)nv > K) {
+      uint32_t ties, eq, span;
+      const uint32_t kL = small_kth(key, is_real, K, s_h, s_tmp, &ties, &eq, 8, &span);
+      const uint32_t kK = kL, kK1 = kL | span;
+      const float keep_thr = band_below(unsortable(kK), delta);    // L - 2 Delta
+      const float in_thr = band_above(unsortable(kK1), delta);     // U + 2 Delta
 #pragma unroll
-    for (int j = 0; j < kSmallPer; ++j) key[j] = key[j] != 0u ? kSure : 0u;
+      for (int j = 0; j < kSmallPer; ++j) {
+        const float v = unsortable(key[j]);
+        key[j] = key[j] == 0u || !(v >= keep_thr) ? 0u : (v > in_thr ? kSure : key[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSmallPer; ++j) key[j] = key[j] != 0u ? kSure : 0u;
+    }
+    // uncertain list (slot order)
+    uint32_t cu = 0, ci = 0;
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j) {
+      cu += is_real(key[j]) ? 1u : 0u;
+      ci += key[j] == kSure ? 1u : 0u;
+      sel |= (key[j] == kSure ? 1u : 0u) << j;
+    }
+    uint32_t all;
+    uint32_t uo = wg8_exclusive_scan(cu | (ci << 16), s_tmp, &all) & 0xFFFFu;
+    nu = (int)(all & 0xFFFFu);
+    need = K - (int)(all >> 16);
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j)
+      if (is_real(key[j])) s_ul[uo++] = (uint16_t)(s0 + j);
+    lds_barrier();
   }
-  // uncertain list (any order: exact keys go back to their slots)
-  uint32_t cu = 0;
-#pragma unroll
-  for (int j = 0; j < kSmallPer; ++j) cu += is_real(key[j]) ? 1u : 0u;
-  uint32_t nu;
-  uint32_t uo = wg8_exclusive_scan(cu, s_tmp, &nu);
-#pragma unroll
-  for (int j = 0; j < kSmallPer; ++j)
-    if (is_real(key[j])) s_ul[uo++] = (uint16_t)(s0 + j);
-  __syncthreads();
+  // member j of the uncertain list: its slot, and where its exact key goes
+  auto u_slot = [&](int j) -> int { return fast ? (int)s_ps[s_pu[j]] : (int)s_ul[j]; };
+  auto u_store = [&](int j, uint32_t k) {
+    if (fast) s_pk[s_pu[j]] = k;
+    else s_key[s_ul[j]] = k;
+  };
+  auto u_exact = [&](int j) -> uint32_t { return fast ? s_pk[s_pu[j]] : s_key[s_ul[j]]; };
 
-  // exact scores of the uncertain members: one wave per member, lane = head;
-  // the key row reaches the lanes through readlane, the next row loads meanwhile
-  if (nu > 0) {
-    uint32_t qrow[DW];   // the lane's query row, packed bf16 pairs
-    {
-      const int hh = lane < P.h_i ? lane : 0;
-      const uint4* src = reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + hh) * D);
+  // exact scores of the uncertain members, kRsMembers per wave at a time, one
+  // lane per head: the members' key rows are staged in LDS as fp32 and read
+  // back as broadcasts, the lane's query row sits in registers; the head sums
+  // run one member per lane.  Rows h >= h_i compute a finite throwaway value.
+  const bool choose = nu > 0 && need > 0 && nu > need;   // otherwise no ranking is needed
+  if (choose) {
+    for (int jb = wave * kRsMembers; jb < nu; jb += kSmallWaves * kRsMembers) {
+      const int nm = min(kRsMembers, nu - jb);
+      uint32_t kw[kRsMembers];
 #pragma unroll
-      for (int i = 0; i < DW / 4; ++i) {
-        const uint4 v = src[i];
-        qrow[4 * i] = v.x;
-        qrow[4 * i + 1] = v.y;
-        qrow[4 * i + 2] = v.z;
-        qrow[4 * i + 3] = v.w;
+      for (int m = 0; m < kRsMembers; ++m) {
+        const int slot = u_slot(jb + min(m, nm - 1));
+        const int64_t row = base + (int64_t)s_pool[slot >> 3] * 8 + (slot & 7);
+        kw[m] = reinterpret_cast<const uint32_t*>(P.ik + (size_t)row * D)[lane < DW ? lane : 0];
       }
-    }
-    auto load_row = [&](int j) -> uint32_t {
-      const int slot = s_ul[min(j, (int)nu - 1)];
-      const int64_t row = base + (int64_t)s_pool[slot >> 3] * 8 + (slot & 7);
-      const int l = lane < DW ? lane : 0;
-      return reinterpret_cast<const uint32_t*>(P.ik + (size_t)row * D)[l];
-    };
-    // wave w scores members 2w + 16 r and 2w + 1 + 16 r, chains interleaved
-    constexpr int kStep = 2 * kSmallWaves;
-    int j = 2 * wave;
-    uint32_t kw0 = 0, kw1 = 0;
-    if (j < (int)nu) {
-      kw0 = load_row(j);
-      kw1 = load_row(j + 1);
-    }
-    for (; j < (int)nu; j += kStep) {
-      const uint32_t c0 = kw0, c1 = kw1;
-      if (j + kStep < (int)nu) {   // in flight during the chains
-        kw0 = load_row(j + kStep);
-        kw1 = load_row(j + kStep + 1);
-      }
-      float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-      for (int d2 = 0; d2 < DW; ++d2) {
-        const uint32_t x0 = (uint32_t)__builtin_amdgcn_readlane((int)c0, d2);
-        const uint32_t x1 = (uint32_t)__builtin_amdgcn_readlane((int)c1, d2);
-        const float ql = __uint_as_float(qrow[d2] << 16), qh = __uint_as_float(qrow[d2] & 0xFFFF0000u);
-        a0 = fmaf(ql, __uint_as_float(x0 << 16), a0);
-        a1 = fmaf(ql, __uint_as_float(x1 << 16), a1);
-        a0 = fmaf(qh, __uint_as_float(x0 & 0xFFFF0000u), a0);
-        a1 = fmaf(qh, __uint_as_float(x1 & 0xFFFF0000u), a1);
+      for (int m = 0; m < kRsMembers; ++m)
+        if (lane < DW)
+          *reinterpret_cast<f32x2*>(&s_kf[wave][m][2 * lane]) =
+              f32x2{__uint_as_float(kw[m] << 16), __uint_as_float(kw[m] & 0xFFFF0000u)};
+      // per head h = lane: fp32 fma chains over d ascending (the oracle's order)
+      float acc[kRsMembers];
+#pragma unroll
+      for (int m = 0; m < kRsMembers; ++m) acc[m] = 0.0f;
+#pragma unroll
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        const float q0 = __uint_as_float(qrow[2 * d4] << 16), q1 = __uint_as_float(qrow[2 * d4] & 0xFFFF0000u);
+        const float q2 = __uint_as_float(qrow[2 * d4 + 1] << 16), q3 = __uint_as_float(qrow[2 * d4 + 1] & 0xFFFF0000u);
+#pragma unroll
+        for (int m = 0; m < kRsMembers; ++m) {
+          const f32x4 kv = *reinterpret_cast<const f32x4*>(&s_kf[wave][m][4 * d4]);
+          acc[m] = fmaf(q0, kv.x, acc[m]);
+          acc[m] = fmaf(q1, kv.y, acc[m]);
+          acc[m] = fmaf(q2, kv.z, acc[m]);
+          acc[m] = fmaf(q3, kv.w, acc[m]);
+        }
       }
-      // ordered head sums s = fma(w_h, r_h, s), h ascending; entries h >= h_i
-      // hold w = 0 and a finite r, which leave s unchanged
-      s_r[wave][0][lane] = a0 > 0.0f ? a0 : 0.0f;
-      s_r[wave][1][lane] = a1 > 0.0f ? a1 : 0.0f;
-      float s0v = 0.0f, s1v = 0.0f;
-#pragma unroll 2
-      for (int h4 = 0; h4 < 16; ++h4) {
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(&s_w[4 * h4]);
-        const f32x4 r0 = *reinterpret_cast<const f32x4*>(&s_r[wave][0][4 * h4]);
-        const f32x4 r1 = *reinterpret_cast<const f32x4*>(&s_r[wave][1][4 * h4]);
-        s0v = fmaf(wv.x, r0.x, s0v);
-        s1v = fmaf(wv.x, r1.x, s1v);
-        s0v = fmaf(wv.y, r0.y, s0v);
-        s1v = fmaf(wv.y, r1.y, s1v);
-        s0v = fmaf(wv.z, r0.z, s0v);
-        s1v = fmaf(wv.z, r1.z, s1v);
-        s0v = fmaf(wv.w, r0.w, s0v);
-        s1v = fmaf(wv.w, r1.w, s1v);
+#pragma unroll
+      for (int m = 0; m < kRsMembers; ++m) s_r[wave][m][lane] = acc[m] > 0.0f ? acc[m] : 0.0f;
+      // ordered head sum s = fma(w_h, r_h, s), h ascending, member m in lane m;
+      // entries h >= h_i hold w = 0 and a finite r, which leave s unchanged
+      if (lane < kRsMembers) {
+        const float* rr = &s_r[wave][lane][0];
+        float sv = 0.0f;
+#pragma unroll 4
+        for (int h4 = 0; h4 < 16; ++h4) {
+          const f32x4 wv = *reinterpret_cast<const f32x4*>(&s_w[4 * h4]);
+          const f32x4 r4 = *reinterpret_cast<const f32x4*>(rr + 4 * h4);
+          sv = fmaf(wv.x, r4.x, sv);
+          sv = fmaf(wv.y, r4.y, sv);
+          sv = fmaf(wv.z, r4.z, sv);
+          sv = fmaf(wv.w, r4.w, sv);
+        }
+        if (lane < nm) u_store(jb + lane, sortable(sv));
       }
-      if (lane == 0) {
-        s_key[s_ul[j]] = sortable(s0v);
-        if (j + 1 < (int)nu) s_key[s_ul[j + 1]] = sortable(s1v);
-      }
-      // the next rows become visible only here, so their wait stays below the chains
-      asm volatile("" : "+v"(kw0), "+v"(kw1));
     }
   }
-  __syncthreads();
+  lds_barrier();
 
-  // final choice: every certain member plus the best `need` uncertain ones,
-  // by (exact score desc, position asc); afterwards every slot is kSure or 0
-  uint32_t ci = 0;
-#pragma unroll
-  for (int j = 0; j < kSmallPer; ++j) ci += key[j] == kSure ? 1u : 0u;
-  uint32_t nin;
-  (void)wg8_exclusive_scan(ci, s_tmp, &nin);
-  const int need = K - (int)nin;
-  if ((int)nu <= need || need <= 0) {
-    const uint32_t to = need > 0 ? kSure : 0u;
-#pragma unroll
-    for (int j = 0; j < kSmallPer; ++j) key[j] = is_real(key[j]) ? to : key[j];
-  } else if ((int)nu <= kWave) {
-    // one wave ranks (exact key, complement of slot) composites pairwise and
-    // marks each uncertain slot in s_key (kSure = chosen, 0 = not)
+  // final choice among the uncertain members: the best `need` by (exact score
+  // desc, position asc).  u_decide records a member's decision where the
+  // write-back below finds it.
+  auto u_decide = [&](int j, bool take) {
+    if (fast) s_pst[s_pu[j]] = take ? 1 : 0;
+    else s_key[s_ul[j]] = take ? kSure : 0u;
+  };
+  if (!choose) {
+    for (int jj = tid; jj < nu; jj += kSmallThreads) u_decide(jj, need > 0);   // all in, or all out
+  } else if (nu <= kWave) {
+    // one wave ranks (exact key, complement of slot) composites pairwise
     if (wave == 0) {
-      uint32_t slot = 0;
       uint64_t comp = 0;
-      if (lane < (int)nu) {
-        slot = s_ul[lane];
-        comp = ((uint64_t)s_key[slot] << 32) | (uint64_t)(0xFFFFFFFFu - slot);
-      }
+      if (lane < nu) comp = ((uint64_t)u_exact(lane) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)u_slot(lane));
       uint32_t r = 0;
-      for (int jj = 0; jj < (int)nu; ++jj) {
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)comp, jj);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(comp >> 32), jj);
-        r += ((((uint64_t)hi << 32) | lo) > comp) ? 1u : 0u;
+      for (int jj = 0; jj < nu; ++jj) {
+        const uint32_t clo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)comp, jj);
+        const uint32_t chi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(comp >> 32), jj);
+        r += ((((uint64_t)chi << 32) | clo) > comp) ? 1u : 0u;
       }
-      if (lane < (int)nu) s_key[slot] = r < (uint32_t)need ? kSure : 0u;
+      if (lane < nu) u_decide(lane, r < (uint32_t)need);
     }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kSmallPer; ++j)
-      if (is_real(key[j])) key[j] = s_key[s0 + j];
   } else {
-    // many uncertain members: radix select on their exact keys, ties at the
-    // cut to the lower slots
-#pragma unroll
-    for (int j = 0; j < kSmallPer; ++j)
-      if (is_real(key[j])) key[j] = max(min(s_key[s0 + j], kSure - 1u), 1u);   // stay real
-    uint32_t ties, eq;
-    const uint32_t kth = small_kth(key, is_real, need, s_h, s_tmp, &ties, &eq);
+    // radix select on the exact keys; ties at the cut go to the lower slots
+    // (the list is in slot order).  Keys are kept inside [1, kSure - 1].
+    auto xk = [&](int i) { return min(max(u_exact(i), 1u), kSure - 1u); };
+    uint32_t ties;
+    const uint32_t kth = wg_kth_largest<kSmallThreads>(nu, need, xk, s_h, s_tmp, &ties);
+    const int upt = (nu + kSmallThreads - 1) / kSmallThreads;
+    const int j0 = min(nu, tid * upt), j1 = min(nu, j0 + upt);
     uint32_t tl = 0;
-#pragma unroll
-    for (int j = 0; j < kSmallPer; ++j) tl += (is_real(key[j]) && key[j] == kth) ? 1u : 0u;
+    for (int jj = j0; jj < j1; ++jj) tl += xk(jj) == kth ? 1u : 0u;
     uint32_t ttot;
-    uint32_t tr = wg8_exclusive_scan(tl, s_tmp, &ttot);   // tied slots before this segment
-#pragma unroll
-    for (int j = 0; j < kSmallPer; ++j) {
-      const uint32_t k = key[j];
-      if (is_real(k)) {
-        const bool tie = k == kth;
-        key[j] = (k > kth || (tie && tr < ties)) ? kSure : 0u;
-        tr += tie ? 1u : 0u;
-      }
+    uint32_t tr = wg8_exclusive_scan(tl, s_tmp, &ttot);
+    for (int jj = j0; jj < j1; ++jj) {
+      const uint32_t k = xk(jj);
+      const bool tie = k == kth;
+      u_decide(jj, k > kth || (tie && tr < ties));
+      tr += tie ? 1u : 0u;
     }
   }
-  uint32_t cnt = 0;
+  lds_barrier();
+  // decisions into the selection mask
+  if (fast) {
+    // chosen pending entries set their slot's bit in the owning thread's word
+    // (slot s lives in thread s / 32, bit s % 32)
+    for (int i = tid; i < np; i += kSmallThreads)
+      if (s_pst[i] == 1) {
+        const uint32_t slot = s_ps[i];
+        atomicOr(&s_selw[slot >> 5], 1u << (slot & 31));
+      }
+    lds_barrier();
+    sel |= s_selw[tid];
+  } else {
 #pragma unroll
-  for (int j = 0; j < kSmallPer; ++j) cnt += key[j] == kSure ? 1u : 0u;
+    for (int j = 0; j < kSmallPer; ++j)
+      if (is_real(key[j])) sel |= (s_key[s0 + j] == kSure ? 1u : 0u) << j;
+  }
+  // selected slots in position order: a prefix sum over the threads' segments
   uint32_t tot;
-  uint32_t o = wg8_exclusive_scan(cnt, s_tmp, &tot);
-#pragma unroll
-  for (int j = 0; j < kSmallPer; ++j) {
-    if (key[j] == kSure) {
-      const int slot = s0 + j;
-      out[o++] = s_pool[slot >> 3] * 8 + (slot & 7);
-    }
+  uint32_t o = wg8_exclusive_scan((uint32_t)__popc(sel), s_tmp, &tot);
+  for (uint32_t m = sel; m; m &= m - 1) {
+    const int slot = s0 + __builtin_ctz(m);
+    out[o++] = s_pool[slot >> 3] * 8 + (slot & 7);
   }
   for (int i = (int)tot + tid; i < K; i += kSmallThreads) out[i] = -1;
 }

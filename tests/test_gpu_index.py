@@ -120,6 +120,37 @@ def test_reindex(lengths, keep):
 
 
 @gpu
+@pytest.mark.parametrize("case", ["equal", "two_values", "scaled_copies"])
+def test_reindex_ties_and_narrow_ranges(case):
+    """Degenerate score sets for the single-work-group Reindex select: every
+    score equal, two distinct values, and many keys that are scaled copies of
+    one row (scores on a few exact multiples)."""
+    note(f"reindex ties {case}")
+
+    def kf(ik):
+        if case == "equal":
+            return ik[:1].expand_as(ik).contiguous()
+        if case == "two_values":
+            ik = ik.clone()
+            ik[::2] = ik[0]
+            ik[1::2] = ik[1]
+            return ik
+        scale = (torch.arange(ik.shape[0]) % 5 + 1).to(torch.float32)[:, None]
+        return (ik[:1].float() * scale).to(torch.bfloat16).expand_as(ik).contiguous()
+    inp = index_inputs([20000, 9000], 64, 128, seed=23, key_fn=kf)
+    _, r_pool = _ref_full(inp, 512, 2048)
+    iq2 = torch.flip(inp["iq"], dims=[1]).contiguous()
+    dev = device()
+    d = to_dev(inp, dev)
+    got = csa2.reindex_topk(iq2.to(dev), d["w"], d["q_seq"], d["nvis"], d["ik"], d["seq_base"],
+                            torch.from_numpy(r_pool).to(dev), k=512)
+    torch.cuda.synchronize()
+    ref = oracle.reindex_topk(bits(iq2), inp["w"].numpy(), inp["q_seq"].numpy(), inp["nvis"].numpy(),
+                              bits(inp["ik"]), inp["seq_base"].numpy(), r_pool, 512, block=8)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+@gpu
 def test_reindex_with_full_query_equals_full_when_pool_covers_context():
     note("reindex == full")
     inp = index_inputs([16000, 7000], 64, 128, seed=22)
