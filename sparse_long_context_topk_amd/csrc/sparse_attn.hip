@@ -122,6 +122,82 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
 
   for (int i = slot_lo + tid; i < sel_hi; i += kThreads) s_pos[i - slot_lo] = P.idx[(size_t)qi * k + i];
 
+  // decode assignment: thread -> key slots 8*kq .. 8*kq+7, channels 8*cg .. 8*cg+7
+  const int kq = tid & 3, cg = tid >> 2;
+  Stage st;
+
+  // Global loads of a sub-tile, one loader per slot class.  Addresses of
+  // empty slots point at the fallback bytes, so no load is conditional.
+  auto load_sel_pos = [&](const int pos[8]) {   // all 32 slots are selected entries
+    st.valid = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const uint8_t* rec = pos[jj] >= 0 ? P.cache + (size_t)(cbase + pos[jj]) * CSA2_KV_RECORD_BYTES : fb;
+      st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
+      st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * (cg >> 3));
+      st.valid |= (pos[jj] >= 0 ? 1u : 0u) << jj;
+    }
+  };
+  auto load_sel = [&](int sub) {      // positions from the LDS copy of the index list
+    const int i0 = sub * kSub + 8 * kq - slot_lo;   // multiple of 8: two 16-byte LDS reads
+    const int4 pa = *reinterpret_cast<const int4*>(&s_pos[i0]);
+    const int4 pb = *reinterpret_cast<const int4*>(&s_pos[i0 + 4]);
+    const int pos[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    load_sel_pos(pos);
+  };
+  auto load_win = [&](int sub) {      // all 32 slots are window rows (or past the window)
+    const int r0 = sub * kSub + 8 * kq - k;
+    st.valid = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const bool ok = r0 + jj < nswa;
+      const uint16_t* src =
+          ok ? P.swa + (size_t)(srow0 + r0 + jj) * 512 + 8 * cg : reinterpret_cast<const uint16_t*>(fb) + 8 * cg;
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
+      st.valid |= (ok ? 1u : 0u) << jj;
+    }
+  };
+  auto load_mixed = [&](int sub) {    // the one sub-tile that straddles slot k
+    const int slot0 = sub * kSub + 8 * kq;
+    st.valid = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int slot = slot0 + jj;
+      st.w[jj][0] = st.w[jj][1] = st.w[jj][2] = st.w[jj][3] = 0u;
+      if (slot < k) {
+        const int pos = P.idx[(size_t)qi * k + slot];
+        if (pos >= 0) {
+          const uint8_t* rec = P.cache + (size_t)(cbase + pos) * CSA2_KV_RECORD_BYTES;
+          st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
+          st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * (cg >> 3));
+          st.valid |= 1u << jj;
+        }
+      } else if (slot - k < nswa) {
+        const uint4 v = *reinterpret_cast<const uint4*>(P.swa + (size_t)(srow0 + slot - k) * 512 + 8 * cg);
+        st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
+        st.valid |= 1u << jj;
+      }
+    }
+  };
+
+  // The first sub-tile's loads are issued before the query's: a selected
+  // sub-tile takes its positions straight from the index list in global memory
+  if (sub0 < sub1) {
+    const int kind = sub_kind(sub0 * kSub, k);
+    if (kind == 0) {
+      const int32_t* ip = P.idx + (size_t)qi * k + sub0 * kSub + 8 * kq;
+      int pos[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) pos[jj] = ip[jj];
+      load_sel_pos(pos);
+    } else if (kind == 1) {
+      load_win(sub0);
+    } else {
+      load_mixed(sub0);
+    }
+  }
+
   // Q^T as the B operand: lane (head n, group g) holds channels 32*ks + 8*g .. +7
   f16x8 qb[16];
   f16x8 ql[QF32 ? 16 : 1];
@@ -151,69 +227,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
       }
     }
   }
-  __syncthreads();   // s_pos
 
-  // decode assignment: thread -> key slots 8*kq .. 8*kq+7, channels 8*cg .. 8*cg+7
-  const int kq = tid & 3, cg = tid >> 2;
-  Stage st;
-
-  // Global loads of a sub-tile, one loader per slot class.  Addresses of
-  // empty slots point at the fallback bytes, so no load is conditional.
-  auto load_sel = [&](int sub) {      // all 32 slots are selected entries
-    const int i0 = sub * kSub + 8 * kq - slot_lo;   // multiple of 8: two 16-byte LDS reads
-    const int4 pa = *reinterpret_cast<const int4*>(&s_pos[i0]);
-    const int4 pb = *reinterpret_cast<const int4*>(&s_pos[i0 + 4]);
-    const int pos[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-    st.valid = 0;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const uint8_t* rec = pos[jj] >= 0 ? P.cache + (size_t)(cbase + pos[jj]) * CSA2_KV_RECORD_BYTES : fb;
-      st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
-      st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * (cg >> 3));
-      st.valid |= (pos[jj] >= 0 ? 1u : 0u) << jj;
-    }
-  };
-  auto load_win = [&](int sub) {      // all 32 slots are window rows (or past the window)
-    const int r0 = sub * kSub + 8 * kq - k;
-    st.valid = 0;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const bool ok = r0 + jj < nswa;
-      const uint16_t* src =
-          ok ? P.swa + (size_t)(srow0 + r0 + jj) * 512 + 8 * cg : reinterpret_cast<const uint16_t*>(fb) + 8 * cg;
-      const uint4 v = *reinterpret_cast<const uint4*>(src);
-      st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
-      st.valid |= (ok ? 1u : 0u) << jj;
-    }
-  };
-  auto load_mixed = [&](int sub) {    // the one sub-tile that straddles slot k
-    const int slot0 = sub * kSub + 8 * kq;
-    st.valid = 0;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int slot = slot0 + jj;
-      st.w[jj][0] = st.w[jj][1] = st.w[jj][2] = st.w[jj][3] = 0u;
-      if (slot < k) {
-        const int pos = s_pos[slot - slot_lo];
-        if (pos >= 0) {
-          const uint8_t* rec = P.cache + (size_t)(cbase + pos) * CSA2_KV_RECORD_BYTES;
-          st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
-          st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * (cg >> 3));
-          st.valid |= 1u << jj;
-        }
-      } else if (slot - k < nswa) {
-        const uint4 v = *reinterpret_cast<const uint4*>(P.swa + (size_t)(srow0 + slot - k) * 512 + 8 * cg);
-        st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
-        st.valid |= 1u << jj;
-      }
-    }
-  };
-  auto load_stage = [&](int sub) {
-    const int kind = sub_kind(sub * kSub, k);
-    if (kind == 0) load_sel(sub);
-    else if (kind == 1) load_win(sub);
-    else load_mixed(sub);
-  };
 
   // Decode the loaded words to fp16 and write both LDS layouts of buffer b.
   auto store_stage = [&](int sub, int b) {
@@ -256,11 +270,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
   for (int t = 0; t < 32; ++t) o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  if (sub0 < sub1) {
-    load_stage(sub0);
-    store_stage(sub0, 0);
-  }
-  __syncthreads();
+  if (sub0 < sub1) store_stage(sub0, 0);
+  lds_barrier();   // s_pos and buffer 0
 
   auto compute = [&](int b) {
     if (head_wave) {
@@ -383,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
     if (kind == 1) load_win(sub + 1);
     else if (kind == 2) load_mixed(sub + 1);
     if (kind != 3) store_stage(sub + 1, b ^ 1);   // the other buffer: last read before the previous barrier
-    __syncthreads();
+    lds_barrier();
   }
 
   if (!head_wave) return;
