@@ -266,6 +266,26 @@ __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist 
   return prefix;
 }
 
+// Compaction chunks of a problem: the block problem's rows hold 1/8 of the
+// candidates.  (Its chunk counters keep the token problem's row pitch.)
+__device__ __forceinline__ int nchunks_of(const Params& P, int kind) {
+  return kind == 1 ? (P.nchunk_cmp + 7) >> 3 : P.nchunk_cmp;
+}
+
+// Grid of the per-chunk kernels: x covers the token (or Reindex) problem's
+// chunks, then the block problem's; y is the query.
+__device__ __forceinline__ void grid_chunk(const Params& P, int* p, int* chunk) {
+  const bool blk = (int)blockIdx.x >= P.nchunk_cmp;
+  *p = (blk ? P.n_q : 0) + (int)blockIdx.y;
+  *chunk = blk ? (int)blockIdx.x - P.nchunk_cmp : (int)blockIdx.x;
+}
+
+// Candidates of problem p (what the prologue records in Meta.nc), from the
+// query's visible length.
+__device__ __forceinline__ int cands_of(const Params& P, int kind, int nvis) {
+  return P.reindex ? 8 * P.keep_in : (kind == 0 ? nvis : (nvis + 7) >> 3);
+}
+
 __device__ __forceinline__ int cand_pos(const Params& P, int q, int kind, uint32_t cand) {
   cand &= ~kCertain;
   if (P.reindex) {
@@ -331,29 +351,34 @@ __global__ __launch_bounds__(kThreads) void k_prologue(Params P) {
 // the K-th score (kAll when at most K candidates exist), computed by every
 // work-group that needs it; the publishing one also records it, with the
 // rounding bound Delta and the count above the bin, in the problem's Meta.
-__device__ uint32_t wg_coarse_bin(const Params& P, int p, bool publish, uint32_t* s_tmp /*>= 12*/) {
+// hv: this thread's 16 bins of the coarse histogram, highest first (bins
+// 4095 - 16 tid down to 4080 - 16 tid), loaded by the caller; kmax2, qw and
+// wabs feed the published rounding bound.
+constexpr int kHPer = kNBins / kThreads;   // histogram bins per thread
+
+__device__ __forceinline__ void load_hist16(const uint32_t* h, uint32_t hv[kHPer]) {
+  const int b_hi = kNBins - kHPer * (int)threadIdx.x - 1;
+#pragma unroll
+  for (int j = 0; j < kHPer; ++j) hv[j] = h[b_hi - j];
+}
+
+__device__ uint32_t wg_coarse_bin(const Params& P, int p, const uint32_t hv[kHPer], bool publish, float kmax2,
+                                  float qw, float wabs, uint32_t* s_tmp /*>= 12*/) {
   const int tid = threadIdx.x;
-  const int q = p % P.n_q, kind = p / P.n_q;
+  const int kind = p / P.n_q;
   const int K = kind == 1 ? P.keep_blocks : P.k;
-  const uint32_t* h = P.hist + (size_t)p * kNBins;
-  constexpr int kPer = kNBins / kThreads;  // 16 bins per thread, highest bins first
+  constexpr int kPer = kHPer;
   const int b_hi = kNBins - kPer * tid - 1;
   if (tid == 0) s_tmp[10] = kAll;          // ordered before its readers by the scan's barriers
   uint32_t loc = 0;
-  uint32_t hv[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    hv[j] = h[b_hi - j];
-    loc += hv[j];
-  }
+  for (int j = 0; j < kPer; ++j) loc += hv[j];
   uint32_t tot;
   const uint32_t above = wg_exclusive_scan(loc, s_tmp, &tot);
   if (publish && tid == 0) {
     // the token problem's scan holds the key-norm maximum; blocks use it too
-    const float kmax2 = __uint_as_float(P.meta[q].maxk2);
-    const Meta m = P.meta[p];
     const float bound = kind == 1 ? P.bound_blk : P.bound_tok;
-    P.meta[p].delta = bound * m.qw * sqrtf(kmax2) * (1.0f + 0.0009765625f) + m.wabs * (float)P.d_i * 7.8886e-31f;
+    P.meta[p].delta = bound * qw * sqrtf(kmax2) * (1.0f + 0.0009765625f) + wabs * (float)P.d_i * 7.8886e-31f;
     P.meta[p].total = tot;
   }
   if (tot > (uint32_t)K && above < (uint32_t)K && above + loc >= (uint32_t)K) {
@@ -619,9 +644,10 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   }
 }
 
-// 16 consecutive scores of one compaction chunk per thread.
-__device__ __forceinline__ int load16(const Params& P, int p, int nc, int my0, float* v) {
-  if (my0 >= nc) return 0;
+// 16 consecutive scores of one compaction chunk per thread (my0 + 15 <
+// stride: the load stays inside the problem's row; entries at or past the
+// candidate count are not counted, see count16).
+__device__ __forceinline__ void load16(const Params& P, int p, int my0, float* v) {
   const float4* s4 = reinterpret_cast<const float4*>(P.scores + (size_t)p * P.stride + my0);
 #pragma unroll
   for (int j = 0; j < kCmpPerThread / 4; ++j) {
@@ -631,8 +657,8 @@ __device__ __forceinline__ int load16(const Params& P, int p, int nc, int my0, f
     v[4 * j + 2] = t.z;
     v[4 * j + 3] = t.w;
   }
-  return min(kCmpPerThread, nc - my0);
 }
+__device__ __forceinline__ int count16(int nc, int my0) { return max(0, min(kCmpPerThread, nc - my0)); }
 
 // ---------------------------------------------------------------- 3. fine histogram
 // Histogram of bits 19..8 of the keys that fall into the coarse bin: the K-th
@@ -643,16 +669,24 @@ __global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
   __shared__ uint32_t s_h[kNBins];
   __shared__ uint32_t s_tmp[16];
   const int tid = threadIdx.x;
-  const int p = blockIdx.y, chunk = blockIdx.x;
-  const int nc = P.meta[p].nc;
-  if (chunk > 0 && chunk * kCmpChunk >= nc) return;
-  const uint32_t bin = wg_coarse_bin(P, p, chunk == 0, s_tmp);
-  if (bin == kAll || chunk * kCmpChunk >= nc) return;
+  int p, chunk;
+  grid_chunk(P, &p, &chunk);
+  const int q = p % P.n_q, kind = p / P.n_q;
+  // every load goes out at once: the chunk's scores (inside the problem's
+  // row: the grid covers the chunks of each kind only), the coarse
+  // histogram, the visible length and the bound's inputs
   const int my0 = chunk * kCmpChunk + tid * kCmpPerThread;
-  for (int i = tid; i < kNBins; i += kThreads) s_h[i] = 0;
-  lds_barrier();
   float v[kCmpPerThread];
-  const int m = load16(P, p, nc, my0, v);
+  load16(P, p, my0, v);
+  uint32_t hv[kHPer];
+  load_hist16(P.hist + (size_t)p * kNBins, hv);
+  const int nc = cands_of(P, kind, P.q_nvis[q]);
+  const float kmax2 = __uint_as_float(P.meta[q].maxk2), qw = P.meta[p].qw, wabs = P.meta[p].wabs;
+  if (chunk > 0 && chunk * kCmpChunk >= nc) return;
+  for (int i = tid; i < kNBins; i += kThreads) s_h[i] = 0;
+  const uint32_t bin = wg_coarse_bin(P, p, hv, chunk == 0, kmax2, qw, wabs, s_tmp);   // its barriers order the clear
+  if (bin == kAll || chunk * kCmpChunk >= nc) return;
+  const int m = count16(nc, my0);
 #pragma unroll
   for (int j = 0; j < kCmpPerThread; ++j) {
     if (j < m && v[j] != -INFINITY) {
@@ -673,29 +707,30 @@ __global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
 // a_K (so L <= a_K and U >= a_K >= a_K1), keep a >= L - 2 Delta (every exact
 // Top-K member) and call a > U + 2 Delta certain.  No bin (at most K
 // candidates): keep everything, all certain.
-__device__ void wg_band_thresholds(const Params& P, int p, bool publish, uint32_t* s_tmp /*>= 16*/,
+// hv: this thread's 16 bins of the fine histogram (as load_hist16); bin,
+// above and delta: the problem's Meta fields.
+__device__ void wg_band_thresholds(const Params& P, int p, const uint32_t hv[kHPer], uint32_t m_bin,
+                                   uint32_t m_above, float m_delta, bool publish, uint32_t* s_tmp /*>= 16*/,
                                    float* keep_thr, float* in_thr) {
   const int tid = threadIdx.x;
   const int kind = p / P.n_q;
   const int K = (kind == 1) ? P.keep_blocks : P.k;
-  const Meta m = P.meta[p];
+  struct {
+    uint32_t bin, above;
+    float delta;
+  } m = {m_bin, m_above, m_delta};
   if (m.bin == kAll) {
     *keep_thr = *in_thr = -INFINITY;
     if (publish && tid == 0) P.meta[p].keep_thr = P.meta[p].in_thr = -INFINITY;
     return;
   }
   const uint32_t need = (uint32_t)K - m.above;   // >= 1
-  const uint32_t* h = P.hist2 + (size_t)p * kNBins;
-  constexpr int kPer = kNBins / kThreads;
+  constexpr int kPer = kHPer;
   const int f_hi = kNBins - kPer * tid - 1;
   if (tid == 0) s_tmp[12] = s_tmp[13] = __float_as_uint(-INFINITY);   // ordered by the scan's barriers
   uint32_t loc = 0;
-  uint32_t hv[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    hv[j] = h[f_hi - j];
-    loc += hv[j];
-  }
+  for (int j = 0; j < kPer; ++j) loc += hv[j];
   uint32_t tot;
   const uint32_t above = wg_exclusive_scan(loc, s_tmp, &tot);
   if (above < need && above + loc >= need) {
@@ -729,14 +764,24 @@ __device__ void wg_band_thresholds(const Params& P, int p, bool publish, uint32_
 __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
   __shared__ uint32_t s_tmp[16];
   const int tid = threadIdx.x;
-  const int p = blockIdx.y, chunk = blockIdx.x;
-  const int nc = P.meta[p].nc;
+  int p, chunk;
+  grid_chunk(P, &p, &chunk);
+  const int q = p % P.n_q, kind = p / P.n_q;
   const int c0 = chunk * kCmpChunk;
-  float keep_thr = -INFINITY, in_thr = -INFINITY;
-  if (chunk == 0 || c0 < nc) wg_band_thresholds(P, p, chunk == 0, s_tmp, &keep_thr, &in_thr);
+  // every load goes out at once: the chunk's scores, the fine histogram, the
+  // visible length and the Meta fields the fine histogram kernel published
   const int my0 = c0 + tid * kCmpPerThread;
   float v[kCmpPerThread];
-  const int m = load16(P, p, nc, my0, v);
+  load16(P, p, my0, v);
+  uint32_t hv[kHPer];
+  load_hist16(P.hist2 + (size_t)p * kNBins, hv);
+  const int nc = cands_of(P, kind, P.q_nvis[q]);
+  const uint32_t m_bin = P.meta[p].bin, m_above = P.meta[p].above;
+  const float m_delta = P.meta[p].delta;
+  float keep_thr = -INFINITY, in_thr = -INFINITY;
+  if (chunk == 0 || c0 < nc)
+    wg_band_thresholds(P, p, hv, m_bin, m_above, m_delta, chunk == 0, s_tmp, &keep_thr, &in_thr);
+  const int m = count16(nc, my0);
   uint32_t keep = 0, cert = 0;
 #pragma unroll
   for (int j = 0; j < kCmpPerThread; ++j) {
@@ -818,12 +863,12 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
   const int nwg = kind ? (int)gridDim.x - P.rs_tok : P.rs_tok;
   const int nvis = P.q_nvis[q];
   const int64_t base = P.seq_base[P.q_seq[q]];
-  const int nch = P.nchunk_cmp;
+  const int nch = nchunks_of(P, kind);
   Entry* band = P.band + (size_t)p * P.stride;
   const uint2* unc = P.unc + (size_t)p * P.stride;
 
   if (tid < kWave) s_w[tid] = tid < P.h_i ? P.w[(size_t)q * P.h_i + tid] : 0.0f;
-  chunk_prefix(P.chunk_unc + (size_t)p * nch, nch, s_uoff, s_tmp);   // ends with a barrier
+  chunk_prefix(P.chunk_unc + (size_t)p * P.nchunk_cmp, nch, s_uoff, s_tmp);   // ends with a barrier
   const int nu = (int)s_uoff[nch];
   if (wg * kWaves >= nu) return;
   uint32_t qrow[DW];   // the lane's query row, packed bf16 pairs
@@ -993,12 +1038,12 @@ __global__ __launch_bounds__(kFinalThreads) void k_final(Params P) {
   __shared__ uint32_t s_rank[kRankMax];
   const int tid = threadIdx.x;
   const int p = blockIdx.x, q = p % P.n_q, kind = p / P.n_q;
-  const int nch = P.nchunk_cmp;
+  const int nch = nchunks_of(P, kind);
   const Entry* band = P.band + (size_t)p * P.stride;
   const int K = (kind == 1) ? P.keep_blocks : P.k;
   int32_t* out = (kind == 1) ? P.pool_out + (size_t)q * P.keep_blocks : P.idx_out + (size_t)q * P.k;
 
-  chunk_prefix<NT>(P.chunk_cnt + (size_t)p * nch, nch, s_off, s_tmp);
+  chunk_prefix<NT>(P.chunk_cnt + (size_t)p * P.nchunk_cmp, nch, s_off, s_tmp);
   const int n2 = (int)s_off[nch];
   // per-thread contiguous segment of the position-ordered band
   const int per = (n2 + NT - 1) / NT;
@@ -1836,9 +1881,11 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   else launch_scan<64>(P, mt, pool, P.reindex, true, gscan, s);
   if (!launch_ok()) return CSA2_E_HIP;
   if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return CSA2_E_HIP;
-  hipLaunchKernelGGL(k_finehist, dim3(P.nchunk_cmp, P.nprob), dim3(kThreads), 0, s, P);
+  // per-chunk kernels: the token (or Reindex) problem's chunks, then the block problem's
+  const dim3 gchunk(P.nchunk_cmp + (pool ? (P.nchunk_cmp + 7) / 8 : 0), P.n_q);
+  hipLaunchKernelGGL(k_finehist, gchunk, dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
-  hipLaunchKernelGGL(k_compact, dim3(P.nchunk_cmp, P.nprob), dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(k_compact, gchunk, dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
   // One resident round (two work-groups per CU at this kernel's register
   // use): about kRescoreWGs work-groups in all, a query's share split 1:7
