@@ -69,7 +69,7 @@ def build_state(wl, dev):
     ik = gen.index_keys(wl, dev)
     s = gen.seq_tensors(wl, dev)
     st = DecodeState(cache=cache, ik=ik, seq_base=s["seq_base"], q_seq=s["q_seq"], q_nvis=s["q_nvis"],
-                     max_nvis=max(wl["lengths"]), k=wl["k"], keep_blocks=wl["keep_blocks"], w_max=wl["w"],
+                     max_nvis=max(wl["q_nvis"]), k=wl["k"], keep_blocks=wl["keep_blocks"], w_max=wl["w"],
                      softmax_scale=512 ** -0.5)
     layers = [LayerInputs(**gen.layer_tensors(wl, i, dev)) for i in range(len(wl["layers"]))]
     app_x, app_rows = gen.append_rows(wl, dev)
@@ -81,7 +81,7 @@ def scan_bytes(wl):
     """Algorithmic bytes of one Full-layer indexer-scan launch: every visible
     key (d_i bf16) once, plus each query's indexer query and head weights."""
     n_q, h_i, d_i = wl["n_q"], wl["h_i"], wl["d_i"]
-    return sum(wl["lengths"]) * d_i * 2 + n_q * (h_i * d_i * 2 + h_i * 4)
+    return sum(wl["q_nvis"]) * d_i * 2 + n_q * (h_i * d_i * 2 + h_i * 4)
 
 
 def step_bytes(wl):

@@ -107,6 +107,21 @@ def workload(name: str, seed: int | None = None, length_div: int = 1) -> dict:
                              "then Reindex; 64 heads, FP4 512-ch KV, indexer 64x128, Top-512, SWA-128",
                   lengths=[1 << 20] * 4, h=64, q_dtype="bf16", kv_dtype="bf16", h_i=64, d_i=128,
                   layers=["full", "reindex"], keep_blocks=2048, append=True)
+    elif name == "c4":
+        # Encoder-side chunk at compression ratio 2: 1,048,576 tokens held as
+        # 524,288 compressed entries (entry j covers tokens 2j, 2j + 1); 4096
+        # causal queries at tokens t0 .. t0 + 4095, each seeing the entries j
+        # with 2j + 1 <= t, and its own window of tokens t - 127 .. t (rows of
+        # one window tensor shared by the chunk).  1 Full + 5 Reuse layers;
+        # every tensor N(0,1) with 1% of the values scaled by 20.
+        n_ent, n_chunk = 1 << 19, 4096
+        t0 = (1 << 20) - n_chunk
+        wl = dict(base, desc="encoder-side chunk at compression ratio 2: 524288 FP4 entries of a 1M-token "
+                             "context, 4096 causal queries, Full + 5 Reuse",
+                  lengths=[n_ent], h=64, q_dtype="bf16", kv_dtype="bf16", h_i=64, d_i=128,
+                  layers=["full"] + ["reuse"] * 5, keep_blocks=0, append=False, outlier_p=0.01,
+                  q_seq=[0] * n_chunk, q_nvis=[(t + 1) // 2 for t in range(t0, t0 + n_chunk)],
+                  swa_shared=True)
     elif name == "c5":
         s = 0xC5A20005 if seed is None else seed
         wl = dict(base, desc="20-layer decoder schedule, 64 sequences, lengths log-uniform in "
@@ -118,9 +133,15 @@ def workload(name: str, seed: int | None = None, length_div: int = 1) -> dict:
     wl["name"] = name
     wl["seed"] = (0xC5A20000 + int(name[1:])) if seed is None else seed
     if length_div > 1:
+        if "q_seq" in wl:
+            raise ValueError("length_div applies to decode workloads only")
         wl["lengths"] = [max(1, L // length_div) for L in wl["lengths"]]
         wl["name"] = f"{name}/{length_div}"
-    wl["n_q"] = len(wl["lengths"])
+    # decode workloads: one query per sequence, seeing the whole sequence
+    wl.setdefault("q_seq", list(range(len(wl["lengths"]))))
+    wl.setdefault("q_nvis", list(wl["lengths"]))
+    wl.setdefault("swa_shared", False)
+    wl["n_q"] = len(wl["q_seq"])
     wl["rows"] = int(sum(wl["lengths"]))
     wl["seq_base"] = [0] + [int(v) for v in np.cumsum(wl["lengths"])[:-1]]
     return wl
@@ -143,23 +164,30 @@ def index_keys(wl, device="cpu", row0=0, nrows=None):
 
 
 def seq_tensors(wl, device="cpu"):
-    n_q = wl["n_q"]
     return dict(seq_base=torch.tensor(wl["seq_base"], dtype=torch.int64, device=device),
-                q_seq=torch.arange(n_q, dtype=torch.int32, device=device),
-                q_nvis=torch.tensor(wl["lengths"], dtype=torch.int32, device=device))
+                q_seq=torch.tensor(wl["q_seq"], dtype=torch.int32, device=device),
+                q_nvis=torch.tensor(wl["q_nvis"], dtype=torch.int32, device=device))
 
 
 def layer_tensors(wl, layer, device="cpu"):
     """Layer `layer`'s own main query, window rows and (Full/Reindex) indexer query."""
     n_q, h, W = wl["n_q"], wl["h"], wl["w"]
     s, tag = wl["seed"], f"layer{layer}"
+    if wl["swa_shared"]:
+        # consecutive queries of one chunk: query i's window is rows i .. i + W - 1
+        swa = normal((n_q + W - 1, 512), s, tag + "-swa", device=device, dtype=torch.bfloat16,
+                     outlier_p=wl["outlier_p"])
+        row0 = torch.arange(n_q, dtype=torch.int64, device=device)
+        wlen = torch.full((n_q,), W, dtype=torch.int32, device=device)
+    else:
+        swa = normal((n_q * W, 512), s, tag + "-swa", device=device, dtype=torch.bfloat16,
+                     outlier_p=wl["outlier_p"])
+        row0 = torch.arange(n_q, dtype=torch.int64, device=device) * W
+        wlen = torch.tensor([min(W, L) for L in wl["lengths"]], dtype=torch.int32, device=device)
     d = dict(mode=wl["layers"][layer],
              q=normal((n_q, h, 512), s, tag + "-q", device=device, dtype=_tdtype(wl["q_dtype"]),
                       outlier_p=wl["outlier_p"]),
-             swa=normal((n_q * W, 512), s, tag + "-swa", device=device, dtype=torch.bfloat16,
-                        outlier_p=wl["outlier_p"]),
-             swa_row0=torch.arange(n_q, dtype=torch.int64, device=device) * W,
-             swa_len=torch.tensor([min(W, L) for L in wl["lengths"]], dtype=torch.int32, device=device))
+             swa=swa, swa_row0=row0, swa_len=wlen)
     if d["mode"] in ("full", "reindex"):
         d["iq"] = normal((n_q, wl["h_i"], wl["d_i"]), s, tag + "-iq", device=device, dtype=torch.bfloat16,
                          outlier_p=wl["outlier_p"])
@@ -168,7 +196,10 @@ def layer_tensors(wl, layer, device="cpu"):
 
 
 def append_rows(wl, device="cpu"):
-    """The new token of every sequence (its last position): raw row and cache row."""
+    """The new token of every sequence (its last position): raw row and cache
+    row; (None, None) for a workload without appends."""
+    if not wl.get("append", True):
+        return None, None
     rows = [wl["seq_base"][i] + wl["lengths"][i] - 1 for i in range(wl["n_q"])]
     x = torch.cat([kv_rows(wl, r, 1, device) for r in rows])
     return x, torch.tensor(rows, dtype=torch.int64, device=device)

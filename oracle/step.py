@@ -29,7 +29,8 @@ def decode_step(layers, ik, seq_base, q_seq, q_nvis, k, keep_blocks, block, raw_
     the time spent inside the oracle's decode-step calls (input plumbing excluded)."""
     secs = 0.0
     t0 = time.perf_counter()
-    quantize_rows(append_x)                # a1: the new token of every sequence
+    if append_x is not None:
+        quantize_rows(append_x)            # a1: the new token of every sequence
     secs += time.perf_counter() - t0
     idx = pool = None
     results = []

@@ -7,7 +7,9 @@ The 1M-context batch is checked on every sequence (the oracle needs about ten
 seconds of host time for it).  The mixed 64-sequence batch runs its full
 20-layer schedule (Full + 3 Reuse, then 4 x (Reindex + 3 Reuse)) with every
 context shortened 16-fold, which keeps contexts above the 16,384-position pool
-and the oracle within seconds."""
+and the oracle within seconds.  The encoder-side chunk (4096 causal queries
+over 524,288 compressed entries, Full + 5 Reuse) runs whole on the GPU and is
+checked on a sample of its queries, which the oracle computes one by one."""
 import os
 
 import numpy as np
@@ -27,15 +29,19 @@ def _host(t):
     return bits(t) if t.dtype == torch.bfloat16 else t.cpu().numpy()
 
 
-def _check_workload(name, length_div=1):
+def _check_workload(name, length_div=1, sample=None):
+    """sample: query indices the oracle checks (default: every query)."""
     dev = device()
     wl = gen.workload(name, length_div=length_div)
     note(f"workload {wl['name']}: {len(wl['lengths'])} sequences, {wl['rows']} rows, layers {wl['layers']}")
     st, layers, app_x, app_rows = bench.build_state(wl, dev)
     res, pool = decode_step(st, layers, append_x=app_x, append_rows=app_rows, keep_outputs=True)
     torch.cuda.synchronize()
-    got = [(i.cpu().numpy(), o.cpu().numpy().astype(np.float64), l.cpu().numpy()) for i, o, l in res]
-    gpool = pool.cpu().numpy() if pool is not None else None
+    n_q = wl["n_q"]
+    sel = np.arange(n_q) if sample is None else np.asarray(sample)
+    ts = torch.from_numpy(sel).to(dev)
+    got = [(i[ts].cpu().numpy(), o[ts].cpu().numpy().astype(np.float64), l[ts].cpu().numpy()) for i, o, l in res]
+    gpool = pool[ts].cpu().numpy() if pool is not None else None
 
     def raw_rows(rows):
         x = gen.kv_rows_at(wl, rows, dev)
@@ -43,15 +49,15 @@ def _check_workload(name, length_div=1):
 
     hl = []
     for lay in layers:
-        d = dict(mode=lay.mode, q=_host(lay.q), swa=bits(lay.swa), swa_row0=_host(lay.swa_row0),
-                 swa_len=_host(lay.swa_len))
+        d = dict(mode=lay.mode, q=_host(lay.q[ts]), swa=bits(lay.swa), swa_row0=_host(lay.swa_row0[ts]),
+                 swa_len=_host(lay.swa_len[ts]))
         if lay.iq is not None:
-            d["iq"], d["w"] = bits(lay.iq), _host(lay.w)
+            d["iq"], d["w"] = bits(lay.iq[ts]), _host(lay.w[ts])
         hl.append(d)
-    n_q = wl["n_q"]
     ref, rpool, secs = oracle_step(hl, bits(st.ik), np.asarray(wl["seq_base"], np.int64),
-                                   np.arange(n_q, dtype=np.int32), np.asarray(wl["lengths"], np.int32),
-                                   wl["k"], wl["keep_blocks"], wl["block"], raw_rows, _host(app_x),
+                                   np.asarray(wl["q_seq"], np.int32)[sel], np.asarray(wl["q_nvis"], np.int32)[sel],
+                                   wl["k"], wl["keep_blocks"], wl["block"], raw_rows,
+                                   _host(app_x) if app_x is not None else None,
                                    st.softmax_scale, n_threads=min(16, os.cpu_count() or 1))
     print(f"oracle step {secs:.1f} s", flush=True)
     worst = 0.0
@@ -81,6 +87,12 @@ def test_c2_full_plus_reuse_128k_batch8():
 @gpu
 def test_c3_full_pool_reindex_1m_batch4():
     _check_workload("c3")
+
+
+@gpu
+def test_c4_encoder_chunk_4096_causal_queries_sampled():
+    # the first and last query, and queries spread over the chunk
+    _check_workload("c4", sample=[0, 1, 1023, 2048, 3071, 4094, 4095, 517])
 
 
 @gpu
