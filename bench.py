@@ -70,7 +70,8 @@ def build_state(wl, dev):
     s = gen.seq_tensors(wl, dev)
     st = DecodeState(cache=cache, ik=ik, seq_base=s["seq_base"], q_seq=s["q_seq"], q_nvis=s["q_nvis"],
                      max_nvis=max(wl["q_nvis"]), k=wl["k"], keep_blocks=wl["keep_blocks"], w_max=wl["w"],
-                     softmax_scale=512 ** -0.5)
+                     softmax_scale=512 ** -0.5,
+                     chunk_base=int(wl["seq_base"][wl["q_seq"][0]]) if wl.get("chunk") else None)
     layers = [LayerInputs(**gen.layer_tensors(wl, i, dev)) for i in range(len(wl["layers"]))]
     app_x, app_rows = gen.append_rows(wl, dev)
     torch.cuda.synchronize()

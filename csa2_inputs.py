@@ -121,7 +121,7 @@ def workload(name: str, seed: int | None = None, length_div: int = 1) -> dict:
                   lengths=[n_ent], h=64, q_dtype="bf16", kv_dtype="bf16", h_i=64, d_i=128,
                   layers=["full"] + ["reuse"] * 5, keep_blocks=0, append=False, outlier_p=0.01,
                   q_seq=[0] * n_chunk, q_nvis=[(t + 1) // 2 for t in range(t0, t0 + n_chunk)],
-                  swa_shared=True)
+                  swa_shared=True, chunk=True)
     elif name == "c5":
         s = 0xC5A20005 if seed is None else seed
         wl = dict(base, desc="20-layer decoder schedule, 64 sequences, lengths log-uniform in "

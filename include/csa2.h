@@ -129,6 +129,27 @@ size_t csa2_index_topk_ws_bytes(int n_q, int32_t max_nvis, int h_i, int d_i, int
                                 int block, int keep_blocks);
 
 /* ------------------------------------------------------------------------
+ * csa2_index_topk_chunk -- Full layer for a chunk of queries of ONE sequence
+ * (the encoder side: chunked prefill, where many causal queries index the same
+ * keys; the encoder's CSA2 layers form groups of 1 Full + 5 Reuse at
+ * compression ratio 2, source as above, section "Каузальный энкодер-декодер").
+ * The same result as csa2_index_topk with every q_seq[i] naming one sequence
+ * whose keys start at row ik_base, and no pool; the scan scores several
+ * queries from each key group it loads, so the keys are read once per few
+ * queries instead of once per query.
+ *   iq, w, n_q, h_i, d_i, q_nvis, max_nvis, k, idx_out: as csa2_index_topk
+ *   ik       indexer keys; query i sees rows ik_base .. ik_base + q_nvis[i] - 1
+ *            (causal visibility: q_nvis per query, e.g. floor((t+1)/2) for a
+ *            query at token t at compression ratio 2)
+ *   ws       as csa2_index_topk with keep_blocks = 0
+ *            (csa2_index_topk_ws_bytes(n_q, max_nvis, h_i, d_i, k, 8, 0))
+ * Supported and alignment: as csa2_index_topk; ik_base >= 0. */
+csa2_status csa2_index_topk_chunk(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
+                                  const int32_t* q_nvis, int32_t max_nvis, const uint16_t* ik,
+                                  int64_t ik_base, int k, int32_t* idx_out,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * csa2_reindex_topk -- Reindex layer: re-score the pool of the last Full
  * layer (its indexer keys `ik`) with this layer's own iq/w, exact Top-K.
  *   pool_blocks [n_q][keep_blocks] block ids as written by csa2_index_topk:

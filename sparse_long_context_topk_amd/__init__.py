@@ -53,6 +53,9 @@ def lib():
                                       i32, i32, vp, vp, sz, vp]
         L.csa2_index_topk_ws_bytes.restype = sz
         L.csa2_index_topk_ws_bytes.argtypes = [i32, ctypes.c_int32, i32, i32, i32, i32, i32]
+        L.csa2_index_topk_chunk.restype = i32
+        L.csa2_index_topk_chunk.argtypes = [vp, vp, i32, i32, i32, vp, ctypes.c_int32, vp, i64, i32, vp, vp,
+                                            ctypes.c_size_t, vp]
         L.csa2_reindex_topk.restype = i32
         L.csa2_reindex_topk.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp,
                                         vp, sz, vp]
@@ -176,6 +179,27 @@ def index_topk(iq, w, q_seq, q_nvis, max_nvis, ik, seq_base, k=512, block=8, kee
                                _stream(dev))
     _check(st, "csa2_index_topk")
     return (idx_out, pool_out) if keep_blocks else idx_out
+
+
+def index_topk_chunk(iq, w, q_nvis, max_nvis, ik, ik_base=0, k=512, idx_out=None, ws=None):
+    """Full layer for a chunk of queries of one sequence (encoder side): query
+    i sees key rows ik_base .. ik_base + q_nvis[i] - 1.  iq [n_q,h_i,d_i] bf16,
+    w [n_q,h_i] f32, q_nvis [n_q] int32, ik [rows,d_i] bf16.  Returns idx
+    [n_q,k] int32 (same result as index_topk with one shared sequence)."""
+    _need(iq, torch.bfloat16, "iq")
+    n_q, h_i, d_i = iq.shape
+    _need(w, torch.float32, "w")
+    _need(q_nvis, torch.int32, "q_nvis")
+    _need(ik, torch.bfloat16, "ik")
+    dev = iq.device
+    if idx_out is None:
+        idx_out = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    nbytes = index_topk_ws_bytes(n_q, max_nvis, h_i, d_i, k, 8, 0)
+    buf = _ws(dev, nbytes, ws)
+    st = lib().csa2_index_topk_chunk(_ptr(iq), _ptr(w), n_q, h_i, d_i, _ptr(q_nvis), int(max_nvis), _ptr(ik),
+                                     int(ik_base), k, _ptr(idx_out), _ptr(buf), buf.numel(), _stream(dev))
+    _check(st, "csa2_index_topk_chunk")
+    return idx_out
 
 
 def reindex_topk_ws_bytes(n_q, h_i, d_i, k, block=8, keep_blocks=2048) -> int:

@@ -122,6 +122,7 @@ struct Params {
   int64_t stride;          // slots per problem in scores / band arrays
   int nchunk_cmp;
   int rs_tok;              // rescoring work-groups per query given to the token problem (the rest: blocks)
+  int64_t base0;           // chunk calls (q_seq == nullptr): every query's sequence starts at key row base0
   float bound_tok, bound_blk;
   float* scores;
   uint32_t* hist;       // [nprob][kNBins] coarse histogram (top 12 bits of the key)
@@ -264,6 +265,11 @@ __device__ uint32_t wg_kth_largest(int n, int K, KeyOf key_of, uint32_t* s_hist 
   }
   *ties = remaining;
   return prefix;
+}
+
+// First key row of query q's sequence.
+__device__ __forceinline__ int64_t seq_base_of(const Params& P, int q) {
+  return P.q_seq ? P.seq_base[P.q_seq[q]] : P.base0;
 }
 
 // Compaction chunks of a problem: the block problem's rows hold 1/8 of the
@@ -427,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   const int p = q;             // token problem
   const int pb = P.n_q + q;    // block problem (POOL)
   const int nvis = P.q_nvis[q];
-  const int64_t base = P.seq_base[P.q_seq[q]];
+  const int64_t base = seq_base_of(P, q);
   const int nc = INDIRECT ? 8 * P.keep_in : nvis;
   const int nblk = (nvis + 7) >> 3;
   const int c0 = blockIdx.x * P.scan_chunk;
@@ -641,6 +647,181 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
       for (int i = 0; i < kWaves; ++i) m0 = max(m0, s_tmp[i]);
       if (m0) atomicMax(&P.meta[p].maxk2, m0);
     }
+  }
+}
+
+// ---------------------------------------------------------------- 2b. chunk scan
+// The queries of one sequence's chunk (encoder-side chunked prefill: many
+// causal queries over the same keys): every work-group scores QB consecutive
+// queries against one range of keys, so each key group it loads feeds QB
+// queries' MFMAs (the keys' bytes are read once per QB queries instead of
+// once per query).  The MFMA computes S = Q . K^T (heads x keys, the
+// transpose of k_scan's tile): lane (key n, group g) then holds 4 heads of each
+// 16-head tile for one key, so the weighted ReLU head sum runs in registers and
+// two lane permutes finish it across the four lane groups.  The products and
+// their k-order are those of k_scan; only the order of the head sum differs,
+// which the rounding bound covers (it holds for any summation order).
+// Positions at or past a query's own visible length are not scores.  One
+// coarse histogram per query.
+constexpr int kChunkKeys = 4096;   // keys per chunk-scan work-group
+
+template <int D, int MT, int QB>
+__global__ __launch_bounds__(kThreads) void k_scan_chunk(Params P) {
+  constexpr int KS = D / 32;
+  constexpr int NBUF = 2;           // one key group in flight, one in use (registers go to the queries)
+  __shared__ uint32_t s_hist[QB][kNBins];
+  __shared__ float s_sc[QB][kChunkKeys];
+  __shared__ uint32_t s_tmp[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int q0 = blockIdx.y * QB;
+  const int nq = min(QB, P.n_q - q0);
+  const int c0 = blockIdx.x * kChunkKeys;
+  int nvis[QB];
+  int nmax = 0;
+#pragma unroll
+  for (int qq = 0; qq < QB; ++qq) {
+    nvis[qq] = qq < nq ? P.q_nvis[q0 + qq] : 0;
+    nmax = max(nmax, nvis[qq]);
+  }
+  const int64_t base = P.base0;   // one sequence
+  for (int i = tid; i < QB * kNBins; i += kThreads) (&s_hist[0][0])[i] = 0;
+
+  // Q as the MFMA A operand: lane (n, g) holds head 16*mt + n, dims 32*ks + 8*g .. +7;
+  // wq: the weights of the heads this lane's accumulators hold (16*mt + 4*g + i)
+  bf16x8 qb[QB][MT][KS];
+  float wq[QB][MT][4];
+#pragma unroll
+  for (int qq = 0; qq < QB; ++qq) {
+    const int q = min(q0 + qq, P.n_q - 1);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int head = 16 * mt + n;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (head < P.h_i)
+          v = *reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + head) * D + 32 * ks + 8 * g);
+        qb[qq][mt][ks] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hw = 16 * mt + 4 * g + i;
+        wq[qq][mt][i] = hw < P.h_i ? P.w[(size_t)q * P.h_i + hw] : 0.0f;
+      }
+    }
+  }
+  lds_barrier();   // the histogram clear; the query loads stay in flight
+
+  float mk2 = 0.0f;
+  const int nslots = min(kChunkKeys, max(nmax - c0, 0));
+  const int ngroups = (nslots + 15) >> 4;
+  const int my_groups = ngroups > wave ? (ngroups - wave + kWaves - 1) / kWaves : 0;
+  auto key_row = [&](int it, bool& valid) -> int64_t {
+    const int cand = c0 + 16 * (wave + kWaves * it) + n;
+    valid = cand < nmax;
+    return base + (valid ? cand : 0);
+  };
+  auto load = [&](int it, uint4* kb) {
+    bool v;
+    const uint4* src = reinterpret_cast<const uint4*>(P.ik + (size_t)key_row(min(it, my_groups - 1), v) * D + 8 * g);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kb[ks] = src[4 * ks];
+  };
+  auto process = [&](int it, const uint4* kin) {
+    const int gi = wave + kWaves * it;
+    bool valid;
+    key_row(it, valid);
+    const uint32_t vm = valid ? 0xFFFFFFFFu : 0u;
+    uint4 kb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kb[ks] = make_uint4(kin[ks].x & vm, kin[ks].y & vm, kin[ks].z & vm, kin[ks].w & vm);
+    float k2 = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t wd[4] = {kb[ks].x, kb[ks].y, kb[ks].z, kb[ks].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2 x = __builtin_bit_cast(bf16x2, wd[j]);
+        k2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, k2, false);
+      }
+    }
+    mk2 = fmaxf(mk2, k2);
+    const int cand = c0 + 16 * gi + n;   // this lane's key
+#pragma unroll
+    for (int qq = 0; qq < QB; ++qq) {
+      f32x4 acc[MT];   // acc[mt][i]: head 16*mt + 4*g + i, key n
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, kb[ks]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[qq][mt][ks], b, acc[mt], 0, 0, 0);
+      }
+      float v = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaf(wq[qq][mt][i], fmaxf(acc[mt][i], 0.0f), v);
+      // + the other three lane groups' heads: rows 0<->1, 2<->3, then halves
+      const auto s1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      v = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
+      const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      const float si = __uint_as_float(s2[0]) + __uint_as_float(s2[1]);
+      const bool cvalid = cand < nvis[qq];
+      if (g == 0) {
+        s_sc[qq][cand - c0] = cvalid ? si : -INFINITY;
+        if (cvalid) atomicAdd(&s_hist[qq][sortable(si) >> kBinShift], 1u);
+      }
+    }
+  };
+
+  uint4 buf[NBUF][KS];
+  if (my_groups > 0) {
+    load(0, buf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int it = 0;
+  for (; it + NBUF <= my_groups; it += NBUF) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      load(it + b + NBUF - 1, buf[(b + NBUF - 1) % NBUF]);
+      __builtin_amdgcn_sched_barrier(0);
+      process(it + b, buf[b]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NBUF - 1; ++b)
+    if (it + b < my_groups) process(it + b, buf[b]);
+
+  // ---- publish: each query's scores and histogram, the key-norm maximum
+  lds_barrier();
+#pragma unroll
+  for (int qq = 0; qq < QB; ++qq) {
+    if (qq < nq) {
+      const int q = q0 + qq;
+      const int ns = min(kChunkKeys, max(nvis[qq] - c0, 0));
+      float* sc = P.scores + (size_t)q * P.stride + c0;
+      for (int i = tid; i < ns; i += kThreads) sc[i] = s_sc[qq][i];
+      uint32_t* gh = P.hist + (size_t)q * kNBins;
+      for (int i = tid; i < kNBins; i += kThreads) {
+        const uint32_t c = s_hist[qq][i];
+        if (c) atomicAdd(&gh[i], c);
+      }
+    }
+  }
+  mk2 = wave_max(mk2);
+  if (lane == 0) s_tmp[wave] = __float_as_uint(mk2);
+  lds_barrier();
+  if (tid < nq) {
+    uint32_t m0 = 0;
+    for (int i = 0; i < kWaves; ++i) m0 = max(m0, s_tmp[i]);
+    if (m0) atomicMax(&P.meta[q0 + tid].maxk2, m0);   // an upper bound for every query of the block
   }
 }
 
@@ -862,7 +1043,7 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
   const int wg = kind ? (int)blockIdx.x - P.rs_tok : (int)blockIdx.x;
   const int nwg = kind ? (int)gridDim.x - P.rs_tok : P.rs_tok;
   const int nvis = P.q_nvis[q];
-  const int64_t base = P.seq_base[P.q_seq[q]];
+  const int64_t base = seq_base_of(P, q);
   const int nch = nchunks_of(P, kind);
   Entry* band = P.band + (size_t)p * P.stride;
   const uint2* unc = P.unc + (size_t)p * P.stride;
@@ -1338,7 +1519,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
   const int K = P.k;
   const int nc = 8 * P.keep_in;
   s_selw[tid] = 0;
-  const int64_t base = P.seq_base[P.q_seq[q]];
+  const int64_t base = seq_base_of(P, q);
   const float* sc = P.scores + (size_t)q * P.stride;
   int32_t* out = P.idx_out + (size_t)q * K;
   const int s0 = tid * kSmallPer;   // this thread's first slot
@@ -1836,7 +2017,21 @@ void launch_scan(const Params& P, int mt, bool pool, bool indirect, bool hist, d
 #undef CSA2_SCAN
 }
 
-csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes, hipStream_t s, size_t need) {
+#ifndef CSA2_CHUNK_QB
+#define CSA2_CHUNK_QB 2
+#endif
+constexpr int kChunkQB = CSA2_CHUNK_QB;   // queries per chunk-scan work-group
+
+template <int D>
+void launch_scan_chunk(const Params& P, int mt, dim3 grid, hipStream_t s) {
+#define CSA2_SCANC(MTV) \
+  if (mt == MTV) { hipLaunchKernelGGL((k_scan_chunk<D, MTV, kChunkQB>), grid, dim3(kThreads), 0, s, P); return; }
+  CSA2_SCANC(1) CSA2_SCANC(2) CSA2_SCANC(3) CSA2_SCANC(4)
+#undef CSA2_SCANC
+}
+
+csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes, hipStream_t s, size_t need,
+                         bool chunk = false) {
   if (ws_bytes < need) return CSA2_E_WORKSPACE;
   const Layout L = make_layout(P.nprob, P.stride, P.nchunk_cmp);
   char* w = static_cast<char*>(ws);
@@ -1877,8 +2072,16 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   hipEvent_t ev0 = g_scan_ev_start, ev1 = g_scan_ev_stop;
   g_scan_ev_start = g_scan_ev_stop = nullptr;
   if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return CSA2_E_HIP;
-  if (P.d_i == 128) launch_scan<128>(P, mt, pool, P.reindex, true, gscan, s);
-  else launch_scan<64>(P, mt, pool, P.reindex, true, gscan, s);
+  if (chunk) {
+    const dim3 gch((unsigned)std::max<int64_t>(1, (max_slots + kChunkKeys - 1) / kChunkKeys),
+                   (unsigned)((P.n_q + kChunkQB - 1) / kChunkQB));
+    if (P.d_i == 128) launch_scan_chunk<128>(P, mt, gch, s);
+    else launch_scan_chunk<64>(P, mt, gch, s);
+  } else if (P.d_i == 128) {
+    launch_scan<128>(P, mt, pool, P.reindex, true, gscan, s);
+  } else {
+    launch_scan<64>(P, mt, pool, P.reindex, true, gscan, s);
+  }
   if (!launch_ok()) return CSA2_E_HIP;
   if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return CSA2_E_HIP;
   // per-chunk kernels: the token (or Reindex) problem's chunks, then the block problem's
@@ -1957,6 +2160,30 @@ extern "C" csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n
   P.nchunk_cmp = (int)(P.stride / kCmpChunk);
   const size_t need = csa2_index_topk_ws_bytes(n_q, max_nvis, h_i, d_i, k, block, keep_blocks);
   return run_pipeline(P, max_nvis, ws, ws_bytes, static_cast<hipStream_t>(stream), need);
+}
+
+extern "C" csa2_status csa2_index_topk_chunk(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
+                                             const int32_t* q_nvis, int32_t max_nvis, const uint16_t* ik,
+                                             int64_t ik_base, int k, int32_t* idx_out, void* ws, size_t ws_bytes,
+                                             void* stream) {
+  if (n_q < 0 || max_nvis < 0 || k < 1 || k > 2048 || ik_base < 0) return CSA2_E_INVAL;
+  if ((int64_t)max_nvis > (int64_t)kMaxChunksLds * kCmpChunk) return CSA2_E_UNSUPPORTED;
+  if (!shape_ok(h_i, d_i)) return CSA2_E_UNSUPPORTED;
+  if (n_q == 0) return CSA2_OK;
+  if (!iq || !w || !q_nvis || !ik || !idx_out || !ws) return CSA2_E_INVAL;
+  if (!aligned(iq, 16) || !aligned(ik, 16) || !aligned(w, 4) || !aligned(ws, 256)) return CSA2_E_INVAL;
+  Params P{};
+  P.iq = iq; P.w = w; P.n_q = n_q; P.h_i = h_i; P.d_i = d_i;
+  P.q_seq = nullptr; P.q_nvis = q_nvis; P.ik = ik; P.seq_base = nullptr; P.base0 = ik_base;
+  P.pool_in = nullptr; P.keep_in = 0; P.k = k; P.keep_blocks = 0;
+  P.idx_out = idx_out; P.pool_out = nullptr;
+  P.nprob = n_q;
+  P.reindex = 0;
+  P.scan_chunk = kMaxScanChunk;
+  P.stride = round_up(std::max<int64_t>(max_nvis, 1), kCmpChunk);
+  P.nchunk_cmp = (int)(P.stride / kCmpChunk);
+  const size_t need = csa2_index_topk_ws_bytes(n_q, max_nvis, h_i, d_i, k, 8, 0);
+  return run_pipeline(P, max_nvis, ws, ws_bytes, static_cast<hipStream_t>(stream), need, true);
 }
 
 extern "C" csa2_status csa2_reindex_topk(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,

@@ -17,7 +17,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import index_topk, quant_append, reindex_topk, sparse_attn, Workspace
+from . import index_topk, index_topk_chunk, quant_append, reindex_topk, sparse_attn, Workspace
 
 FULL, REINDEX, REUSE = "full", "reindex", "reuse"
 
@@ -59,6 +59,7 @@ class DecodeState:
     keep_blocks: int = 2048               # pool size built by the Full layer (0: none)
     w_max: int = 128
     softmax_scale: float = 512 ** -0.5
+    chunk_base: int | None = None         # all queries in one sequence whose keys start at this row (no pool)
     ws_index: Workspace = field(default_factory=Workspace)
     ws_attn: Workspace = field(default_factory=Workspace)
 
@@ -77,9 +78,15 @@ def decode_step(st: DecodeState, layers: list[LayerInputs], append_x=None, appen
         if lay.mode == FULL:
             if scan_events is not None:
                 record_scan_events(*scan_events)
-            r = index_topk(lay.iq, lay.w, st.q_seq, st.q_nvis, st.max_nvis, st.ik, st.seq_base, k=st.k,
-                           keep_blocks=st.keep_blocks, ws=st.ws_index)
-            idx, pool = (r if st.keep_blocks else (r, None))
+            if st.chunk_base is not None:
+                if st.keep_blocks:
+                    raise ValueError("a chunk of one sequence's queries builds no pool")
+                idx, pool = index_topk_chunk(lay.iq, lay.w, st.q_nvis, st.max_nvis, st.ik, st.chunk_base, k=st.k,
+                                             ws=st.ws_index), None
+            else:
+                r = index_topk(lay.iq, lay.w, st.q_seq, st.q_nvis, st.max_nvis, st.ik, st.seq_base, k=st.k,
+                               keep_blocks=st.keep_blocks, ws=st.ws_index)
+                idx, pool = (r if st.keep_blocks else (r, None))
         elif lay.mode == REINDEX:
             if pool is None:
                 raise ValueError("a Reindex layer needs a preceding Full layer that built a pool")

@@ -62,6 +62,23 @@ def test_index_topk_argument_checks():
     assert 0 < need < need_pool
 
 
+def test_index_topk_chunk_argument_checks():
+    L = csa2.lib()
+    args = dict(iq=FAKE, w=FAKE, n_q=2, h_i=64, d_i=128, q_nvis=FAKE, max_nvis=1000, ik=FAKE, base=0, k=512,
+                idx=FAKE, ws=FAKE, ws_bytes=1, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.csa2_index_topk_chunk(a["iq"], a["w"], a["n_q"], a["h_i"], a["d_i"], a["q_nvis"], a["max_nvis"],
+                                       a["ik"], a["base"], a["k"], a["idx"], a["ws"], a["ws_bytes"], a["stream"])
+    assert call(k=0) == 1 and call(k=4096) == 1 and call(n_q=-1) == 1 and call(base=-5) == 1
+    assert call(d_i=96) == 2 and call(h_i=65) == 2
+    assert call(ik=None) == 1 and call(q_nvis=None) == 1
+    assert call(ik=ctypes.c_void_p((1 << 20) + 2)) == 1           # unaligned
+    assert call() == 3                                             # workspace too small
+    assert call(n_q=0) == 0                                        # nothing to do
+
+
 def test_attn_and_quant_argument_checks():
     L = csa2.lib()
     sp = lambda **kw: L.csa2_sparse_attn(FAKE, kw.get("qdt", 1), 2, kw.get("h", 64), kw.get("d", 512),

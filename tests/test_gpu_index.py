@@ -151,6 +151,29 @@ def test_reindex_ties_and_narrow_ranges(case):
 
 
 @gpu
+@pytest.mark.parametrize("n_q,h_i,d_i", [(7, 64, 128), (6, 20, 128), (5, 33, 64), (1, 4, 64)])
+def test_chunk_of_one_sequence(n_q, h_i, d_i):
+    """Causal queries of one sequence (the encoder-side chunk path): each sees
+    its own prefix of the keys; odd query counts leave the last work-group of
+    the multi-query scan half empty."""
+    note(f"chunk n_q={n_q} h_i={h_i} d_i={d_i}")
+    L, base = 30000, 777
+    inp = index_inputs([base + L], h_i, d_i, seed=31 + n_q)
+    nvis = np.array([max(0, L - 4099 * i) for i in range(n_q)][::-1], np.int32)   # ragged, ascending
+    nvis[0] = min(nvis[0], 300)                                                    # one short query
+    iq = inp["iq"][:1].expand(n_q, h_i, d_i).contiguous()
+    iq = (iq.float() * torch.linspace(0.5, 1.5, n_q)[:, None, None]).to(torch.bfloat16)
+    w = inp["w"][:1].expand(n_q, h_i).contiguous()
+    dev = device()
+    got = csa2.index_topk_chunk(iq.to(dev), w.to(dev), torch.from_numpy(nvis).to(dev), int(nvis.max()),
+                                inp["ik"].to(dev), ik_base=base, k=512)
+    torch.cuda.synchronize()
+    ref = oracle.index_topk(bits(iq), w.numpy(), np.zeros(n_q, np.int32), nvis, bits(inp["ik"]),
+                            np.array([base], np.int64), 512, block=8, keep_blocks=0)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+@gpu
 def test_reindex_with_full_query_equals_full_when_pool_covers_context():
     note("reindex == full")
     inp = index_inputs([16000, 7000], 64, 128, seed=22)
