@@ -169,6 +169,16 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
+// Sum over the four rows of the wave (lanes l, l^16, l^32, l^48 -- the four
+// lane groups holding parts of one MFMA column), in every lane: two VALU lane
+// permutes (rows 0<->1, 2<->3, then the halves).
+__device__ __forceinline__ float sum_rows4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Exclusive prefix sum over the NT-thread work-group (s_tmp: >= NT / 64
 // entries); returns this thread's offset and writes the total.
 template <int NT = kThreads>
@@ -535,7 +545,9 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
       for (int mt = 0; mt < MT; ++mt) v = fmaf(wr[mt], fmaxf(acc[mt][i], 0.0f), v);
       s[i] = sum16(v);
     }
-    // squared key norm of key n (an upper bound is all the error bound needs)
+    // squared norm of key n: this lane's quarter of its dims, then the four
+    // lane groups' quarters (the bound needs the whole norm; the final factor
+    // 1 + 2^-10 on its square root covers the roundings here)
     float k2 = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -546,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
         k2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, k2, false);
       }
     }
-    mk2 = fmaxf(mk2, k2);   // invalid keys were zeroed
+    mk2 = fmaxf(mk2, sum_rows4(k2));   // invalid keys were zeroed
     // every lane stores one score: lanes n, n+4, n+8, n+12 write the same value
     const int i0 = n & 3;
     const int cand = c0 + 16 * gi + 4 * g + i0;
@@ -748,7 +760,7 @@ __global__ __launch_bounds__(kThreads) void k_scan_chunk(Params P) {
         k2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, k2, false);
       }
     }
-    mk2 = fmaxf(mk2, k2);
+    mk2 = fmaxf(mk2, sum_rows4(k2));   // the whole norm of key n (as in k_scan)
     const int cand = c0 + 16 * gi + n;   // this lane's key
 #pragma unroll
     for (int qq = 0; qq < QB; ++qq) {
@@ -767,11 +779,7 @@ __global__ __launch_bounds__(kThreads) void k_scan_chunk(Params P) {
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) v = fmaf(wq[qq][mt][i], fmaxf(acc[mt][i], 0.0f), v);
-      // + the other three lane groups' heads: rows 0<->1, 2<->3, then halves
-      const auto s1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-      v = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
-      const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-      const float si = __uint_as_float(s2[0]) + __uint_as_float(s2[1]);
+      const float si = sum_rows4(v);   // + the other three lane groups' heads
       const bool cvalid = cand < nvis[qq];
       if (g == 0) {
         s_sc[qq][cand - c0] = cvalid ? si : -INFINITY;
