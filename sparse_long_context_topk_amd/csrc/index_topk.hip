@@ -12,8 +12,7 @@
 // and the pool of up to 2048 blocks of 8 positions.
 //
 // How (one pass over the keys at HBM speed, exact result):
-//  1. k_prologue   zeroes the problem's histograms and Meta, and computes
-//                  QW = sum_h |w_h| ||q_h|| for the rounding bound.
+//  1. k_prologue   zeroes the problem's histograms and Meta.
 //  2. k_scan       streams the indexer keys once (8192 keys per work-group,
 //                  NBUF - 1 groups of 16 keys per wave in flight ahead of the
 //                  math, scores staged in LDS and written once at the end).
@@ -25,16 +24,17 @@
 //                  with a DPP butterfly: the pool costs no extra HBM traffic and
 //                  no extra MFMA.  Work-groups add into a 4096-bin histogram of
 //                  the top 12 bits of the scores' sortable keys and track the
-//                  largest squared key norm.
+//                  largest key magnitude t_k = sum_d u_d |k_d| (u_frag).
 //  3. k_finehist   every work-group finds the coarse bin holding the K-th
 //                  score, then histograms bits 19..8 of the keys in that bin:
 //                  the K-th approximate score a_K is located in a fine bin
 //                  [L, U].
 //  4. k_compact    every work-group derives the band from the fine histogram
-//                  and the rounding bound Delta = C * QW * max||k||
-//                  (Cauchy-Schwarz on the dot-product rounding, ReLU is
-//                  1-Lipschitz, plus the head-sum and block-mean roundings; C
-//                  from the fp32 error constants with a 2x margin):
+//                  and the rounding bound Delta = C * max t_k (each per-head
+//                  dot's rounding is at most a constant times
+//                  sum_d |q_hd k_d|, ReLU is 1-Lipschitz, plus the head-sum
+//                  and block-mean roundings; C from the fp32 error constants
+//                  with a 2x margin):
 //                  every exact Top-K member has approximate score >= L - 2 Delta
 //                  (it is >= the K-th exact score >= a_K - Delta); a member with
 //                  approximate score > U + 2 Delta is certainly in (only members
@@ -85,15 +85,16 @@ constexpr uint32_t kCertain = 0x80000000u;
 constexpr uint32_t kAll = 0xFFFFFFFFu;
 
 struct Meta {
-  uint32_t maxk2;   // scan (token problem): largest squared key norm, float bits
+  uint32_t maxt;    // scan (token problem): largest key magnitude t_k = sum_d u_d |k_d|, float bits
   uint32_t bin;     // coarse bin holding the K-th score; kAll: every candidate is kept
   uint32_t above;   // valid candidates in coarse bins above `bin`
   uint32_t total;   // valid candidates
-  float qw, wabs, delta;
+  float wabs;       // sum_h |w_h| (the bound's underflow term)
+  float delta;      // rounding bound of the scores
   float keep_thr;   // band: approximate score >= keep_thr
   float in_thr;     // certainly selected: approximate score > in_thr
   int32_t nc;       // candidate slots
-  uint32_t pad[6];
+  uint32_t pad[7];
 };
 static_assert(sizeof(Meta) == 64, "Meta is one 64-byte line");
 
@@ -132,7 +133,7 @@ struct Params {
   uint32_t* chunk_unc;  // [nprob][nchunk_cmp] uncertain members per chunk
   Entry* band;          // [nprob][stride] band members, chunk c at c*kCmpChunk, in position order
   uint2* unc;           // [nprob][stride] uncertain members: {chunk-local index, candidate}
-  float* kpart;         // Reindex scan: [n_q][scan work-groups] largest squared key norm of each
+  float* kpart;         // Reindex scan: [n_q][scan work-groups] largest key magnitude t_k of each
 };
 
 // ---------------------------------------------------------------- helpers
@@ -167,6 +168,60 @@ __device__ __forceinline__ float sum16(float v) {
   v = sum8(v);
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row mirror
   return v;
+}
+
+// The rounding bound's key magnitude.  For a query with heads q_h and weights
+// w_h, every per-head dot product's rounding error (exact chain or MFMA) is at
+// most a constant times sum_d |q_hd k_d|, so the score's error is at most a
+// constant times t_k = sum_h |w_h| sum_d |q_hd| |k_d| = sum_d u_d |k_d| with
+// u_d = sum_h |w_h| |q_hd|.  (t_k <= QW ||k|| by Cauchy-Schwarz, QW =
+// sum_h |w_h| ||q_h||; on Gaussian data it is about two thirds of it.)
+//
+// u_frag: this lane's 32 dims of u (lane (n, g) of an MFMA key fragment
+// holds dims 32 ks + 8 g .. +7), from the query fragments qb (lane (n, g):
+// head 16 mt + n, the same dims) -- a sum over the 16 lanes of the row and
+// over mt -- rounded up to bf16 and packed in pairs, so that an upper bound
+// stays an upper bound.
+template <int MT, int KS>
+__device__ __forceinline__ void u_frag(const bf16x8 (&qb)[MT][KS], const float (&wr)[MT], uint32_t (&up)[KS][4]) {
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      uint32_t pk = 0;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        float a = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint4 u4 = __builtin_bit_cast(uint4, qb[mt][ks]);
+          const uint32_t wd = jj == 0 ? u4.x : jj == 1 ? u4.y : jj == 2 ? u4.z : u4.w;
+          const float qv = e == 0 ? __uint_as_float(wd << 16) : __uint_as_float(wd & 0xFFFF0000u);
+          a = fmaf(fabsf(wr[mt]), fabsf(qv), a);
+        }
+        a = sum16(a);
+        const uint32_t bits = (__float_as_uint(a) + 0xFFFFu) & 0xFFFF0000u;   // bf16, rounded up (a >= 0)
+        pk |= e == 0 ? (bits >> 16) : bits;
+      }
+      up[ks][jj] = pk;
+    }
+  }
+}
+
+// This lane's part of t_k for the key in fragment kb (its 32 dims); the key's
+// t_k is the sum over the four lane groups (sum_rows4).
+template <int KS>
+__device__ __forceinline__ float t_part(const uint4 (&kb)[KS], const uint32_t (&up)[KS][4]) {
+  float t = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint32_t wd[4] = {kb[ks].x, kb[ks].y, kb[ks].z, kb[ks].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[j] & 0x7FFF7FFFu),
+                                          __builtin_bit_cast(bf16x2, up[ks][j]), t, false);
+  }
+  return t;
 }
 
 // Sum over the four rows of the wave (lanes l, l^16, l^32, l^48 -- the four
@@ -324,40 +379,19 @@ __global__ __launch_bounds__(kThreads) void k_prologue(Params P) {
   }
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
-    float qn = 0.0f, wa = 0.0f;
-    if (lane < P.h_i) {
-      const uint4* qh = reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + lane) * D);
-      uint4 v[D / 8];
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) v[i] = qh[i];
-      float ss = 0.0f;
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float lo = __uint_as_float(wd[j] << 16), hi = __uint_as_float(wd[j] & 0xFFFF0000u);
-          ss = fmaf(lo, lo, ss);
-          ss = fmaf(hi, hi, ss);
-        }
-      }
-      wa = fabsf(P.w[(size_t)q * P.h_i + lane]);
-      qn = wa * sqrtf(ss);
-    }
-    qn = wave_sum(qn);
+    float wa = lane < P.h_i ? fabsf(P.w[(size_t)q * P.h_i + lane]) : 0.0f;
     wa = wave_sum(wa);
     if (lane == 0) {
       Meta m;
-      m.maxk2 = 0;
+      m.maxt = 0;
       m.bin = kAll;
       m.above = m.total = 0;
-      m.qw = qn * (1.0f + 0.0009765625f);
       m.wabs = wa;
       m.delta = 0.0f;
       m.keep_thr = m.in_thr = -INFINITY;
       const int nvis = P.q_nvis[q];
       m.nc = P.reindex ? 8 * P.keep_in : (kind == 0 ? nvis : (nvis + 7) / 8);
-      for (int i = 0; i < 6; ++i) m.pad[i] = 0;
+      for (int i = 0; i < 7; ++i) m.pad[i] = 0;
       P.meta[p] = m;
     }
   }
@@ -368,8 +402,8 @@ __global__ __launch_bounds__(kThreads) void k_prologue(Params P) {
 // work-group that needs it; the publishing one also records it, with the
 // rounding bound Delta and the count above the bin, in the problem's Meta.
 // hv: this thread's 16 bins of the coarse histogram, highest first (bins
-// 4095 - 16 tid down to 4080 - 16 tid), loaded by the caller; kmax2, qw and
-// wabs feed the published rounding bound.
+// 4095 - 16 tid down to 4080 - 16 tid), loaded by the caller; maxt (the
+// largest key magnitude t_k, see u_frag) and wabs feed the published bound.
 constexpr int kHPer = kNBins / kThreads;   // histogram bins per thread
 
 __device__ __forceinline__ void load_hist16(const uint32_t* h, uint32_t hv[kHPer]) {
@@ -378,8 +412,8 @@ __device__ __forceinline__ void load_hist16(const uint32_t* h, uint32_t hv[kHPer
   for (int j = 0; j < kHPer; ++j) hv[j] = h[b_hi - j];
 }
 
-__device__ uint32_t wg_coarse_bin(const Params& P, int p, const uint32_t hv[kHPer], bool publish, float kmax2,
-                                  float qw, float wabs, uint32_t* s_tmp /*>= 12*/) {
+__device__ uint32_t wg_coarse_bin(const Params& P, int p, const uint32_t hv[kHPer], bool publish, float maxt,
+                                  float wabs, uint32_t* s_tmp /*>= 12*/) {
   const int tid = threadIdx.x;
   const int kind = p / P.n_q;
   const int K = kind == 1 ? P.keep_blocks : P.k;
@@ -394,7 +428,7 @@ __device__ uint32_t wg_coarse_bin(const Params& P, int p, const uint32_t hv[kHPe
   if (publish && tid == 0) {
     // the token problem's scan holds the key-norm maximum; blocks use it too
     const float bound = kind == 1 ? P.bound_blk : P.bound_tok;
-    P.meta[p].delta = bound * qw * sqrtf(kmax2) * (1.0f + 0.0009765625f) + wabs * (float)P.d_i * 7.8886e-31f;
+    P.meta[p].delta = bound * maxt * (1.0f + 0.0009765625f) + wabs * (float)P.d_i * 7.8886e-31f;
     P.meta[p].total = tot;
   }
   if (tot > (uint32_t)K && above < (uint32_t)K && above + loc >= (uint32_t)K) {
@@ -479,12 +513,14 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     }
     wr[mt] = head < P.h_i ? P.w[(size_t)q * P.h_i + head] : 0.0f;
   }
+  uint32_t up[KS][4];   // this lane's dims of u (the bound's key magnitude)
+  u_frag<MT, KS>(qb, wr, up);
   // LDS-only barrier: orders the histogram clear and the pool ids before any
   // wave uses them, without waiting for the query loads still in flight (the
   // first key loads below then overlap them)
   lds_barrier();
 
-  float mk2 = 0.0f;
+  float mk2 = 0.0f;   // largest key magnitude t_k of the chunk
   float* sc = P.scores + (size_t)p * P.stride;
   float* scb = P.scores + (size_t)pb * P.stride;
   const int nslots = min(P.scan_chunk, max(nc - c0, 0));
@@ -545,20 +581,10 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
       for (int mt = 0; mt < MT; ++mt) v = fmaf(wr[mt], fmaxf(acc[mt][i], 0.0f), v);
       s[i] = sum16(v);
     }
-    // squared norm of key n: this lane's quarter of its dims, then the four
-    // lane groups' quarters (the bound needs the whole norm; the final factor
-    // 1 + 2^-10 on its square root covers the roundings here)
-    float k2 = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t wd[4] = {kb[ks].x, kb[ks].y, kb[ks].z, kb[ks].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x2 x = __builtin_bit_cast(bf16x2, wd[j]);
-        k2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, k2, false);
-      }
-    }
-    mk2 = fmaxf(mk2, sum_rows4(k2));   // invalid keys were zeroed
+    // key n's magnitude t_k for the bound: this lane's quarter of its dims,
+    // then the four lane groups' quarters (the final factor 1 + 2^-10 covers
+    // the roundings here; invalid keys were zeroed)
+    mk2 = fmaxf(mk2, sum_rows4(t_part<KS>(kb, up)));
     // every lane stores one score: lanes n, n+4, n+8, n+12 write the same value
     const int i0 = n & 3;
     const int cand = c0 + 16 * gi + 4 * g + i0;
@@ -657,7 +683,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     if (tid == 0) {
       uint32_t m0 = 0;
       for (int i = 0; i < kWaves; ++i) m0 = max(m0, s_tmp[i]);
-      if (m0) atomicMax(&P.meta[p].maxk2, m0);
+      if (m0) atomicMax(&P.meta[p].maxt, m0);   // non-negative floats order as their bits
     }
   }
 }
@@ -724,9 +750,30 @@ __global__ __launch_bounds__(kThreads) void k_scan_chunk(Params P) {
       }
     }
   }
+  // the bound's key magnitude with the block's largest u (dim by dim over its
+  // queries, each u from its fragments and the weights of heads 16 mt + n):
+  // an upper bound of every query's own t_k, for one dot per key
+  uint32_t up[KS][4];
+#pragma unroll
+  for (int qq = 0; qq < QB; ++qq) {
+    const int q = min(q0 + qq, P.n_q - 1);
+    float wn[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) wn[mt] = 16 * mt + n < P.h_i ? P.w[(size_t)q * P.h_i + 16 * mt + n] : 0.0f;
+    uint32_t uq[KS][4];
+    u_frag<MT, KS>(qb[qq], wn, uq);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // bf16 pairs of non-negative values: the larger of each half
+        const uint32_t a = qq ? up[ks][j] : 0u, b = uq[ks][j];
+        up[ks][j] = max(a & 0xFFFF0000u, b & 0xFFFF0000u) | max(a & 0xFFFFu, b & 0xFFFFu);
+      }
+  }
   lds_barrier();   // the histogram clear; the query loads stay in flight
 
-  float mk2 = 0.0f;
+  float mk2 = 0.0f;   // the largest key magnitude (block's u) of the chunk
   const int nslots = min(kChunkKeys, max(nmax - c0, 0));
   const int ngroups = (nslots + 15) >> 4;
   const int my_groups = ngroups > wave ? (ngroups - wave + kWaves - 1) / kWaves : 0;
@@ -750,17 +797,7 @@ __global__ __launch_bounds__(kThreads) void k_scan_chunk(Params P) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       kb[ks] = make_uint4(kin[ks].x & vm, kin[ks].y & vm, kin[ks].z & vm, kin[ks].w & vm);
-    float k2 = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t wd[4] = {kb[ks].x, kb[ks].y, kb[ks].z, kb[ks].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x2 x = __builtin_bit_cast(bf16x2, wd[j]);
-        k2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, k2, false);
-      }
-    }
-    mk2 = fmaxf(mk2, sum_rows4(k2));   // the whole norm of key n (as in k_scan)
+    mk2 = fmaxf(mk2, sum_rows4(t_part<KS>(kb, up)));   // as in k_scan
     const int cand = c0 + 16 * gi + n;   // this lane's key
 #pragma unroll
     for (int qq = 0; qq < QB; ++qq) {
@@ -829,7 +866,7 @@ __global__ __launch_bounds__(kThreads) void k_scan_chunk(Params P) {
   if (tid < nq) {
     uint32_t m0 = 0;
     for (int i = 0; i < kWaves; ++i) m0 = max(m0, s_tmp[i]);
-    if (m0) atomicMax(&P.meta[q0 + tid].maxk2, m0);   // an upper bound for every query of the block
+    if (m0) atomicMax(&P.meta[q0 + tid].maxt, m0);   // an upper bound of each query's own largest t_k
   }
 }
 
@@ -870,10 +907,10 @@ __global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
   uint32_t hv[kHPer];
   load_hist16(P.hist + (size_t)p * kNBins, hv);
   const int nc = cands_of(P, kind, P.q_nvis[q]);
-  const float kmax2 = __uint_as_float(P.meta[q].maxk2), qw = P.meta[p].qw, wabs = P.meta[p].wabs;
+  const float maxt = __uint_as_float(P.meta[q].maxt), wabs = P.meta[p].wabs;
   if (chunk > 0 && chunk * kCmpChunk >= nc) return;
   for (int i = tid; i < kNBins; i += kThreads) s_h[i] = 0;
-  const uint32_t bin = wg_coarse_bin(P, p, hv, chunk == 0, kmax2, qw, wabs, s_tmp);   // its barriers order the clear
+  const uint32_t bin = wg_coarse_bin(P, p, hv, chunk == 0, maxt, wabs, s_tmp);   // its barriers order the clear
   if (bin == kAll || chunk * kCmpChunk >= nc) return;
   const int m = count16(nc, my0);
 #pragma unroll
@@ -1519,7 +1556,6 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
   __shared__ uint32_t s_selw[kSmallThreads];   // fast path: chosen pending slots, one word per thread
   __shared__ uint32_t s_tmp[32];
   __shared__ float s_par[4];
-  __shared__ float s_qn[kWave];
   __shared__ __attribute__((aligned(16))) float s_w[kWave];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1534,8 +1570,6 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
 
   // every load of the prologue is issued before any of them is used; indices
   // are clamped so that no load is conditional
-  constexpr int kSeg = D / 8;               // query dims per thread: eight threads per head
-  const int h = tid >> 3, part = tid & 7;
   const int nwg = (nc + P.scan_chunk - 1) / P.scan_chunk;   // <= 64
   float4 raw[kSmallPer / 4];
 #pragma unroll
@@ -1545,12 +1579,6 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
 #pragma unroll
   for (int k = 0; k < kSmallMax / 8 / kSmallThreads; ++k)
     praw[k] = P.pool_in[(size_t)q * P.keep_in + min(tid + kSmallThreads * k, P.keep_in - 1)];
-  uint4 qseg[kSeg / 8];
-  {
-    const uint4* qh = reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + min(h, P.h_i - 1)) * D + part * kSeg);
-#pragma unroll
-    for (int i = 0; i < kSeg / 8; ++i) qseg[i] = qh[i];
-  }
   const float wraw = P.w[(size_t)q * P.h_i + min(tid & 63, P.h_i - 1)];
   const float kraw = P.kpart[(size_t)q * nwg + min(tid & 63, nwg - 1)];
 
@@ -1584,37 +1612,16 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
   for (int k = 0; k < kSmallMax / 8 / kSmallThreads; ++k)
     if (tid + kSmallThreads * k < nc / 8) s_pool[tid + kSmallThreads * k] = praw[k];
   if (tid < kWave) s_w[tid] = tid < P.h_i ? wraw : 0.0f;
-  // rounding bound Delta = C * QW * max||k|| (as the multi-kernel path)
-  {
-    float ss = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kSeg / 8; ++i) {
-      const uint32_t wd[4] = {qseg[i].x, qseg[i].y, qseg[i].z, qseg[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float lo = __uint_as_float(wd[j] << 16), hi = __uint_as_float(wd[j] & 0xFFFF0000u);
-        ss = fmaf(lo, lo, ss);
-        ss = fmaf(hi, hi, ss);
-      }
-    }
-    // sum over the eight threads of a head (lanes 8j .. 8j + 7)
-    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0xB1, 0xF, 0xF, false));
-    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x4E, 0xF, 0xF, false));
-    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x141, 0xF, 0xF, false));
-    if (part == 0) s_qn[h] = h < P.h_i ? sqrtf(ss) : 0.0f;   // times |w_h| below
-    if (wave == 0) {
-      const uint32_t mk = wave_max_dpp(lane < nwg ? __float_as_uint(kraw) : 0u);   // non-negative floats order as integers
-      if (lane == 0) s_par[1] = __uint_as_float(mk);
-    }
-  }
-  lds_barrier();
+  // rounding bound Delta = C * max t_k over the pool's keys (the scan's
+  // work-groups each left the largest key magnitude they saw), as the
+  // multi-kernel path
   if (wave == 0) {
-    const float qn = wave_sum(fabsf(s_w[lane]) * s_qn[lane]);
-    const float wa = wave_sum(fabsf(s_w[lane]));
+    const uint32_t mk = wave_max_dpp(lane < nwg ? __float_as_uint(kraw) : 0u);   // non-negative floats order as integers
+    const float wa = wave_sum(fabsf(wraw) * (lane < P.h_i ? 1.0f : 0.0f));
     if (lane == 0)
-      s_par[0] = P.bound_tok * (qn * (1.0f + 0.0009765625f)) * sqrtf(s_par[1]) * (1.0f + 0.0009765625f) +
-                 wa * (float)P.d_i * 7.8886e-31f;
+      s_par[0] = P.bound_tok * __uint_as_float(mk) * (1.0f + 0.0009765625f) + wa * (float)P.d_i * 7.8886e-31f;
   }
+  lds_barrier();   // every wave's range and count, the pool ids, the weights
   uint32_t lo = 0xFFFFFFFFu, hi = 0u, nv = 0;
 #pragma unroll
   for (int i = 0; i < kSmallWaves; ++i) {
@@ -1990,10 +1997,12 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 double gamma_n(double n, double u) { return n * u / (1.0 - n * u); }
 
-// Delta = C * QW * max||k||.  C covers the exact score's fp32 fma chain (unit
-// roundoff 2^-24) and any MFMA accumulation order or truncation (2^-23) of the
-// d_i-term dot products, the head sum, and for blocks the 8-term member sums
-// and the division by the member count; doubled for safety.
+// Delta = C * max_k t_k.  Per head, the exact fp32 chain (unit roundoff 2^-24)
+// and any MFMA accumulation order or truncation (2^-23) of the d_i-term dot
+// products each err by at most gamma * sum_d |q_hd k_d|; weighted by |w_h|
+// and summed over heads this is gamma * t_k, to which the two head sums' and,
+// for blocks, the 8-term member sums' and the division's roundings add.  C
+// covers all of these, doubled for safety.
 float bound_constant(int d_i, bool block) {
   const double u = std::ldexp(1.0, -24), u2 = std::ldexp(1.0, -23);
   double e = gamma_n(d_i, u) + gamma_n(d_i + 2, u2);

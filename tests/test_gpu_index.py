@@ -213,12 +213,13 @@ def test_mfma_scores_within_proven_bound():
     exact = np.array([oracle.index_score(iqb, w, ikb[t]) for t in range(L)])
     qf = inp["iq"][0].double().numpy()
     kf = inp["ik"].double().numpy()
-    qw = float(np.sum(np.abs(w) * np.linalg.norm(qf, axis=1)))
+    # t_k = sum_h |w_h| sum_d |q_hd| |k_d|, the key magnitude the kernels' bound uses
+    t = np.abs(kf) @ (np.abs(w)[:, None] * np.abs(qf)).sum(axis=0)
     u, u2 = 2.0 ** -24, 2.0 ** -23
     gam = lambda n, uu: n * uu / (1 - n * uu)
     gd, gm, gh = gam(d_i, u), gam(d_i + 2, u2), gam(66, u)
     c = 2 * (gd + gm + gh * (2 + gd + gm))
-    bound = c * qw * np.linalg.norm(kf, axis=1)
+    bound = c * t
     ratio = np.abs(approx - exact) / bound
     print(f"max |mfma - exact| / bound = {ratio.max():.3e}")
     assert np.all(np.abs(approx - exact) <= bound)
