@@ -75,6 +75,8 @@ def lib():
         L.csa2_ref_reindex_topk.restype = i32
         L.csa2_ref_reindex_topk.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32,
                                             i32, i32, vp, i32]
+        L.csa2_ref_block_keys.restype = i32
+        L.csa2_ref_block_keys.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
         L.csa2_ref_sparse_attn.restype = i32
         L.csa2_ref_sparse_attn.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32,
                                            vp, vp, vp, f32, vp, vp, i32]
@@ -197,6 +199,39 @@ def reindex_topk(iq, w, q_seq, q_nvis, ik, seq_base, pool_blocks, k, block=8, n_
     if rc:
         raise ValueError("csa2_ref_reindex_topk: invalid arguments")
     return idx
+
+
+# ---------------------------------------------------------------- pool-based Full
+def block_keys(ik, seq_base, seq_len, kbar, kbar_base, blk_from=None, block=8, max_blocks=None):
+    """Write the bf16 mean keys of blocks into kbar (uint16 [rows, d_i], updated in
+    place): for sequence s, blocks blk_from[s] <= b < ceil(seq_len[s]/block), at most
+    max_blocks of them, go to row kbar_base[s] + b.  Defaults: every block."""
+    ik = _c(ik, np.uint16)
+    d_i = ik.shape[1]
+    seq_len = _c(seq_len, np.int32)
+    n_seq = seq_len.shape[0]
+    blk_from = np.zeros(n_seq, np.int32) if blk_from is None else _c(blk_from, np.int32)
+    if max_blocks is None:
+        max_blocks = int(((seq_len.astype(np.int64) + block - 1) // block).max(initial=0))
+    if kbar.dtype != np.uint16 or not kbar.flags["C_CONTIGUOUS"]:
+        raise TypeError("kbar must be a contiguous uint16 array")
+    rc = lib().csa2_ref_block_keys(_p(ik), d_i, _p(_c(seq_base, np.int64)), _p(seq_len), _p(blk_from),
+                                   n_seq, block, int(max_blocks), _p(kbar), _p(_c(kbar_base, np.int64)))
+    if rc:
+        raise ValueError("csa2_ref_block_keys: invalid arguments")
+    return kbar
+
+
+def pool_full_topk(iq, w, q_seq, q_nvis, ik, seq_base, kbar, kbar_base, k, keep_blocks, block=8,
+                   n_threads=0):
+    """Full layer of the pool-based variant: the Top-keep_blocks blocks by the
+    token score of their stored keys (kbar), then the Top-K positions of that
+    pool re-scored with the same query.  Returns (idx [n_q,k], pool [n_q,keep_blocks])."""
+    q_nvis = _c(q_nvis, np.int32)
+    q_nblk = ((q_nvis.astype(np.int64) + block - 1) // block).astype(np.int32)
+    pool = index_topk(iq, w, q_seq, q_nblk, kbar, kbar_base, keep_blocks, n_threads=n_threads)
+    idx = reindex_topk(iq, w, q_seq, q_nvis, ik, seq_base, pool, k, block=block, n_threads=n_threads)
+    return idx, pool
 
 
 # ---------------------------------------------------------------- a7

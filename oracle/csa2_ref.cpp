@@ -344,6 +344,41 @@ int csa2_ref_reindex_topk(const uint16_t* iq, const float* w, int n_q, int h_i, 
 }
 
 /* ======================================================================
+ * Block keys for the pool-based Full variant.  The hierarchical indexer
+ * groups positions into blocks of 8 and keeps at most 2048 of them [W1, CSA2
+ * section]; the pages do not say how a block is scored nor whether the Full
+ * layer itself picks its Top-512 inside that pool.  In the variant where it
+ * does, the Full layer must not read every token key, so a block is scored
+ * from a stored key of its own.  Reading: the block key is the mean of the
+ * member keys, summed in fp32 from +0 in ascending position order, divided by
+ * the member count (IEEE), rounded to bf16 (nearest-even); a partial last
+ * block averages its members.  The block's score is then the ordinary token
+ * score (csa2_ref_index_score) of that key.
+ * For sequence s, blocks b with blk_from[s] <= b < ceil(seq_len[s] / block)
+ * and b - blk_from[s] < max_blocks are written to kbar[kbar_base[s] + b];
+ * other blocks are left alone.
+ * ====================================================================== */
+int csa2_ref_block_keys(const uint16_t* ik, int d_i, const int64_t* seq_base, const int32_t* seq_len,
+                        const int32_t* blk_from, int n_seq, int block, int max_blocks,
+                        uint16_t* kbar, const int64_t* kbar_base) {
+  if (d_i < 1 || n_seq < 0 || block < 1 || max_blocks < 0) return 1;
+  for (int s = 0; s < n_seq; ++s) {
+    const int64_t nb = ((int64_t)seq_len[s] + block - 1) / block;
+    const int64_t b1 = std::min<int64_t>(nb, (int64_t)blk_from[s] + max_blocks);
+    for (int64_t b = std::max<int64_t>(0, blk_from[s]); b < b1; ++b) {
+      const int64_t t0 = b * block, t1 = std::min<int64_t>(seq_len[s], t0 + block);
+      const float cnt = (float)(t1 - t0);
+      for (int d = 0; d < d_i; ++d) {
+        float sum = 0.0f;
+        for (int64_t t = t0; t < t1; ++t) sum = sum + bf16_to_float(ik[(size_t)(seq_base[s] + t) * d_i + d]);
+        kbar[(size_t)(kbar_base[s] + b) * d_i + d] = csa2_ref_bf16_bits(sum / cnt);
+      }
+    }
+  }
+  return 0;
+}
+
+/* ======================================================================
  * a6+a7: attention of one decode query over the selected main-KV entries
  * merged with the layer's sliding-window rows.  Every layer runs a 128-token
  * sliding window [W1, encoder-decoder section] and keeps its own main Q and

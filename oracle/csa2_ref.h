@@ -69,6 +69,14 @@ int csa2_ref_reindex_topk(const uint16_t* iq, const float* w, int n_q, int h_i, 
                           const int32_t* pool_blocks, int block, int keep_blocks,
                           int k, int32_t* idx_out, int n_threads);
 
+/* ---- pool-based Full variant: stored block keys ------------------------
+ * kbar[kbar_base[s] + b][d] = bf16(mean of the block's member keys, fp32 sum
+ * in ascending order), for blocks blk_from[s] <= b < ceil(seq_len[s]/block),
+ * at most max_blocks of them per sequence. */
+int csa2_ref_block_keys(const uint16_t* ik, int d_i, const int64_t* seq_base, const int32_t* seq_len,
+                        const int32_t* blk_from, int n_seq, int block, int max_blocks,
+                        uint16_t* kbar, const int64_t* kbar_base);
+
 /* ---- a6+a7(+a8): sparse attention over selected FP4 entries + SWA ------ */
 int csa2_ref_sparse_attn(const void* q, int q_dtype, int n_q, int h, int d,
                          const int32_t* q_seq, const uint8_t* cache, const int64_t* seq_base,
