@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c5"])
+    p.add_argument("--full-from-pool", action="store_true",
+                   help="the pool-based Full variant: the Full layer picks its Top-K inside its own pool, "
+                        "scanning stored block keys instead of every token key (reported as its own workload)")
     p.add_argument("--cpu-baseline", default="auto", choices=["auto", "off"])
     p.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the oracle sample (0: workload default)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -52,6 +55,7 @@ def parse():
 
 
 def build_state(wl, dev):
+    import numpy as np
     import torch
 
     import csa2_inputs as gen
@@ -72,6 +76,19 @@ def build_state(wl, dev):
                      max_nvis=max(wl["q_nvis"]), k=wl["k"], keep_blocks=wl["keep_blocks"], w_max=wl["w"],
                      softmax_scale=512 ** -0.5,
                      chunk_base=int(wl["seq_base"][wl["q_seq"][0]]) if wl.get("chunk") else None)
+    if wl.get("pool_full"):
+        # stored block keys of every sequence, built before timing (a step
+        # refreshes only the block of the appended position)
+        lens = torch.tensor(wl["lengths"], dtype=torch.int32, device=dev)
+        nblk = [(L + 7) // 8 for L in wl["lengths"]]
+        kb_base = torch.tensor(np.concatenate([[0], np.cumsum(nblk)[:-1]]), dtype=torch.int64, device=dev)
+        st.pool_full = True
+        st.kbar = torch.empty((max(sum(nblk), 1), wl["d_i"]), dtype=torch.bfloat16, device=dev)
+        st.kbar_base, st.seq_len = kb_base, lens
+        st.blk_last = torch.tensor([(L - 1) // 8 for L in wl["lengths"]], dtype=torch.int32, device=dev)
+        st.q_nblk = torch.tensor([(n + 7) // 8 for n in wl["q_nvis"]], dtype=torch.int32, device=dev)
+        st.max_nblk = max((n + 7) // 8 for n in wl["q_nvis"])
+        csa2.block_keys(ik, st.seq_base, lens, st.kbar, kb_base, max(nblk))
     layers = [LayerInputs(**gen.layer_tensors(wl, i, dev)) for i in range(len(wl["layers"]))]
     app_x, app_rows = gen.append_rows(wl, dev)
     torch.cuda.synchronize()
@@ -80,9 +97,12 @@ def build_state(wl, dev):
 
 def scan_bytes(wl):
     """Algorithmic bytes of one Full-layer indexer-scan launch: every visible
-    key (d_i bf16) once, plus each query's indexer query and head weights."""
+    key (d_i bf16) once, plus each query's indexer query and head weights.  In
+    the pool-based Full variant the scan reads the stored block keys instead
+    (one per 8 visible positions)."""
     n_q, h_i, d_i = wl["n_q"], wl["h_i"], wl["d_i"]
-    return sum(wl["q_nvis"]) * d_i * 2 + n_q * (h_i * d_i * 2 + h_i * 4)
+    keys = sum((n + 7) // 8 for n in wl["q_nvis"]) if wl.get("pool_full") else sum(wl["q_nvis"])
+    return keys * d_i * 2 + n_q * (h_i * d_i * 2 + h_i * 4)
 
 
 def step_bytes(wl):
@@ -91,7 +111,12 @@ def step_bytes(wl):
     qb = 4 if wl["q_dtype"] == "f32" else 2
     b = n_q * (1024 + 288)                                   # append: read a bf16 row, write a record
     for mode in wl["layers"]:
-        if mode == "full":
+        if mode == "full" and wl.get("pool_full"):
+            b += n_q * 9 * d_i * 2                               # block-key refresh: 8 keys in, 1 out
+            b += scan_bytes(wl) + n_q * wl["keep_blocks"] * 4    # block scan -> pool
+            b += sum(min(L, 8 * wl["keep_blocks"]) for L in wl["lengths"]) * d_i * 2
+            b += n_q * (h_i * d_i * 2 + h_i * 4 + k * 4)         # pool re-scored with the Full query
+        elif mode == "full":
             b += scan_bytes(wl) + n_q * k * 4 + (n_q * wl["keep_blocks"] * 4)
         elif mode == "reindex":
             b += sum(min(L, 8 * wl["keep_blocks"]) for L in wl["lengths"]) * d_i * 2
@@ -154,7 +179,7 @@ def cpu_baseline(wl, st, layers, app_x, dev, nseq, gpu_results):
     oracle.lib()
     res, _, secs = oracle_step(hl, ik, cbase, np.arange(nseq, dtype=np.int32), np.array(lens, np.int32),
                                wl["k"], wl["keep_blocks"], wl["block"], raw_rows, ax, st.softmax_scale,
-                               n_threads=threads)
+                               n_threads=threads, pool_full=bool(wl.get("pool_full")))
     # parity of the sample against the timed GPU step's outputs
     idx_ok, err = True, 0.0
     for (gidx, gout, _), (ridx, rout, _) in zip(gpu_results, res):
@@ -211,6 +236,11 @@ def main():
         copy_calibration(a.copy_calibration, dev)
         return
     wl = gen.workload(a.workload)
+    if a.full_from_pool:
+        if not wl["keep_blocks"] or "full" not in wl["layers"]:
+            sys.exit(f"--full-from-pool needs a workload with a Full layer and a pool ({a.workload} has none)")
+        wl["pool_full"] = True
+        wl["desc"] += "; pool-based Full variant (Full picks its Top-K inside its own pool of stored block keys)"
     log(f"workload {wl['name']}: {wl['desc']}; building inputs")
     t0 = time.time()
     st, layers, app_x, app_rows = build_state(wl, dev)
@@ -250,7 +280,10 @@ def main():
         achieved = sb / (scan_ms * 1e-3) / 1e9
         sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
         traffic = traffic_from_profile(sha)
-        roofline = {"bound": "hbm", "kernel": "k_scan (indexer scan, Full layer)", "achieved": round(achieved, 1),
+        kname = "k_scan over block keys (pool-based Full)" if wl.get("pool_full") else "k_scan (indexer scan, Full layer)"
+        if wl.get("pool_full"):
+            traffic = None   # the committed counters cover the token scan
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                     "traffic": traffic, "algorithmic_bytes_per_launch": sb, "launch_ms": round(scan_ms, 5)}
     sbytes = step_bytes(wl)

@@ -23,6 +23,9 @@
  *   Full:    csa2_quant_append (new rows) -> csa2_index_topk -> csa2_sparse_attn
  *   Reindex: csa2_reindex_topk -> csa2_sparse_attn
  *   Reuse:   csa2_sparse_attn with the idx of the group's Full/Reindex layer
+ * and, in the pool-based Full variant (see csa2_block_keys), a Full layer is
+ *   csa2_quant_append -> csa2_block_keys (the appended position's block) ->
+ *   csa2_index_topk over the block keys -> csa2_reindex_topk -> csa2_sparse_attn
  *
  * Conventions shared by every entry point:
  *  - Every data pointer is DEVICE memory owned by the caller.  The library
@@ -164,6 +167,30 @@ csa2_status csa2_reindex_topk(const uint16_t* iq, const float* w, int n_q, int h
                               const int32_t* pool_blocks, int block, int keep_blocks,
                               int k, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 size_t csa2_reindex_topk_ws_bytes(int n_q, int h_i, int d_i, int k, int block, int keep_blocks);
+
+/* ------------------------------------------------------------------------
+ * csa2_block_keys -- stored block keys for the pool-based Full variant: a
+ * Full layer that picks its Top-512 inside its own pool (the hierarchical
+ * indexer's blocks of 8 positions, at most 2048 kept; source as above,
+ * section "Сжатое разреженное внимание 2 (CSA2)").  Such a layer scores
+ * blocks from one stored key per block instead of every token key:
+ *   kbar[kbar_base[s] + b][d] = bf16_RNE( (sum over the block's positions
+ *            8b .. min(8b+8, seq_len[s]) - 1, ascending, of float(ik[row][d]),
+ *            fp32 from +0) / member count (IEEE) ),  row = seq_base[s] + position
+ *   for every sequence s < n_seq and block b with blk_from[s] <= b <
+ *   ceil(seq_len[s] / 8) and b - blk_from[s] < max_blocks; other rows of kbar
+ *   are not touched.  blk_from may be NULL (every sequence from block 0).
+ *   A decode step that appends position p refreshes block p / 8 only
+ *   (blk_from[s] = p / 8, max_blocks = 1).
+ * The variant's Full layer is then: csa2_index_topk over kbar (q_nvis =
+ * ceil(visible positions / 8), seq_base = kbar_base, k = keep_blocks, no
+ * pool) -> the pool's block ids, ascending; then csa2_reindex_topk with the
+ * Full layer's own iq/w over that pool -> its Top-K.
+ * Supported: d_i a multiple of 8 in [8, 1024], n_seq <= 65535.  Alignment:
+ * ik, kbar 16 B; seq_base, kbar_base 8 B; seq_len, blk_from 4 B. */
+csa2_status csa2_block_keys(const uint16_t* ik, int d_i, const int64_t* seq_base, const int32_t* seq_len,
+                            const int32_t* blk_from, int n_seq, int max_blocks, uint16_t* kbar,
+                            const int64_t* kbar_base, void* stream);
 
 /* ------------------------------------------------------------------------
  * csa2_sparse_attn -- gather + dequantise the selected FP4 entries and run

@@ -17,17 +17,26 @@ import time
 
 import numpy as np
 
-from . import index_topk, quantize_rows, reindex_topk, sparse_attn
+from . import block_keys, index_topk, pool_full_topk, quantize_rows, reindex_topk, sparse_attn
 
 
 def decode_step(layers, ik, seq_base, q_seq, q_nvis, k, keep_blocks, block, raw_rows_fn, append_x,
-                scale, n_threads=0):
+                scale, n_threads=0, pool_full=False):
     """layers: list of dicts of host arrays: mode, q (float32 or uint16 bf16 bits),
     swa (uint16), swa_row0, swa_len and, for full/reindex, iq (uint16) and w.
     raw_rows_fn(rows) -> raw main-KV rows (float32 or uint16) of global cache rows.
     Returns (results, pool, seconds): results = [(idx, out, lse)] per layer and
-    the time spent inside the oracle's decode-step calls (input plumbing excluded)."""
+    the time spent inside the oracle's decode-step calls (input plumbing excluded).
+    pool_full: the Full layer picks its Top-K inside its own pool, built from
+    stored block keys (computed here for every query's visible prefix, outside
+    the timed calls, as they are resident before a decode step)."""
     secs = 0.0
+    if pool_full:
+        qbase = np.asarray(seq_base, np.int64)[np.asarray(q_seq)]
+        nblk = (np.asarray(q_nvis, np.int64) + block - 1) // block
+        kb_base = np.concatenate([[0], np.cumsum(nblk)[:-1]]).astype(np.int64)
+        kbar = np.zeros((max(int(nblk.sum()), 1), ik.shape[1]), np.uint16)
+        block_keys(ik, qbase, q_nvis, kbar, kb_base, block=block)
     t0 = time.perf_counter()
     if append_x is not None:
         quantize_rows(append_x)            # a1: the new token of every sequence
@@ -37,7 +46,10 @@ def decode_step(layers, ik, seq_base, q_seq, q_nvis, k, keep_blocks, block, raw_
     for lay in layers:
         mode = lay["mode"]
         t0 = time.perf_counter()
-        if mode == "full":
+        if mode == "full" and pool_full:
+            idx, pool = pool_full_topk(lay["iq"], lay["w"], np.arange(len(q_seq), dtype=np.int32), q_nvis, ik,
+                                       qbase, kbar, kb_base, k, keep_blocks, block=block, n_threads=n_threads)
+        elif mode == "full":
             r = index_topk(lay["iq"], lay["w"], q_seq, q_nvis, ik, seq_base, k, block=block,
                            keep_blocks=keep_blocks, n_threads=n_threads)
             idx, pool = r if keep_blocks else (r, None)

@@ -1,6 +1,6 @@
 """CSA2 decode hot path for AMD MI355X (gfx950): Python binding of libcsa2.so.
 
-The four calls below are the C-ABI entry points of ``include/csa2.h`` with the
+The calls below are the C-ABI entry points of ``include/csa2.h`` with the
 same names; this module only marshals torch tensors (device memory) and the
 current HIP stream into them and turns a non-OK status into an exception.
 Every step runs in the library's HIP kernels.  There is no fallback: if the
@@ -12,6 +12,8 @@ DeepSeek-V4.1-Flash Ñ ĞºĞ¾Ğ½Ñ‚ĞµĞºÑÑ‚Ğ¾Ğ¼ Ğ² 1 Ğ¼Ğ»Ğ½ Ñ‚Ğ¾ĞºĞµĞ½Ğ¾Ğ², KV-ĞºÑÑ
   Full layer:    quant_append (new rows) -> index_topk -> sparse_attn
   Reindex layer: reindex_topk -> sparse_attn
   Reuse layer:   sparse_attn with the group head's idx
+  pool-based Full variant: block_keys (appended block) -> index_topk over the
+                 block keys (the pool) -> reindex_topk with the Full query
 """
 from __future__ import annotations
 
@@ -66,6 +68,8 @@ def lib():
                                        f32, vp, vp, vp, sz, vp]
         L.csa2_sparse_attn_ws_bytes.restype = sz
         L.csa2_sparse_attn_ws_bytes.argtypes = [i32, i32, i32, i32]
+        L.csa2_block_keys.restype = i32
+        L.csa2_block_keys.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp, vp]
         L.csa2_status_string.restype = ctypes.c_char_p
         L.csa2_status_string.argtypes = [i32]
         L.csa2_last_hip_error.restype = i32
@@ -227,6 +231,25 @@ def reindex_topk(iq, w, q_seq, q_nvis, ik, seq_base, pool_blocks, k=512, block=8
                                  _ptr(buf), buf.numel(), _stream(dev))
     _check(st, "csa2_reindex_topk")
     return idx_out
+
+
+def block_keys(ik, seq_base, seq_len, kbar, kbar_base, max_blocks, blk_from=None) -> None:
+    """Pool-based Full variant: write the bf16 mean keys of blocks of 8 positions
+    into kbar [rows,d_i] bf16 at kbar_base[s] + b, for blocks blk_from[s] (0 if
+    None) .. +max_blocks-1 that lie inside seq_len[s].  ik [rows,d_i] bf16,
+    seq_base/kbar_base [n_seq] int64, seq_len/blk_from [n_seq] int32."""
+    _need(ik, torch.bfloat16, "ik")
+    _need(seq_base, torch.int64, "seq_base")
+    _need(seq_len, torch.int32, "seq_len")
+    _need(kbar, torch.bfloat16, "kbar")
+    _need(kbar_base, torch.int64, "kbar_base")
+    if blk_from is not None:
+        _need(blk_from, torch.int32, "blk_from")
+    if ik.dim() != 2 or kbar.dim() != 2 or kbar.shape[1] != ik.shape[1]:
+        raise ValueError("ik and kbar must be [rows, d_i] with the same d_i")
+    st = lib().csa2_block_keys(_ptr(ik), ik.shape[1], _ptr(seq_base), _ptr(seq_len), _ptr(blk_from),
+                               seq_len.numel(), int(max_blocks), _ptr(kbar), _ptr(kbar_base), _stream(ik.device))
+    _check(st, "csa2_block_keys")
 
 
 def sparse_attn_ws_bytes(n_q, h, k, w_max) -> int:

@@ -1958,6 +1958,16 @@ using namespace csa2::idx;
 
 namespace {
 
+// Keys per scan work-group: the largest power of two up to kMaxScanChunk that
+// still gives at least two work-groups per CU (512), down to 1024 keys, so
+// that short contexts (or the block keys of the pool-based variant) still fill
+// the 256 CUs.
+int scan_chunk_for(int n_q, int64_t max_nvis) {
+  int chunk = kMaxScanChunk;
+  while (chunk > 1024 && (int64_t)n_q * ((max_nvis + chunk - 1) / chunk) < 512) chunk >>= 1;
+  return chunk;
+}
+
 thread_local int g_last_hip_error = 0;
 thread_local hipEvent_t g_scan_ev_start = nullptr;
 thread_local hipEvent_t g_scan_ev_stop = nullptr;
@@ -2172,7 +2182,7 @@ extern "C" csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n
   P.idx_out = idx_out; P.pool_out = pool_out;
   P.nprob = n_q * (keep_blocks > 0 ? 2 : 1);
   P.reindex = 0;
-  P.scan_chunk = kMaxScanChunk;
+  P.scan_chunk = scan_chunk_for(n_q, max_nvis);
   P.stride = round_up(std::max<int64_t>(max_nvis, 1), kCmpChunk);
   P.nchunk_cmp = (int)(P.stride / kCmpChunk);
   const size_t need = csa2_index_topk_ws_bytes(n_q, max_nvis, h_i, d_i, k, block, keep_blocks);

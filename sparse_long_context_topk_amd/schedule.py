@@ -17,7 +17,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import index_topk, index_topk_chunk, quant_append, reindex_topk, sparse_attn, Workspace
+from . import block_keys, index_topk, index_topk_chunk, quant_append, reindex_topk, sparse_attn, Workspace
 
 FULL, REINDEX, REUSE = "full", "reindex", "reuse"
 
@@ -60,6 +60,15 @@ class DecodeState:
     w_max: int = 128
     softmax_scale: float = 512 ** -0.5
     chunk_base: int | None = None         # all queries in one sequence whose keys start at this row (no pool)
+    # pool-based Full variant: the Full layer picks its Top-K inside its own pool,
+    # scanning stored block keys (kbar) instead of every token key
+    pool_full: bool = False
+    kbar: torch.Tensor | None = None      # [block rows, d_i] bf16, block b of sequence s at kbar_base[s] + b
+    kbar_base: torch.Tensor | None = None # [n_seq] int64
+    q_nblk: torch.Tensor | None = None    # [n_q] int32: ceil(q_nvis / 8), the blocks each query sees
+    max_nblk: int = 0
+    seq_len: torch.Tensor | None = None   # [n_seq] int32 positions per sequence
+    blk_last: torch.Tensor | None = None  # [n_seq] int32: block of each sequence's newest position
     ws_index: Workspace = field(default_factory=Workspace)
     ws_attn: Workspace = field(default_factory=Workspace)
 
@@ -83,6 +92,16 @@ def decode_step(st: DecodeState, layers: list[LayerInputs], append_x=None, appen
                     raise ValueError("a chunk of one sequence's queries builds no pool")
                 idx, pool = index_topk_chunk(lay.iq, lay.w, st.q_nvis, st.max_nvis, st.ik, st.chunk_base, k=st.k,
                                              ws=st.ws_index), None
+            elif st.pool_full:
+                if not st.keep_blocks:
+                    raise ValueError("the pool-based Full variant needs keep_blocks > 0")
+                if append_x is not None:
+                    # the appended position's block key changes with it
+                    block_keys(st.ik, st.seq_base, st.seq_len, st.kbar, st.kbar_base, 1, blk_from=st.blk_last)
+                pool = index_topk(lay.iq, lay.w, st.q_seq, st.q_nblk, st.max_nblk, st.kbar, st.kbar_base,
+                                  k=st.keep_blocks, ws=st.ws_index)
+                idx = reindex_topk(lay.iq, lay.w, st.q_seq, st.q_nvis, st.ik, st.seq_base, pool, k=st.k,
+                                   ws=st.ws_index)
             else:
                 r = index_topk(lay.iq, lay.w, st.q_seq, st.q_nvis, st.max_nvis, st.ik, st.seq_base, k=st.k,
                                keep_blocks=st.keep_blocks, ws=st.ws_index)

@@ -100,3 +100,14 @@ def test_workspace_sizes_grow_with_inputs():
     assert b > a > 0
     assert L.csa2_reindex_topk_ws_bytes(4, 64, 128, 512, 8, 2048) > 0
     assert L.csa2_sparse_attn_ws_bytes(64, 64, 512, 128) >= L.csa2_sparse_attn_ws_bytes(1, 64, 512, 128)
+
+
+def test_block_keys_argument_checks():
+    L = csa2.lib()
+    bk = lambda **kw: L.csa2_block_keys(kw.get("ik", FAKE), kw.get("d", 128), FAKE, FAKE, kw.get("frm", None),
+                                        kw.get("n_seq", 2), kw.get("mb", 4), kw.get("kbar", FAKE), FAKE, None)
+    assert bk(d=100) == 2 and bk(d=0) == 2 and bk(d=2048) == 2
+    assert bk(n_seq=-1) == 1 and bk(mb=-1) == 1
+    assert bk(ik=None) == 1 and bk(kbar=None) == 1
+    assert bk(ik=ctypes.c_void_p((1 << 20) + 8)) == 1 and bk(frm=ctypes.c_void_p((1 << 20) + 2)) == 1
+    assert bk(n_seq=0) == 0 and bk(mb=0) == 0 and bk(ik=None, mb=0) == 0   # nothing to do, nothing enqueued

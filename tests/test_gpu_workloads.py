@@ -29,10 +29,15 @@ def _host(t):
     return bits(t) if t.dtype == torch.bfloat16 else t.cpu().numpy()
 
 
-def _check_workload(name, length_div=1, sample=None):
-    """sample: query indices the oracle checks (default: every query)."""
+def _check_workload(name, length_div=1, sample=None, pool_full=False):
+    """sample: query indices the oracle checks (default: every query);
+    pool_full: the Full layer picks its Top-K inside its own pool (bench.py
+    --full-from-pool)."""
     dev = device()
     wl = gen.workload(name, length_div=length_div)
+    if pool_full:
+        wl["pool_full"] = True
+        wl["name"] += " (pool-based Full)"
     note(f"workload {wl['name']}: {len(wl['lengths'])} sequences, {wl['rows']} rows, layers {wl['layers']}")
     st, layers, app_x, app_rows = bench.build_state(wl, dev)
     res, pool = decode_step(st, layers, append_x=app_x, append_rows=app_rows, keep_outputs=True)
@@ -58,7 +63,7 @@ def _check_workload(name, length_div=1, sample=None):
                                    np.asarray(wl["q_seq"], np.int32)[sel], np.asarray(wl["q_nvis"], np.int32)[sel],
                                    wl["k"], wl["keep_blocks"], wl["block"], raw_rows,
                                    _host(app_x) if app_x is not None else None,
-                                   st.softmax_scale, n_threads=min(16, os.cpu_count() or 1))
+                                   st.softmax_scale, n_threads=min(16, os.cpu_count() or 1), pool_full=pool_full)
     print(f"oracle step {secs:.1f} s", flush=True)
     worst = 0.0
     for li, ((gi, go, gl), (ri, ro, rl)) in enumerate(zip(got, ref)):
@@ -90,6 +95,11 @@ def test_c3_full_pool_reindex_1m_batch4():
 
 
 @gpu
+def test_c3_pool_based_full_variant_1m_batch4():
+    _check_workload("c3", pool_full=True)
+
+
+@gpu
 def test_c4_encoder_chunk_4096_causal_queries_sampled():
     # the first and last query, and queries spread over the chunk
     _check_workload("c4", sample=[0, 1, 1023, 2048, 3071, 4094, 4095, 517])
@@ -98,3 +108,8 @@ def test_c4_encoder_chunk_4096_causal_queries_sampled():
 @gpu
 def test_c5_twenty_layer_schedule_mixed_lengths():
     _check_workload("c5", length_div=16)
+
+
+@gpu
+def test_c5_twenty_layer_schedule_pool_based_full():
+    _check_workload("c5", length_div=16, pool_full=True)
