@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--full-from-pool", action="store_true",
                    help="the pool-based Full variant: the Full layer picks its Top-K inside its own pool, "
                         "scanning stored block keys instead of every token key (reported as its own workload)")
+    p.add_argument("--graph", action="store_true",
+                   help="also capture the step as a HIP graph and report the replayed step's rate as `value` "
+                        "(the eager steps still time the scan for `roofline`)")
     p.add_argument("--cpu-baseline", default="auto", choices=["auto", "off"])
     p.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the oracle sample (0: workload default)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -168,11 +171,15 @@ def cpu_baseline(wl, st, layers, app_x, dev, nseq, gpu_results):
         return t.cpu().numpy() if t.dtype != torch.bfloat16 else bits(t)
 
     hl = []
-    for lay in layers:
-        d = dict(mode=lay.mode, q=host(lay.q[:nseq]), swa=bits(lay.swa), swa_row0=host(lay.swa_row0[:nseq]),
+    for li, lay in enumerate(layers):
+        # the generated window rows (the timed steps have written their new rows into lay.swa)
+        swa = bits(gen.layer_tensors(wl, li, dev)["swa"])
+        d = dict(mode=lay.mode, q=host(lay.q[:nseq]), swa=swa, swa_row0=host(lay.swa_row0[:nseq]),
                  swa_len=host(lay.swa_len[:nseq]))
         if lay.iq is not None:
             d["iq"], d["w"] = bits(lay.iq[:nseq]), host(lay.w[:nseq])
+        if lay.swa_new is not None:
+            d["swa_new"], d["swa_dst"] = bits(lay.swa_new[:nseq]), host(lay.swa_dst[:nseq])
         hl.append(d)
     ax = host(app_x[:nseq])
     threads = max(1, min(nseq, 16, os.cpu_count() or 1))
@@ -271,6 +278,21 @@ def main():
     ms = t_start.elapsed_time(t_stop) / K
     log(f"timed {K} steps: {ms:.4f} ms/step")
     ql_per_step = wl["n_q"] * len(wl["layers"])
+    eager_ms = ms
+    if a.graph:
+        from sparse_long_context_topk_amd.schedule import StepGraph
+        gr = StepGraph(st, layers, append_x=app_x, append_rows=app_rows)
+        for _ in range(a.warmup):
+            gr.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(K):
+            gr.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms = g0.elapsed_time(g1) / K
+        log(f"timed {K} graph replays: {ms:.4f} ms/step (eager {eager_ms:.4f})")
     value = ql_per_step / (ms * 1e-3)
 
     roofline = None
@@ -281,8 +303,8 @@ def main():
         sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
         traffic = traffic_from_profile(sha)
         kname = "k_scan over block keys (pool-based Full)" if wl.get("pool_full") else "k_scan (indexer scan, Full layer)"
-        if wl.get("pool_full"):
-            traffic = None   # the committed counters cover the token scan
+        if wl.get("pool_full") or a.workload != "c3":
+            traffic = None   # the committed counters cover the 1M batch-4 token scan only
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                     "traffic": traffic, "algorithmic_bytes_per_launch": sb, "launch_ms": round(scan_ms, 5)}
@@ -319,6 +341,8 @@ def main():
         "step_hbm": {"algorithmic_bytes": sbytes, "GB/s": round(sbytes / (ms * 1e-3) / 1e9, 1),
                      "frac": round(sbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
         "roofline": roofline,
+        "step_launch": ({"mode": "hip_graph", "eager_ms_per_step": round(eager_ms, 5)} if a.graph
+                        else {"mode": "eager"}),
         "cpu_baseline": cpu,
         "parity_sample": parity,
     }

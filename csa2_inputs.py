@@ -188,6 +188,13 @@ def layer_tensors(wl, layer, device="cpu"):
              q=normal((n_q, h, 512), s, tag + "-q", device=device, dtype=_tdtype(wl["q_dtype"]),
                       outlier_p=wl["outlier_p"]),
              swa=swa, swa_row0=row0, swa_len=wlen)
+    if wl.get("append", True) and not wl["swa_shared"]:
+        # the decode step's new window row of every sequence (its newest
+        # position L - 1), written into its 128-row ring at row (L - 1) mod W
+        d["swa_new"] = normal((n_q, 512), s, tag + "-swa-new", device=device, dtype=torch.bfloat16,
+                              outlier_p=wl["outlier_p"])
+        d["swa_dst"] = torch.tensor([i * W + (L - 1) % W for i, L in enumerate(wl["lengths"])],
+                                    dtype=torch.int64, device=device)
     if d["mode"] in ("full", "reindex"):
         d["iq"] = normal((n_q, wl["h_i"], wl["d_i"]), s, tag + "-iq", device=device, dtype=torch.bfloat16,
                          outlier_p=wl["outlier_p"])

@@ -23,6 +23,8 @@
  *   Full:    csa2_quant_append (new rows) -> csa2_index_topk -> csa2_sparse_attn
  *   Reindex: csa2_reindex_topk -> csa2_sparse_attn
  *   Reuse:   csa2_sparse_attn with the idx of the group's Full/Reindex layer
+ * with each layer's new window row written by csa2_window_append before its
+ * csa2_sparse_attn,
  * and, in the pool-based Full variant (see csa2_block_keys), a Full layer is
  *   csa2_quant_append -> csa2_block_keys (the appended position's block) ->
  *   csa2_index_topk over the block keys -> csa2_reindex_topk -> csa2_sparse_attn
@@ -191,6 +193,23 @@ size_t csa2_reindex_topk_ws_bytes(int n_q, int h_i, int d_i, int k, int block, i
 csa2_status csa2_block_keys(const uint16_t* ik, int d_i, const int64_t* seq_base, const int32_t* seq_len,
                             const int32_t* blk_from, int n_seq, int max_blocks, uint16_t* kbar,
                             const int64_t* kbar_base, void* stream);
+
+/* ------------------------------------------------------------------------
+ * csa2_window_append -- write rows into a layer's sliding-window KV (every
+ * layer keeps its own 128-token window KV; source as above, sections
+ * "Каузальный энкодер-декодер" and "Сжатое разреженное внимание 2 (CSA2)").
+ *   x        [n_rows][512], x_dtype CSA2_F32 (rounded to the nearest bf16,
+ *            ties to even) or CSA2_BF16 (copied)
+ *   dst_row  [n_rows] row of swa each row goes to; rows outside
+ *            [0, swa_rows) are skipped
+ *   swa      [swa_rows][512] bf16 window rows
+ * Used as a ring of 128 rows per (layer, sequence): position p goes to ring
+ * row p mod 128, so the ring holds the last min(L, 128) positions and
+ * csa2_sparse_attn takes its first min(L, 128) rows as the window (the
+ * softmax does not depend on the order of its keys).
+ * Alignment: x, swa 16 B; dst_row 8 B. */
+csa2_status csa2_window_append(const void* x, int x_dtype, int64_t n_rows, const int64_t* dst_row,
+                               uint16_t* swa, int64_t swa_rows, void* stream);
 
 /* ------------------------------------------------------------------------
  * csa2_sparse_attn -- gather + dequantise the selected FP4 entries and run

@@ -23,7 +23,9 @@ from . import block_keys, index_topk, pool_full_topk, quantize_rows, reindex_top
 def decode_step(layers, ik, seq_base, q_seq, q_nvis, k, keep_blocks, block, raw_rows_fn, append_x,
                 scale, n_threads=0, pool_full=False):
     """layers: list of dicts of host arrays: mode, q (float32 or uint16 bf16 bits),
-    swa (uint16), swa_row0, swa_len and, for full/reindex, iq (uint16) and w.
+    swa (uint16), swa_row0, swa_len, optionally swa_new (uint16 [n_q, 512]) and
+    swa_dst (the step's new window rows and their rows in swa) and, for
+    full/reindex, iq (uint16) and w.
     raw_rows_fn(rows) -> raw main-KV rows (float32 or uint16) of global cache rows.
     Returns (results, pool, seconds): results = [(idx, out, lse)] per layer and
     the time spent inside the oracle's decode-step calls (input plumbing excluded).
@@ -63,8 +65,13 @@ def decode_step(layers, ik, seq_base, q_seq, q_nvis, k, keep_blocks, block, raw_
         recs = quantize_rows(raw_rows_fn(uniq)) if len(uniq) else np.zeros((1, 288), np.uint8)
         cidx = np.where(rows >= 0, np.searchsorted(uniq, rows), -1).astype(np.int32)
         zq = np.zeros(len(q_seq), np.int32)
+        swa = lay["swa"]
+        if lay.get("swa_new") is not None:
+            # this step's window rows enter the layer's ring (bf16 rows: a copy)
+            swa = np.array(swa, copy=True)
+            swa[np.asarray(lay["swa_dst"], np.int64)] = lay["swa_new"]
         t0 = time.perf_counter()
-        out, lse = sparse_attn(lay["q"], zq, recs, np.zeros(1, np.int64), cidx, lay["swa"], lay["swa_row0"],
+        out, lse = sparse_attn(lay["q"], zq, recs, np.zeros(1, np.int64), cidx, swa, lay["swa_row0"],
                                lay["swa_len"], scale, n_threads=n_threads)
         secs += time.perf_counter() - t0
         results.append((idx, out, lse))

@@ -68,6 +68,8 @@ def lib():
                                        f32, vp, vp, vp, sz, vp]
         L.csa2_sparse_attn_ws_bytes.restype = sz
         L.csa2_sparse_attn_ws_bytes.argtypes = [i32, i32, i32, i32]
+        L.csa2_window_append.restype = i32
+        L.csa2_window_append.argtypes = [vp, i32, i64, vp, vp, i64, vp]
         L.csa2_block_keys.restype = i32
         L.csa2_block_keys.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp, vp]
         L.csa2_status_string.restype = ctypes.c_char_p
@@ -152,6 +154,24 @@ def quant_append(x: torch.Tensor, dst_row: torch.Tensor, cache: torch.Tensor) ->
     st = lib().csa2_quant_append(_ptr(x), F32 if x.dtype == torch.float32 else BF16, x.shape[0],
                                  _ptr(dst_row), _ptr(cache), cache.shape[0], _stream(x.device))
     _check(st, "csa2_quant_append")
+
+
+def window_append(x: torch.Tensor, dst_row: torch.Tensor, swa: torch.Tensor) -> None:
+    """Write rows x[n,512] (fp32, rounded to bf16, or bf16) into a layer's window
+    rows swa[rows,512] (bf16) at dst_row[n] (int64); a ring of 128 rows per
+    sequence takes position p at ring row p mod 128."""
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _need(x, x.dtype, "x")
+    _need(dst_row, torch.int64, "dst_row")
+    _need(swa, torch.bfloat16, "swa")
+    if x.dim() != 2 or x.shape[1] != KV_CH or swa.dim() != 2 or swa.shape[1] != KV_CH:
+        raise ValueError("x must be [n,512] and swa [rows,512]")
+    if dst_row.numel() != x.shape[0]:
+        raise ValueError("dst_row must have one entry per row of x")
+    st = lib().csa2_window_append(_ptr(x), F32 if x.dtype == torch.float32 else BF16, x.shape[0], _ptr(dst_row),
+                                  _ptr(swa), swa.shape[0], _stream(x.device))
+    _check(st, "csa2_window_append")
 
 
 def index_topk_ws_bytes(n_q, max_nvis, h_i, d_i, k, block=8, keep_blocks=0) -> int:

@@ -7,6 +7,7 @@ extern "C" int csa2_internal_last_hip_error_index(void);
 extern "C" int csa2_internal_last_hip_error_attn(void);
 extern "C" int csa2_internal_last_hip_error_quant(void);
 extern "C" int csa2_internal_last_hip_error_blocks(void);
+extern "C" int csa2_internal_last_hip_error_window(void);
 
 extern "C" const char* csa2_status_string(csa2_status s) {
   switch (s) {
@@ -24,5 +25,6 @@ extern "C" int csa2_last_hip_error(void) {
   if (!e) e = csa2_internal_last_hip_error_attn();
   if (!e) e = csa2_internal_last_hip_error_quant();
   if (!e) e = csa2_internal_last_hip_error_blocks();
+  if (!e) e = csa2_internal_last_hip_error_window();
   return e;
 }

@@ -17,7 +17,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import block_keys, index_topk, index_topk_chunk, quant_append, reindex_topk, sparse_attn, Workspace
+from . import (block_keys, index_topk, index_topk_chunk, quant_append, reindex_topk, sparse_attn, window_append,
+               Workspace)
 
 FULL, REINDEX, REUSE = "full", "reindex", "reuse"
 
@@ -43,6 +44,8 @@ class LayerInputs:
     swa_len: torch.Tensor                 # [n_q] int32
     iq: torch.Tensor | None = None        # [n_q, h_i, d_i] bf16
     w: torch.Tensor | None = None         # [n_q, h_i] f32
+    swa_new: torch.Tensor | None = None   # [n_q, 512] this step's window row of each query's sequence
+    swa_dst: torch.Tensor | None = None   # [n_q] int64 its row in swa (ring row: newest position mod 128)
 
 
 @dataclass
@@ -76,7 +79,8 @@ class DecodeState:
 def decode_step(st: DecodeState, layers: list[LayerInputs], append_x=None, append_rows=None,
                 scan_events=None, keep_outputs=True):
     """Run one decode step over `layers`.  append_x/append_rows: new main-KV
-    rows quantised into the cache before the Full layer indexes.  Returns a
+    rows quantised into the cache before the Full layer indexes; each layer's
+    new window rows (swa_new) go into its ring before its attention.  Returns a
     list of (idx, out, lse) per layer (idx shared by a group's Reuse layers)."""
     from . import record_scan_events
     if append_x is not None:
@@ -115,8 +119,37 @@ def decode_step(st: DecodeState, layers: list[LayerInputs], append_x=None, appen
             raise ValueError(f"unknown layer mode {lay.mode}")
         if idx is None:
             raise ValueError("a Reuse layer needs a preceding Full or Reindex layer")
+        if lay.swa_new is not None:
+            window_append(lay.swa_new, lay.swa_dst, lay.swa)
         out, lse = sparse_attn(lay.q, st.q_seq, st.cache, st.seq_base, idx, lay.swa, lay.swa_row0,
                                lay.swa_len, st.w_max, st.softmax_scale, ws=st.ws_attn)
         if keep_outputs:
             results.append((idx, out, lse))
     return results, pool
+
+
+class StepGraph:
+    """One decode step captured as a HIP graph and replayed.
+
+    Every kernel launch of the step becomes a node of one graph, so a replay
+    costs the host a single launch and the GPU runs the nodes back to back.
+    The graph reads the tensors it was captured with (the state, the layers'
+    queries and window rows, the appended rows): update them in place between
+    replays.  Its outputs (per layer idx, out, lse, and the pool) live in the
+    graph's own memory and each replay overwrites them.  The library itself
+    allocates nothing and issues no memset, so the captured launches are the
+    eager ones."""
+
+    def __init__(self, st: DecodeState, layers: list[LayerInputs], append_x=None, append_rows=None):
+        # an eager step first, so every workspace has its final size before capture
+        decode_step(st, layers, append_x=append_x, append_rows=append_rows, keep_outputs=False)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.results, self.pool = decode_step(st, layers, append_x=append_x, append_rows=append_rows,
+                                                  keep_outputs=True)
+
+    def replay(self):
+        """Enqueue one step on the current stream; returns the (overwritten) outputs."""
+        self.graph.replay()
+        return self.results, self.pool

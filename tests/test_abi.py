@@ -111,3 +111,13 @@ def test_block_keys_argument_checks():
     assert bk(ik=None) == 1 and bk(kbar=None) == 1
     assert bk(ik=ctypes.c_void_p((1 << 20) + 8)) == 1 and bk(frm=ctypes.c_void_p((1 << 20) + 2)) == 1
     assert bk(n_seq=0) == 0 and bk(mb=0) == 0 and bk(ik=None, mb=0) == 0   # nothing to do, nothing enqueued
+
+
+def test_window_append_argument_checks():
+    L = csa2.lib()
+    wa = lambda **kw: L.csa2_window_append(kw.get("x", FAKE), kw.get("dt", 1), kw.get("n", 4), kw.get("dst", FAKE),
+                                           kw.get("swa", FAKE), kw.get("rows", 10), None)
+    assert wa(n=-1) == 1 and wa(rows=-1) == 1 and wa(dt=3) == 1
+    assert wa(x=None) == 1 and wa(dst=None) == 1 and wa(swa=None) == 1
+    assert wa(x=ctypes.c_void_p((1 << 20) + 4)) == 1 and wa(dst=ctypes.c_void_p((1 << 20) + 4)) == 1
+    assert wa(n=0) == 0 and wa(x=None, n=0) == 0

@@ -40,6 +40,7 @@ def _check_workload(name, length_div=1, sample=None, pool_full=False):
         wl["name"] += " (pool-based Full)"
     note(f"workload {wl['name']}: {len(wl['lengths'])} sequences, {wl['rows']} rows, layers {wl['layers']}")
     st, layers, app_x, app_rows = bench.build_state(wl, dev)
+    swa0 = [bits(lay.swa) for lay in layers]   # generated window rows, before the step writes its new ones
     res, pool = decode_step(st, layers, append_x=app_x, append_rows=app_rows, keep_outputs=True)
     torch.cuda.synchronize()
     n_q = wl["n_q"]
@@ -53,11 +54,13 @@ def _check_workload(name, length_div=1, sample=None, pool_full=False):
         return x.cpu().numpy() if x.dtype == torch.float32 else bits(x)
 
     hl = []
-    for lay in layers:
-        d = dict(mode=lay.mode, q=_host(lay.q[ts]), swa=bits(lay.swa), swa_row0=_host(lay.swa_row0[ts]),
+    for lay, sw in zip(layers, swa0):
+        d = dict(mode=lay.mode, q=_host(lay.q[ts]), swa=sw, swa_row0=_host(lay.swa_row0[ts]),
                  swa_len=_host(lay.swa_len[ts]))
         if lay.iq is not None:
             d["iq"], d["w"] = bits(lay.iq[ts]), _host(lay.w[ts])
+        if lay.swa_new is not None:
+            d["swa_new"], d["swa_dst"] = bits(lay.swa_new[ts]), _host(lay.swa_dst[ts])
         hl.append(d)
     ref, rpool, secs = oracle_step(hl, bits(st.ik), np.asarray(wl["seq_base"], np.int64),
                                    np.asarray(wl["q_seq"], np.int32)[sel], np.asarray(wl["q_nvis"], np.int32)[sel],
