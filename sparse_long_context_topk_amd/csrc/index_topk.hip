@@ -704,7 +704,8 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
 constexpr int kChunkKeys = 4096;   // keys per chunk-scan work-group
 
 template <int D, int MT, int QB>
-__global__ __launch_bounds__(kThreads) void k_scan_chunk(Params P) {
+__global__ __launch_bounds__(kThreads, 2) void k_scan_chunk(Params P) {   // two waves per SIMD
+  static_assert(QB >= 1 && QB <= 4, "lane group g stores query g's scores");
   constexpr int KS = D / 32;
   constexpr int NBUF = 2;           // one key group in flight, one in use (registers go to the queries)
   __shared__ uint32_t s_hist[QB][kNBins];
@@ -713,9 +714,12 @@ __global__ __launch_bounds__(kThreads) void k_scan_chunk(Params P) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int q0 = blockIdx.y * QB;
+  // x: the query group (the fast dimension of the launch order), y: the key
+  // range -- the work-groups resident together, spread over the XCDs, then
+  // share one 1 MiB key range, which each XCD's L2 holds
+  const int q0 = blockIdx.x * QB;
   const int nq = min(QB, P.n_q - q0);
-  const int c0 = blockIdx.x * kChunkKeys;
+  const int c0 = blockIdx.y * kChunkKeys;
   int nvis[QB];
   int nmax = 0;
 #pragma unroll
@@ -788,17 +792,14 @@ __global__ __launch_bounds__(kThreads) void k_scan_chunk(Params P) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kb[ks] = src[4 * ks];
   };
-  auto process = [&](int it, const uint4* kin) {
+  auto process = [&](int it, const uint4 (&kb)[KS]) {
     const int gi = wave + kWaves * it;
-    bool valid;
-    key_row(it, valid);
-    const uint32_t vm = valid ? 0xFFFFFFFFu : 0u;
-    uint4 kb[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kb[ks] = make_uint4(kin[ks].x & vm, kin[ks].y & vm, kin[ks].z & vm, kin[ks].w & vm);
+    // no masking: a slot past the visible keys loaded the sequence's first key
+    // (key_row), whose t_k belongs to the maximum anyway and whose scores are
+    // not stored
     mk2 = fmaxf(mk2, sum_rows4(t_part<KS>(kb, up)));   // as in k_scan
     const int cand = c0 + 16 * gi + n;   // this lane's key
+    float sq[QB];
 #pragma unroll
     for (int qq = 0; qq < QB; ++qq) {
       f32x4 acc[MT];   // acc[mt][i]: head 16*mt + 4*g + i, key n
@@ -816,19 +817,31 @@ __global__ __launch_bounds__(kThreads) void k_scan_chunk(Params P) {
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) v = fmaf(wq[qq][mt][i], fmaxf(acc[mt][i], 0.0f), v);
-      const float si = sum_rows4(v);   // + the other three lane groups' heads
-      const bool cvalid = cand < nvis[qq];
-      if (g == 0) {
-        s_sc[qq][cand - c0] = cvalid ? si : -INFINITY;
-        if (cvalid) atomicAdd(&s_hist[qq][sortable(si) >> kBinShift], 1u);
+      sq[qq] = sum_rows4(v);   // + the other three lane groups' heads
+    }
+    // lane group g stores query g's score and counts it: one store and one
+    // LDS atomic instruction for the QB queries
+    if (g < QB) {
+      float si = sq[0];
+      int nv = nvis[0];
+#pragma unroll
+      for (int qq = 1; qq < QB; ++qq) {
+        si = g == qq ? sq[qq] : si;
+        nv = g == qq ? nvis[qq] : nv;
       }
+      const bool cvalid = cand < nv;
+      s_sc[g][cand - c0] = cvalid ? si : -INFINITY;
+      if (cvalid) atomicAdd(&s_hist[g][sortable(si) >> kBinShift], 1u);
     }
   };
 
   uint4 buf[NBUF][KS];
   if (my_groups > 0) {
-    load(0, buf[0]);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b) {
+      load(b, buf[b]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   int it = 0;
   for (; it + NBUF <= my_groups; it += NBUF) {
@@ -2100,8 +2113,8 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   g_scan_ev_start = g_scan_ev_stop = nullptr;
   if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return CSA2_E_HIP;
   if (chunk) {
-    const dim3 gch((unsigned)std::max<int64_t>(1, (max_slots + kChunkKeys - 1) / kChunkKeys),
-                   (unsigned)((P.n_q + kChunkQB - 1) / kChunkQB));
+    const dim3 gch((unsigned)((P.n_q + kChunkQB - 1) / kChunkQB),
+                   (unsigned)std::max<int64_t>(1, (max_slots + kChunkKeys - 1) / kChunkKeys));
     if (P.d_i == 128) launch_scan_chunk<128>(P, mt, gch, s);
     else launch_scan_chunk<64>(P, mt, gch, s);
   } else if (P.d_i == 128) {

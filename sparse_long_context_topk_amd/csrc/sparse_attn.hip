@@ -12,7 +12,8 @@
 //
 // Work decomposition: one work-group per (query, split of the key slots);
 // slots [0, k) are the selected entries, [k, k + swa_len) the window rows.
-// A split is a run of 32-slot sub-tiles.  The split's slot positions are
+// A split takes every nsplit-th 32-slot sub-tile (so the window's sub-tiles,
+// whose rows are the largest, are spread over the splits).  The split's slot positions are
 // staged in LDS first; then, double-buffered, the loads of sub-tile s+1 are
 // in flight while the MFMA work of sub-tile s runs, and are decoded into the
 // other LDS buffer after it.
@@ -113,14 +114,18 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
   const int k = P.k;
   const int nswa = P.swa_len ? P.swa_len[qi] : 0;
   const int64_t srow0 = nswa ? P.swa_row0[qi] : 0;
-  const int sub0 = split * P.sub_per_split;
-  const int sub1 = min(sub0 + P.sub_per_split, P.nsub);
-  const int slot_lo = sub0 * kSub;
-  const int sel_hi = min(sub1 * kSub, k);
+  // this split's sub-tiles: split, split + nsplit, split + 2 nsplit, ... (every
+  // split gets its share of the window's sub-tiles, whose rows are the largest)
+  const int ns = P.nsplit;
+  const int nmine = split < P.nsub ? (P.nsub - split + ns - 1) / ns : 0;
   // fallback address for slots without a key: any readable bytes (the query)
   const uint8_t* fb = static_cast<const uint8_t*>(P.q);
 
-  for (int i = slot_lo + tid; i < sel_hi; i += kThreads) s_pos[i - slot_lo] = P.idx[(size_t)qi * k + i];
+  // selected positions of this split's sub-tiles: local sub-tile j at s_pos[32 j ..]
+  for (int i = tid; i < nmine * kSub; i += kThreads) {
+    const int slot = (split + (i / kSub) * ns) * kSub + (i % kSub);
+    if (slot < k) s_pos[i] = P.idx[(size_t)qi * k + slot];
+  }
 
   // decode assignment: thread -> key slots 8*kq .. 8*kq+7, channels 8*cg .. 8*cg+7
   const int kq = tid & 3, cg = tid >> 2;
@@ -138,8 +143,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
       st.valid |= (pos[jj] >= 0 ? 1u : 0u) << jj;
     }
   };
-  auto load_sel = [&](int sub) {      // positions from the LDS copy of the index list
-    const int i0 = sub * kSub + 8 * kq - slot_lo;   // multiple of 8: two 16-byte LDS reads
+  auto load_sel = [&](int j) {        // local sub-tile j; positions from the LDS copy of the index list
+    const int i0 = j * kSub + 8 * kq;   // multiple of 8: two 16-byte LDS reads
     const int4 pa = *reinterpret_cast<const int4*>(&s_pos[i0]);
     const int4 pb = *reinterpret_cast<const int4*>(&s_pos[i0 + 4]);
     const int pos[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
@@ -183,18 +188,18 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
 
   // The first sub-tile's loads are issued before the query's: a selected
   // sub-tile takes its positions straight from the index list in global memory
-  if (sub0 < sub1) {
-    const int kind = sub_kind(sub0 * kSub, k);
+  if (nmine > 0) {
+    const int kind = sub_kind(split * kSub, k);
     if (kind == 0) {
-      const int32_t* ip = P.idx + (size_t)qi * k + sub0 * kSub + 8 * kq;
+      const int32_t* ip = P.idx + (size_t)qi * k + split * kSub + 8 * kq;
       int pos[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) pos[jj] = ip[jj];
       load_sel_pos(pos);
     } else if (kind == 1) {
-      load_win(sub0);
+      load_win(split);
     } else {
-      load_mixed(sub0);
+      load_mixed(split);
     }
   }
 
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
   for (int t = 0; t < 32; ++t) o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  if (sub0 < sub1) store_stage(sub0, 0);
+  if (nmine > 0) store_stage(split, 0);
   lds_barrier();   // s_pos and buffer 0
 
   auto compute = [&](int b) {
@@ -380,20 +385,22 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
   // Selected-entry sub-tiles (all but the last few) are prefetched: their
   // loads stay in flight during this sub-tile's MFMA work.  Window and
   // straddling sub-tiles load after it.
-  for (int sub = sub0; sub < sub1; ++sub) {
-    const int b = (sub - sub0) & 1;
-    const int kind = sub + 1 < sub1 ? sub_kind((sub + 1) * kSub, k) : 3;
-    if (kind == 0) load_sel(sub + 1);
+  for (int j = 0; j < nmine; ++j) {
+    const int b = j & 1;
+    const int nsub = split + (j + 1) * ns;   // the next sub-tile
+    const int kind = j + 1 < nmine ? sub_kind(nsub * kSub, k) : 3;
+    if (kind == 0) load_sel(j + 1);
+    else if (kind == 1) load_win(nsub);
     compute(b);
-    if (kind == 0) {
+    if (kind == 0 || kind == 1) {
       // the loaded words become visible to the decode only here, so the
       // compiler cannot hoist the decode (and its wait) above the MFMA work
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) asm volatile("" : "+v"(st.w[jj][0]), "+v"(st.w[jj][1]));
+      for (int jj = 0; jj < 8; ++jj)
+        asm volatile("" : "+v"(st.w[jj][0]), "+v"(st.w[jj][1]), "+v"(st.w[jj][2]), "+v"(st.w[jj][3]));
     }
-    if (kind == 1) load_win(sub + 1);
-    else if (kind == 2) load_mixed(sub + 1);
-    if (kind != 3) store_stage(sub + 1, b ^ 1);   // the other buffer: last read before the previous barrier
+    if (kind == 2) load_mixed(nsub);
+    if (kind != 3) store_stage(nsub, b ^ 1);   // the other buffer: last read before the previous barrier
     lds_barrier();
   }
 
