@@ -24,7 +24,7 @@
  *   Reindex: csa2_reindex_topk -> csa2_sparse_attn
  *   Reuse:   csa2_sparse_attn with the idx of the group's Full/Reindex layer
  * with each layer's new window row written by csa2_window_append before its
- * csa2_sparse_attn,
+ * csa2_sparse_attn (or both in one csa2_sparse_attn_append),
  * and, in the pool-based Full variant (see csa2_block_keys), a Full layer is
  *   csa2_quant_append -> csa2_block_keys (the appended position's block) ->
  *   csa2_index_topk over the block keys -> csa2_reindex_topk -> csa2_sparse_attn
@@ -236,6 +236,27 @@ csa2_status csa2_sparse_attn(const void* q, int q_dtype, int n_q, int h, int d,
                              const uint16_t* swa, const int64_t* swa_row0, const int32_t* swa_len,
                              int w_max, float softmax_scale, float* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
+/* ------------------------------------------------------------------------
+ * csa2_sparse_attn_append -- csa2_window_append and csa2_sparse_attn in one
+ * call (a decode step writes each layer's new window row and then attends
+ * over the window that contains it; source as for both).  The same result as
+ *   csa2_window_append(swa_new, CSA2_BF16, n_q, swa_dst, swa, swa_rows)
+ *   followed by csa2_sparse_attn(... swa ...)
+ * with one launch fewer: query i's new row swa_new[i] ([n_q][512] bf16) is
+ * written to row swa_dst[i] of swa (skipped outside [0, swa_rows)), and a
+ * window slot of query i on that row takes swa_new[i] directly.
+ * Requirement beyond csa2_sparse_attn: a row written for query i is in no
+ * other query's window of the same call (each query's ring is its own);
+ * otherwise call the two entry points in order.
+ * Other arguments, workspace, supported shapes and alignment: as
+ * csa2_sparse_attn; swa_new 16 B, swa_dst 8 B aligned. */
+csa2_status csa2_sparse_attn_append(const void* q, int q_dtype, int n_q, int h, int d,
+                                    const int32_t* q_seq, const uint8_t* cache, const int64_t* seq_base,
+                                    const int32_t* idx, int k, uint16_t* swa, int64_t swa_rows,
+                                    const int64_t* swa_row0, const int32_t* swa_len, int w_max,
+                                    const uint16_t* swa_new, const int64_t* swa_dst,
+                                    float softmax_scale, float* out, float* lse, void* ws,
+                                    size_t ws_bytes, void* stream);
 size_t csa2_sparse_attn_ws_bytes(int n_q, int h, int k, int w_max);
 
 /* ------------------------------------------------------------------------

@@ -66,6 +66,9 @@ def lib():
         L.csa2_sparse_attn.restype = i32
         L.csa2_sparse_attn.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp, i32,
                                        f32, vp, vp, vp, sz, vp]
+        L.csa2_sparse_attn_append.restype = i32
+        L.csa2_sparse_attn_append.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, i64, vp, vp, i32,
+                                              vp, vp, f32, vp, vp, vp, sz, vp]
         L.csa2_sparse_attn_ws_bytes.restype = sz
         L.csa2_sparse_attn_ws_bytes.argtypes = [i32, i32, i32, i32]
         L.csa2_window_append.restype = i32
@@ -277,9 +280,11 @@ def sparse_attn_ws_bytes(n_q, h, k, w_max) -> int:
 
 
 def sparse_attn(q, q_seq, cache, seq_base, idx, swa, swa_row0, swa_len, w_max, softmax_scale,
-                out=None, lse=None, want_lse=True, ws=None):
+                out=None, lse=None, want_lse=True, ws=None, swa_new=None, swa_dst=None):
     """q [n_q,h,512] fp32|bf16; idx [n_q,k] int32 (-1 skipped); swa [rows,512] bf16 with
-    per-query rows swa_row0[i] .. + swa_len[i]-1.  Returns (out [n_q,h,512] f32, lse [n_q,h] f32)."""
+    per-query rows swa_row0[i] .. + swa_len[i]-1.  Returns (out [n_q,h,512] f32, lse [n_q,h] f32).
+    swa_new [n_q,512] bf16 / swa_dst [n_q] int64: this step's window rows, written into swa at
+    swa_dst in the same call (csa2_sparse_attn_append)."""
     if q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("q must be float32 or bfloat16")
     _need(q, q.dtype, "q")
@@ -300,6 +305,18 @@ def sparse_attn(q, q_seq, cache, seq_base, idx, swa, swa_row0, swa_len, w_max, s
         lse = torch.empty((n_q, h), dtype=torch.float32, device=dev)
     nbytes = sparse_attn_ws_bytes(n_q, h, k, w_max)
     buf = _ws(dev, nbytes, ws)
+    if swa_new is not None:
+        _need(swa_new, torch.bfloat16, "swa_new")
+        _need(swa_dst, torch.int64, "swa_dst")
+        if swa_new.shape != (n_q, KV_CH) or swa_dst.numel() != n_q or w_max <= 0:
+            raise ValueError("swa_new must be [n_q,512] with one swa_dst per query, and a window given")
+        st = lib().csa2_sparse_attn_append(_ptr(q), F32 if q.dtype == torch.float32 else BF16, n_q, h, d,
+                                           _ptr(q_seq), _ptr(cache), _ptr(seq_base), _ptr(idx), k, _ptr(swa),
+                                           swa.shape[0], _ptr(swa_row0), _ptr(swa_len), int(w_max),
+                                           _ptr(swa_new), _ptr(swa_dst), float(softmax_scale), _ptr(out),
+                                           _ptr(lse) if want_lse else None, _ptr(buf), buf.numel(), _stream(dev))
+        _check(st, "csa2_sparse_attn_append")
+        return out, lse
     st = lib().csa2_sparse_attn(_ptr(q), F32 if q.dtype == torch.float32 else BF16, n_q, h, d, _ptr(q_seq),
                                 _ptr(cache), _ptr(seq_base), _ptr(idx), k,
                                 _ptr(swa) if w_max > 0 else None, _ptr(swa_row0) if w_max > 0 else None,

@@ -51,6 +51,13 @@ struct Params {
   const int32_t* idx;
   int k;
   const uint16_t* swa;
+  // this call's new window rows (optional): swa_new[i] goes to row swa_dst[i]
+  // of swa (written by work-group (i, 0)); a window slot on that row reads
+  // swa_new[i] itself, so no work-group depends on the write
+  const uint16_t* swa_new;
+  const int64_t* swa_dst;
+  uint16_t* swa_out;
+  int64_t swa_rows;
   const int64_t* swa_row0;
   const int32_t* swa_len;
   float scale_log2;
@@ -114,6 +121,14 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
   const int k = P.k;
   const int nswa = P.swa_len ? P.swa_len[qi] : 0;
   const int64_t srow0 = nswa ? P.swa_row0[qi] : 0;
+  const int64_t wdst = P.swa_new ? P.swa_dst[qi] : -1;   // this call's new window row of the query
+  // the window row `row` of this query, 8 channels from channel 8 cg
+  auto win_src = [&](int64_t row, int cgi) -> const uint16_t* {
+    return row == wdst ? P.swa_new + (size_t)qi * 512 + 8 * cgi : P.swa + (size_t)row * 512 + 8 * cgi;
+  };
+  if (wdst >= 0 && wdst < P.swa_rows && split == 0 && tid < 64)
+    reinterpret_cast<uint4*>(P.swa_out + (size_t)wdst * 512)[tid] =
+        reinterpret_cast<const uint4*>(P.swa_new + (size_t)qi * 512)[tid];
   // this split's sub-tiles: split, split + nsplit, split + 2 nsplit, ... (every
   // split gets its share of the window's sub-tiles, whose rows are the largest)
   const int ns = P.nsplit;
@@ -157,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
     for (int jj = 0; jj < 8; ++jj) {
       const bool ok = r0 + jj < nswa;
       const uint16_t* src =
-          ok ? P.swa + (size_t)(srow0 + r0 + jj) * 512 + 8 * cg : reinterpret_cast<const uint16_t*>(fb) + 8 * cg;
+          ok ? win_src(srow0 + r0 + jj, cg) : reinterpret_cast<const uint16_t*>(fb) + 8 * cg;
       const uint4 v = *reinterpret_cast<const uint4*>(src);
       st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
       st.valid |= (ok ? 1u : 0u) << jj;
@@ -179,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
           st.valid |= 1u << jj;
         }
       } else if (slot - k < nswa) {
-        const uint4 v = *reinterpret_cast<const uint4*>(P.swa + (size_t)(srow0 + slot - k) * 512 + 8 * cg);
+        const uint4 v = *reinterpret_cast<const uint4*>(win_src(srow0 + slot - k, cg));
         st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
         st.valid |= 1u << jj;
       }
@@ -543,12 +558,13 @@ extern "C" size_t csa2_sparse_attn_ws_bytes(int n_q, int h, int k, int w_max) {
          align256((size_t)n_q * s.nsplit * h * 2 * sizeof(float));
 }
 
-extern "C" csa2_status csa2_sparse_attn(const void* q, int q_dtype, int n_q, int h, int d,
-                                        const int32_t* q_seq, const uint8_t* cache, const int64_t* seq_base,
-                                        const int32_t* idx, int k, const uint16_t* swa,
-                                        const int64_t* swa_row0, const int32_t* swa_len, int w_max,
-                                        float softmax_scale, float* out, float* lse, void* ws,
-                                        size_t ws_bytes, void* stream) {
+namespace {
+
+csa2_status attn_call(const void* q, int q_dtype, int n_q, int h, int d, const int32_t* q_seq,
+                      const uint8_t* cache, const int64_t* seq_base, const int32_t* idx, int k,
+                      const uint16_t* swa, const int64_t* swa_row0, const int32_t* swa_len, int w_max,
+                      float softmax_scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream,
+                      const uint16_t* swa_new, const int64_t* swa_dst, int64_t swa_rows) {
   if (n_q < 0 || k < 0 || k > 2048 || w_max < 0 || w_max > 1024) return CSA2_E_INVAL;
   if (q_dtype != CSA2_F32 && q_dtype != CSA2_BF16) return CSA2_E_INVAL;
   if (d != CSA2_KV_CH || h < 16 || h > 64 || h % 16 != 0) return CSA2_E_UNSUPPORTED;
@@ -559,11 +575,15 @@ extern "C" csa2_status csa2_sparse_attn(const void* q, int q_dtype, int n_q, int
   if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(swa) & 15) ||
       (reinterpret_cast<uintptr_t>(cache) & 3) || (reinterpret_cast<uintptr_t>(ws) & 255))
     return CSA2_E_INVAL;
+  if (swa_new && (!swa || !swa_dst || swa_rows < 0 || (reinterpret_cast<uintptr_t>(swa_new) & 15) ||
+                  (reinterpret_cast<uintptr_t>(swa_dst) & 7)))
+    return CSA2_E_INVAL;
   if (ws_bytes < csa2_sparse_attn_ws_bytes(n_q, h, k, w_max)) return CSA2_E_WORKSPACE;
   const Split s = choose_split(n_q, k, w_max);
   Params P{};
   P.q = q; P.n_q = n_q; P.h = h; P.q_seq = q_seq; P.cache = cache; P.seq_base = seq_base;
   P.idx = idx; P.k = k; P.swa = swa; P.swa_row0 = swa_row0; P.swa_len = w_max > 0 ? swa_len : nullptr;
+  P.swa_new = swa_new; P.swa_dst = swa_dst; P.swa_out = const_cast<uint16_t*>(swa); P.swa_rows = swa_rows;
   P.scale_log2 = softmax_scale * kLog2e;
   P.out = out; P.lse = lse;
   P.nsplit = s.nsplit; P.sub_per_split = s.per; P.nsub = s.nsub;
@@ -588,4 +608,28 @@ extern "C" csa2_status csa2_sparse_attn(const void* q, int q_dtype, int n_q, int
     }
   }
   return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" csa2_status csa2_sparse_attn(const void* q, int q_dtype, int n_q, int h, int d,
+                                        const int32_t* q_seq, const uint8_t* cache, const int64_t* seq_base,
+                                        const int32_t* idx, int k, const uint16_t* swa,
+                                        const int64_t* swa_row0, const int32_t* swa_len, int w_max,
+                                        float softmax_scale, float* out, float* lse, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  return attn_call(q, q_dtype, n_q, h, d, q_seq, cache, seq_base, idx, k, swa, swa_row0, swa_len, w_max,
+                   softmax_scale, out, lse, ws, ws_bytes, stream, nullptr, nullptr, 0);
+}
+
+extern "C" csa2_status csa2_sparse_attn_append(const void* q, int q_dtype, int n_q, int h, int d,
+                                               const int32_t* q_seq, const uint8_t* cache, const int64_t* seq_base,
+                                               const int32_t* idx, int k, uint16_t* swa, int64_t swa_rows,
+                                               const int64_t* swa_row0, const int32_t* swa_len, int w_max,
+                                               const uint16_t* swa_new, const int64_t* swa_dst,
+                                               float softmax_scale, float* out, float* lse, void* ws,
+                                               size_t ws_bytes, void* stream) {
+  if (!swa_new) return CSA2_E_INVAL;
+  return attn_call(q, q_dtype, n_q, h, d, q_seq, cache, seq_base, idx, k, swa, swa_row0, swa_len, w_max,
+                   softmax_scale, out, lse, ws, ws_bytes, stream, swa_new, swa_dst, swa_rows);
 }

@@ -17,8 +17,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import (block_keys, index_topk, index_topk_chunk, quant_append, reindex_topk, sparse_attn, window_append,
-               Workspace)
+from . import block_keys, index_topk, index_topk_chunk, quant_append, reindex_topk, sparse_attn, Workspace
 
 FULL, REINDEX, REUSE = "full", "reindex", "reuse"
 
@@ -119,10 +118,10 @@ def decode_step(st: DecodeState, layers: list[LayerInputs], append_x=None, appen
             raise ValueError(f"unknown layer mode {lay.mode}")
         if idx is None:
             raise ValueError("a Reuse layer needs a preceding Full or Reindex layer")
-        if lay.swa_new is not None:
-            window_append(lay.swa_new, lay.swa_dst, lay.swa)
+        # the layer's new window row enters its ring in the attention call itself
         out, lse = sparse_attn(lay.q, st.q_seq, st.cache, st.seq_base, idx, lay.swa, lay.swa_row0,
-                               lay.swa_len, st.w_max, st.softmax_scale, ws=st.ws_attn)
+                               lay.swa_len, st.w_max, st.softmax_scale, ws=st.ws_attn, swa_new=lay.swa_new,
+                               swa_dst=lay.swa_dst)
         if keep_outputs:
             results.append((idx, out, lse))
     return results, pool

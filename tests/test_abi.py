@@ -121,3 +121,14 @@ def test_window_append_argument_checks():
     assert wa(x=None) == 1 and wa(dst=None) == 1 and wa(swa=None) == 1
     assert wa(x=ctypes.c_void_p((1 << 20) + 4)) == 1 and wa(dst=ctypes.c_void_p((1 << 20) + 4)) == 1
     assert wa(n=0) == 0 and wa(x=None, n=0) == 0
+
+
+def test_attention_append_argument_checks():
+    L = csa2.lib()
+    ap = lambda **kw: L.csa2_sparse_attn_append(FAKE, 1, 2, 64, 512, FAKE, FAKE, FAKE, FAKE, 512, kw.get("swa", FAKE),
+                                                kw.get("rows", 256), FAKE, FAKE, 128, kw.get("new", FAKE),
+                                                kw.get("dst", FAKE), ctypes.c_float(0.04), FAKE, None, FAKE,
+                                                kw.get("ws", 0), None)
+    assert ap(new=None) == 1 and ap(dst=None) == 1 and ap(swa=None) == 1 and ap(rows=-1) == 1
+    assert ap(new=ctypes.c_void_p((1 << 20) + 8)) == 1 and ap(dst=ctypes.c_void_p((1 << 20) + 4)) == 1
+    assert ap() == 3   # every check passes but the (zero) workspace: nothing is enqueued

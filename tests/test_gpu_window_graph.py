@@ -70,3 +70,39 @@ def test_captured_step_replays_equal_eager(name, div, pool_full):
         # eager work between replays
         decode_step(st, layers, append_x=app_x, append_rows=app_rows, keep_outputs=False)
         torch.cuda.synchronize()
+
+
+@gpu
+@pytest.mark.parametrize("qdt,lens", [(torch.bfloat16, [1, 77, 128, 5000]), (torch.float32, [300, 128, 2])])
+def test_attention_with_window_append_equals_two_calls(qdt, lens):
+    # csa2_sparse_attn_append must give the window rows and the outputs of
+    # csa2_window_append followed by csa2_sparse_attn, bit for bit
+    dev = device()
+    note(f"attention + window append {qdt} {lens}")
+    g = torch.Generator().manual_seed(411)
+    n_q, W, h = len(lens), 128, 64
+    L = max(lens)
+    raw = torch.randn((n_q * L, 512), generator=g)
+    cache = torch.empty((n_q * L, 288), dtype=torch.uint8, device=dev)
+    csa2.quant_append(raw.to(dev), torch.arange(n_q * L, dtype=torch.int64, device=dev), cache)
+    idx = torch.full((n_q, 512), -1, dtype=torch.int32)
+    for i, n in enumerate(lens):
+        sel = torch.randperm(n, generator=g)[:min(512, n)].sort().values
+        idx[i, :len(sel)] = sel.to(torch.int32)
+    q = torch.randn((n_q, h, 512), generator=g).to(qdt)
+    swa0 = torch.randn((n_q * W, 512), generator=g).to(torch.bfloat16)
+    new = torch.randn((n_q, 512), generator=g).to(torch.bfloat16)
+    row0 = torch.arange(n_q, dtype=torch.int64) * W
+    wlen = torch.tensor([min(W, n) for n in lens], dtype=torch.int32)
+    dst = torch.tensor([i * W + (n - 1) % W for i, n in enumerate(lens)], dtype=torch.int64)
+    sb = torch.arange(n_q, dtype=torch.int64) * L
+    qs = torch.arange(n_q, dtype=torch.int32)
+    d = lambda t: t.to(dev)
+    sa, sb_ = d(swa0), d(swa0)
+    csa2.window_append(d(new), d(dst), sa)
+    o1, l1 = csa2.sparse_attn(d(q), d(qs), cache, d(sb), d(idx), sa, d(row0), d(wlen), W, 0.044)
+    o2, l2 = csa2.sparse_attn(d(q), d(qs), cache, d(sb), d(idx), sb_, d(row0), d(wlen), W, 0.044,
+                              swa_new=d(new), swa_dst=d(dst))
+    torch.cuda.synchronize()
+    assert torch.equal(sa.cpu(), sb_.cpu())
+    assert torch.equal(o1.cpu(), o2.cpu()) and torch.equal(l1.cpu(), l2.cpu())
