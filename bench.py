@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c5"])
+    p.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--full-from-pool", action="store_true",
                    help="the pool-based Full variant: the Full layer picks its Top-K inside its own pool, "
                         "scanning stored block keys instead of every token key (reported as its own workload)")
@@ -98,6 +98,15 @@ def build_state(wl, dev):
     return st, layers, app_x, app_rows
 
 
+def chunk_flops(wl):
+    """FLOPs of one encoder-chunk scan launch: every (query, visible key) pair
+    costs 2 * h_i * d_i (the per-head dot products)."""
+    return sum(wl["q_nvis"]) * 2 * wl["h_i"] * wl["d_i"]
+
+
+PEAK_MFMA_BF16_TFLOPS = 2500.0
+
+
 def scan_bytes(wl):
     """Algorithmic bytes of one Full-layer indexer-scan launch: every visible
     key (d_i bf16) once, plus each query's indexer query and head weights.  In
@@ -109,23 +118,33 @@ def scan_bytes(wl):
 
 
 def step_bytes(wl):
-    """Algorithmic bytes of one whole step (what the method must move)."""
+    """Algorithmic bytes of one whole step (what the method must move): each
+    key once per scanning query (once per chunk for the encoder chunk, whose
+    queries share them), the pool's keys, the selected records and window
+    rows each query attends over (a chunk's shared window rows once), queries
+    in and outputs out, and the appended rows."""
     n_q, h_i, d_i, h, k, W = wl["n_q"], wl["h_i"], wl["d_i"], wl["h"], wl["k"], wl["w"]
     qb = 4 if wl["q_dtype"] == "f32" else 2
-    b = n_q * (1024 + 288)                                   # append: read a bf16 row, write a record
+    nvis = wl["q_nvis"]
+    b = 0
+    if wl.get("append", True):
+        b += len(wl["lengths"]) * (1024 + 288)               # append: read a bf16 row, write a record
     for mode in wl["layers"]:
-        if mode == "full" and wl.get("pool_full"):
+        if mode == "full" and wl.get("chunk"):
+            b += max(nvis) * d_i * 2 + n_q * (h_i * d_i * 2 + h_i * 4 + k * 4)
+        elif mode == "full" and wl.get("pool_full"):
             b += n_q * 9 * d_i * 2                               # block-key refresh: 8 keys in, 1 out
             b += scan_bytes(wl) + n_q * wl["keep_blocks"] * 4    # block scan -> pool
-            b += sum(min(L, 8 * wl["keep_blocks"]) for L in wl["lengths"]) * d_i * 2
+            b += sum(min(L, 8 * wl["keep_blocks"]) for L in nvis) * d_i * 2
             b += n_q * (h_i * d_i * 2 + h_i * 4 + k * 4)         # pool re-scored with the Full query
         elif mode == "full":
             b += scan_bytes(wl) + n_q * k * 4 + (n_q * wl["keep_blocks"] * 4)
         elif mode == "reindex":
-            b += sum(min(L, 8 * wl["keep_blocks"]) for L in wl["lengths"]) * d_i * 2
+            b += sum(min(L, 8 * wl["keep_blocks"]) for L in nvis) * d_i * 2
             b += n_q * (h_i * d_i * 2 + h_i * 4 + wl["keep_blocks"] * 4 + k * 4)
-        # attention: selected records, window rows, q in, out
-        b += sum(min(k, L) * 288 + min(W, L) * 1024 for L in wl["lengths"])
+        # attention: selected records and window rows, q in, out
+        b += sum(min(k, L) * 288 for L in nvis)
+        b += (n_q + W - 1) * 1024 if wl.get("swa_shared") else sum(min(W, L) * 1024 for L in nvis)
         b += n_q * h * 512 * (qb + 4)
     return b
 
@@ -142,6 +161,52 @@ def traffic_from_profile(kernel_sha):
     if not m_sha or not m_b or m_sha.group(1) != kernel_sha:
         return None
     return float(m_b.group(1))
+
+
+def cpu_baseline_chunk(wl, st, layers, dev, nq, gpu_results):
+    """Time the CPU oracle on `nq` queries spread over the encoder chunk (all
+    its layers, the same inputs); the sample's indices and outputs are checked
+    against the timed GPU step's."""
+    import numpy as np
+    import torch
+
+    import csa2_inputs as gen
+    import oracle
+    from oracle.step import decode_step as oracle_step
+
+    bits = gen.bf16_bits
+    n = wl["n_q"]
+    sel = np.unique(np.linspace(0, n - 1, nq).astype(np.int64))
+    ts = torch.from_numpy(sel).to(dev)
+    host = lambda t: t.cpu().numpy() if t.dtype != torch.bfloat16 else bits(t)
+    hl = []
+    for li, lay in enumerate(layers):
+        hl.append(dict(mode=lay.mode, q=host(lay.q[ts]), swa=bits(lay.swa), swa_row0=host(lay.swa_row0[ts]),
+                       swa_len=host(lay.swa_len[ts])))
+        if lay.iq is not None:
+            hl[-1]["iq"], hl[-1]["w"] = bits(lay.iq[ts]), host(lay.w[ts])
+    threads = max(1, min(16, os.cpu_count() or 1))
+    oracle.lib()
+
+    def raw_rows(rows):
+        x = gen.kv_rows_at(wl, rows, dev)
+        return x.cpu().numpy() if x.dtype == torch.float32 else bits(x)
+
+    res, _, secs = oracle_step(hl, bits(st.ik), np.asarray(wl["seq_base"], np.int64),
+                               np.asarray(wl["q_seq"], np.int32)[sel], np.asarray(wl["q_nvis"], np.int32)[sel],
+                               wl["k"], 0, wl["block"], raw_rows, None, st.softmax_scale, n_threads=threads)
+    idx_ok, err = True, 0.0
+    for (gidx, gout, _), (ridx, rout, _) in zip(gpu_results, res):
+        idx_ok &= bool(np.array_equal(gidx[ts].cpu().numpy(), ridx))
+        o = gout[ts].cpu().numpy()
+        den = np.abs(rout).max(axis=-1)
+        den[den == 0] = 1
+        err = max(err, float((np.abs(o - rout).max(axis=-1) / den).max()))
+    ql = len(sel) * len(wl["layers"])
+    return ({"value": ql / secs, "unit": "query·layers/s", "cores": threads, "kind": "oracle",
+             "sample": f"{len(sel)} of {n} chunk queries (spread over the chunk), all {len(wl['layers'])} layers "
+                       f"= {ql} query-layers in {secs:.2f} s"},
+            {"idx_bitexact": idx_ok, "attn_max_normwise_err": err, "queries": int(len(sel))})
 
 
 def cpu_baseline(wl, st, layers, app_x, dev, nseq, gpu_results):
@@ -296,7 +361,16 @@ def main():
     value = ql_per_step / (ms * 1e-3)
 
     roofline = None
-    if has_full:
+    if has_full and wl.get("chunk"):
+        # the encoder chunk's scan is a dense causal contraction: MFMA-bound
+        scan_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / K
+        fl = chunk_flops(wl)
+        achieved = fl / (scan_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "k_scan_chunk (encoder-chunk indexer scan, bf16 MFMA)",
+                    "achieved": round(achieved, 1), "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
+                    "algorithmic_flops_per_launch": fl, "launch_ms": round(scan_ms, 5)}
+    elif has_full:
         scan_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / K
         sb = scan_bytes(wl)
         achieved = sb / (scan_ms * 1e-3) / 1e9
@@ -313,11 +387,14 @@ def main():
     cpu = None
     parity = None
     if a.cpu_baseline == "auto":
-        nseq = a.cpu_seqs or {"c1": 1, "c2": 8, "c3": 4, "c5": 2}[a.workload]
-        log(f"cpu baseline: oracle on {nseq} sequence(s)")
+        nseq = a.cpu_seqs or {"c1": 1, "c2": 8, "c3": 4, "c4": 8, "c5": 2}[a.workload]
+        log(f"cpu baseline: oracle on {nseq} sequence(s) or chunk queries")
         gres, _ = step(keep=True)
         torch.cuda.synchronize()
-        cpu, parity = cpu_baseline(wl, st, layers, app_x, dev, nseq, gres)
+        if wl.get("chunk"):
+            cpu, parity = cpu_baseline_chunk(wl, st, layers, dev, nseq, gres)
+        else:
+            cpu, parity = cpu_baseline(wl, st, layers, app_x, dev, nseq, gres)
         log(f"cpu baseline {cpu['value']:.3f} q.l/s; sample parity {parity}")
 
     line = {

@@ -223,3 +223,21 @@ def test_mfma_scores_within_proven_bound():
     ratio = np.abs(approx - exact) / bound
     print(f"max |mfma - exact| / bound = {ratio.max():.3e}")
     assert np.all(np.abs(approx - exact) <= bound)
+
+
+@gpu
+@pytest.mark.parametrize("n_q,L,chunk", [(1, 3000, 1024), (8, 131072 // 16, 1024), (40, 30000, 2048),
+                                         (64, 32768, 4096), (4, 1 << 20, 8192)])
+def test_full_with_pool_at_every_scan_chunk_size(n_q, L, chunk):
+    # the scan's keys per work-group follow the batch shape (8192 down to 1024,
+    # keeping at least 512 work-groups); each shape here selects the size named,
+    # with the pool and ragged lengths (every 3rd sequence is shorter)
+    note(f"full + pool, scan chunk {chunk}: n_q={n_q} L={L}")
+    lengths = [L if i % 3 else max(1, L - 4093 * (i + 1)) for i in range(n_q)]
+    h_i, d_i = (4, 64) if L * n_q >= (1 << 20) else (64, 128)   # oracle work within seconds
+    inp = index_inputs(lengths, h_i, d_i, seed=500 + n_q)
+    keep = 2048 if L > 16384 else 256
+    got_idx, got_pool = _gpu_full(inp, 512, keep_blocks=keep)
+    ref_idx, ref_pool = _ref_full(inp, 512, keep_blocks=keep)
+    assert np.array_equal(got_pool, ref_pool)
+    assert np.array_equal(got_idx, ref_idx)
