@@ -1981,6 +1981,15 @@ int scan_chunk_for(int n_q, int64_t max_nvis) {
   return chunk;
 }
 
+// Pool slots per Reindex scan work-group: 256, doubled up to 2048 while that
+// still leaves at least 512 work-groups (large batches amortise each
+// work-group's query load and bound setup over more keys).
+int reindex_chunk_for(int n_q, int64_t slots) {
+  int chunk = 256;
+  while (chunk < 2048 && (int64_t)n_q * ((slots + 2 * chunk - 1) / (2 * chunk)) >= 512) chunk <<= 1;
+  return chunk;
+}
+
 thread_local int g_last_hip_error = 0;
 thread_local hipEvent_t g_scan_ev_start = nullptr;
 thread_local hipEvent_t g_scan_ev_stop = nullptr;
@@ -2244,8 +2253,8 @@ extern "C" csa2_status csa2_reindex_topk(const uint16_t* iq, const float* w, int
   P.idx_out = idx_out; P.pool_out = nullptr;
   P.nprob = n_q;
   P.reindex = 1;
-  P.scan_chunk = 256;
   const int64_t slots = 8LL * keep_blocks;
+  P.scan_chunk = reindex_chunk_for(n_q, slots);
   P.stride = round_up(slots, kCmpChunk);
   P.nchunk_cmp = (int)(P.stride / kCmpChunk);
   const size_t need = csa2_reindex_topk_ws_bytes(n_q, h_i, d_i, k, block, keep_blocks);

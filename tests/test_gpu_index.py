@@ -241,3 +241,26 @@ def test_full_with_pool_at_every_scan_chunk_size(n_q, L, chunk):
     ref_idx, ref_pool = _ref_full(inp, 512, keep_blocks=keep)
     assert np.array_equal(got_pool, ref_pool)
     assert np.array_equal(got_idx, ref_idx)
+
+
+@gpu
+@pytest.mark.parametrize("n_q,chunk", [(4, 256), (20, 512), (40, 1024), (80, 2048)])
+def test_reindex_at_every_scan_chunk_size(n_q, chunk):
+    # the Reindex scan's pool slots per work-group grow with the batch (256 up
+    # to 2048 while at least 512 work-groups remain); each batch here selects
+    # the size named (pools of 2048 blocks, ragged lengths)
+    note(f"reindex, scan chunk {chunk}: n_q={n_q}")
+    lengths = [20000 - 37 * i for i in range(n_q)]
+    inp = index_inputs(lengths, 4, 64, seed=600 + n_q)
+    _, pool = _ref_full(inp, 512, keep_blocks=2048)
+    rng = np.random.default_rng(601)
+    iq2 = torch.from_numpy(rng.standard_normal(inp["iq"].shape).astype(np.float32)).to(torch.bfloat16)
+    w2 = torch.from_numpy(rng.uniform(0, 1, inp["w"].shape).astype(np.float32))
+    dev = device()
+    d = to_dev(inp, dev)
+    got = csa2.reindex_topk(iq2.to(dev), w2.to(dev), d["q_seq"], d["nvis"], d["ik"], d["seq_base"],
+                            torch.from_numpy(pool).to(dev), k=512)
+    torch.cuda.synchronize()
+    ref = oracle.reindex_topk(bits(iq2), w2.numpy(), inp["q_seq"].numpy(), inp["nvis"].numpy(), bits(inp["ik"]),
+                              inp["seq_base"].numpy(), pool, 512, block=8)
+    assert np.array_equal(got.cpu().numpy(), ref)
