@@ -340,26 +340,32 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run, mx);
+      // The running reference m_run moves only when a score exceeds it by more
+      // than 8 (base 2): otherwise P = 2^(z - m_run) <= 256, still exact to
+      // fp16's relative precision, and O and l keep their reference (the
+      // softmax, and the merge of splits by their (m, l), do not depend on
+      // which reference is used).  So the costly rescale of O is rare.
+      const bool bump = mx > m_run + 8.0f;   // true on the first key (m_run = -inf)
+      const float m_use = bump ? mx : m_run;
       float alpha, pv[8];
-      if (m_new == -INFINITY) {
+      if (m_use == -INFINITY) {
         alpha = 1.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) pv[j] = 0.0f;
       } else {
-        alpha = exp2f(m_run - m_new);
+        alpha = bump ? exp2f(m_run - m_use) : 1.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = exp2f(z[j] - m_new);
+        for (int j = 0; j < 8; ++j) pv[j] = exp2f(z[j] - m_use);
       }
       float ps = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) ps += pv[j];
       l_run = l_run * alpha + ps;
       // rescale O rows (heads 4*g + i live in this lane's accumulators); a
-      // wave whose maxima did not move, or whose O is still zero (no key seen
-      // yet), skips it
-      const bool rescale = alpha != 1.0f && m_run != -INFINITY;
-      m_run = m_new;
+      // wave whose references did not move, or whose O is still zero (no key
+      // seen yet), skips it
+      const bool rescale = bump && m_run != -INFINITY;
+      m_run = m_use;
       if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
         float a4[4];
 #pragma unroll
