@@ -13,7 +13,8 @@
 //
 // How (one pass over the keys at HBM speed, exact result):
 //  1. k_prologue   zeroes the problem's histograms and Meta.
-//  2. k_scan       streams the indexer keys once (8192 keys per work-group,
+//  2. k_scan       streams the indexer keys once (up to 8192 keys per
+//                  work-group, fewer when that keeps 512 work-groups busy;
 //                  NBUF - 1 groups of 16 keys per wave in flight ahead of the
 //                  math, scores staged in LDS and written once at the end).
 //                  Scores come from bf16 MFMA
@@ -52,8 +53,9 @@
 // Degenerate inputs (ties everywhere) only make the band large; the result
 // stays exact.
 // A Reindex pool of at most 16,384 slots skips steps 1 and 3-6: its scan keeps
-// each work-group's key-norm maximum instead of histograms, and one work-group
-// per query (section 7) selects from the scores it holds in registers.
+// each work-group's largest key magnitude t_k instead of histograms, and one
+// work-group per query (section 7) selects from the scores it holds in
+// registers.
 #include "csa2_device.h"
 
 #include <algorithm>
@@ -426,7 +428,7 @@ __device__ uint32_t wg_coarse_bin(const Params& P, int p, const uint32_t hv[kHPe
   uint32_t tot;
   const uint32_t above = wg_exclusive_scan(loc, s_tmp, &tot);
   if (publish && tid == 0) {
-    // the token problem's scan holds the key-norm maximum; blocks use it too
+    // the token problem's scan holds the largest t_k; blocks use it too
     const float bound = kind == 1 ? P.bound_blk : P.bound_tok;
     P.meta[p].delta = bound * maxt * (1.0f + 0.0009765625f) + wabs * (float)P.d_i * 7.8886e-31f;
     P.meta[p].total = tot;
@@ -455,9 +457,9 @@ __device__ uint32_t wg_coarse_bin(const Params& P, int p, const uint32_t hv[kHPe
 // ---------------------------------------------------------------- 2. scan
 // POOL: also score the 8-position blocks (Full layers building a pool).
 // INDIRECT: candidates are the slots of a pool (Reindex layers).
-// HIST: build the coarse score histograms (and the key-norm maximum) that the
+// HIST: build the coarse score histograms (and the largest t_k) that the
 // multi-kernel selection uses; without it the scan records each work-group's
-// key-norm maximum for the single-work-group selection.
+// largest t_k for the single-work-group selection.
 template <int D, int MT, bool POOL, bool INDIRECT, bool HIST>
 __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   constexpr int KS = D / 32;   // MFMA k-steps; also 16-byte loads per lane per key
@@ -651,7 +653,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   for (int b = 0; b < NBUF - 1; ++b)
     if (it + b < my_groups) process(it + b, buf[b]);
 
-  // ---- publish scores, histograms and the key-norm maximum
+  // ---- publish scores, histograms and the largest t_k
   lds_barrier();
   for (int i = tid; i < nslots; i += kThreads) sc[c0 + i] = s_sc[i];
   if constexpr (POOL) {
@@ -857,7 +859,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_chunk(Params P) {   // two
   for (int b = 0; b < NBUF - 1; ++b)
     if (it + b < my_groups) process(it + b, buf[b]);
 
-  // ---- publish: each query's scores and histogram, the key-norm maximum
+  // ---- publish: each query's scores and histogram, the largest t_k
   lds_barrier();
 #pragma unroll
   for (int qq = 0; qq < QB; ++qq) {

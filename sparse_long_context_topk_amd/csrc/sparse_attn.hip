@@ -63,7 +63,7 @@ struct Params {
   float scale_log2;
   float* out;
   float* lse;
-  int nsplit, sub_per_split, nsub;
+  int nsplit, nsub;
   float* part_o;   // [n_q][nsplit][h][512]
   float* part_ml;  // [n_q][nsplit][h][2]
 };
@@ -592,7 +592,7 @@ csa2_status attn_call(const void* q, int q_dtype, int n_q, int h, int d, const i
   P.swa_new = swa_new; P.swa_dst = swa_dst; P.swa_out = const_cast<uint16_t*>(swa); P.swa_rows = swa_rows;
   P.scale_log2 = softmax_scale * kLog2e;
   P.out = out; P.lse = lse;
-  P.nsplit = s.nsplit; P.sub_per_split = s.per; P.nsub = s.nsub;
+  P.nsplit = s.nsplit; P.nsub = s.nsub;
   char* w = static_cast<char*>(ws);
   P.part_o = reinterpret_cast<float*>(w);
   P.part_ml = reinterpret_cast<float*>(w + align256((size_t)n_q * s.nsplit * h * 512 * sizeof(float)));
