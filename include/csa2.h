@@ -171,6 +171,29 @@ csa2_status csa2_reindex_topk(const uint16_t* iq, const float* w, int n_q, int h
 size_t csa2_reindex_topk_ws_bytes(int n_q, int h_i, int d_i, int k, int block, int keep_blocks);
 
 /* ------------------------------------------------------------------------
+ * csa2_topk_merge -- exact Top-K of each query among given candidate
+ * positions: the merge step of one context split over several devices.  Each
+ * device runs csa2_index_topk on its position range and keeps its local
+ * Top-K; the global Top-K lies in the union of the local ones and a
+ * position's score does not depend on the device that computes it (defined to
+ * the bit per (query, key)), so the exact Top-K among the union is the whole
+ * context's (source as for csa2_index_topk: Top-512 by (score, position)).
+ *   cand     [n_q][n_cand] positions of query i's sequence, ascending and
+ *            distinct, -1 padded at the end (e.g. the shards' lists, each
+ *            offset to global positions, concatenated in shard order)
+ *   iq, w, h_i, d_i, q_seq, ik, seq_base, k: as csa2_index_topk
+ *   idx_out  [n_q][k]: the k candidates with the largest scores (ties: lower
+ *            position), ascending, -1 padded
+ * ws: csa2_topk_merge_ws_bytes(n_q, n_cand, h_i, d_i, k) bytes (the
+ * candidates' keys are gathered there, then selected as by csa2_index_topk).
+ * Supported: as csa2_index_topk; n_cand <= 2^25, n_q <= 65535. */
+csa2_status csa2_topk_merge(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
+                            const int32_t* q_seq, const uint16_t* ik, const int64_t* seq_base,
+                            const int32_t* cand, int n_cand, int k, int32_t* idx_out, void* ws,
+                            size_t ws_bytes, void* stream);
+size_t csa2_topk_merge_ws_bytes(int n_q, int n_cand, int h_i, int d_i, int k);
+
+/* ------------------------------------------------------------------------
  * csa2_block_keys -- stored block keys for the pool-based Full variant: a
  * Full layer that picks its Top-512 inside its own pool (the hierarchical
  * indexer's blocks of 8 positions, at most 2048 kept; source as above,

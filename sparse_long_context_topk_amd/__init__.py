@@ -71,6 +71,10 @@ def lib():
                                               vp, vp, f32, vp, vp, vp, sz, vp]
         L.csa2_sparse_attn_ws_bytes.restype = sz
         L.csa2_sparse_attn_ws_bytes.argtypes = [i32, i32, i32, i32]
+        L.csa2_topk_merge.restype = i32
+        L.csa2_topk_merge.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
+        L.csa2_topk_merge_ws_bytes.restype = sz
+        L.csa2_topk_merge_ws_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.csa2_window_append.restype = i32
         L.csa2_window_append.argtypes = [vp, i32, i64, vp, vp, i64, vp]
         L.csa2_block_keys.restype = i32
@@ -226,6 +230,28 @@ def index_topk_chunk(iq, w, q_nvis, max_nvis, ik, ik_base=0, k=512, idx_out=None
     st = lib().csa2_index_topk_chunk(_ptr(iq), _ptr(w), n_q, h_i, d_i, _ptr(q_nvis), int(max_nvis), _ptr(ik),
                                      int(ik_base), k, _ptr(idx_out), _ptr(buf), buf.numel(), _stream(dev))
     _check(st, "csa2_index_topk_chunk")
+    return idx_out
+
+
+def topk_merge(iq, w, q_seq, ik, seq_base, cand, k=512, idx_out=None, ws=None):
+    """Exact Top-K of each query among candidate positions cand [n_q,n_cand] int32
+    (ascending, distinct, -1 padded at the end), e.g. the concatenated local Top-K
+    lists of a context's shards.  Returns idx [n_q,k] int32."""
+    _need(iq, torch.bfloat16, "iq")
+    n_q, h_i, d_i = iq.shape
+    _need(w, torch.float32, "w")
+    _need(q_seq, torch.int32, "q_seq")
+    _need(ik, torch.bfloat16, "ik")
+    _need(seq_base, torch.int64, "seq_base")
+    _need(cand, torch.int32, "cand")
+    n_cand = cand.shape[1] if cand.dim() == 2 else 0
+    dev = iq.device
+    if idx_out is None:
+        idx_out = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    buf = _ws(dev, lib().csa2_topk_merge_ws_bytes(n_q, max(n_cand, 1), h_i, d_i, k), ws)
+    st = lib().csa2_topk_merge(_ptr(iq), _ptr(w), n_q, h_i, d_i, _ptr(q_seq), _ptr(ik), _ptr(seq_base), _ptr(cand),
+                               n_cand, k, _ptr(idx_out), _ptr(buf), buf.numel(), _stream(dev))
+    _check(st, "csa2_topk_merge")
     return idx_out
 
 

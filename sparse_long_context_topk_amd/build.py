@@ -8,7 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcsa2.so")
-SOURCES = ["api.hip", "quant_append.hip", "block_keys.hip", "window_append.hip", "index_topk.hip", "sparse_attn.hip"]
+SOURCES = ["api.hip", "quant_append.hip", "block_keys.hip", "window_append.hip", "index_topk.hip", "topk_merge.hip", "sparse_attn.hip"]
 HEADERS = ["csa2_device.h", os.path.join("..", "..", "include", "csa2.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -8,6 +8,7 @@ extern "C" int csa2_internal_last_hip_error_attn(void);
 extern "C" int csa2_internal_last_hip_error_quant(void);
 extern "C" int csa2_internal_last_hip_error_blocks(void);
 extern "C" int csa2_internal_last_hip_error_window(void);
+extern "C" int csa2_internal_last_hip_error_merge(void);
 
 extern "C" const char* csa2_status_string(csa2_status s) {
   switch (s) {
@@ -26,5 +27,6 @@ extern "C" int csa2_last_hip_error(void) {
   if (!e) e = csa2_internal_last_hip_error_quant();
   if (!e) e = csa2_internal_last_hip_error_blocks();
   if (!e) e = csa2_internal_last_hip_error_window();
+  if (!e) e = csa2_internal_last_hip_error_merge();
   return e;
 }

@@ -132,3 +132,15 @@ def test_attention_append_argument_checks():
     assert ap(new=None) == 1 and ap(dst=None) == 1 and ap(swa=None) == 1 and ap(rows=-1) == 1
     assert ap(new=ctypes.c_void_p((1 << 20) + 8)) == 1 and ap(dst=ctypes.c_void_p((1 << 20) + 4)) == 1
     assert ap() == 3   # every check passes but the (zero) workspace: nothing is enqueued
+
+
+def test_topk_merge_argument_checks():
+    L = csa2.lib()
+    mg = lambda **kw: L.csa2_topk_merge(FAKE, FAKE, kw.get("n_q", 2), 64, kw.get("d", 128), FAKE, kw.get("ik", FAKE),
+                                        FAKE, kw.get("cand", FAKE), kw.get("nc", 1024), kw.get("k", 512), FAKE,
+                                        FAKE, kw.get("ws", 0), None)
+    assert mg(d=100) == 2 and mg(nc=(1 << 25) + 1) == 2
+    assert mg(k=0) == 1 and mg(k=4096) == 1 and mg(nc=-1) == 1 and mg(cand=None) == 1
+    assert mg(ik=ctypes.c_void_p((1 << 20) + 8)) == 1
+    assert mg() == 3 and mg(n_q=0) == 0
+    assert L.csa2_topk_merge_ws_bytes(2, 1024, 64, 128, 512) > 2 * 1024 * 128 * 2

@@ -354,3 +354,23 @@ def test_pool_full_matches_brute_force():
     pos = np.array([8 * b + o for b in ref_pool if b >= 0 for o in range(8) if 8 * b + o < 777])
     tsc = [oracle.index_score(iq[1], w[1], ik[sb[1] + p]) for p in pos]
     assert np.array_equal(idx[0], _brute_topk(tsc, k, pos))
+
+
+def test_sharded_topk_merge_equals_full_context():
+    # a context split into position ranges: the Top-K among the union of the
+    # shards' local Top-Ks (rescored, positions kept) is the whole context's
+    # Top-K, ties included (the score of a position does not depend on the
+    # shard).  Brute-force merge over the oracle's own per-shard selections.
+    iq, w, qs, nv, ik, sb = _inputs(1, 5000, seed=24)
+    ik[1000:1500] = ik[3000:3500]                       # ties across shards
+    full = oracle.index_topk(iq, w, qs, nv, ik, sb, 512)[0]
+    for G in (2, 3, 7):
+        edges = np.linspace(0, 5000, G + 1).astype(int)
+        cand = []
+        for a, b in zip(edges[:-1], edges[1:]):
+            loc = oracle.index_topk(iq, w, np.zeros(1, np.int32), np.array([b - a], np.int32), ik[a:b],
+                                    np.zeros(1, np.int64), 512)[0]
+            cand.extend(int(a + p) for p in loc if p >= 0)
+        cand = np.array(cand, np.int32)
+        sc = [oracle.index_score(iq[0], w[0], ik[p]) for p in cand]
+        assert np.array_equal(oracle.topk(np.array(sc, np.float32), 512, cand), full)
