@@ -28,6 +28,12 @@
 // is exactly the A-operand layout P needs, so P never moves between lanes.
 // An online softmax (base-2 exponent, running max per head) carries across
 // sub-tiles; splits are merged by k_merge with their (max, sum) pairs.
+//
+// Two kernels share this scheme: k_attn2 (bf16 queries) gives the loads and
+// the decode to four waves of their own, so they overlap the multiply waves'
+// MFMA work; k_attn<true> (fp32 queries, which carry a second fp16 term per
+// channel and need the registers) runs both in its four waves, one after the
+// other.
 #include "csa2_device.h"
 
 namespace csa2 {
@@ -460,6 +466,359 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
   }
 }
 
+// ---------------------------------------------------------------- large batches
+// k_attn2: the bf16-query kernel.  k_attn's four waves decode a sub-tile and
+// then multiply it, in series, and its LDS leaves one work-group per CU.  Here
+// a work-group has eight waves: waves 0-3 multiply exactly as k_attn's (16
+// heads each, the same MFMA and online softmax code), waves 4-7 only load and
+// decode: while the multiply waves work on sub-tile j, the decode waves write
+// sub-tile j + 1 into the other LDS buffer, with the loads of j + 2 and j + 3
+// in flight.  One barrier per sub-tile; two waves per SIMD.
+constexpr int kStages = 2;   // sub-tiles whose loads the decode waves keep in flight (3 or 4 time the same)
+__global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
+  __shared__ __attribute__((aligned(16))) _Float16 s_k[2][kSub * kKRow];
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[2][512 * kVRow];
+  __shared__ uint32_t s_valid[2][kSub];
+  __shared__ int32_t s_pos[kMaxSlotsWG];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int qi = blockIdx.x, split = blockIdx.y;
+  const bool mwave = wave < 4;   // multiply waves; waves 4-7 decode
+  const bool head_wave = mwave && 16 * wave < P.h;
+  const int head = 16 * wave + n;
+  const int64_t cbase = P.seq_base[P.q_seq[qi]];
+  const int k = P.k;
+  const int nswa = P.swa_len ? P.swa_len[qi] : 0;
+  const int64_t srow0 = nswa ? P.swa_row0[qi] : 0;
+  const int64_t wdst = P.swa_new ? P.swa_dst[qi] : -1;   // this call's new window row of the query
+  auto win_src = [&](int64_t row, int cgi) -> const uint16_t* {
+    return row == wdst ? P.swa_new + (size_t)qi * 512 + 8 * cgi : P.swa + (size_t)row * 512 + 8 * cgi;
+  };
+  if (wdst >= 0 && wdst < P.swa_rows && split == 0 && tid < 64)
+    reinterpret_cast<uint4*>(P.swa_out + (size_t)wdst * 512)[tid] =
+        reinterpret_cast<const uint4*>(P.swa_new + (size_t)qi * 512)[tid];
+  const int ns = P.nsplit;
+  const int nmine = split < P.nsub ? (P.nsub - split + ns - 1) / ns : 0;
+  const uint8_t* fb = static_cast<const uint8_t*>(P.q);
+  for (int i = tid; i < nmine * kSub; i += 2 * kThreads) {
+    const int slot = (split + (i / kSub) * ns) * kSub + (i % kSub);
+    if (slot < k) s_pos[i] = P.idx[(size_t)qi * k + slot];
+  }
+
+  // The two roles run separate loops (their registers are never live at the
+  // same time); both pass one barrier after the prologue and one per sub-tile.
+  if (!mwave) {
+    // decode assignment as k_attn's: thread -> key slots 8*kq .. 8*kq+7,
+    // channels 8*cg .. 8*cg+7
+    const int dt = tid - kThreads;
+    const int kq = dt & 3, cg = dt >> 2;
+  // Global loads of a sub-tile, one loader per slot class.  Addresses of
+  // empty slots point at the fallback bytes, so no load is conditional.
+  auto load_sel_pos = [&](Stage& st, const int pos[8]) {   // all 32 slots are selected entries
+    st.valid = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const uint8_t* rec = pos[jj] >= 0 ? P.cache + (size_t)(cbase + pos[jj]) * CSA2_KV_RECORD_BYTES : fb;
+      st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
+      st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * (cg >> 3));
+      st.valid |= (pos[jj] >= 0 ? 1u : 0u) << jj;
+    }
+  };
+  auto load_sel = [&](Stage& st, int j) {        // local sub-tile j; positions from the LDS copy of the index list
+    const int i0 = j * kSub + 8 * kq;   // multiple of 8: two 16-byte LDS reads
+    const int4 pa = *reinterpret_cast<const int4*>(&s_pos[i0]);
+    const int4 pb = *reinterpret_cast<const int4*>(&s_pos[i0 + 4]);
+    const int pos[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    load_sel_pos(st, pos);
+  };
+  auto load_win = [&](Stage& st, int sub) {      // all 32 slots are window rows (or past the window)
+    const int r0 = sub * kSub + 8 * kq - k;
+    st.valid = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const bool ok = r0 + jj < nswa;
+      const uint16_t* src =
+          ok ? win_src(srow0 + r0 + jj, cg) : reinterpret_cast<const uint16_t*>(fb) + 8 * cg;
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
+      st.valid |= (ok ? 1u : 0u) << jj;
+    }
+  };
+  auto load_mixed = [&](Stage& st, int sub) {    // the one sub-tile that straddles slot k
+    const int slot0 = sub * kSub + 8 * kq;
+    st.valid = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int slot = slot0 + jj;
+      st.w[jj][0] = st.w[jj][1] = st.w[jj][2] = st.w[jj][3] = 0u;
+      if (slot < k) {
+        const int pos = P.idx[(size_t)qi * k + slot];
+        if (pos >= 0) {
+          const uint8_t* rec = P.cache + (size_t)(cbase + pos) * CSA2_KV_RECORD_BYTES;
+          st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
+          st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * (cg >> 3));
+          st.valid |= 1u << jj;
+        }
+      } else if (slot - k < nswa) {
+        const uint4 v = *reinterpret_cast<const uint4*>(win_src(srow0 + slot - k, cg));
+        st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
+        st.valid |= 1u << jj;
+      }
+    }
+  };
+
+    auto load_first = [&](Stage& st, int sub) {   // positions straight from the index list
+      const int kind = sub_kind(sub * kSub, k);
+      if (kind == 0) {
+        const int32_t* ip = P.idx + (size_t)qi * k + sub * kSub + 8 * kq;
+        int pos[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) pos[jj] = ip[jj];
+        load_sel_pos(st, pos);
+      } else if (kind == 1) {
+        load_win(st, sub);
+      } else {
+        load_mixed(st, sub);
+      }
+    };
+    auto load_next = [&](Stage& st, int j) {   // local sub-tile j >= 2 (staged positions readable)
+      const int sub = split + j * ns;
+      const int kind = sub_kind(sub * kSub, k);
+      if (kind == 0) load_sel(st, j);
+      else if (kind == 1) load_win(st, sub);
+      else load_mixed(st, sub);
+    };
+  // Decode the loaded words to fp16 and write both LDS layouts of buffer b.
+  auto store_stage = [&](const Stage& st, int sub, int b) {
+    const int slot0 = sub * kSub;
+    const int sc_shift = 8 * ((cg >> 1) & 3);   // this thread's scale byte in the loaded scale dword
+    uint32_t vals[8][4];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const bool is_sel = slot0 + 8 * kq + jj < k;
+      const uint32_t keep = (st.valid >> jj) & 1u ? 0xFFFFFFFFu : 0u;
+      uint32_t dv[4], sv[4];
+      decode8(st.w[jj][0], (_Float16)e4m3_to_f32((st.w[jj][1] >> sc_shift) & 0xFFu), dv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sv[j] = pack_f16(__uint_as_float(st.w[jj][j] << 16), __uint_as_float(st.w[jj][j] & 0xFFFF0000u));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vals[jj][j] = (is_sel ? dv[j] : sv[j]) & keep;
+      if (cg == 0) s_valid[b][8 * kq + jj] = keep & 1u;
+      *reinterpret_cast<uint4*>(&s_k[b][(8 * kq + jj) * kKRow + 8 * cg]) =
+          make_uint4(vals[jj][0], vals[jj][1], vals[jj][2], vals[jj][3]);
+    }
+    // channel-major copy: row (channel 8*cg + c) gets key slots 8*kq .. 8*kq+7
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int jp = 0; jp < 4; ++jp) {
+        const uint32_t a = vals[2 * jp][c >> 1], bb = vals[2 * jp + 1][c >> 1];
+        // take the low (c even) or high (c odd) fp16 of each
+        pk[jp] = (c & 1) ? __builtin_amdgcn_perm(bb, a, 0x07060302u) : __builtin_amdgcn_perm(bb, a, 0x05040100u);
+      }
+      uint2* dst = reinterpret_cast<uint2*>(&s_v[b][(8 * cg + c) * kVRow + 8 * kq]);
+      dst[0] = make_uint2(pk[0], pk[1]);
+      dst[1] = make_uint2(pk[2], pk[3]);
+    }
+  };
+
+    // sub-tile x's words sit in stg[x % kStages]: the loads of kStages sub-tiles
+    // ahead of the one being decoded stay in flight
+    Stage stg[kStages];
+#pragma unroll
+    for (int x = 0; x < kStages; ++x)
+      if (x < nmine) load_first(stg[x], split + x * ns);
+    if (nmine > 0) store_stage(stg[0], split, 0);
+    lds_barrier();   // s_pos and buffer 0
+    if (nmine > kStages) load_next(stg[0], kStages);
+    for (int j0 = 0; j0 < nmine; j0 += kStages) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) {
+        const int j = j0 + u;
+        if (j < nmine) {   // uniform
+          if (j + 1 < nmine) {
+            Stage& S = stg[(u + 1) % kStages];   // sub-tile j + 1
+            store_stage(S, split + (j + 1) * ns, (j + 1) & 1);   // its buffer was last read before the previous barrier
+            if (j + 1 + kStages < nmine) load_next(S, j + 1 + kStages);
+          }
+          lds_barrier();
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- multiply waves: Q^T as the B operand, lane (head n, group g) holds
+  // channels 32*ks + 8*g .. +7 (rounded to fp16, as k_attn)
+  f16x8 qb[16];
+  if (head_wave) {
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(P.q) +
+                                                      ((size_t)qi * P.h + head) * 512 + 32 * ks + 8 * g);
+      const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qb[ks][2 * e] = (_Float16)__uint_as_float(wd[e] << 16);
+        qb[ks][2 * e + 1] = (_Float16)__uint_as_float(wd[e] & 0xFFFF0000u);
+      }
+    }
+  }
+  f32x4 o[32];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  lds_barrier();   // s_pos and buffer 0
+
+  auto compute = [&](int b) {
+    if (head_wave) {
+      // ---- S^T = K Q^T : lane (head n, g) gets keys 16*kt + 4*g + i
+      // the two key tiles' chains interleaved (independent accumulators); each
+      // k-step's fragments are read one k-step ahead of their MFMAs
+      f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+      const _Float16* krow0 = &s_k[b][n * kKRow + 8 * g];
+      const _Float16* krow1 = &s_k[b][(16 + n) * kKRow + 8 * g];
+      f16x8 n0 = *reinterpret_cast<const f16x8*>(krow0);
+      f16x8 n1 = *reinterpret_cast<const f16x8*>(krow1);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const f16x8 a0 = n0, a1 = n1;
+        if (ks + 1 < 16) {
+          n0 = *reinterpret_cast<const f16x8*>(krow0 + 32 * (ks + 1));
+          n1 = *reinterpret_cast<const f16x8*>(krow1 + 32 * (ks + 1));
+        }
+        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[ks], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[ks], sacc[1], 0, 0, 0);
+      }
+      {
+        constexpr int kM = 2;   // MFMAs per k-step
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int r = 0; r < 15; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);
+      }
+      float z[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * kt + 4 * g + i;
+          const float v = s_valid[b][key] ? sacc[kt][i] * P.scale_log2 : -INFINITY;
+          z[4 * kt + i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      // The running reference m_run moves only when a score exceeds it by more
+      // than 8 (base 2): otherwise P = 2^(z - m_run) <= 256, still exact to
+      // fp16's relative precision, and O and l keep their reference (the
+      // softmax, and the merge of splits by their (m, l), do not depend on
+      // which reference is used).  So the costly rescale of O is rare.
+      const bool bump = mx > m_run + 8.0f;   // true on the first key (m_run = -inf)
+      const float m_use = bump ? mx : m_run;
+      float alpha, pv[8];
+      if (m_use == -INFINITY) {
+        alpha = 1.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = 0.0f;
+      } else {
+        alpha = bump ? exp2f(m_run - m_use) : 1.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = exp2f(z[j] - m_use);
+      }
+      float ps = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ps += pv[j];
+      l_run = l_run * alpha + ps;
+      // rescale O rows (heads 4*g + i live in this lane's accumulators); a
+      // wave whose references did not move, or whose O is still zero (no key
+      // seen yet), skips it
+      const bool rescale = bump && m_run != -INFINITY;
+      m_run = m_use;
+      if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+        float a4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, kWave);
+#pragma unroll
+        for (int t = 0; t < 32; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[t][i] *= a4[i];
+      }
+      // P as the A operand: slots 0..3 = keys 4g+i, slots 4..7 = keys 16+4g+i
+      f16x8 pa;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pa[j] = (_Float16)pv[j];
+      // ---- O += P V  (each V fragment read one MFMA ahead)
+      auto vfrag = [&](int t) {
+        const _Float16* vrow = &s_v[b][(16 * t + n) * kVRow];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * g);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
+        return __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      };
+      f16x8 nv = vfrag(0);
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
+        const f16x8 bv = nv;
+        if (t + 1 < 32) nv = vfrag(t + 1);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, o[t], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int r = 0; r < 30; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+  };
+
+  for (int j = 0; j < nmine; ++j) {
+    if (head_wave) compute(j & 1);
+    lds_barrier();
+  }
+
+  if (!head_wave) return;
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16, kWave);
+  l_tot += __shfl_xor(l_tot, 32, kWave);
+  // per-row (head 4*g + i) values for this lane's accumulators
+  float lrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l_tot, 4 * g + i, kWave);
+  if (P.nsplit == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 16 * wave + 4 * g + i;
+      const float inv = lrow[i] > 0.0f ? 1.0f / lrow[i] : 0.0f;
+      float* dst = P.out + ((size_t)qi * P.h + hh) * 512 + n;
+#pragma unroll
+      for (int t = 0; t < 32; ++t) dst[16 * t] = o[t][i] * inv;
+    }
+    if (P.lse && g == 0)
+      P.lse[(size_t)qi * P.h + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 16 * wave + 4 * g + i;
+      float* dst = P.part_o + (((size_t)qi * P.nsplit + split) * P.h + hh) * 512 + n;
+#pragma unroll
+      for (int t = 0; t < 32; ++t) dst[16 * t] = o[t][i];
+    }
+    if (g == 0) {
+      float* ml = P.part_ml + (((size_t)qi * P.nsplit + split) * P.h + head) * 2;
+      ml[0] = m_run;
+      ml[1] = l_tot;
+    }
+  }
+}
+
 // Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 // One work-group per (query, head); every thread sums two channels over the
 // splits (ascending), its first 32 splits' values loading while the first
@@ -599,7 +958,7 @@ csa2_status attn_call(const void* q, int q_dtype, int n_q, int h, int d, const i
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(n_q, s.nsplit);
   if (q_dtype == CSA2_F32) hipLaunchKernelGGL(k_attn<true>, grid, dim3(kThreads), 0, st, P);
-  else hipLaunchKernelGGL(k_attn<false>, grid, dim3(kThreads), 0, st, P);
+  else hipLaunchKernelGGL(k_attn2, grid, dim3(2 * kThreads), 0, st, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     g_attn_hip_error = (int)e;
