@@ -36,6 +36,8 @@
 // other.
 #include "csa2_device.h"
 
+#include <type_traits>
+
 namespace csa2 {
 namespace attn {
 
@@ -75,15 +77,19 @@ struct Params {
 };
 
 // 8 E2M1 codes (one little-endian dword, channel 2i in the low nibble of byte
-// i) times an fp16 scale -> 4 packed fp16 pairs.  Magnitudes come from a byte
-// table (the fp16 high byte of 0, .5, 1, 1.5, 2, 3, 4, 6; the low byte is 0),
-// the sign bit is moved to bit 15, then one packed fp16 multiply by the scale
-// (exact, see above).
-__device__ __forceinline__ void decode8(uint32_t c, _Float16 sc, uint32_t out[4]) {
-  const uint32_t lut_lo = 0x3E3C3800u, lut_hi = 0x46444240u;
+// i) times an E4M3 scale byte -> 4 packed fp16 pairs.  The scale goes to fp16
+// by moving bits: (b & 0x7F) << 7 read as an fp16 is the E4M3 magnitude times
+// 2^-8 (exponent bias 15 instead of 7, E4M3 subnormals landing on fp16
+// subnormals), so the code magnitudes come from a byte table of the fp16 high
+// bytes of 2^8 x (0, .5, 1, 1.5, 2, 3, 4, 6) (the low byte is 0); the signs go
+// to bit 15, then one packed fp16 multiply.  Both factors are exact in fp16 and
+// so is their product (exact, see above).
+__device__ __forceinline__ void decode8(uint32_t c, uint32_t sbyte, uint32_t out[4]) {
+  const uint32_t lut_lo = 0x5E5C5800u, lut_hi = 0x66646260u;
   uint32_t ev = __builtin_amdgcn_perm(lut_hi, lut_lo, c & 0x07070707u) | ((c << 4) & 0x80808080u);
   uint32_t od = __builtin_amdgcn_perm(lut_hi, lut_lo, (c >> 4) & 0x07070707u) | (c & 0x80808080u);
-  const f16x2 s2 = {sc, sc};
+  const uint32_t sb = ((sbyte & 0x7Fu) << 7) | ((sbyte & 0x80u) << 8);
+  const f16x2 s2 = __builtin_bit_cast(f16x2, sb | (sb << 16));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     // result bytes: 0, even byte i, 0, odd byte i  (selector 0x0C yields 0x00)
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
       const bool is_sel = slot0 + 8 * kq + jj < k;
       const uint32_t keep = (st.valid >> jj) & 1u ? 0xFFFFFFFFu : 0u;
       uint32_t dv[4], sv[4];
-      decode8(st.w[jj][0], (_Float16)e4m3_to_f32((st.w[jj][1] >> sc_shift) & 0xFFu), dv);
+      decode8(st.w[jj][0], (st.w[jj][1] >> sc_shift) & 0xFFu, dv);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         sv[j] = pack_f16(__uint_as_float(st.w[jj][j] << 16), __uint_as_float(st.w[jj][j] & 0xFFFF0000u));
@@ -473,7 +479,12 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
 // heads each, the same MFMA and online softmax code), waves 4-7 only load and
 // decode: while the multiply waves work on sub-tile j, the decode waves write
 // sub-tile j + 1 into the other LDS buffer, with the loads of j + 2 and j + 3
-// in flight.  One barrier per sub-tile; two waves per SIMD.
+// in flight.  One barrier per sub-tile; two waves per SIMD.  A SIMD's two
+// waves share its VALU issue and the CU's LDS, which bound a sub-tile (about
+// 5k cycles, a fifth of it MFMA work), so the decode is kept lean: a
+// sub-tile's slot class is known before its decode and picks a decode without
+// the other class's work, the FP4 scale is decoded by moving bits, and a
+// gather address is one multiply-add from a per-thread base.
 constexpr int kStages = 2;   // sub-tiles whose loads the decode waves keep in flight (3 or 4 time the same)
 __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
   __shared__ __attribute__((aligned(16))) _Float16 s_k[2][kSub * kKRow];
@@ -513,60 +524,65 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
     // channels 8*cg .. 8*cg+7
     const int dt = tid - kThreads;
     const int kq = dt & 3, cg = dt >> 2;
-  // Global loads of a sub-tile, one loader per slot class.  Addresses of
-  // empty slots point at the fallback bytes, so no load is conditional.
-  auto load_sel_pos = [&](Stage& st, const int pos[8]) {   // all 32 slots are selected entries
-    st.valid = 0;
+    // Global loads of a sub-tile, one loader per slot class.  Addresses of
+    // empty slots point at the fallback bytes, so no load is conditional.
+    // cq: this thread's codes dword in the query's first record (fq: in the
+    // fallback bytes); sdist: the distance from it to its scale dword
+    const uint8_t* const cq = P.cache + (size_t)cbase * CSA2_KV_RECORD_BYTES + 4 * cg;
+    const uint8_t* const fq = fb + 4 * cg;
+    const int64_t sdist = 256 + 4 * (cg >> 3) - 4 * cg;
+    auto load_sel_pos = [&](Stage& st, const int pos[8]) {   // all 32 slots are selected entries
+      st.valid = 0;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const uint8_t* rec = pos[jj] >= 0 ? P.cache + (size_t)(cbase + pos[jj]) * CSA2_KV_RECORD_BYTES : fb;
-      st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
-      st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * (cg >> 3));
-      st.valid |= (pos[jj] >= 0 ? 1u : 0u) << jj;
-    }
-  };
-  auto load_sel = [&](Stage& st, int j) {        // local sub-tile j; positions from the LDS copy of the index list
-    const int i0 = j * kSub + 8 * kq;   // multiple of 8: two 16-byte LDS reads
-    const int4 pa = *reinterpret_cast<const int4*>(&s_pos[i0]);
-    const int4 pb = *reinterpret_cast<const int4*>(&s_pos[i0 + 4]);
-    const int pos[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-    load_sel_pos(st, pos);
-  };
-  auto load_win = [&](Stage& st, int sub) {      // all 32 slots are window rows (or past the window)
-    const int r0 = sub * kSub + 8 * kq - k;
-    st.valid = 0;
+      for (int jj = 0; jj < 8; ++jj) {
+        const uint8_t* rc = pos[jj] >= 0 ? cq + (uint64_t)(uint32_t)pos[jj] * CSA2_KV_RECORD_BYTES : fq;
+        st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rc);
+        st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rc + sdist);
+        st.valid |= (pos[jj] >= 0 ? 1u : 0u) << jj;
+      }
+    };
+    auto load_sel = [&](Stage& st, int j) {        // local sub-tile j; positions from the LDS copy of the index list
+      const int i0 = j * kSub + 8 * kq;   // multiple of 8: two 16-byte LDS reads
+      const int4 pa = *reinterpret_cast<const int4*>(&s_pos[i0]);
+      const int4 pb = *reinterpret_cast<const int4*>(&s_pos[i0 + 4]);
+      const int pos[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+      load_sel_pos(st, pos);
+    };
+    auto load_win = [&](Stage& st, int sub) {      // all 32 slots are window rows (or past the window)
+      const int r0 = sub * kSub + 8 * kq - k;
+      st.valid = 0;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const bool ok = r0 + jj < nswa;
-      const uint16_t* src =
-          ok ? win_src(srow0 + r0 + jj, cg) : reinterpret_cast<const uint16_t*>(fb) + 8 * cg;
-      const uint4 v = *reinterpret_cast<const uint4*>(src);
-      st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
-      st.valid |= (ok ? 1u : 0u) << jj;
-    }
-  };
-  auto load_mixed = [&](Stage& st, int sub) {    // the one sub-tile that straddles slot k
-    const int slot0 = sub * kSub + 8 * kq;
-    st.valid = 0;
+      for (int jj = 0; jj < 8; ++jj) {
+        const bool ok = r0 + jj < nswa;
+        const uint16_t* src =
+            ok ? win_src(srow0 + r0 + jj, cg) : reinterpret_cast<const uint16_t*>(fb) + 8 * cg;
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
+        st.valid |= (ok ? 1u : 0u) << jj;
+      }
+    };
+    auto load_mixed = [&](Stage& st, int sub) {    // the one sub-tile that straddles slot k
+      const int slot0 = sub * kSub + 8 * kq;
+      st.valid = 0;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int slot = slot0 + jj;
-      st.w[jj][0] = st.w[jj][1] = st.w[jj][2] = st.w[jj][3] = 0u;
-      if (slot < k) {
-        const int pos = P.idx[(size_t)qi * k + slot];
-        if (pos >= 0) {
-          const uint8_t* rec = P.cache + (size_t)(cbase + pos) * CSA2_KV_RECORD_BYTES;
-          st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
-          st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * (cg >> 3));
+      for (int jj = 0; jj < 8; ++jj) {
+        const int slot = slot0 + jj;
+        st.w[jj][0] = st.w[jj][1] = st.w[jj][2] = st.w[jj][3] = 0u;
+        if (slot < k) {
+          const int pos = P.idx[(size_t)qi * k + slot];
+          if (pos >= 0) {
+            const uint8_t* rec = P.cache + (size_t)(cbase + pos) * CSA2_KV_RECORD_BYTES;
+            st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
+            st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * (cg >> 3));
+            st.valid |= 1u << jj;
+          }
+        } else if (slot - k < nswa) {
+          const uint4 v = *reinterpret_cast<const uint4*>(win_src(srow0 + slot - k, cg));
+          st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
           st.valid |= 1u << jj;
         }
-      } else if (slot - k < nswa) {
-        const uint4 v = *reinterpret_cast<const uint4*>(win_src(srow0 + slot - k, cg));
-        st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
-        st.valid |= 1u << jj;
       }
-    }
-  };
+    };
 
     auto load_first = [&](Stage& st, int sub) {   // positions straight from the index list
       const int kind = sub_kind(sub * kSub, k);
@@ -590,40 +606,59 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
       else load_mixed(st, sub);
     };
   // Decode the loaded words to fp16 and write both LDS layouts of buffer b.
-  auto store_stage = [&](const Stage& st, int sub, int b) {
-    const int slot0 = sub * kSub;
-    const int sc_shift = 8 * ((cg >> 1) & 3);   // this thread's scale byte in the loaded scale dword
-    uint32_t vals[8][4];
+    // The slot class is a compile-time argument (0: selected entries only,
+    // 1: window rows only, 2: both), so a sub-tile of one class runs only its
+    // own decode: the decode waves' VALU issue, which they share with the
+    // multiply waves on every SIMD, is what bounds a sub-tile.
+    auto store_stage = [&](const Stage& st, int sub, int b, auto cls) {
+      constexpr int kCls = decltype(cls)::value;
+      const int slot0 = sub * kSub;
+      const int sc_shift = 8 * ((cg >> 1) & 3);   // this thread's scale byte in the loaded scale dword
+      uint32_t vals[8][4];
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const bool is_sel = slot0 + 8 * kq + jj < k;
-      const uint32_t keep = (st.valid >> jj) & 1u ? 0xFFFFFFFFu : 0u;
-      uint32_t dv[4], sv[4];
-      decode8(st.w[jj][0], (_Float16)e4m3_to_f32((st.w[jj][1] >> sc_shift) & 0xFFu), dv);
+      for (int jj = 0; jj < 8; ++jj) {
+        const bool is_sel = slot0 + 8 * kq + jj < k;
+        const uint32_t keep = (st.valid >> jj) & 1u ? 0xFFFFFFFFu : 0u;
+        uint32_t dv[4], sv[4];
+        if constexpr (kCls != 1)
+          decode8(st.w[jj][0], (st.w[jj][1] >> sc_shift) & 0xFFu, dv);
+        if constexpr (kCls != 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sv[j] = pack_f16(__uint_as_float(st.w[jj][j] << 16), __uint_as_float(st.w[jj][j] & 0xFFFF0000u));
+          for (int j = 0; j < 4; ++j)
+            sv[j] = pack_f16(__uint_as_float(st.w[jj][j] << 16), __uint_as_float(st.w[jj][j] & 0xFFFF0000u));
+        }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) vals[jj][j] = (is_sel ? dv[j] : sv[j]) & keep;
-      if (cg == 0) s_valid[b][8 * kq + jj] = keep & 1u;
-      *reinterpret_cast<uint4*>(&s_k[b][(8 * kq + jj) * kKRow + 8 * cg]) =
-          make_uint4(vals[jj][0], vals[jj][1], vals[jj][2], vals[jj][3]);
-    }
-    // channel-major copy: row (channel 8*cg + c) gets key slots 8*kq .. 8*kq+7
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int jp = 0; jp < 4; ++jp) {
-        const uint32_t a = vals[2 * jp][c >> 1], bb = vals[2 * jp + 1][c >> 1];
-        // take the low (c even) or high (c odd) fp16 of each
-        pk[jp] = (c & 1) ? __builtin_amdgcn_perm(bb, a, 0x07060302u) : __builtin_amdgcn_perm(bb, a, 0x05040100u);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (kCls == 0) vals[jj][j] = dv[j] & keep;
+          else if constexpr (kCls == 1) vals[jj][j] = sv[j] & keep;
+          else vals[jj][j] = (is_sel ? dv[j] : sv[j]) & keep;
+        }
+        if (cg == 0) s_valid[b][8 * kq + jj] = keep & 1u;
+        *reinterpret_cast<uint4*>(&s_k[b][(8 * kq + jj) * kKRow + 8 * cg]) =
+            make_uint4(vals[jj][0], vals[jj][1], vals[jj][2], vals[jj][3]);
       }
-      uint2* dst = reinterpret_cast<uint2*>(&s_v[b][(8 * cg + c) * kVRow + 8 * kq]);
-      dst[0] = make_uint2(pk[0], pk[1]);
-      dst[1] = make_uint2(pk[2], pk[3]);
-    }
-  };
+      // channel-major copy: row (channel 8*cg + c) gets key slots 8*kq .. 8*kq+7
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int jp = 0; jp < 4; ++jp) {
+          const uint32_t a = vals[2 * jp][c >> 1], bb = vals[2 * jp + 1][c >> 1];
+          // take the low (c even) or high (c odd) fp16 of each
+          pk[jp] = (c & 1) ? __builtin_amdgcn_perm(bb, a, 0x07060302u) : __builtin_amdgcn_perm(bb, a, 0x05040100u);
+        }
+        uint2* dst = reinterpret_cast<uint2*>(&s_v[b][(8 * cg + c) * kVRow + 8 * kq]);
+        dst[0] = make_uint2(pk[0], pk[1]);
+        dst[1] = make_uint2(pk[2], pk[3]);
+      }
+    };
+
+    auto store_any = [&](const Stage& st, int sub, int b) {
+      const int kind = sub_kind(sub * kSub, k);
+      if (kind == 0) store_stage(st, sub, b, std::integral_constant<int, 0>{});
+      else if (kind == 1) store_stage(st, sub, b, std::integral_constant<int, 1>{});
+      else store_stage(st, sub, b, std::integral_constant<int, 2>{});
+    };
 
     // sub-tile x's words sit in stg[x % kStages]: the loads of kStages sub-tiles
     // ahead of the one being decoded stay in flight
@@ -631,17 +666,35 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
 #pragma unroll
     for (int x = 0; x < kStages; ++x)
       if (x < nmine) load_first(stg[x], split + x * ns);
-    if (nmine > 0) store_stage(stg[0], split, 0);
+    if (nmine > 0) store_any(stg[0], split, 0);
     lds_barrier();   // s_pos and buffer 0
     if (nmine > kStages) load_next(stg[0], kStages);
-    for (int j0 = 0; j0 < nmine; j0 += kStages) {
+    // Local sub-tiles are in ascending slot order, so the selected-only ones
+    // come first.  While the sub-tile being loaded is one of them, the loop
+    // below issues only the branch-free gather loads: with no load under a
+    // branch, the compiler's wait before a decode counts just the older loads
+    // (the newer sub-tiles' loads stay in flight).
+    const int k_full = k / kSub;   // sub-tiles below this hold selected entries only
+    const int n_sel = split < k_full ? min(nmine, (k_full - split + ns - 1) / ns) : 0;
+    const int n_a = max(0, n_sel - 1 - kStages) / kStages * kStages;   // j < n_a: sub-tile j + 1 + kStages is selected-only
+    for (int j0 = 0; j0 < n_a; j0 += kStages) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) {
+        const int j = j0 + u;
+        Stage& S = stg[(u + 1) % kStages];   // sub-tile j + 1
+        store_stage(S, split + (j + 1) * ns, (j + 1) & 1, std::integral_constant<int, 0>{});
+        load_sel(S, j + 1 + kStages);
+        lds_barrier();
+      }
+    }
+    for (int j0 = n_a; j0 < nmine; j0 += kStages) {
 #pragma unroll
       for (int u = 0; u < kStages; ++u) {
         const int j = j0 + u;
         if (j < nmine) {   // uniform
           if (j + 1 < nmine) {
             Stage& S = stg[(u + 1) % kStages];   // sub-tile j + 1
-            store_stage(S, split + (j + 1) * ns, (j + 1) & 1);   // its buffer was last read before the previous barrier
+            store_any(S, split + (j + 1) * ns, (j + 1) & 1);   // its buffer was last read before the previous barrier
             if (j + 1 + kStages < nmine) load_next(S, j + 1 + kStages);
           }
           lds_barrier();
