@@ -45,6 +45,7 @@ constexpr int kThreads = 256;
 constexpr int kSub = 32;            // key slots per sub-tile
 constexpr int kKRow = 512 + 8;      // fp16 per key row in the key-major tile (16 B pad)
 constexpr int kVRow = kSub + 4;     // fp16 per channel row in the channel-major tile (8 B pad)
+constexpr int kVRow2 = kSub;       // k_attn2's channel-major rows (unpadded, chunks swizzled)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSlotsWG = 3072;   // key slots one work-group stages: k <= 2048 plus a window <= 1024
@@ -488,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
 constexpr int kStages = 2;   // sub-tiles whose loads the decode waves keep in flight (3 or 4 time the same)
 __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
   __shared__ __attribute__((aligned(16))) _Float16 s_k[2][kSub * kKRow];
-  __shared__ __attribute__((aligned(16))) _Float16 s_v[2][512 * kVRow];
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[2][512 * kVRow2];
   __shared__ uint32_t s_valid[2][kSub];
   __shared__ int32_t s_pos[kMaxSlotsWG];
 
@@ -498,6 +499,14 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
   const bool mwave = wave < 4;   // multiply waves; waves 4-7 decode
   const bool head_wave = mwave && 16 * wave < P.h;
   const int head = 16 * wave + n;
+  // Key-major tile: key slot s of a sub-tile sits in row key_row(s), so that
+  // MFMA tile kt's row r holds key 8 (r >> 2) + 4 kt + (r & 3).
+  auto key_row = [](int s) { return 16 * ((s >> 2) & 1) + 4 * (s >> 3) + (s & 3); };
+  // Channel-major tile, unpadded 64-byte rows: 16-byte chunk ch (keys 8 ch ..
+  // 8 ch + 7) of channel row r sits at chunk ch ^ ((r >> 1) & 3) -- the reads
+  // of 8 consecutive rows and the writes of 4 chunks x 2 rows of opposite
+  // parity each cover a 128-byte LDS line once.
+  auto v_addr = [](int r, int ch) { return r * kVRow2 + 8 * (ch ^ ((r >> 1) & 3)); };
   const int64_t cbase = P.seq_base[P.q_seq[qi]];
   const int k = P.k;
   const int nswa = P.swa_len ? P.swa_len[qi] : 0;
@@ -524,6 +533,8 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
     // channels 8*cg .. 8*cg+7
     const int dt = tid - kThreads;
     const int kq = dt & 3, cg = dt >> 2;
+    const int cpar = cg & 1;   // odd channel groups swap their rows in pairs
+    const uint32_t sel_even = cpar ? 0x07060302u : 0x05040100u, sel_odd = cpar ? 0x05040100u : 0x07060302u;
     // Global loads of a sub-tile, one loader per slot class.  Addresses of
     // empty slots point at the fallback bytes, so no load is conditional.
     // cq: this thread's codes dword in the query's first record (fq: in the
@@ -634,22 +645,20 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
           else vals[jj][j] = (is_sel ? dv[j] : sv[j]) & keep;
         }
         if (cg == 0) s_valid[b][8 * kq + jj] = keep & 1u;
-        *reinterpret_cast<uint4*>(&s_k[b][(8 * kq + jj) * kKRow + 8 * cg]) =
+        *reinterpret_cast<uint4*>(&s_k[b][key_row(8 * kq + jj) * kKRow + 8 * cg]) =
             make_uint4(vals[jj][0], vals[jj][1], vals[jj][2], vals[jj][3]);
       }
-      // channel-major copy: row (channel 8*cg + c) gets key slots 8*kq .. 8*kq+7
+      // channel-major copy: channel row 8 cg + c' gets keys 8 kq .. 8 kq + 7 as
+      // one 16-byte chunk (see v_addr); the odd channel groups write their rows
+      // in swapped pairs (c' = c ^ 1), so the two halves of a 128-byte LDS
+      // line are written by one instruction's eight lanes
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? sel_odd : sel_even;   // the fp16 half of channel c'
         uint32_t pk[4];
 #pragma unroll
-        for (int jp = 0; jp < 4; ++jp) {
-          const uint32_t a = vals[2 * jp][c >> 1], bb = vals[2 * jp + 1][c >> 1];
-          // take the low (c even) or high (c odd) fp16 of each
-          pk[jp] = (c & 1) ? __builtin_amdgcn_perm(bb, a, 0x07060302u) : __builtin_amdgcn_perm(bb, a, 0x05040100u);
-        }
-        uint2* dst = reinterpret_cast<uint2*>(&s_v[b][(8 * cg + c) * kVRow + 8 * kq]);
-        dst[0] = make_uint2(pk[0], pk[1]);
-        dst[1] = make_uint2(pk[2], pk[3]);
+        for (int jp = 0; jp < 4; ++jp) pk[jp] = __builtin_amdgcn_perm(vals[2 * jp + 1][c >> 1], vals[2 * jp][c >> 1], sel);
+        *reinterpret_cast<uint4*>(&s_v[b][v_addr(8 * cg + (c ^ cpar), kq)]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
     };
 
@@ -728,7 +737,8 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
 
   auto compute = [&](int b) {
     if (head_wave) {
-      // ---- S^T = K Q^T : lane (head n, g) gets keys 16*kt + 4*g + i
+      // ---- S^T = K Q^T : tile kt's row r holds key 8 (r >> 2) + 4 kt + (r & 3),
+      // so lane (head n, g) gets keys 8 g + 4 kt + i: eight consecutive keys
       // the two key tiles' chains interleaved (independent accumulators); each
       // k-step's fragments are read one k-step ahead of their MFMAs
       f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
@@ -762,7 +772,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = 16 * kt + 4 * g + i;
+          const int key = 8 * g + 4 * kt + i;
           const float v = s_valid[b][key] ? sacc[kt][i] * P.scale_log2 : -INFINITY;
           z[4 * kt + i] = v;
           mx = fmaxf(mx, v);
@@ -804,16 +814,13 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[t][i] *= a4[i];
       }
-      // P as the A operand: slots 0..3 = keys 4g+i, slots 4..7 = keys 16+4g+i
+      // P as the A operand: slot e = key 8 g + e
       f16x8 pa;
 #pragma unroll
       for (int j = 0; j < 8; ++j) pa[j] = (_Float16)pv[j];
       // ---- O += P V  (each V fragment read one MFMA ahead)
-      auto vfrag = [&](int t) {
-        const _Float16* vrow = &s_v[b][(16 * t + n) * kVRow];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 4 * g);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + 4 * g);
-        return __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      auto vfrag = [&](int t) {   // V^T fragment: channel 16 t + n, keys 8 g .. 8 g + 7
+        return *reinterpret_cast<const f16x8*>(&s_v[b][v_addr(16 * t + n, g)]);
       };
       f16x8 nv = vfrag(0);
 #pragma unroll
