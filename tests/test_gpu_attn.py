@@ -126,3 +126,26 @@ def test_deterministic():
     a = _run(c)[0]
     b = _run(c)[0]
     assert np.array_equal(a, b)
+
+
+@gpu
+@pytest.mark.parametrize("n_q,h,k,nswa", [(128, 64, 500, 128), (300, 32, 512, 100)])
+def test_many_queries_long_splits(n_q, h, k, nswa):
+    """Calls with few splits per query (128 queries: 2 splits of 10 sub-tiles;
+    300: 1 split of 20), where the bf16 kernel's decode runs its selected-only
+    loop for most sub-tiles; k = 500 leaves a sub-tile that straddles the
+    window, h = 32 leaves two multiply waves idle, and a tenth of the selected
+    entries are padding (-1) scattered through the lists."""
+    note(f"attn many queries n_q={n_q} h={h} k={k} nswa={nswa}")
+
+    def pad(i):
+        i = i.copy()
+        rng = np.random.default_rng(n_q)
+        i[rng.random(i.shape) < 0.1] = -1
+        return i
+    c = _case(n_q, h, 640, k, nswa, torch.bfloat16, seed=n_q + k, idx_fn=pad)
+    o, l, ro, rl = _run(c)
+    err = normwise_err(o, ro)
+    print(f"normwise err {err:.3e}")
+    assert err <= TOL
+    assert np.allclose(l, rl, rtol=1e-4, atol=1e-4)
