@@ -291,6 +291,31 @@ def copy_calibration(mib, dev):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
+def attainable_copy(dev, mib=1024, reps=10):
+    """The HBM bandwidth a plain device copy reaches on this part (1 GiB read +
+    1 GiB written per launch), timed after the measured steps: the attainable
+    ceiling beside the published peak."""
+    import torch
+
+    n = mib << 20
+    src = torch.full((n,), 7, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    secs = e0.elapsed_time(e1) * 1e-3 / reps
+    gbps = 2 * n / secs / 1e9
+    del src, dst
+    return {"kernel": "device copy, 1 GiB read + 1 GiB written per launch", "GB/s": round(gbps, 1),
+            "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -397,6 +422,8 @@ def main():
             cpu, parity = cpu_baseline(wl, st, layers, app_x, dev, nseq, gres)
         log(f"cpu baseline {cpu['value']:.3f} q.l/s; sample parity {parity}")
 
+    attainable = attainable_copy(dev)
+    log(f"attainable copy {attainable['GB/s']} GB/s")
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -418,6 +445,7 @@ def main():
         "step_hbm": {"algorithmic_bytes": sbytes, "GB/s": round(sbytes / (ms * 1e-3) / 1e9, 1),
                      "frac": round(sbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
         "roofline": roofline,
+        "attainable_hbm": attainable,
         "step_launch": ({"mode": "hip_graph", "eager_ms_per_step": round(eager_ms, 5)} if a.graph
                         else {"mode": "eager"}),
         "cpu_baseline": cpu,
