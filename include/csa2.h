@@ -185,7 +185,9 @@ size_t csa2_reindex_topk_ws_bytes(int n_q, int h_i, int d_i, int k, int block, i
  *   idx_out  [n_q][k]: the k candidates with the largest scores (ties: lower
  *            position), ascending, -1 padded
  * ws: csa2_topk_merge_ws_bytes(n_q, n_cand, h_i, d_i, k) bytes (the
- * candidates' keys are gathered there, then selected as by csa2_index_topk).
+ * candidates' keys are gathered there, then selected exactly: by
+ * csa2_reindex_topk over all their blocks of 8 when n_cand <= 16384, else by
+ * csa2_index_topk; the result is the same Top-K either way).
  * Supported: as csa2_index_topk; n_cand <= 2^25, n_q <= 65535. */
 csa2_status csa2_topk_merge(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
                             const int32_t* q_seq, const uint16_t* ik, const int64_t* seq_base,

@@ -11,9 +11,12 @@
 // (wire.sakhanda.co), section "Сжатое разреженное внимание 2 (CSA2)").
 //
 // How: the candidates' keys are gathered into a contiguous row per query in
-// the workspace (k_merge_gather), the exact Full-layer selection runs over
-// that short "sequence" (csa2_index_topk: MFMA scores, bound, exact rescoring),
-// and the chosen local indices are mapped back to positions (k_merge_remap).
+// the workspace (k_merge_gather), the exact selection runs over that short
+// "sequence" (MFMA scores, bound, exact rescoring), and the chosen local
+// indices are mapped back to positions (k_merge_remap).  Up to 16,384
+// candidates the selection is csa2_reindex_topk over the pool of all the
+// row's blocks of 8 (its one-work-group select: three launches in all);
+// beyond, csa2_index_topk's multi-kernel select.
 // Candidates are ascending, so a lower local index is a lower position and
 // ties resolve as over the whole context.
 #include "csa2_device.h"
@@ -33,7 +36,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_gather(const uint16_t* 
                                                                 uint16_t* __restrict__ keys,
                                                                 int32_t* __restrict__ nvalid,
                                                                 int32_t* __restrict__ ident,
-                                                                int64_t* __restrict__ kbase) {
+                                                                int64_t* __restrict__ kbase,
+                                                                int32_t* __restrict__ pool, int nb) {
   const int pieces = d_i >> 3;
   const int per_block = kMergeThreads / pieces;
   const int c = blockIdx.x * per_block + threadIdx.x / pieces;
@@ -44,6 +48,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_gather(const uint16_t* 
     kbase[q] = (int64_t)q * n_cand;
   }
   if (c >= n_cand) return;
+  if (pool && pc == 0 && (c & 7) == 0) pool[(size_t)q * nb + (c >> 3)] = c >> 3;   // every block of the row
   const int32_t* cq = cand + (size_t)q * n_cand;
   const int32_t pos = cq[c];
   // the candidate count: the list is -1 padded at its end only
@@ -74,8 +79,10 @@ thread_local int g_merge_hip_error = 0;
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kMergeSmall = 16384;   // candidates up to which the Reindex select runs
+
 struct MergeLayout {
-  size_t keys, nvalid, ident, kbase, local, inner, total;
+  size_t keys, nvalid, ident, kbase, local, pool, inner, total;
 };
 
 MergeLayout merge_layout(int n_q, int n_cand, int d_i, int k, int h_i) {
@@ -86,7 +93,12 @@ MergeLayout merge_layout(int n_q, int n_cand, int d_i, int k, int h_i) {
   L.ident = o;  o = a256(o + (size_t)n_q * 4);
   L.kbase = o;  o = a256(o + (size_t)n_q * 8);
   L.local = o;  o = a256(o + (size_t)n_q * k * 4);
-  L.inner = o;  o = a256(o + csa2_index_topk_ws_bytes(n_q, n_cand, h_i, d_i, k, 8, 0));
+  const int nb = (n_cand + 7) / 8;
+  const bool small = n_cand <= kMergeSmall;
+  L.pool = o;   o = a256(o + (small ? (size_t)n_q * nb * 4 : 0));
+  L.inner = o;
+  o = a256(o + (small ? csa2_reindex_topk_ws_bytes(n_q, h_i, d_i, k, 8, nb)
+                      : csa2_index_topk_ws_bytes(n_q, n_cand, h_i, d_i, k, 8, 0)));
   L.total = o;
   return L;
 }
@@ -120,6 +132,9 @@ extern "C" csa2_status csa2_topk_merge(const uint16_t* iq, const float* w, int n
   int32_t* ident = reinterpret_cast<int32_t*>(w8 + L.ident);
   int64_t* kbase = reinterpret_cast<int64_t*>(w8 + L.kbase);
   int32_t* local = reinterpret_cast<int32_t*>(w8 + L.local);
+  const bool small = n_cand <= kMergeSmall;
+  const int nb = (n_cand + 7) / 8;
+  int32_t* pool = small ? reinterpret_cast<int32_t*>(w8 + L.pool) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 gremap((k + csa2::kMergeThreads - 1) / csa2::kMergeThreads, n_q);
   hipError_t e;
@@ -136,14 +151,17 @@ extern "C" csa2_status csa2_topk_merge(const uint16_t* iq, const float* w, int n
   const int per_block = csa2::kMergeThreads / (d_i >> 3);
   hipLaunchKernelGGL(csa2::k_merge_gather, dim3((n_cand + per_block - 1) / per_block, n_q),
                      dim3(csa2::kMergeThreads), 0, st, ik, d_i, q_seq, seq_base, cand, n_cand, keys, nvalid, ident,
-                     kbase);
+                     kbase, pool, nb);
   e = hipGetLastError();
   if (e != hipSuccess) {
     g_merge_hip_error = (int)e;
     return CSA2_E_HIP;
   }
-  const csa2_status s = csa2_index_topk(iq, w, n_q, h_i, d_i, ident, nvalid, n_cand, keys, kbase, k, local, 8, 0,
-                                        nullptr, w8 + L.inner, L.total - L.inner, stream);
+  const csa2_status s =
+      small ? csa2_reindex_topk(iq, w, n_q, h_i, d_i, ident, nvalid, keys, kbase, pool, 8, nb, k, local, w8 + L.inner,
+                                L.total - L.inner, stream)
+            : csa2_index_topk(iq, w, n_q, h_i, d_i, ident, nvalid, n_cand, keys, kbase, k, local, 8, 0, nullptr,
+                              w8 + L.inner, L.total - L.inner, stream);
   if (s != CSA2_OK) return s;
   hipLaunchKernelGGL(csa2::k_merge_remap, gremap, dim3(csa2::kMergeThreads), 0, st, local, k, cand, n_cand,
                      idx_out);

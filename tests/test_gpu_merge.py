@@ -53,14 +53,16 @@ def test_sharded_context_merges_to_the_full_topk(L, G, h_i, d_i):
 
 
 @gpu
-def test_merge_of_arbitrary_candidates_ties_and_padding():
+@pytest.mark.parametrize("n_cand", [2000, 20000])
+def test_merge_of_arbitrary_candidates_ties_and_padding(n_cand):
+    """2000 candidates take the one-work-group select, 20000 (over 16,384) the
+    multi-kernel one; both must give the oracle's Top-K among the candidates."""
     dev = device()
-    note("topk merge: arbitrary candidates")
+    note(f"topk merge: arbitrary candidates n_cand={n_cand}")
     L, k = 30000, 300
     inp = index_inputs([L, L], 64, 128, seed=710)
     inp["ik"][5000:6000] = inp["ik"][9000:10000]        # equal keys: ties resolve by position
     rng = np.random.default_rng(711)
-    n_cand = 2000
     cand = np.full((2, n_cand), -1, np.int32)
     cand[0] = np.sort(rng.choice(L, n_cand, replace=False))
     short = np.sort(rng.choice(np.arange(4000, 11000), 250, replace=False))   # fewer than k candidates
