@@ -484,6 +484,11 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   const int nc = INDIRECT ? 8 * P.keep_in : nvis;
   const int nblk = (nvis + 7) >> 3;
   const int c0 = blockIdx.x * P.scan_chunk;
+  // a chunk past the query's visible keys (the grid spans the longest
+  // context) has no score, block or histogram count to publish
+  if constexpr (HIST) {
+    if (c0 >= nc) return;
+  }
 
   if constexpr (HIST) {
     for (int i = tid; i < kNBins; i += kThreads) {
@@ -914,17 +919,19 @@ __global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
   int p, chunk;
   grid_chunk(P, &p, &chunk);
   const int q = p % P.n_q, kind = p / P.n_q;
-  // every load goes out at once: the chunk's scores (inside the problem's
-  // row: the grid covers the chunks of each kind only), the coarse
-  // histogram, the visible length and the bound's inputs
+  // the visible length first: a chunk past the problem's candidates (the grid
+  // spans the longest context; shorter ones leave most chunks empty) leaves
+  // before loading anything.  Then every load goes out at once: the chunk's
+  // scores (inside the problem's row), the coarse histogram and the bound's
+  // inputs
+  const int nc = cands_of(P, kind, P.q_nvis[q]);
+  if (chunk > 0 && chunk * kCmpChunk >= nc) return;
   const int my0 = chunk * kCmpChunk + tid * kCmpPerThread;
   float v[kCmpPerThread];
   load16(P, p, my0, v);
   uint32_t hv[kHPer];
   load_hist16(P.hist + (size_t)p * kNBins, hv);
-  const int nc = cands_of(P, kind, P.q_nvis[q]);
   const float maxt = __uint_as_float(P.meta[q].maxt), wabs = P.meta[p].wabs;
-  if (chunk > 0 && chunk * kCmpChunk >= nc) return;
   for (int i = tid; i < kNBins; i += kThreads) s_h[i] = 0;
   const uint32_t bin = wg_coarse_bin(P, p, hv, chunk == 0, maxt, wabs, s_tmp);   // its barriers order the clear
   if (bin == kAll || chunk * kCmpChunk >= nc) return;
@@ -1010,14 +1017,24 @@ __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
   grid_chunk(P, &p, &chunk);
   const int q = p % P.n_q, kind = p / P.n_q;
   const int c0 = chunk * kCmpChunk;
-  // every load goes out at once: the chunk's scores, the fine histogram, the
-  // visible length and the Meta fields the fine histogram kernel published
+  // the visible length first: a chunk past the problem's candidates only
+  // records empty counts (the later kernels sum the counts of every chunk of
+  // the row) and loads nothing.  Then every load goes out at once: the
+  // chunk's scores, the fine histogram and the Meta fields the fine
+  // histogram kernel published
+  const int nc = cands_of(P, kind, P.q_nvis[q]);
+  if (chunk > 0 && c0 >= nc) {
+    if (tid == 0) {
+      P.chunk_cnt[(size_t)p * P.nchunk_cmp + chunk] = 0;
+      P.chunk_unc[(size_t)p * P.nchunk_cmp + chunk] = 0;
+    }
+    return;
+  }
   const int my0 = c0 + tid * kCmpPerThread;
   float v[kCmpPerThread];
   load16(P, p, my0, v);
   uint32_t hv[kHPer];
   load_hist16(P.hist2 + (size_t)p * kNBins, hv);
-  const int nc = cands_of(P, kind, P.q_nvis[q]);
   const uint32_t m_bin = P.meta[p].bin, m_above = P.meta[p].above;
   const float m_delta = P.meta[p].delta;
   float keep_thr = -INFINITY, in_thr = -INFINITY;
