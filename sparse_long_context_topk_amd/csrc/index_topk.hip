@@ -55,7 +55,8 @@
 // A Reindex pool of at most 16,384 slots skips steps 1 and 3-6: its scan keeps
 // each work-group's largest key magnitude t_k instead of histograms, and one
 // work-group per query (section 7) selects from the scores it holds in
-// registers.
+// registers.  A Full call without a pool whose contexts are all that short
+// takes the same path over every block of the context (a null pool).
 #include "csa2_device.h"
 
 #include <algorithm>
@@ -113,7 +114,7 @@ struct Params {
   const int32_t* q_nvis;
   const uint16_t* ik;
   const int64_t* seq_base;
-  const int32_t* pool_in;  // Reindex: [n_q][keep_in]
+  const int32_t* pool_in;  // Reindex: [n_q][keep_in]; null: every block 0 .. keep_in-1 in order
   int keep_in;
   int k;                   // Top-K of the token problem
   int keep_blocks;         // Top-K of the block problem (0: none)
@@ -362,7 +363,7 @@ __device__ __forceinline__ int cands_of(const Params& P, int kind, int nvis) {
 __device__ __forceinline__ int cand_pos(const Params& P, int q, int kind, uint32_t cand) {
   cand &= ~kCertain;
   if (P.reindex) {
-    const int b = P.pool_in[(size_t)q * P.keep_in + (cand >> 3)];
+    const int b = P.pool_in ? P.pool_in[(size_t)q * P.keep_in + (cand >> 3)] : (int)(cand >> 3);
     return b * 8 + (int)(cand & 7);
   }
   (void)kind;
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     // block ids of this chunk's pool slots (scan_chunk / 8 <= 512 of them)
     for (int i = tid; i < P.scan_chunk / 8; i += kThreads) {
       const int slot = c0 / 8 + i;
-      s_pool[i] = slot < P.keep_in ? P.pool_in[(size_t)q * P.keep_in + slot] : -1;
+      s_pool[i] = slot < P.keep_in ? (P.pool_in ? P.pool_in[(size_t)q * P.keep_in + slot] : slot) : -1;
     }
   }
 
@@ -1611,7 +1612,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
   int32_t praw[kSmallMax / 8 / kSmallThreads];
 #pragma unroll
   for (int k = 0; k < kSmallMax / 8 / kSmallThreads; ++k)
-    praw[k] = P.pool_in[(size_t)q * P.keep_in + min(tid + kSmallThreads * k, P.keep_in - 1)];
+    praw[k] = P.pool_in ? P.pool_in[(size_t)q * P.keep_in + min(tid + kSmallThreads * k, P.keep_in - 1)]
+                        : min(tid + kSmallThreads * k, P.keep_in - 1);
   const float wraw = P.w[(size_t)q * P.h_i + min(tid & 63, P.h_i - 1)];
   const float kraw = P.kpart[(size_t)q * nwg + min(tid & 63, nwg - 1)];
 
@@ -2220,6 +2222,23 @@ extern "C" csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n
   Params P{};
   P.iq = iq; P.w = w; P.n_q = n_q; P.h_i = h_i; P.d_i = d_i;
   P.q_seq = q_seq; P.q_nvis = q_nvis; P.ik = ik; P.seq_base = seq_base;
+  if (keep_blocks == 0 && max_nvis <= kSmallMax) {
+    // Short contexts without a pool: the Reindex path over every block of the
+    // context in order (a null pool) -- the same exact Top-K over the positions
+    // < q_nvis, from the scan and the one-work-group select (two launches
+    // instead of six).  Its workspace (stride 8 ceil(max_nvis / 8) rounded up)
+    // fits in this call's.
+    P.pool_in = nullptr; P.keep_in = std::max(1, (max_nvis + 7) / 8); P.k = k; P.keep_blocks = 0;
+    P.idx_out = idx_out; P.pool_out = nullptr;
+    P.nprob = n_q;
+    P.reindex = 1;
+    const int64_t slots = 8LL * P.keep_in;
+    P.scan_chunk = reindex_chunk_for(n_q, slots);
+    P.stride = round_up(slots, kCmpChunk);
+    P.nchunk_cmp = (int)(P.stride / kCmpChunk);
+    const size_t need = csa2_index_topk_ws_bytes(n_q, max_nvis, h_i, d_i, k, block, keep_blocks);
+    return run_pipeline(P, slots, ws, ws_bytes, static_cast<hipStream_t>(stream), need);
+  }
   P.pool_in = nullptr; P.keep_in = 0; P.k = k; P.keep_blocks = keep_blocks;
   P.idx_out = idx_out; P.pool_out = pool_out;
   P.nprob = n_q * (keep_blocks > 0 ? 2 : 1);
