@@ -476,9 +476,9 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
 // ---------------------------------------------------------------- large batches
 // k_attn2: the bf16-query kernel.  k_attn's four waves decode a sub-tile and
 // then multiply it, in series, and its LDS leaves one work-group per CU.  Here
-// a work-group has eight waves: waves 0-3 multiply exactly as k_attn's (16
-// heads each, the same MFMA and online softmax code), waves 4-7 only load and
-// decode: while the multiply waves work on sub-tile j, the decode waves write
+// a work-group has eight waves: waves 0-3 multiply as k_attn's do (16 heads
+// each, the same MFMA shapes and online softmax; the LDS tiles are laid out
+// differently, see key_row and v_addr), waves 4-7 only load and decode: while the multiply waves work on sub-tile j, the decode waves write
 // sub-tile j + 1 into the other LDS buffer, with the loads of j + 2 and j + 3
 // in flight.  One barrier per sub-tile; two waves per SIMD.  A SIMD's two
 // waves share its VALU issue and the CU's LDS, which bound a sub-tile (about
