@@ -880,64 +880,61 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One work-group per (query, head); every thread sums two channels over the
-// splits (ascending), its first 32 splits' values loading while the first
-// wave turns the (m_s, l_s) pairs into weights.
+// One wave per (query, head), four heads per work-group: lane s holds split
+// s's (m_s, l_s) and forms its weight, then every lane sums channels 8 lane ..
+// 8 lane + 7 over the splits in ascending order (16-byte loads of each
+// split's partial row, the weights broadcast from their lanes), eight splits'
+// loads in flight at a time.
 __global__ __launch_bounds__(kThreads) void k_merge(Params P) {
-  __shared__ float s_w[kMaxSplit];
-  __shared__ float s_ml[2];
-  const int qi = blockIdx.x, hh = blockIdx.y, c = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int qi = blockIdx.x, hh = blockIdx.y * (kThreads / kWave) + (threadIdx.x >> 6);
+  if (hh >= P.h) return;   // whole wave
   const int ns = P.nsplit;
   const size_t row0 = (size_t)qi * ns * P.h + hh;   // row of split 0; split s adds s * h
-  const float* po = P.part_o + row0 * 512;
-  const size_t so = (size_t)P.h * 512;
-  // the first kBatch splits' partials load while the weights are formed
-  constexpr int kBatch = 32;
-  float x0[kBatch], x1[kBatch];
+  float m = -INFINITY, l = 0.0f;
+  if (lane < ns) {
+    const float2 v = *reinterpret_cast<const float2*>(P.part_ml + (row0 + (size_t)lane * P.h) * 2);
+    m = v.x;
+    l = v.y;
+  }
+  const float M = wave_max(m);
+  const float w = (lane < ns && m != -INFINITY) ? exp2f(m - M) : 0.0f;
+  const float L = wave_sum(w * l);
+  const float4* po = reinterpret_cast<const float4*>(P.part_o + row0 * 512) + 2 * lane;
+  const size_t so4 = (size_t)P.h * 128;   // float4s between splits
+  float acc[8];
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    x0[u] = x1[u] = 0.0f;
-    if (u < ns) {   // uniform
-      x0[u] = po[u * so + c];
-      x1[u] = po[u * so + c + 256];
-    }
-  }
-  if (threadIdx.x < 64) {
-    const int s = threadIdx.x;
-    float m = -INFINITY, l = 0.0f;
-    if (s < ns) {
-      const float2 v = *reinterpret_cast<const float2*>(P.part_ml + (row0 + (size_t)s * P.h) * 2);
-      m = v.x;
-      l = v.y;
-    }
-    const float M = wave_max(m);
-    const float w = (s < ns && m != -INFINITY) ? exp2f(m - M) : 0.0f;
-    const float L = wave_sum(w * l);
-    if (s < ns) s_w[s] = w;
-    if (s == 0) {
-      s_ml[0] = M;
-      s_ml[1] = L;
-    }
-  }
-  __syncthreads();
-  float acc0 = 0.0f, acc1 = 0.0f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  constexpr int kB = 8;
+  for (int s0 = 0; s0 < ns; s0 += kB) {
+    float4 x[kB][2];
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    if (u < ns) {
-      acc0 = fmaf(s_w[u], x0[u], acc0);
-      acc1 = fmaf(s_w[u], x1[u], acc1);
+    for (int u = 0; u < kB; ++u) {
+      if (s0 + u < ns) {   // uniform
+        x[u][0] = po[(size_t)(s0 + u) * so4];
+        x[u][1] = po[(size_t)(s0 + u) * so4 + 1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      if (s0 + u < ns) {
+        const float wu = __shfl(w, s0 + u, kWave);
+        const float xv[8] = {x[u][0].x, x[u][0].y, x[u][0].z, x[u][0].w, x[u][1].x, x[u][1].y, x[u][1].z, x[u][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wu, xv[e], acc[e]);
+      }
     }
   }
-  for (int s = kBatch; s < ns; ++s) {
-    acc0 = fmaf(s_w[s], po[s * so + c], acc0);
-    acc1 = fmaf(s_w[s], po[s * so + c + 256], acc1);
-  }
-  const float L = s_ml[1];
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  float* dst = P.out + ((size_t)qi * P.h + hh) * 512;
-  dst[c] = acc0 * inv;
-  dst[c + 256] = acc1 * inv;
-  if (P.lse && c == 0) P.lse[(size_t)qi * P.h + hh] = L > 0.0f ? (s_ml[0] + log2f(L)) * kLn2 : -INFINITY;
+  float* dst = P.out + ((size_t)qi * P.h + hh) * 512 + 8 * lane;
+  if ((reinterpret_cast<uintptr_t>(P.out) & 15) == 0) {
+    reinterpret_cast<float4*>(dst)[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    reinterpret_cast<float4*>(dst)[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = acc[e] * inv;
+  }
+  if (P.lse && lane == 0) P.lse[(size_t)qi * P.h + hh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 }  // namespace attn
@@ -1025,7 +1022,7 @@ csa2_status attn_call(const void* q, int q_dtype, int n_q, int h, int d, const i
     return CSA2_E_HIP;
   }
   if (s.nsplit > 1) {
-    hipLaunchKernelGGL(k_merge, dim3(n_q, h), dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL(k_merge, dim3(n_q, (h + 3) / 4), dim3(kThreads), 0, st, P);
     e = hipGetLastError();
     if (e != hipSuccess) {
       g_attn_hip_error = (int)e;
