@@ -537,8 +537,10 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   const int my_groups = ngroups > wave ? (ngroups - wave + kWaves - 1) / kWaves : 0;
 
   // Row of the key that lane (n, g) loads for local group `it` (the wave's
-  // it-th group), clamped to a visible row so that every load is in bounds
-  // and unconditional; `valid` says whether the key counts.
+  // it-th group); a slot without a key reads row 0 of the key array, so that
+  // every load is in bounds and unconditional (a pool slot's loads run even
+  // for a sequence with no visible position, whose base row may lie past the
+  // array's end); `valid` says whether the key counts.
   auto key_row = [&](int it, bool& valid) -> int64_t {
     const int cand = c0 + 16 * (wave + kWaves * it) + n;
     int pos;
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
       pos = cand;
       valid = cand < nc;
     }
-    return base + (valid ? pos : 0);
+    return valid ? base + pos : (int64_t)0;
   };
   auto load = [&](int it, uint4* kb) {
     bool v;

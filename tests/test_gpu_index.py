@@ -40,6 +40,20 @@ def test_full_ragged_lengths(h_i, d_i):
 
 
 @gpu
+@pytest.mark.parametrize("h_i,d_i", [(4, 64), (64, 128), (33, 64)])
+def test_full_short_ragged_lengths(h_i, d_i):
+    """Every context <= 16,384 and no pool: the call selects through the
+    Reindex kernels over all blocks of each context.  The edge lengths, with
+    an empty sequence last (its base row is the key array's end)."""
+    note(f"full short ragged h_i={h_i} d_i={d_i}")
+    inp = index_inputs([L for L in EDGE_LENGTHS if L <= 16384] + [0], h_i, d_i, seed=150 + h_i)
+    got = _gpu_full(inp, 512)
+    ref = _ref_full(inp, 512)
+    assert np.array_equal(got, ref)
+    assert np.all(got[-1] == -1)
+
+
+@gpu
 @pytest.mark.parametrize("k", [1, 64, 512, 2048])
 def test_full_k_values(k):
     note(f"full k={k}")
