@@ -163,6 +163,28 @@ def traffic_from_profile(kernel_sha):
     return float(m_b.group(1))
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def _oracle_threads(n_indep):
+    """Threads for the oracle's multi-thread leg: one per independent query of
+    the sample, at most the host's CPUs and at most 16 (a GPU machine's share)."""
+    return max(1, min(n_indep, 16, os.cpu_count() or 1))
+
+
+def _cpu_record(value, threads, sample, value_1t, sample_1t):
+    return {"value": value, "unit": "query·layers/s", "cores": threads, "threads": threads, "kind": "oracle",
+            "sample": sample, "cpu": _cpu_model(), "host_logical_cpus": os.cpu_count(),
+            "one_thread": {"value": value_1t, "unit": "query·layers/s", "sample": sample_1t}}
+
+
 def cpu_baseline_chunk(wl, st, layers, dev, nq, gpu_results):
     """Time the CPU oracle on `nq` queries spread over the encoder chunk (all
     its layers, the same inputs); the sample's indices and outputs are checked
@@ -185,7 +207,7 @@ def cpu_baseline_chunk(wl, st, layers, dev, nq, gpu_results):
                        swa_len=host(lay.swa_len[ts])))
         if lay.iq is not None:
             hl[-1]["iq"], hl[-1]["w"] = bits(lay.iq[ts]), host(lay.w[ts])
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = _oracle_threads(len(sel))
     oracle.lib()
 
     def raw_rows(rows):
@@ -203,9 +225,19 @@ def cpu_baseline_chunk(wl, st, layers, dev, nq, gpu_results):
         den[den == 0] = 1
         err = max(err, float((np.abs(o - rout).max(axis=-1) / den).max()))
     ql = len(sel) * len(wl["layers"])
-    return ({"value": ql / secs, "unit": "query·layers/s", "cores": threads, "kind": "oracle",
-             "sample": f"{len(sel)} of {n} chunk queries (spread over the chunk), all {len(wl['layers'])} layers "
-                       f"= {ql} query-layers in {secs:.2f} s"},
+    # one thread on one of the sampled queries, all layers
+    one = sel[len(sel) // 2:len(sel) // 2 + 1]
+    _, _, secs1 = oracle_step([{**d, **{key: d[key][len(sel) // 2:len(sel) // 2 + 1]
+                                         for key in ("q", "swa_row0", "swa_len", "iq", "w") if key in d}}
+                               for d in hl], bits(st.ik), np.asarray(wl["seq_base"], np.int64),
+                              np.asarray(wl["q_seq"], np.int32)[one], np.asarray(wl["q_nvis"], np.int32)[one],
+                              wl["k"], 0, wl["block"], raw_rows, None, st.softmax_scale, n_threads=1)
+    ql1 = len(wl["layers"])
+    return (_cpu_record(ql / secs, threads,
+                        f"{len(sel)} of {n} chunk queries (spread over the chunk), all {len(wl['layers'])} layers "
+                        f"= {ql} query-layers in {secs:.2f} s on {threads} threads (OpenMP over queries)",
+                        ql1 / secs1, f"chunk query {int(one[0])}, all {ql1} layers = {ql1} query-layers in "
+                                     f"{secs1:.2f} s on 1 thread"),
             {"idx_bitexact": idx_ok, "attn_max_normwise_err": err, "queries": int(len(sel))})
 
 
@@ -247,7 +279,7 @@ def cpu_baseline(wl, st, layers, app_x, dev, nseq, gpu_results):
             d["swa_new"], d["swa_dst"] = bits(lay.swa_new[:nseq]), host(lay.swa_dst[:nseq])
         hl.append(d)
     ax = host(app_x[:nseq])
-    threads = max(1, min(nseq, 16, os.cpu_count() or 1))
+    threads = _oracle_threads(nseq)
     oracle.lib()
     res, _, secs = oracle_step(hl, ik, cbase, np.arange(nseq, dtype=np.int32), np.array(lens, np.int32),
                                wl["k"], wl["keep_blocks"], wl["block"], raw_rows, ax, st.softmax_scale,
@@ -261,18 +293,19 @@ def cpu_baseline(wl, st, layers, app_x, dev, nseq, gpu_results):
         den[den == 0] = 1
         err = max(err, float((np.abs(o - rout).max(axis=-1) / den).max()))
     ql = nseq * len(wl["layers"])
-    cpu_model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu_model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return ({"value": ql / secs, "unit": "query·layers/s", "cores": threads, "kind": "oracle",
-             "sample": f"{nseq} of {wl['n_q']} sequences (full contexts {sorted(set(lens))}), all "
-                       f"{len(wl['layers'])} layers of one step = {ql} query-layers in {secs:.2f} s",
-             "cpu": cpu_model},
+    # one thread on the first sequence of the sample, the same step
+    hl1 = [{key: (v[:1] if key in ("q", "swa_row0", "swa_len", "iq", "w", "swa_new", "swa_dst") else v)
+            for key, v in d.items()} for d in hl]
+    _, _, secs1 = oracle_step(hl1, ik[:lens[0]], cbase[:1], np.zeros(1, np.int32), np.array(lens[:1], np.int32),
+                              wl["k"], wl["keep_blocks"], wl["block"], raw_rows, ax[:1], st.softmax_scale,
+                              n_threads=1, pool_full=bool(wl.get("pool_full")))
+    ql1 = len(wl["layers"])
+    return (_cpu_record(ql / secs, threads,
+                        f"{nseq} of {wl['n_q']} sequences (full contexts {sorted(set(lens))}), all "
+                        f"{len(wl['layers'])} layers of one step = {ql} query-layers in {secs:.2f} s on {threads} "
+                        f"threads (OpenMP over queries)",
+                        ql1 / secs1, f"sequence 0 (context {lens[0]}), all {ql1} layers of one step = {ql1} "
+                                     f"query-layers in {secs1:.2f} s on 1 thread"),
             {"idx_bitexact": idx_ok, "attn_max_normwise_err": err, "sequences": nseq})
 
 

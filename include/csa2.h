@@ -44,9 +44,13 @@
  *    0 <= p < nvis.  Row `seq_base[s] + p` addresses both the FP4 cache and
  *    the indexer-key array for position p of sequence s.
  *  - Outputs are written completely, including the -1 padding.
- *  - No state is kept between calls; calls on different streams may overlap
- *    if their outputs and workspaces are distinct.  No exception, abort or
- *    print ever leaves the library.
+ *  - No device or host state is kept between calls, except two per-thread
+ *    host slots: the HIP error behind the calling thread's most recent call
+ *    (csa2_last_hip_error) and the measurement hook of the instrumentation
+ *    section at the end (csa2_record_scan_events), which only a caller that
+ *    sets it uses.  Calls on different streams may overlap if their outputs
+ *    and workspaces are distinct.  No exception, abort or print ever leaves
+ *    the library.
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -284,19 +288,24 @@ csa2_status csa2_sparse_attn_append(const void* q, int q_dtype, int n_q, int h, 
                                     size_t ws_bytes, void* stream);
 size_t csa2_sparse_attn_ws_bytes(int n_q, int h, int k, int w_max);
 
-/* ------------------------------------------------------------------------
- * csa2_record_scan_events -- measurement hook.  The next csa2_index_topk or
- * csa2_reindex_topk call made on the calling thread records the hipEvent_t
- * `start` right before and `stop` right after its indexer-scan kernel, on
- * that call's stream, and then forgets both.  Either may be NULL.  Lets a
- * caller time the dominant kernel with its own events while the whole step
- * runs normally. */
-void csa2_record_scan_events(void* start, void* stop);
-
 /* ------------------------------------------------------------------------ */
 const char* csa2_status_string(csa2_status s);
-/* hipError_t of the last CSA2_E_HIP returned on the calling thread. */
+/* hipError_t behind the calling thread's most recent csa2_* call (any entry
+ * point above): hipSuccess (0) unless that call returned CSA2_E_HIP.  One
+ * slot per thread, cleared on entry to every call. */
 int csa2_last_hip_error(void);
+
+/* ========================================================================
+ * Instrumentation (not part of the computation).
+ *
+ * csa2_record_scan_events -- measurement hook, the one piece of per-thread
+ * state a caller sets.  The next csa2_index_topk, csa2_index_topk_chunk or
+ * csa2_reindex_topk call made on the calling thread records the hipEvent_t
+ * `start` right before and `stop` right after its indexer-scan kernel, on
+ * that call's stream, and then forgets both (so the hook applies to exactly
+ * one call).  Either may be NULL.  Lets a caller time the dominant kernel
+ * with its own events while the whole step runs normally. */
+void csa2_record_scan_events(void* start, void* stop);
 
 #ifdef __cplusplus
 }

@@ -3,12 +3,12 @@
 
 #include "../../include/csa2.h"
 
-extern "C" int csa2_internal_last_hip_error_index(void);
-extern "C" int csa2_internal_last_hip_error_attn(void);
-extern "C" int csa2_internal_last_hip_error_quant(void);
-extern "C" int csa2_internal_last_hip_error_blocks(void);
-extern "C" int csa2_internal_last_hip_error_window(void);
-extern "C" int csa2_internal_last_hip_error_merge(void);
+namespace csa2 {
+namespace {
+thread_local int g_last_hip_error = 0;   // one slot per thread, for every entry point
+}
+__attribute__((visibility("hidden"))) void set_last_hip_error(int e) { g_last_hip_error = e; }
+}  // namespace csa2
 
 extern "C" const char* csa2_status_string(csa2_status s) {
   switch (s) {
@@ -21,12 +21,4 @@ extern "C" const char* csa2_status_string(csa2_status s) {
   return "unknown status";
 }
 
-extern "C" int csa2_last_hip_error(void) {
-  int e = csa2_internal_last_hip_error_index();
-  if (!e) e = csa2_internal_last_hip_error_attn();
-  if (!e) e = csa2_internal_last_hip_error_quant();
-  if (!e) e = csa2_internal_last_hip_error_blocks();
-  if (!e) e = csa2_internal_last_hip_error_window();
-  if (!e) e = csa2_internal_last_hip_error_merge();
-  return e;
-}
+extern "C" int csa2_last_hip_error(void) { return csa2::g_last_hip_error; }

@@ -78,15 +78,10 @@ __global__ __launch_bounds__(kBlockKeyThreads) void k_block_keys(const uint16_t*
 
 }  // namespace csa2
 
-namespace {
-thread_local int g_block_hip_error = 0;
-}
-
-extern "C" int csa2_internal_last_hip_error_blocks(void) { return g_block_hip_error; }
-
 extern "C" csa2_status csa2_block_keys(const uint16_t* ik, int d_i, const int64_t* seq_base, const int32_t* seq_len,
                                        const int32_t* blk_from, int n_seq, int max_blocks, uint16_t* kbar,
                                        const int64_t* kbar_base, void* stream) {
+  csa2::set_last_hip_error(0);
   if (n_seq < 0 || max_blocks < 0) return CSA2_E_INVAL;
   if (d_i < 8 || d_i > 1024 || (d_i & 7)) return CSA2_E_UNSUPPORTED;
   if (n_seq == 0 || max_blocks == 0) return CSA2_OK;
@@ -104,7 +99,7 @@ extern "C" csa2_status csa2_block_keys(const uint16_t* ik, int d_i, const int64_
                      kbar_base);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
-    g_block_hip_error = (int)e;
+    csa2::set_last_hip_error((int)e);
     return CSA2_E_HIP;
   }
   return CSA2_OK;

@@ -16,6 +16,11 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// The hipError_t behind the most recent csa2_* call of the calling thread: one
+// slot per thread (defined in api.hip); every entry point clears it on entry
+// and sets it when a launch fails.
+__attribute__((visibility("hidden"))) void set_last_hip_error(int e);
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).

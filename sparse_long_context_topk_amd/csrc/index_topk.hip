@@ -2014,7 +2014,6 @@ int reindex_chunk_for(int n_q, int64_t slots) {
   return chunk;
 }
 
-thread_local int g_last_hip_error = 0;
 thread_local hipEvent_t g_scan_ev_start = nullptr;
 thread_local hipEvent_t g_scan_ev_stop = nullptr;
 
@@ -2070,7 +2069,7 @@ float bound_constant(int d_i, bool block) {
 bool launch_ok() {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
-    g_last_hip_error = (int)e;
+    set_last_hip_error((int)e);
     return false;
   }
   return true;
@@ -2184,8 +2183,6 @@ bool shape_ok(int h_i, int d_i) { return h_i >= 1 && h_i <= 64 && (d_i == 64 || 
 
 }  // namespace
 
-extern "C" int csa2_internal_last_hip_error_index(void) { return g_last_hip_error; }
-
 extern "C" void csa2_record_scan_events(void* start, void* stop) {
   g_scan_ev_start = static_cast<hipEvent_t>(start);
   g_scan_ev_stop = static_cast<hipEvent_t>(stop);
@@ -2212,6 +2209,7 @@ extern "C" csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n
                                        const uint16_t* ik, const int64_t* seq_base, int k, int32_t* idx_out,
                                        int block, int keep_blocks, int32_t* pool_out, void* ws, size_t ws_bytes,
                                        void* stream) {
+  csa2::set_last_hip_error(0);
   if (n_q < 0 || max_nvis < 0 || k < 1 || k > 2048 || keep_blocks < 0 || keep_blocks > 4096)
     return CSA2_E_INVAL;
   if ((int64_t)max_nvis > (int64_t)kMaxChunksLds * kCmpChunk) return CSA2_E_UNSUPPORTED;
@@ -2256,6 +2254,7 @@ extern "C" csa2_status csa2_index_topk_chunk(const uint16_t* iq, const float* w,
                                              const int32_t* q_nvis, int32_t max_nvis, const uint16_t* ik,
                                              int64_t ik_base, int k, int32_t* idx_out, void* ws, size_t ws_bytes,
                                              void* stream) {
+  csa2::set_last_hip_error(0);
   if (n_q < 0 || max_nvis < 0 || k < 1 || k > 2048 || ik_base < 0) return CSA2_E_INVAL;
   if ((int64_t)max_nvis > (int64_t)kMaxChunksLds * kCmpChunk) return CSA2_E_UNSUPPORTED;
   if (!shape_ok(h_i, d_i)) return CSA2_E_UNSUPPORTED;
@@ -2281,6 +2280,7 @@ extern "C" csa2_status csa2_reindex_topk(const uint16_t* iq, const float* w, int
                                          const int64_t* seq_base, const int32_t* pool_blocks, int block,
                                          int keep_blocks, int k, int32_t* idx_out, void* ws, size_t ws_bytes,
                                          void* stream) {
+  csa2::set_last_hip_error(0);
   if (n_q < 0 || k < 1 || k > 2048 || keep_blocks < 1 || keep_blocks > 4096) return CSA2_E_INVAL;
   if (!shape_ok(h_i, d_i)) return CSA2_E_UNSUPPORTED;
   if (block != 8) return CSA2_E_UNSUPPORTED;

@@ -77,14 +77,9 @@ __global__ __launch_bounds__(256) void k_quant_append(const void* x, int x_dtype
 
 }  // namespace csa2
 
-namespace {
-thread_local int g_quant_hip_error = 0;
-}
-
-extern "C" int csa2_internal_last_hip_error_quant(void) { return g_quant_hip_error; }
-
 extern "C" csa2_status csa2_quant_append(const void* x, int x_dtype, int64_t n_rows, const int64_t* dst_row,
                                          uint8_t* cache, int64_t cache_rows, void* stream) {
+  csa2::set_last_hip_error(0);
   if (n_rows < 0 || cache_rows < 0) return CSA2_E_INVAL;
   if (x_dtype != CSA2_F32 && x_dtype != CSA2_BF16) return CSA2_E_INVAL;
   if (n_rows == 0) return CSA2_OK;
@@ -99,7 +94,7 @@ extern "C" csa2_status csa2_quant_append(const void* x, int x_dtype, int64_t n_r
                      x, x_dtype, n_rows, dst_row, cache, cache_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
-    g_quant_hip_error = (int)e;
+    csa2::set_last_hip_error((int)e);
     return CSA2_E_HIP;
   }
   return CSA2_OK;

@@ -945,8 +945,6 @@ using namespace csa2::attn;
 
 namespace {
 
-thread_local int g_attn_hip_error = 0;
-
 struct Split {
   int nsub, nsplit, per;
 };
@@ -970,8 +968,6 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-extern "C" int csa2_internal_last_hip_error_attn(void) { return g_attn_hip_error; }
-
 extern "C" size_t csa2_sparse_attn_ws_bytes(int n_q, int h, int k, int w_max) {
   if (n_q <= 0 || h <= 0) return 0;
   const Split s = choose_split(n_q, k, w_max);
@@ -987,6 +983,7 @@ csa2_status attn_call(const void* q, int q_dtype, int n_q, int h, int d, const i
                       const uint16_t* swa, const int64_t* swa_row0, const int32_t* swa_len, int w_max,
                       float softmax_scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream,
                       const uint16_t* swa_new, const int64_t* swa_dst, int64_t swa_rows) {
+  set_last_hip_error(0);
   if (n_q < 0 || k < 0 || k > 2048 || w_max < 0 || w_max > 1024) return CSA2_E_INVAL;
   if (q_dtype != CSA2_F32 && q_dtype != CSA2_BF16) return CSA2_E_INVAL;
   if (d != CSA2_KV_CH || h < 16 || h > 64 || h % 16 != 0) return CSA2_E_UNSUPPORTED;
@@ -1018,14 +1015,14 @@ csa2_status attn_call(const void* q, int q_dtype, int n_q, int h, int d, const i
   else hipLaunchKernelGGL(k_attn2, grid, dim3(2 * kThreads), 0, st, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
-    g_attn_hip_error = (int)e;
+    set_last_hip_error((int)e);
     return CSA2_E_HIP;
   }
   if (s.nsplit > 1) {
     hipLaunchKernelGGL(k_merge, dim3(n_q, (h + 3) / 4), dim3(kThreads), 0, st, P);
     e = hipGetLastError();
     if (e != hipSuccess) {
-      g_attn_hip_error = (int)e;
+      set_last_hip_error((int)e);
       return CSA2_E_HIP;
     }
   }
@@ -1051,7 +1048,10 @@ extern "C" csa2_status csa2_sparse_attn_append(const void* q, int q_dtype, int n
                                                const uint16_t* swa_new, const int64_t* swa_dst,
                                                float softmax_scale, float* out, float* lse, void* ws,
                                                size_t ws_bytes, void* stream) {
-  if (!swa_new) return CSA2_E_INVAL;
+  if (!swa_new) {
+    set_last_hip_error(0);
+    return CSA2_E_INVAL;
+  }
   return attn_call(q, q_dtype, n_q, h, d, q_seq, cache, seq_base, idx, k, swa, swa_row0, swa_len, w_max,
                    softmax_scale, out, lse, ws, ws_bytes, stream, swa_new, swa_dst, swa_rows);
 }

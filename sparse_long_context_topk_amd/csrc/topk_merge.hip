@@ -75,8 +75,6 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_remap(const int32_t* __
 
 namespace {
 
-thread_local int g_merge_hip_error = 0;
-
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kMergeSmall = 16384;   // candidates up to which the Reindex select runs
@@ -105,8 +103,6 @@ MergeLayout merge_layout(int n_q, int n_cand, int d_i, int k, int h_i) {
 
 }  // namespace
 
-extern "C" int csa2_internal_last_hip_error_merge(void) { return g_merge_hip_error; }
-
 extern "C" size_t csa2_topk_merge_ws_bytes(int n_q, int n_cand, int h_i, int d_i, int k) {
   if (n_q <= 0 || n_cand <= 0 || d_i <= 0 || k <= 0) return 0;
   return merge_layout(n_q, n_cand, d_i, k, h_i).total;
@@ -116,6 +112,7 @@ extern "C" csa2_status csa2_topk_merge(const uint16_t* iq, const float* w, int n
                                        const int32_t* q_seq, const uint16_t* ik, const int64_t* seq_base,
                                        const int32_t* cand, int n_cand, int k, int32_t* idx_out, void* ws,
                                        size_t ws_bytes, void* stream) {
+  csa2::set_last_hip_error(0);
   if (n_q < 0 || n_cand < 0 || k < 1 || k > 2048) return CSA2_E_INVAL;
   if (d_i != 64 && d_i != 128) return CSA2_E_UNSUPPORTED;
   if (n_cand > (1 << 25)) return CSA2_E_UNSUPPORTED;
@@ -143,7 +140,7 @@ extern "C" csa2_status csa2_topk_merge(const uint16_t* iq, const float* w, int n
                        static_cast<const int32_t*>(nullptr), k, static_cast<const int32_t*>(nullptr), 0, idx_out);
     e = hipGetLastError();
     if (e != hipSuccess) {
-      g_merge_hip_error = (int)e;
+      csa2::set_last_hip_error((int)e);
       return CSA2_E_HIP;
     }
     return CSA2_OK;
@@ -154,7 +151,7 @@ extern "C" csa2_status csa2_topk_merge(const uint16_t* iq, const float* w, int n
                      kbase, pool, nb);
   e = hipGetLastError();
   if (e != hipSuccess) {
-    g_merge_hip_error = (int)e;
+    csa2::set_last_hip_error((int)e);
     return CSA2_E_HIP;
   }
   const csa2_status s =
@@ -167,7 +164,7 @@ extern "C" csa2_status csa2_topk_merge(const uint16_t* iq, const float* w, int n
                      idx_out);
   e = hipGetLastError();
   if (e != hipSuccess) {
-    g_merge_hip_error = (int)e;
+    csa2::set_last_hip_error((int)e);
     return CSA2_E_HIP;
   }
   return CSA2_OK;

@@ -50,14 +50,9 @@ __global__ __launch_bounds__(256) void k_window_append(const void* __restrict__ 
 
 }  // namespace csa2
 
-namespace {
-thread_local int g_window_hip_error = 0;
-}
-
-extern "C" int csa2_internal_last_hip_error_window(void) { return g_window_hip_error; }
-
 extern "C" csa2_status csa2_window_append(const void* x, int x_dtype, int64_t n_rows, const int64_t* dst_row,
                                           uint16_t* swa, int64_t swa_rows, void* stream) {
+  csa2::set_last_hip_error(0);
   if (n_rows < 0 || swa_rows < 0) return CSA2_E_INVAL;
   if (x_dtype != CSA2_F32 && x_dtype != CSA2_BF16) return CSA2_E_INVAL;
   if (n_rows == 0) return CSA2_OK;
@@ -71,7 +66,7 @@ extern "C" csa2_status csa2_window_append(const void* x, int x_dtype, int64_t n_
                      x, x_dtype == CSA2_F32 ? 1 : 0, n_rows, dst_row, swa, swa_rows);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
-    g_window_hip_error = (int)e;
+    csa2::set_last_hip_error((int)e);
     return CSA2_E_HIP;
   }
   return CSA2_OK;
