@@ -67,6 +67,8 @@ def lib():
         L.csa2_ref_dequant_record.argtypes = [vp, vp]
         L.csa2_ref_index_score.restype = f32
         L.csa2_ref_index_score.argtypes = [vp, vp, i32, i32, vp]
+        L.csa2_ref_block_score.restype = f32
+        L.csa2_ref_block_score.argtypes = [vp, vp, i32, i32, vp, i32]
         L.csa2_ref_topk.restype = None
         L.csa2_ref_topk.argtypes = [vp, vp, i64, i32, vp]
         L.csa2_ref_index_topk.restype = i32
@@ -157,6 +159,17 @@ def index_score(iq: np.ndarray, w: np.ndarray, key: np.ndarray) -> float:
     key = _c(key, np.uint16)
     h_i, d_i = iq.shape
     return lib().csa2_ref_index_score(_p(iq), _p(w), h_i, d_i, _p(key))
+
+
+def block_score(iq: np.ndarray, w: np.ndarray, keys: np.ndarray) -> float:
+    """Score of one pool block whose members are the rows of keys (uint16
+    [n_members, d_i]): the mean of the members' per-head dots (fp32 sum in row
+    order, IEEE division), then ReLU and the head chain as for a token."""
+    iq = _c(iq, np.uint16)
+    w = _c(w, np.float32)
+    keys = _c(keys, np.uint16)
+    h_i, d_i = iq.shape
+    return lib().csa2_ref_block_score(_p(iq), _p(w), h_i, d_i, _p(keys), keys.shape[0])
 
 
 def topk(scores: np.ndarray, k: int, pos: np.ndarray | None = None) -> np.ndarray:

@@ -230,6 +230,24 @@ float csa2_ref_index_score(const uint16_t* iq, const float* w, int h_i, int d_i,
   return s;
 }
 
+/* Score of one pool block: the members' per-head dots summed in fp32 in
+ * ascending position order from +0, divided by the member count (IEEE),
+ * then ReLU and the head fma chain as for a token (reading documented at
+ * csa2_ref_index_topk below). */
+float csa2_ref_block_score(const uint16_t* iq, const float* w, int h_i, int d_i,
+                           const uint16_t* keys, int n_members) {
+  const float cnt = (float)n_members;
+  float s = 0.0f;
+  for (int h = 0; h < h_i; ++h) {
+    float sum = 0.0f;
+    for (int t = 0; t < n_members; ++t) sum = sum + head_dot(iq + (size_t)h * d_i, keys + (size_t)t * d_i, d_i);
+    float mean = sum / cnt;
+    float r = (mean > 0.0f) ? mean : 0.0f;
+    s = std::fma(w[h], r, s);
+  }
+  return s;
+}
+
 /* ======================================================================
  * a4: Top-K.  Order candidates by score descending, equal scores by the
  * lower position first (-0 and +0 compare equal); keep the first min(K, n);
@@ -289,17 +307,7 @@ int csa2_ref_index_topk(const uint16_t* iq, const float* w, int n_q, int h_i, in
       std::vector<float> bs((size_t)nb);
       for (int64_t b = 0; b < nb; ++b) {
         int64_t t0 = b * block, t1 = std::min<int64_t>(nvis, t0 + block);
-        float cnt = (float)(t1 - t0);
-        float s = 0.0f;
-        for (int h = 0; h < h_i; ++h) {
-          float sum = 0.0f;
-          for (int64_t t = t0; t < t1; ++t)
-            sum = sum + head_dot(qv + (size_t)h * d_i, keys + (size_t)t * d_i, d_i);
-          float mean = sum / cnt;
-          float r = (mean > 0.0f) ? mean : 0.0f;
-          s = std::fma(wv[h], r, s);
-        }
-        bs[(size_t)b] = s;
+        bs[(size_t)b] = csa2_ref_block_score(qv, wv, h_i, d_i, keys + (size_t)t0 * d_i, (int)(t1 - t0));
       }
       csa2_ref_topk(bs.data(), nullptr, nb, keep_blocks, pool_out + (size_t)q * keep_blocks);
     }

@@ -52,6 +52,11 @@ void csa2_ref_dequant_record(const uint8_t* rec, float* out512);
 float csa2_ref_index_score(const uint16_t* iq, const float* w, int h_i, int d_i,
                            const uint16_t* key);
 
+/* ---- a3: score of one pool block of n_members consecutive keys (the mean of
+ *      the members' per-head dots, fp32 sum ascending, IEEE division) ------ */
+float csa2_ref_block_score(const uint16_t* iq, const float* w, int h_i, int d_i,
+                           const uint16_t* keys, int n_members);
+
 /* ---- a4: Top-K by (score desc, position asc), output ascending, -1 pad - */
 void csa2_ref_topk(const float* scores, const int32_t* pos, int64_t n, int k, int32_t* out);
 

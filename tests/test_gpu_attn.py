@@ -149,3 +149,71 @@ def test_many_queries_long_splits(n_q, h, k, nswa):
     print(f"normwise err {err:.3e}")
     assert err <= TOL
     assert np.allclose(l, rl, rtol=1e-4, atol=1e-4)
+
+
+@gpu
+@pytest.mark.parametrize("n_q,h,qdt", [(3, 64, torch.bfloat16), (2, 16, torch.float32), (40, 64, torch.bfloat16)])
+def test_largest_selection_and_window(n_q, h, qdt):
+    """The largest supported lists: k = 2048 selected entries and windows of up
+    to w_max = 1024 rows (3072 keys per query)."""
+    note(f"attn k=2048 w_max=1024 n_q={n_q} h={h} {qdt}")
+    c = _case(n_q, h, 4096, 2048, 1024, qdt, seed=70 + n_q)
+    o, l, ro, rl = _run(c)
+    err = normwise_err(o, ro)
+    print(f"normwise err {err:.3e}")
+    assert err <= TOL
+    assert np.allclose(l, rl, rtol=1e-4, atol=1e-4)
+
+
+def _scaled_rows(n, seed, group_scale):
+    """N(0,1) rows whose 16-channel groups are multiplied by group_scale[row, group]."""
+    x = gen.normal((n, 512), seed, "kv-small", dtype=torch.float32)
+    return (x.view(n, 32, 16) * torch.from_numpy(group_scale)[:, :, None]).view(n, 512).to(torch.bfloat16)
+
+
+@gpu
+def test_subnormal_and_zero_scales():
+    """FP4 records whose E4M3 scales are subnormal (groups scaled by 2^-7 and
+    2^-8: amax / 6 falls in [2^-9, 2^-6)) or zero (groups scaled by 2^-12, and
+    all-zero groups), gathered with k = 2048 and a 1024-row window of the same
+    magnitude, so that the decoded values of these groups carry the output."""
+    note("attn subnormal and zero scales")
+    n_q, L, k = 4, 4096, 2048
+    rng = np.random.default_rng(77)
+    fac = rng.choice([2.0 ** -7, 2.0 ** -8, 2.0 ** -12, 0.0], size=(n_q * L, 32), p=[0.45, 0.35, 0.1, 0.1])
+    raw = _scaled_rows(n_q * L, 77, fac.astype(np.float32))
+    cache = oracle.quantize_rows(bits(raw))
+    sc = cache[:, 256:288]
+    subn = ((sc & 0x78) == 0) & ((sc & 0x07) != 0)
+    print(f"scales: {subn.mean():.2f} subnormal, {(sc == 0).mean():.2f} zero")
+    assert subn.mean() > 0.5 and (sc == 0).mean() > 0.1
+    c = _case(n_q, 64, L, k, 1024, torch.bfloat16, seed=78)
+    c["cache"] = cache
+    c["swa"] = (c["swa"].float() * 2.0 ** -7).to(torch.bfloat16)
+    o, l, ro, rl = _run(c, scale=8.0)
+    err = normwise_err(o, ro)
+    print(f"normwise err {err:.3e}")
+    assert err <= TOL
+    # window off: the output is made of the decoded FP4 values alone
+    c["swa_len"][:] = 0
+    o, l, ro, rl = _run(c, scale=8.0)
+    assert normwise_err(o, ro) <= TOL
+
+
+@gpu
+def test_bf16_values_near_the_fp16_range_limit():
+    """bf16 queries and window rows are converted to fp16 for the MFMA: values
+    up to the documented limit (|x| < 65504) stay exact in range; elements of
+    magnitude up to 60,000 in the query and in the window rows."""
+    note("attn fp16 range edge")
+    c = _case(3, 64, 2048, 512, 128, torch.bfloat16, seed=79)
+    q = c["q"].float()
+    q[:, :, ::37] = 60000.0 * torch.sign(q[:, :, ::37])
+    c["q"] = q.to(torch.bfloat16)
+    s = c["swa"].float()
+    s[::5, ::41] = -59904.0
+    c["swa"] = s.to(torch.bfloat16)
+    o, l, ro, rl = _run(c, scale=2.0 ** -40)
+    err = normwise_err(o, ro)
+    print(f"normwise err {err:.3e}")
+    assert err <= TOL

@@ -54,10 +54,14 @@ def test_full_short_ragged_lengths(h_i, d_i):
 
 
 @gpu
+@pytest.mark.parametrize("lengths", [[20000, 3000, 1], [9000, 3000, 1]], ids=["multi_kernel", "short"])
 @pytest.mark.parametrize("k", [1, 64, 512, 2048])
-def test_full_k_values(k):
-    note(f"full k={k}")
-    inp = index_inputs([9000, 3000, 1], 64, 128, seed=7 + k)
+def test_full_k_values(k, lengths):
+    # a context above 16,384 positions takes the multi-kernel selection (fine
+    # histogram, compaction, rescoring, final select); all contexts at or below
+    # it take the one-work-group select over every block of the context
+    note(f"full k={k} lengths={lengths}")
+    inp = index_inputs(lengths, 64, 128, seed=7 + k)
     assert np.array_equal(_gpu_full(inp, k), _ref_full(inp, k))
 
 
@@ -278,3 +282,141 @@ def test_reindex_at_every_scan_chunk_size(n_q, chunk):
     ref = oracle.reindex_topk(bits(iq2), w2.numpy(), inp["q_seq"].numpy(), inp["nvis"].numpy(), bits(inp["ik"]),
                               inp["seq_base"].numpy(), pool, 512, block=8)
     assert np.array_equal(got.cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------- rounding bound of the MFMA scores
+def _bound_consts(d_i):
+    """The scan's rounding constants: per key, |approximate - exact fp32 chain|
+    <= C * t_k with t_k = sum_h |w_h| sum_d |q_hd| |k_d| (tokens), and for a
+    block <= C_blk * (its members' largest t_k)."""
+    u, u2 = 2.0 ** -24, 2.0 ** -23
+    gam = lambda n, uu: n * uu / (1 - n * uu)
+    e = gam(d_i, u) + gam(d_i + 2, u2)
+    eb = e + 2 * gam(8, u) + 8 * u
+    gh = gam(66, u)
+    return 2 * (e + gh * (2 + e)), 2 * (eb + gh * (2 + eb))
+
+
+def _t_of(iq_bits, w, ik_bits):
+    qf = (iq_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    kf = (ik_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.abs(kf) @ (np.abs(w.astype(np.float64))[:, None] * np.abs(qf)).sum(axis=0)
+
+
+@gpu
+def test_full_pool_scan_scores_within_proven_bound():
+    """The 1M decode path's scan (Full layer with the pool): every token score
+    and every block score it leaves in the workspace lies within the rounding
+    bound the selection relies on, against the exact fp32 chains of the score
+    definition -- contexts above 16,384 positions, a partial last block in both
+    sequences, keys with 20x outliers.  Block scores include the partial
+    blocks' mean (a reciprocal of the member count)."""
+    note("mfma bound: full + pool scan")
+    lengths, h_i, d_i, keep = [20003, 17001], 64, 128, 2048
+    inp = index_inputs(lengths, h_i, d_i, seed=19)
+    total = sum(lengths)
+    inp["ik"] = (inp["ik"].float() * torch.where(torch.arange(total)[:, None] % 97 == 0, 20.0, 1.0)).to(torch.bfloat16)
+    ws = csa2.Workspace()
+    g_idx, g_pool = _gpu_full(inp, 512, keep, ws=ws)
+    r_idx, r_pool = _ref_full(inp, 512, keep)
+    assert np.array_equal(g_idx, r_idx) and np.array_equal(g_pool, r_pool)
+    n_q = len(lengths)
+    stride = (max(lengths) + 4095) // 4096 * 4096
+    sc = ws.buf[:2 * n_q * stride * 4].view(torch.float32).cpu().numpy().astype(np.float64).reshape(2 * n_q, stride)
+    c_tok, c_blk = _bound_consts(d_i)
+    iqb, ikb, w, sb = bits(inp["iq"]), bits(inp["ik"]), inp["w"].numpy(), inp["seq_base"].numpy()
+    worst_t = worst_b = 0.0
+    for q, L in enumerate(lengths):
+        keys = ikb[sb[q]:sb[q] + L]
+        exact = np.array([oracle.index_score(iqb[q], w[q], keys[t]) for t in range(L)])
+        t = _t_of(iqb[q], w[q], keys)
+        err = np.abs(sc[q, :L] - exact)
+        assert np.all(err <= c_tok * t), f"query {q}: token score outside the bound"
+        worst_t = max(worst_t, float((err / (c_tok * t)).max()))
+        nb = (L + 7) // 8
+        bex = np.array([oracle.block_score(iqb[q], w[q], keys[8 * b:min(L, 8 * b + 8)]) for b in range(nb)])
+        tb = np.array([t[8 * b:min(L, 8 * b + 8)].max() for b in range(nb)])
+        errb = np.abs(sc[n_q + q, :nb] - bex)
+        assert np.all(errb <= c_blk * tb), f"query {q}: block score outside the bound"
+        worst_b = max(worst_b, float((errb / (c_blk * tb)).max()))
+        assert L % 8 != 0                                   # the last block is partial
+    print(f"max |mfma - exact| / bound: tokens {worst_t:.3e}, blocks {worst_b:.3e}")
+
+
+@gpu
+def test_chunk_scan_scores_within_proven_bound():
+    """The encoder-chunk scan (several causal queries of one sequence per
+    work-group, head sums in a different order): every score it leaves in the
+    workspace lies within the rounding bound of the exact chain."""
+    note("mfma bound: chunk scan")
+    L, base, n_q, h_i, d_i = 12000, 100, 5, 64, 128
+    inp = index_inputs([base + L], h_i, d_i, seed=41)
+    inp["ik"] = (inp["ik"].float() * torch.where(torch.arange(base + L)[:, None] % 89 == 0, 20.0, 1.0)).to(torch.bfloat16)
+    nvis = np.array([L - 2001 * i for i in range(n_q)][::-1], np.int32)
+    rng = np.random.default_rng(41)
+    iq = torch.from_numpy(rng.standard_normal((n_q, h_i, d_i)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy(rng.uniform(0, 1, (n_q, h_i)).astype(np.float32))
+    dev = device()
+    ws = csa2.Workspace()
+    got = csa2.index_topk_chunk(iq.to(dev), w.to(dev), torch.from_numpy(nvis).to(dev), int(nvis.max()),
+                                inp["ik"].to(dev), ik_base=base, k=512, ws=ws)
+    torch.cuda.synchronize()
+    iqb, ikb, wn = bits(iq), bits(inp["ik"]), w.numpy()
+    ref = oracle.index_topk(iqb, wn, np.zeros(n_q, np.int32), nvis, ikb, np.array([base], np.int64), 512)
+    assert np.array_equal(got.cpu().numpy(), ref)
+    stride = (int(nvis.max()) + 4095) // 4096 * 4096
+    sc = ws.buf[:n_q * stride * 4].view(torch.float32).cpu().numpy().astype(np.float64).reshape(n_q, stride)
+    c_tok, _ = _bound_consts(d_i)
+    worst = 0.0
+    for q in range(n_q):
+        keys = ikb[base:base + nvis[q]]
+        exact = np.array([oracle.index_score(iqb[q], wn[q], keys[t]) for t in range(nvis[q])])
+        t = _t_of(iqb[q], wn[q], keys)
+        err = np.abs(sc[q, :nvis[q]] - exact)
+        assert np.all(err <= c_tok * t), f"query {q}: chunk score outside the bound"
+        worst = max(worst, float((err / (c_tok * t)).max()))
+    print(f"max |mfma - exact| / bound (chunk scan) = {worst:.3e}")
+
+
+# ---------------------------------------------------------------- bf16 subnormal inputs
+def _subnormal_mix(t, frac, seed):
+    """Replace a fraction of the elements with bf16 subnormals (|x| < 2^-126)."""
+    g = torch.Generator().manual_seed(seed)
+    m = torch.rand(t.shape, generator=g) < frac
+    tiny = (torch.randn(t.shape, generator=g) * 2.0 ** -129).to(torch.bfloat16)
+    return torch.where(m, tiny, t)
+
+
+@gpu
+def test_subnormal_keys_and_queries():
+    """bf16-subnormal key and query elements: a sequence with 30 % subnormal key
+    elements, one whose keys are all subnormal (every score is then a tiny fp32
+    value, many of them subnormal, and the rounding bound's underflow term
+    leaves every key undecided), and queries with 20 % subnormal elements;
+    Full with the pool, Reindex over it, and the short no-pool path."""
+    note("index subnormal inputs")
+    lengths = [20000, 17000, 3000]
+    inp = index_inputs(lengths, 64, 128, seed=43)
+    ik = _subnormal_mix(inp["ik"], 0.3, 1)
+    s1 = inp["seq_base"][1].item()
+    ik[s1:s1 + lengths[1]] = (inp["ik"][s1:s1 + lengths[1]].float() * 2.0 ** -129).to(torch.bfloat16)
+    inp["ik"] = ik
+    inp["iq"] = _subnormal_mix(inp["iq"], 0.2, 2)
+    kb = bits(inp["ik"])
+    exp_field = (kb >> 7) & 0xFF
+    assert np.mean((exp_field == 0) & ((kb & 0x7F) != 0)) > 0.2
+    g_idx, g_pool = _gpu_full(inp, 512, 2048)
+    r_idx, r_pool = _ref_full(inp, 512, 2048)
+    assert np.array_equal(g_idx, r_idx) and np.array_equal(g_pool, r_pool)
+    iq2 = torch.flip(inp["iq"], dims=[1]).contiguous()
+    dev = device()
+    d = to_dev(inp, dev)
+    got = csa2.reindex_topk(iq2.to(dev), d["w"], d["q_seq"], d["nvis"], d["ik"], d["seq_base"],
+                            torch.from_numpy(r_pool).to(dev), k=512)
+    torch.cuda.synchronize()
+    ref = oracle.reindex_topk(bits(iq2), inp["w"].numpy(), inp["q_seq"].numpy(), inp["nvis"].numpy(),
+                              bits(inp["ik"]), inp["seq_base"].numpy(), r_pool, 512, block=8)
+    assert np.array_equal(got.cpu().numpy(), ref)
+    short = dict(inp)
+    short["nvis"] = torch.tensor([9000, 9000, 3000], dtype=torch.int32)   # every context <= 16,384, no pool
+    assert np.array_equal(_gpu_full(short, 512), _ref_full(short, 512))

@@ -9,7 +9,8 @@ seconds of host time for it).  The mixed 64-sequence batch runs its full
 context shortened 16-fold, which keeps contexts above the 16,384-position pool
 and the oracle within seconds.  The encoder-side chunk (4096 causal queries
 over 524,288 compressed entries, Full + 5 Reuse) runs whole on the GPU and is
-checked on a sample of its queries, which the oracle computes one by one."""
+checked on a sample of its queries, which the oracle computes one by one; so
+is the mixed batch at its real lengths, on six of its sequences."""
 import os
 
 import numpy as np
@@ -104,13 +105,22 @@ def test_c3_pool_based_full_variant_1m_batch4():
 
 @gpu
 def test_c4_encoder_chunk_4096_causal_queries_sampled():
-    # the first and last query, and queries spread over the chunk
-    _check_workload("c4", sample=[0, 1, 1023, 2048, 3071, 4094, 4095, 517])
+    # the first and last queries, two more, and every 151st from query 63 (33 in all)
+    sample = sorted(set([0, 1, 4094, 4095, 517, 2048] + list(range(63, 4096, 151))))
+    _check_workload("c4", sample=sample)
 
 
 @gpu
 def test_c5_twenty_layer_schedule_mixed_lengths():
     _check_workload("c5", length_div=16)
+
+
+@gpu
+def test_c5_twenty_layer_schedule_full_size_sampled():
+    # the real lengths (4K .. 1M, 14.8M positions in all), the whole batch on
+    # the GPU; the oracle checks six sequences: the three shortest
+    # (4176, 4379, 5229 positions) and the three longest (up to 1,016,271)
+    _check_workload("c5", sample=[56, 31, 3, 5, 7, 19])
 
 
 @gpu

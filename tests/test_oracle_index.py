@@ -374,3 +374,31 @@ def test_sharded_topk_merge_equals_full_context():
         cand = np.array(cand, np.int32)
         sc = [oracle.index_score(iq[0], w[0], ik[p]) for p in cand]
         assert np.array_equal(oracle.topk(np.array(sc, np.float32), 512, cand), full)
+
+
+def test_block_score_function_special_cases():
+    # a block of one member scores exactly as that member (sum from +0 of one
+    # dot, divided by 1); a block of n equal integer-valued members scores as
+    # each member (the sum and the division by n are exact); random blocks lie
+    # within the fp32 rounding bound of the fp64 mean-of-dots definition
+    rng = np.random.default_rng(25)
+    h_i, d_i = 8, 64
+    for _ in range(20):
+        iq = bf16(rng.standard_normal((h_i, d_i)))
+        w = rng.uniform(0, 1, h_i).astype(np.float32)
+        k1 = bf16(rng.standard_normal((1, d_i)))
+        assert oracle.block_score(iq, w, k1) == oracle.index_score(iq, w, k1[0])
+        qi = bf16(rng.integers(-3, 4, (h_i, d_i)))
+        wi = rng.choice([0.0, 0.5, 1.0], h_i).astype(np.float32)
+        ki = bf16(rng.integers(-3, 4, (1, d_i)))
+        for n in (2, 3, 5, 8):
+            assert oracle.block_score(qi, wi, np.repeat(ki, n, axis=0)) == oracle.index_score(qi, wi, ki[0])
+        keys = bf16(rng.standard_normal((8, d_i)))
+        qf, kf = bf16f(iq).astype(np.float64), bf16f(keys).astype(np.float64)
+        dots = qf @ kf.T                                 # [h_i, 8]
+        exact = float(np.sum(w * np.maximum(dots.mean(axis=1), 0)))
+        u = 2.0 ** -24
+        g = lambda m: m * u / (1 - m * u)
+        absdots = (np.abs(qf) @ np.abs(kf).T).mean(axis=1)
+        bound = float(np.sum(w * ((g(d_i) + g(8) + u) * absdots))) * (1 + g(h_i)) + g(h_i) * exact
+        assert abs(oracle.block_score(iq, w, keys) - exact) <= bound
