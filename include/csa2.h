@@ -175,6 +175,30 @@ csa2_status csa2_reindex_topk(const uint16_t* iq, const float* w, int n_q, int h
 size_t csa2_reindex_topk_ws_bytes(int n_q, int h_i, int d_i, int k, int block, int keep_blocks);
 
 /* ------------------------------------------------------------------------
+ * csa2_reindex_topk_noalloc -- csa2_reindex_topk for callers that cannot
+ * allocate device memory (code under HIP-graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments and result without
+ * ws / ws_bytes.  Its workspace is a fixed array of
+ * CSA2_NOALLOC_SCRATCH_BYTES of device memory inside the library, one per GPU
+ * it runs on, held until the process ends.  The call never allocates or
+ * frees; its first call on a device (the device current on the calling
+ * thread) looks up that device's array.
+ *   Limit: csa2_reindex_topk_ws_bytes(n_q, h_i, d_i, k, block, keep_blocks)
+ *   <= CSA2_NOALLOC_SCRATCH_BYTES (32 MiB: e.g. 64 queries at a 2048-block
+ *   pool need 22 MiB, 47 queries at a 4096-block pool 31 MiB); larger calls
+ *   return CSA2_E_WORKSPACE and enqueue nothing.
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents: calls that overlap on one GPU (different streams or
+ *   threads with no ordering between them) race and give wrong results.
+ *   Calls on one stream are ordered and safe. */
+#define CSA2_NOALLOC_SCRATCH_BYTES (32u << 20)
+csa2_status csa2_reindex_topk_noalloc(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
+                                      const int32_t* q_seq, const int32_t* q_nvis,
+                                      const uint16_t* ik, const int64_t* seq_base,
+                                      const int32_t* pool_blocks, int block, int keep_blocks,
+                                      int k, int32_t* idx_out, void* stream);
+
+/* ------------------------------------------------------------------------
  * csa2_topk_merge -- exact Top-K of each query among given candidate
  * positions: the merge step of one context split over several devices.  Each
  * device runs csa2_index_topk on its position range and keeps its local

@@ -63,6 +63,8 @@ def lib():
                                         vp, sz, vp]
         L.csa2_reindex_topk_ws_bytes.restype = sz
         L.csa2_reindex_topk_ws_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.csa2_reindex_topk_noalloc.restype = i32
+        L.csa2_reindex_topk_noalloc.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp]
         L.csa2_sparse_attn.restype = i32
         L.csa2_sparse_attn.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp, i32,
                                        f32, vp, vp, vp, sz, vp]
@@ -279,6 +281,32 @@ def reindex_topk(iq, w, q_seq, q_nvis, ik, seq_base, pool_blocks, k=512, block=8
                                  _ptr(seq_base), _ptr(pool_blocks), block, keep_blocks, k, _ptr(idx_out),
                                  _ptr(buf), buf.numel(), _stream(dev))
     _check(st, "csa2_reindex_topk")
+    return idx_out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def reindex_topk_noalloc(iq, w, q_seq, q_nvis, ik, seq_base, pool_blocks, k=512, block=8, idx_out=None):
+    """reindex_topk without a caller workspace (csa2_reindex_topk_noalloc): the
+    library's fixed per-GPU scratch array serves as the workspace, so the call
+    allocates nothing when idx_out is given.  Calls overlapping on one GPU race."""
+    _need(iq, torch.bfloat16, "iq")
+    n_q, h_i, d_i = iq.shape
+    _need(w, torch.float32, "w")
+    _need(q_seq, torch.int32, "q_seq")
+    _need(q_nvis, torch.int32, "q_nvis")
+    _need(ik, torch.bfloat16, "ik")
+    _need(seq_base, torch.int64, "seq_base")
+    _need(pool_blocks, torch.int32, "pool_blocks")
+    keep_blocks = pool_blocks.shape[1]
+    dev = iq.device
+    if idx_out is None:
+        idx_out = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    st = lib().csa2_reindex_topk_noalloc(_ptr(iq), _ptr(w), n_q, h_i, d_i, _ptr(q_seq), _ptr(q_nvis), _ptr(ik),
+                                         _ptr(seq_base), _ptr(pool_blocks), block, keep_blocks, k, _ptr(idx_out),
+                                         _stream(dev))
+    _check(st, "csa2_reindex_topk_noalloc")
     return idx_out
 
 

@@ -62,6 +62,7 @@
 #include <algorithm>
 #include <type_traits>
 #include <cmath>
+#include <mutex>
 
 namespace csa2 {
 namespace idx {
@@ -2300,4 +2301,64 @@ extern "C" csa2_status csa2_reindex_topk(const uint16_t* iq, const float* w, int
   P.nchunk_cmp = (int)(P.stride / kCmpChunk);
   const size_t need = csa2_reindex_topk_ws_bytes(n_q, h_i, d_i, k, block, keep_blocks);
   return run_pipeline(P, slots, ws, ws_bytes, static_cast<hipStream_t>(stream), need);
+}
+
+// ---------------------------------------------------------------- allocation-free Reindex
+// A fixed scratch array in device memory, one per GPU the library runs on
+// (held until the process ends), for callers that cannot allocate: the
+// workspace of csa2_reindex_topk_noalloc.  Host code never passes `scratch`
+// itself (in host code the name is a stand-in, not a device address): its
+// device address is looked up once per device and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (nullptr on failure,
+// with the HIP error recorded).
+void* scratch_for_current_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_last_hip_error((int)e);
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_last_hip_error((int)hipErrorInvalidDevice);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      set_last_hip_error((int)(e != hipSuccess ? e : hipErrorInvalidSymbol));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" csa2_status csa2_reindex_topk_noalloc(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
+                                                 const int32_t* q_seq, const int32_t* q_nvis, const uint16_t* ik,
+                                                 const int64_t* seq_base, const int32_t* pool_blocks, int block,
+                                                 int keep_blocks, int k, int32_t* idx_out, void* stream) {
+  csa2::set_last_hip_error(0);
+  if (n_q < 0 || k < 1 || k > 2048 || keep_blocks < 1 || keep_blocks > 4096) return CSA2_E_INVAL;
+  if (!shape_ok(h_i, d_i)) return CSA2_E_UNSUPPORTED;
+  if (block != 8) return CSA2_E_UNSUPPORTED;
+  if (n_q == 0) return CSA2_OK;
+  const size_t need = csa2_reindex_topk_ws_bytes(n_q, h_i, d_i, k, block, keep_blocks);
+  if (need > (size_t)CSA2_NOALLOC_SCRATCH_BYTES) return CSA2_E_WORKSPACE;
+  void* ws = scratch_for_current_device();
+  if (!ws) return CSA2_E_HIP;
+  // the same kernels as csa2_reindex_topk; none of them needs the scratch
+  // cleared beforehand (each launch writes what the next one reads, and the
+  // multi-kernel path's first launch zeroes its histograms)
+  return csa2_reindex_topk(iq, w, n_q, h_i, d_i, q_seq, q_nvis, ik, seq_base, pool_blocks, block, keep_blocks, k,
+                           idx_out, ws, (size_t)CSA2_NOALLOC_SCRATCH_BYTES, stream);
 }
