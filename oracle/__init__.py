@@ -79,6 +79,10 @@ def lib():
                                             i32, i32, vp, i32]
         L.csa2_ref_block_keys.restype = i32
         L.csa2_ref_block_keys.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
+        L.csa2_ref_index_keys_fp8.restype = i32
+        L.csa2_ref_index_keys_fp8.argtypes = [vp, i64, i32, vp, vp]
+        L.csa2_ref_dequant_keys_fp8.restype = None
+        L.csa2_ref_dequant_keys_fp8.argtypes = [vp, vp, i64, i32, vp]
         L.csa2_ref_sparse_attn.restype = i32
         L.csa2_ref_sparse_attn.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, i32,
                                            vp, vp, vp, f32, vp, vp, i32]
@@ -245,6 +249,29 @@ def pool_full_topk(iq, w, q_seq, q_nvis, ik, seq_base, kbar, kbar_base, k, keep_
     pool = index_topk(iq, w, q_seq, q_nblk, kbar, kbar_base, keep_blocks, n_threads=n_threads)
     idx = reindex_topk(iq, w, q_seq, q_nvis, ik, seq_base, pool, k, block=block, n_threads=n_threads)
     return idx, pool
+
+
+# ---------------------------------------------------------------- FP8 indexer keys (variant)
+def index_keys_fp8(ik):
+    """bf16 key rows (uint16 [rows, d_i]) -> (E4M3 codes uint8 [rows, d_i],
+    exponent bytes uint8 [rows]): one power-of-two scale 2^(exps - 127) per row."""
+    ik = _c(ik, np.uint16)
+    rows, d_i = ik.shape
+    codes = np.empty((rows, d_i), np.uint8)
+    exps = np.empty(rows, np.uint8)
+    if lib().csa2_ref_index_keys_fp8(_p(ik), rows, d_i, _p(codes), _p(exps)):
+        raise ValueError("csa2_ref_index_keys_fp8: invalid arguments")
+    return codes, exps
+
+
+def dequant_keys_fp8(codes, exps):
+    """The stored keys code * 2^(exps - 127) as bf16 bits (exact)."""
+    codes = _c(codes, np.uint8)
+    exps = _c(exps, np.uint8)
+    rows, d_i = codes.shape
+    out = np.empty((rows, d_i), np.uint16)
+    lib().csa2_ref_dequant_keys_fp8(_p(codes), _p(exps), rows, d_i, _p(out))
+    return out
 
 
 # ---------------------------------------------------------------- a7

@@ -387,6 +387,84 @@ int csa2_ref_block_keys(const uint16_t* ik, int d_i, const int64_t* seq_base, co
 }
 
 /* ======================================================================
+ * Low-precision indexer keys (a variant; the pages do not give the indexer
+ * key's precision, only that the whole model's global KV is 890 bytes per
+ * token and that the main KV is FP4 [W1, opening paragraph and FP4
+ * section]).  Reading: each key row is stored as OCP E4M3FN codes with one
+ * power-of-two scale per row.
+ *   E = the smallest integer with amax <= 448 * 2^E (amax = the row's largest
+ *       magnitude), raised to at least -124 (a zero row takes -124);
+ *   code_d = the E4M3FN value nearest to k_d / 2^E, ties to the even code,
+ *       sign copied from k_d (so -0 gives 0x80);
+ *   exponent byte = E + 127.
+ * The stored key is code_d * 2^E.  An E4M3 value has at most 4 significant
+ * bits and its quantum is 2^-9, so with E >= -124 every stored key element is
+ * a bf16 value: the variant's indexer score is the ordinary score of these
+ * bf16 keys, and its Full and Reindex selections are csa2_ref_index_topk and
+ * csa2_ref_reindex_topk on them.
+ * ====================================================================== */
+namespace {
+
+/* nearest E4M3FN code (sign 0) to y in [0, 448], ties to even */
+int e4m3_rne_mag(double y) {
+  double q;
+  int e = 0;
+  if (y >= std::ldexp(1.0, -6)) {
+    int ex;
+    std::frexp(y, &ex);        /* y = f 2^ex, f in [0.5, 1) */
+    e = ex - 1;                /* y in [2^e, 2^(e+1)) */
+    q = std::ldexp(1.0, e - 3);
+  } else {
+    q = std::ldexp(1.0, -9);   /* subnormal quantum */
+  }
+  double m = std::nearbyint(y / q);   /* default rounding: ties to even; y / q is exact */
+  if (q == std::ldexp(1.0, -9) && y < std::ldexp(1.0, -6)) return (int)m;   /* 0..8; 8 is 2^-6 (code 0x08) */
+  if (m == 16.0) {
+    m = 8.0;
+    e += 1;
+  }
+  return ((e + 7) << 3) | ((int)m - 8);
+}
+
+int fp8_key_exponent(double amax) {
+  if (amax == 0.0) return -124;
+  int ex;
+  const double f = 2.0 * std::frexp(amax, &ex);   /* amax = f 2^(ex-1), f in [1, 2) */
+  const int u = ex - 1;
+  int E = f <= 1.75 ? u - 8 : u - 7;               /* 448 2^E = 1.75 2^(E+8) */
+  return E < -124 ? -124 : E;
+}
+
+}  // namespace
+
+int csa2_ref_index_keys_fp8(const uint16_t* ik, int64_t rows, int d_i, uint8_t* codes, uint8_t* exps) {
+  if (rows < 0 || d_i < 1) return 1;
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t* k = ik + (size_t)r * d_i;
+    double amax = 0.0;
+    for (int d = 0; d < d_i; ++d) amax = std::max(amax, std::fabs(bf16_to_double(k[d])));
+    const int E = fp8_key_exponent(amax);
+    exps[r] = (uint8_t)(E + 127);
+    for (int d = 0; d < d_i; ++d) {
+      const double x = bf16_to_double(k[d]);
+      const double y = std::ldexp(std::fabs(x), -E);   /* exact */
+      codes[(size_t)r * d_i + d] = (uint8_t)(e4m3_rne_mag(y) | (std::signbit(x) ? 0x80 : 0));
+    }
+  }
+  return 0;
+}
+
+void csa2_ref_dequant_keys_fp8(const uint8_t* codes, const uint8_t* exps, int64_t rows, int d_i, uint16_t* out) {
+  for (int64_t r = 0; r < rows; ++r) {
+    const int E = (int)exps[r] - 127;
+    for (int d = 0; d < d_i; ++d) {
+      const double v = std::ldexp(csa2_ref_e4m3_value(codes[(size_t)r * d_i + d]), E);
+      out[(size_t)r * d_i + d] = csa2_ref_bf16_bits((float)v);   /* exact: see above */
+    }
+  }
+}
+
+/* ======================================================================
  * a6+a7: attention of one decode query over the selected main-KV entries
  * merged with the layer's sliding-window rows.  Every layer runs a 128-token
  * sliding window [W1, encoder-decoder section] and keeps its own main Q and

@@ -82,6 +82,13 @@ int csa2_ref_block_keys(const uint16_t* ik, int d_i, const int64_t* seq_base, co
                         const int32_t* blk_from, int n_seq, int block, int max_blocks,
                         uint16_t* kbar, const int64_t* kbar_base);
 
+/* ---- FP8 indexer keys (variant): per row, E = smallest integer with
+ *      amax <= 448 * 2^E, at least -124; code = nearest E4M3FN to k / 2^E
+ *      (ties even, sign copied); exps[r] = E + 127.  The stored key
+ *      code * 2^E is a bf16 value. ------------------------------------------- */
+int csa2_ref_index_keys_fp8(const uint16_t* ik, int64_t rows, int d_i, uint8_t* codes, uint8_t* exps);
+void csa2_ref_dequant_keys_fp8(const uint8_t* codes, const uint8_t* exps, int64_t rows, int d_i, uint16_t* out);
+
 /* ---- a6+a7(+a8): sparse attention over selected FP4 entries + SWA ------ */
 int csa2_ref_sparse_attn(const void* q, int q_dtype, int n_q, int h, int d,
                          const int32_t* q_seq, const uint8_t* cache, const int64_t* seq_base,
