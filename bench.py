@@ -47,6 +47,10 @@ def parse():
     p.add_argument("--full-from-pool", action="store_true",
                    help="the pool-based Full variant: the Full layer picks its Top-K inside its own pool, "
                         "scanning stored block keys instead of every token key (reported as its own workload)")
+    p.add_argument("--fp8-keys", action="store_true",
+                   help="the low-precision indexer-key variant: indexer keys stored as E4M3 codes with one "
+                        "power-of-two scale per row (129 bytes per 128-dim key); the Full and Reindex layers score "
+                        "the stored keys (reported as its own workload)")
     p.add_argument("--graph", action="store_true",
                    help="also capture the step as a HIP graph and report the replayed step's rate as `value` "
                         "(the eager steps still time the scan for `roofline`)")
@@ -92,6 +96,10 @@ def build_state(wl, dev):
         st.q_nblk = torch.tensor([(n + 7) // 8 for n in wl["q_nvis"]], dtype=torch.int32, device=dev)
         st.max_nblk = max((n + 7) // 8 for n in wl["q_nvis"])
         csa2.block_keys(ik, st.seq_base, lens, st.kbar, kb_base, max(nblk))
+    if wl.get("fp8_keys"):
+        # the keys' FP8 copy, written before timing as a cache would hold it
+        st.ik8, st.ik8_exp = csa2.index_keys_fp8(ik)
+        st.fp8_keys = True
     layers = [LayerInputs(**gen.layer_tensors(wl, i, dev)) for i in range(len(wl["layers"]))]
     app_x, app_rows = gen.append_rows(wl, dev)
     torch.cuda.synchronize()
@@ -114,7 +122,12 @@ def scan_bytes(wl):
     (one per 8 visible positions)."""
     n_q, h_i, d_i = wl["n_q"], wl["h_i"], wl["d_i"]
     keys = sum((n + 7) // 8 for n in wl["q_nvis"]) if wl.get("pool_full") else sum(wl["q_nvis"])
-    return keys * d_i * 2 + n_q * (h_i * d_i * 2 + h_i * 4)
+    return keys * key_bytes(wl) + n_q * (h_i * d_i * 2 + h_i * 4)
+
+
+def key_bytes(wl):
+    """Bytes of one stored indexer key: bf16, or FP8 codes plus the row's exponent byte."""
+    return wl["d_i"] + 1 if wl.get("fp8_keys") else 2 * wl["d_i"]
 
 
 def step_bytes(wl):
@@ -140,7 +153,7 @@ def step_bytes(wl):
         elif mode == "full":
             b += scan_bytes(wl) + n_q * k * 4 + (n_q * wl["keep_blocks"] * 4)
         elif mode == "reindex":
-            b += sum(min(L, 8 * wl["keep_blocks"]) for L in nvis) * d_i * 2
+            b += sum(min(L, 8 * wl["keep_blocks"]) for L in nvis) * key_bytes(wl)
             b += n_q * (h_i * d_i * 2 + h_i * 4 + wl["keep_blocks"] * 4 + k * 4)
         # attention: selected records and window rows, q in, out
         b += sum(min(k, L) * 288 for L in nvis)
@@ -256,6 +269,9 @@ def cpu_baseline(wl, st, layers, app_x, dev, nseq, gpu_results):
     base = [int(wl["seq_base"][i]) for i in sel]
     cbase = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
     ik = np.concatenate([bits(st.ik[b:b + L]) for b, L in zip(base, lens)])
+    if wl.get("fp8_keys"):
+        # the variant scores the stored FP8 keys: the oracle quantises the same bf16 keys itself
+        ik = oracle.dequant_keys_fp8(*oracle.index_keys_fp8(ik))
 
     def raw_rows(crow):
         # compact row -> (sequence, position) -> global row of the generator
@@ -366,6 +382,11 @@ def main():
         copy_calibration(a.copy_calibration, dev)
         return
     wl = gen.workload(a.workload)
+    if a.fp8_keys:
+        if a.full_from_pool or wl.get("chunk") or wl["d_i"] != 128:
+            sys.exit("--fp8-keys serves the decode workloads with a 128-dim indexer (c2, c3, c5)")
+        wl["fp8_keys"] = True
+        wl["desc"] += "; FP8 indexer keys (E4M3 codes, one power-of-two scale per row)"
     if a.full_from_pool:
         if not wl["keep_blocks"] or "full" not in wl["layers"]:
             sys.exit(f"--full-from-pool needs a workload with a Full layer and a pool ({a.workload} has none)")
@@ -435,7 +456,9 @@ def main():
         sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
         traffic = traffic_from_profile(sha)
         kname = "k_scan over block keys (pool-based Full)" if wl.get("pool_full") else "k_scan (indexer scan, Full layer)"
-        if wl.get("pool_full") or a.workload != "c3":
+        if wl.get("fp8_keys"):
+            kname = "k_scan over FP8 keys (indexer scan, Full layer)"
+        if wl.get("pool_full") or wl.get("fp8_keys") or a.workload != "c3":
             traffic = None   # the committed counters cover the 1M batch-4 token scan only
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),

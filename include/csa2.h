@@ -199,6 +199,46 @@ csa2_status csa2_reindex_topk_noalloc(const uint16_t* iq, const float* w, int n_
                                       int k, int32_t* idx_out, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Low-precision indexer keys (a variant).  The pages give the whole model's
+ * global KV per token (890 bytes) and the main KV's FP4 format, not the
+ * indexer key's precision (source as above: the opening paragraph and
+ * section "FP4 KV, ограниченное повторное проигрывание и другие
+ * расширения").  In this variant each key row is stored as OCP E4M3FN codes
+ * with one power-of-two scale per row, 129 bytes per 128-dim key instead of
+ * 256, and the score is the ordinary score (see csa2_index_topk) of the
+ * stored keys, so the selections stay exact with respect to them.
+ *
+ * csa2_index_keys_fp8 -- quantise key rows:
+ *   ik       [rows][d_i] bf16 keys;  codes [rows][d_i] E4M3FN bytes;
+ *   exps     [rows] bytes, E + 127, where E is the smallest integer with
+ *            max_d |ik[r][d]| <= 448 * 2^E, raised to at least -124 (a zero
+ *            row takes -124);
+ *   codes[r][d] = the E4M3FN value nearest to ik[r][d] / 2^E (ties to the
+ *            even code, sign copied, so -0 gives 0x80).
+ *   The stored key codes[r][d] * 2^E is a bf16 value (at most 4 significant
+ *   bits, quantum >= 2^-133).
+ * Supported: d_i in {64, 128}.  Alignment: ik 16 B, codes 8 B. */
+csa2_status csa2_index_keys_fp8(const uint16_t* ik, int d_i, int64_t rows, uint8_t* codes, uint8_t* exps,
+                                void* stream);
+
+/* csa2_index_topk_fp8, csa2_reindex_topk_fp8 -- csa2_index_topk and
+ * csa2_reindex_topk over FP8 keys: the same arguments, results and
+ * workspace, with the key rows given as ik8 [rows][d_i] codes and ik8_exp
+ * [rows] exponent bytes (as written by csa2_index_keys_fp8) instead of ik;
+ * every score is that of the stored key ik8 * 2^(ik8_exp - 127).
+ * Supported: d_i = 128.  Alignment: ik8 8 B. */
+csa2_status csa2_index_topk_fp8(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
+                                const int32_t* q_seq, const int32_t* q_nvis, int32_t max_nvis,
+                                const uint8_t* ik8, const uint8_t* ik8_exp, const int64_t* seq_base,
+                                int k, int32_t* idx_out, int block, int keep_blocks, int32_t* pool_out,
+                                void* ws, size_t ws_bytes, void* stream);
+csa2_status csa2_reindex_topk_fp8(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
+                                  const int32_t* q_seq, const int32_t* q_nvis, const uint8_t* ik8,
+                                  const uint8_t* ik8_exp, const int64_t* seq_base,
+                                  const int32_t* pool_blocks, int block, int keep_blocks, int k,
+                                  int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * csa2_topk_merge -- exact Top-K of each query among given candidate
  * positions: the merge step of one context split over several devices.  Each
  * device runs csa2_index_topk on its position range and keeps its local

@@ -439,6 +439,7 @@ int fp8_key_exponent(double amax) {
 
 int csa2_ref_index_keys_fp8(const uint16_t* ik, int64_t rows, int d_i, uint8_t* codes, uint8_t* exps) {
   if (rows < 0 || d_i < 1) return 1;
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r) {
     const uint16_t* k = ik + (size_t)r * d_i;
     double amax = 0.0;
@@ -455,6 +456,7 @@ int csa2_ref_index_keys_fp8(const uint16_t* ik, int64_t rows, int d_i, uint8_t* 
 }
 
 void csa2_ref_dequant_keys_fp8(const uint8_t* codes, const uint8_t* exps, int64_t rows, int d_i, uint16_t* out) {
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r) {
     const int E = (int)exps[r] - 127;
     for (int d = 0; d < d_i; ++d) {

@@ -55,6 +55,14 @@ def lib():
                                       i32, i32, vp, vp, sz, vp]
         L.csa2_index_topk_ws_bytes.restype = sz
         L.csa2_index_topk_ws_bytes.argtypes = [i32, ctypes.c_int32, i32, i32, i32, i32, i32]
+        L.csa2_index_keys_fp8.restype = i32
+        L.csa2_index_keys_fp8.argtypes = [vp, i32, i64, vp, vp, vp]
+        L.csa2_index_topk_fp8.restype = i32
+        L.csa2_index_topk_fp8.argtypes = [vp, vp, i32, i32, i32, vp, vp, ctypes.c_int32, vp, vp, vp, i32, vp,
+                                          i32, i32, vp, vp, sz, vp]
+        L.csa2_reindex_topk_fp8.restype = i32
+        L.csa2_reindex_topk_fp8.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp,
+                                            vp, sz, vp]
         L.csa2_index_topk_chunk.restype = i32
         L.csa2_index_topk_chunk.argtypes = [vp, vp, i32, i32, i32, vp, ctypes.c_int32, vp, i64, i32, vp, vp,
                                             ctypes.c_size_t, vp]
@@ -212,6 +220,72 @@ def index_topk(iq, w, q_seq, q_nvis, max_nvis, ik, seq_base, k=512, block=8, kee
                                _stream(dev))
     _check(st, "csa2_index_topk")
     return (idx_out, pool_out) if keep_blocks else idx_out
+
+
+def index_keys_fp8(ik, codes=None, exps=None):
+    """Quantise bf16 key rows ik [rows, d_i] to FP8 (E4M3FN codes uint8 [rows, d_i]
+    and one exponent byte per row, uint8 [rows]; the stored key is
+    code * 2^(exp - 127)).  Returns (codes, exps)."""
+    _need(ik, torch.bfloat16, "ik")
+    rows, d_i = ik.shape
+    dev = ik.device
+    if codes is None:
+        codes = torch.empty((rows, d_i), dtype=torch.uint8, device=dev)
+    if exps is None:
+        exps = torch.empty((rows,), dtype=torch.uint8, device=dev)
+    _need(codes, torch.uint8, "codes")
+    _need(exps, torch.uint8, "exps")
+    st = lib().csa2_index_keys_fp8(_ptr(ik), d_i, rows, _ptr(codes), _ptr(exps), _stream(dev))
+    _check(st, "csa2_index_keys_fp8")
+    return codes, exps
+
+
+def index_topk_fp8(iq, w, q_seq, q_nvis, max_nvis, ik8, ik8_exp, seq_base, k=512, block=8, keep_blocks=0,
+                   idx_out=None, pool_out=None, ws=None):
+    """index_topk over FP8 keys (ik8 [rows, 128] uint8 codes, ik8_exp [rows] uint8)."""
+    _need(iq, torch.bfloat16, "iq")
+    n_q, h_i, d_i = iq.shape
+    _need(w, torch.float32, "w")
+    _need(q_seq, torch.int32, "q_seq")
+    _need(q_nvis, torch.int32, "q_nvis")
+    _need(ik8, torch.uint8, "ik8")
+    _need(ik8_exp, torch.uint8, "ik8_exp")
+    _need(seq_base, torch.int64, "seq_base")
+    dev = iq.device
+    if idx_out is None:
+        idx_out = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    if keep_blocks and pool_out is None:
+        pool_out = torch.empty((n_q, keep_blocks), dtype=torch.int32, device=dev)
+    buf = _ws(dev, index_topk_ws_bytes(n_q, max_nvis, h_i, d_i, k, block, keep_blocks), ws)
+    st = lib().csa2_index_topk_fp8(_ptr(iq), _ptr(w), n_q, h_i, d_i, _ptr(q_seq), _ptr(q_nvis), int(max_nvis),
+                                   _ptr(ik8), _ptr(ik8_exp), _ptr(seq_base), k, _ptr(idx_out), block, keep_blocks,
+                                   _ptr(pool_out) if keep_blocks else None, _ptr(buf), buf.numel(), _stream(dev))
+    _check(st, "csa2_index_topk_fp8")
+    return (idx_out, pool_out) if keep_blocks else idx_out
+
+
+def reindex_topk_fp8(iq, w, q_seq, q_nvis, ik8, ik8_exp, seq_base, pool_blocks, k=512, block=8, idx_out=None,
+                     ws=None):
+    """reindex_topk over FP8 keys."""
+    _need(iq, torch.bfloat16, "iq")
+    n_q, h_i, d_i = iq.shape
+    _need(w, torch.float32, "w")
+    _need(q_seq, torch.int32, "q_seq")
+    _need(q_nvis, torch.int32, "q_nvis")
+    _need(ik8, torch.uint8, "ik8")
+    _need(ik8_exp, torch.uint8, "ik8_exp")
+    _need(seq_base, torch.int64, "seq_base")
+    _need(pool_blocks, torch.int32, "pool_blocks")
+    keep_blocks = pool_blocks.shape[1]
+    dev = iq.device
+    if idx_out is None:
+        idx_out = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    buf = _ws(dev, reindex_topk_ws_bytes(n_q, h_i, d_i, k, block, keep_blocks), ws)
+    st = lib().csa2_reindex_topk_fp8(_ptr(iq), _ptr(w), n_q, h_i, d_i, _ptr(q_seq), _ptr(q_nvis), _ptr(ik8),
+                                     _ptr(ik8_exp), _ptr(seq_base), _ptr(pool_blocks), block, keep_blocks, k,
+                                     _ptr(idx_out), _ptr(buf), buf.numel(), _stream(dev))
+    _check(st, "csa2_reindex_topk_fp8")
+    return idx_out
 
 
 def index_topk_chunk(iq, w, q_nvis, max_nvis, ik, ik_base=0, k=512, idx_out=None, ws=None):

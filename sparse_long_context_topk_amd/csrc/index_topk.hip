@@ -114,6 +114,10 @@ struct Params {
   const int32_t* q_seq;
   const int32_t* q_nvis;
   const uint16_t* ik;
+  // FP8 keys (the low-precision indexer-key variant), used instead of ik when
+  // set: E4M3 codes [rows][d_i] and one exponent byte per row (scale 2^(e - 127))
+  const uint8_t* ik8;
+  const uint8_t* ik8e;
   const int64_t* seq_base;
   const int32_t* pool_in;  // Reindex: [n_q][keep_in]; null: every block 0 .. keep_in-1 in order
   int keep_in;
@@ -371,6 +375,20 @@ __device__ __forceinline__ int cand_pos(const Params& P, int q, int kind, uint32
   return (int)cand;
 }
 
+// Dims 2 p and 2 p + 1 of key row `row` as a bf16 pair (low half: dim 2 p).
+// FP8 keys decode exactly: v_cvt_scalef32_pk_bf16_fp8 multiplies by the power
+// of two of its scale argument, and an E4M3 value times the row's scale
+// 2^E (E >= -124) is a bf16 value.
+template <int D>
+__device__ __forceinline__ uint32_t key_pair(const Params& P, int64_t row, int p) {
+  if (P.ik8) {
+    const uint32_t c = reinterpret_cast<const uint16_t*>(P.ik8 + (size_t)row * D)[p];
+    const float sc = __uint_as_float((uint32_t)P.ik8e[row] << 23);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, sc, false));
+  }
+  return reinterpret_cast<const uint32_t*>(P.ik + (size_t)row * D)[p];
+}
+
 // ---------------------------------------------------------------- 1. prologue
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_prologue(Params P) {
@@ -462,7 +480,7 @@ __device__ uint32_t wg_coarse_bin(const Params& P, int p, const uint32_t hv[kHPe
 // HIST: build the coarse score histograms (and the largest t_k) that the
 // multi-kernel selection uses; without it the scan records each work-group's
 // largest t_k for the single-work-group selection.
-template <int D, int MT, bool POOL, bool INDIRECT, bool HIST>
+template <int D, int MT, bool POOL, bool INDIRECT, bool HIST, bool FP8>
 __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   constexpr int KS = D / 32;   // MFMA k-steps; also 16-byte loads per lane per key
   constexpr int NBUF = CSA2_SCAN_NBUF;   // key groups in registers: NBUF-1 in flight, one in use (2: measured
@@ -555,11 +573,25 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     }
     return valid ? base + pos : (int64_t)0;
   };
+  // bf16 keys: 16 bytes (dims 32 ks + 8 g .. + 7) per k-step; FP8 keys: 8
+  // code bytes per k-step in .xy and the row's exponent byte in [0].z
   auto load = [&](int it, uint4* kb) {
     bool v;
-    const uint4* src = reinterpret_cast<const uint4*>(P.ik + (size_t)key_row(min(it, my_groups - 1), v) * D + 8 * g);
+    const int64_t row = key_row(min(it, my_groups - 1), v);
+    if constexpr (FP8) {
+      const uint8_t* src = P.ik8 + (size_t)row * D + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kb[ks] = src[4 * ks];
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint2 c = *reinterpret_cast<const uint2*>(src + 32 * ks);
+        kb[ks].x = c.x;
+        kb[ks].y = c.y;
+      }
+      kb[0].z = P.ik8e[row];
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(P.ik + (size_t)row * D + 8 * g);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kb[ks] = src[4 * ks];
+    }
   };
 
   auto process = [&](int it, const uint4* kin) {
@@ -570,9 +602,21 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     // select here would become a branch and stall the load pipeline)
     const uint32_t vm = valid ? 0xFFFFFFFFu : 0u;
     uint4 kb[KS];
+    if constexpr (FP8) {
+      const float sc = __uint_as_float(kin[0].z << 23);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kb[ks] = make_uint4(kin[ks].x & vm, kin[ks].y & vm, kin[ks].z & vm, kin[ks].w & vm);
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kin[ks].x, sc, false));
+        const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kin[ks].x, sc, true));
+        const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kin[ks].y, sc, false));
+        const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kin[ks].y, sc, true));
+        kb[ks] = make_uint4(a & vm, b & vm, c & vm, d & vm);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kb[ks] = make_uint4(kin[ks].x & vm, kin[ks].y & vm, kin[ks].z & vm, kin[ks].w & vm);
+    }
     // S (16 keys x 16 heads per tile) = K . Q^T ; lane (n, g) gets keys 4g+i, head 16*mt+n
     f32x4 acc[MT];
 #pragma unroll
@@ -1198,7 +1242,7 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
     for (int k = 0; k < KPER; ++k) {
       const int e = lane + 64 * k, t = e / DW, d2 = e % DW;
       const int tt = t < c.nmem ? t : 0;
-      wv[k] = reinterpret_cast<const uint32_t*>(P.ik + (size_t)(base + c.first + tt) * D)[d2];
+      wv[k] = key_pair<D>(P, base + c.first + tt, d2);
     }
   };
   auto stage_keys = [&](const Cand& c, const uint32_t* wv) {
@@ -1871,7 +1915,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
       for (int m = 0; m < kRsMembers; ++m) {
         const int slot = u_slot(jb + min(m, nm - 1));
         const int64_t row = base + (int64_t)s_pool[slot >> 3] * 8 + (slot & 7);
-        kw[m] = reinterpret_cast<const uint32_t*>(P.ik + (size_t)row * D)[lane < DW ? lane : 0];
+        kw[m] = key_pair<D>(P, row, lane < DW ? lane : 0);
       }
 #pragma unroll
       for (int m = 0; m < kRsMembers; ++m)
@@ -2076,18 +2120,30 @@ bool launch_ok() {
   return true;
 }
 
-template <int D>
-void launch_scan(const Params& P, int mt, bool pool, bool indirect, bool hist, dim3 grid, hipStream_t s) {
-#define CSA2_SCAN(MTV)                                                                                       \
-  if (mt == MTV) {                                                                                           \
-    if (indirect && hist) hipLaunchKernelGGL((k_scan<D, MTV, false, true, true>), grid, dim3(kThreads), 0, s, P); \
-    else if (indirect) hipLaunchKernelGGL((k_scan<D, MTV, false, true, false>), grid, dim3(kThreads), 0, s, P);  \
-    else if (pool) hipLaunchKernelGGL((k_scan<D, MTV, true, false, true>), grid, dim3(kThreads), 0, s, P);       \
-    else hipLaunchKernelGGL((k_scan<D, MTV, false, false, true>), grid, dim3(kThreads), 0, s, P);                \
-    return;                                                                                                  \
+template <int D, bool FP8>
+void launch_scan_t(const Params& P, int mt, bool pool, bool indirect, bool hist, dim3 grid, hipStream_t s) {
+#define CSA2_SCAN(MTV)                                                                                            \
+  if (mt == MTV) {                                                                                                \
+    if (indirect && hist) hipLaunchKernelGGL((k_scan<D, MTV, false, true, true, FP8>), grid, dim3(kThreads), 0, s, P); \
+    else if (indirect) hipLaunchKernelGGL((k_scan<D, MTV, false, true, false, FP8>), grid, dim3(kThreads), 0, s, P);  \
+    else if (pool) hipLaunchKernelGGL((k_scan<D, MTV, true, false, true, FP8>), grid, dim3(kThreads), 0, s, P);       \
+    else hipLaunchKernelGGL((k_scan<D, MTV, false, false, true, FP8>), grid, dim3(kThreads), 0, s, P);                \
+    return;                                                                                                       \
   }
   CSA2_SCAN(1) CSA2_SCAN(2) CSA2_SCAN(3) CSA2_SCAN(4)
 #undef CSA2_SCAN
+}
+
+// FP8 keys are built for d_i = 128 only (the entry points check it).
+template <int D>
+void launch_scan(const Params& P, int mt, bool pool, bool indirect, bool hist, dim3 grid, hipStream_t s) {
+  if constexpr (D == 128) {
+    if (P.ik8) {
+      launch_scan_t<D, true>(P, mt, pool, indirect, hist, grid, s);
+      return;
+    }
+  }
+  launch_scan_t<D, false>(P, mt, pool, indirect, hist, grid, s);
 }
 
 #ifndef CSA2_CHUNK_QB
@@ -2205,24 +2261,35 @@ extern "C" size_t csa2_reindex_topk_ws_bytes(int n_q, int h_i, int d_i, int k, i
   return make_layout(n_q, stride, (int)(stride / kCmpChunk)).total;
 }
 
-extern "C" csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
-                                       const int32_t* q_seq, const int32_t* q_nvis, int32_t max_nvis,
-                                       const uint16_t* ik, const int64_t* seq_base, int k, int32_t* idx_out,
-                                       int block, int keep_blocks, int32_t* pool_out, void* ws, size_t ws_bytes,
-                                       void* stream) {
+namespace {
+
+// Keys of an index call: bf16 rows (ik) or FP8 rows with their exponent
+// bytes (ik8, ik8e; d_i = 128 only).  Returns false when the pointers do not
+// fit the contract.
+bool keys_ok(int d_i, const uint16_t* ik, const uint8_t* ik8, const uint8_t* ik8e) {
+  if (ik8) return d_i == 128 && ik8e && !ik && aligned(ik8, 8);
+  return ik && !ik8e && aligned(ik, 16);
+}
+
+csa2_status index_call(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i, const int32_t* q_seq,
+                       const int32_t* q_nvis, int32_t max_nvis, const uint16_t* ik, const uint8_t* ik8,
+                       const uint8_t* ik8e, const int64_t* seq_base, int k, int32_t* idx_out, int block,
+                       int keep_blocks, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
   csa2::set_last_hip_error(0);
   if (n_q < 0 || max_nvis < 0 || k < 1 || k > 2048 || keep_blocks < 0 || keep_blocks > 4096)
     return CSA2_E_INVAL;
   if ((int64_t)max_nvis > (int64_t)kMaxChunksLds * kCmpChunk) return CSA2_E_UNSUPPORTED;
   if (!shape_ok(h_i, d_i)) return CSA2_E_UNSUPPORTED;
+  if (ik8 && d_i != 128) return CSA2_E_UNSUPPORTED;
   if (keep_blocks > 0 && block != 8) return CSA2_E_UNSUPPORTED;
   if (n_q == 0) return CSA2_OK;
-  if (!iq || !w || !q_seq || !q_nvis || !ik || !seq_base || !idx_out || !ws) return CSA2_E_INVAL;
+  if (!iq || !w || !q_seq || !q_nvis || !seq_base || !idx_out || !ws) return CSA2_E_INVAL;
   if (keep_blocks > 0 && !pool_out) return CSA2_E_INVAL;
-  if (!aligned(iq, 16) || !aligned(ik, 16) || !aligned(w, 4) || !aligned(ws, 256)) return CSA2_E_INVAL;
+  if (!keys_ok(d_i, ik, ik8, ik8e)) return CSA2_E_INVAL;
+  if (!aligned(iq, 16) || !aligned(w, 4) || !aligned(ws, 256)) return CSA2_E_INVAL;
   Params P{};
   P.iq = iq; P.w = w; P.n_q = n_q; P.h_i = h_i; P.d_i = d_i;
-  P.q_seq = q_seq; P.q_nvis = q_nvis; P.ik = ik; P.seq_base = seq_base;
+  P.q_seq = q_seq; P.q_nvis = q_nvis; P.ik = ik; P.ik8 = ik8; P.ik8e = ik8e; P.seq_base = seq_base;
   if (keep_blocks == 0 && max_nvis <= kSmallMax) {
     // Short contexts without a pool: the Reindex path over every block of the
     // context in order (a null pool) -- the same exact Top-K over the positions
@@ -2249,6 +2316,54 @@ extern "C" csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n
   P.nchunk_cmp = (int)(P.stride / kCmpChunk);
   const size_t need = csa2_index_topk_ws_bytes(n_q, max_nvis, h_i, d_i, k, block, keep_blocks);
   return run_pipeline(P, max_nvis, ws, ws_bytes, static_cast<hipStream_t>(stream), need);
+}
+
+csa2_status reindex_call(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i, const int32_t* q_seq,
+                         const int32_t* q_nvis, const uint16_t* ik, const uint8_t* ik8, const uint8_t* ik8e,
+                         const int64_t* seq_base, const int32_t* pool_blocks, int block, int keep_blocks, int k,
+                         int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  csa2::set_last_hip_error(0);
+  if (n_q < 0 || k < 1 || k > 2048 || keep_blocks < 1 || keep_blocks > 4096) return CSA2_E_INVAL;
+  if (!shape_ok(h_i, d_i)) return CSA2_E_UNSUPPORTED;
+  if (ik8 && d_i != 128) return CSA2_E_UNSUPPORTED;
+  if (block != 8) return CSA2_E_UNSUPPORTED;
+  if (n_q == 0) return CSA2_OK;
+  if (!iq || !w || !q_seq || !q_nvis || !seq_base || !pool_blocks || !idx_out || !ws) return CSA2_E_INVAL;
+  if (!keys_ok(d_i, ik, ik8, ik8e)) return CSA2_E_INVAL;
+  if (!aligned(iq, 16) || !aligned(w, 4) || !aligned(ws, 256)) return CSA2_E_INVAL;
+  Params P{};
+  P.iq = iq; P.w = w; P.n_q = n_q; P.h_i = h_i; P.d_i = d_i;
+  P.q_seq = q_seq; P.q_nvis = q_nvis; P.ik = ik; P.ik8 = ik8; P.ik8e = ik8e; P.seq_base = seq_base;
+  P.pool_in = pool_blocks; P.keep_in = keep_blocks; P.k = k; P.keep_blocks = 0;
+  P.idx_out = idx_out; P.pool_out = nullptr;
+  P.nprob = n_q;
+  P.reindex = 1;
+  const int64_t slots = 8LL * keep_blocks;
+  P.scan_chunk = reindex_chunk_for(n_q, slots);
+  P.stride = round_up(slots, kCmpChunk);
+  P.nchunk_cmp = (int)(P.stride / kCmpChunk);
+  const size_t need = csa2_reindex_topk_ws_bytes(n_q, h_i, d_i, k, block, keep_blocks);
+  return run_pipeline(P, slots, ws, ws_bytes, static_cast<hipStream_t>(stream), need);
+}
+
+}  // namespace
+
+extern "C" csa2_status csa2_index_topk(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
+                                       const int32_t* q_seq, const int32_t* q_nvis, int32_t max_nvis,
+                                       const uint16_t* ik, const int64_t* seq_base, int k, int32_t* idx_out,
+                                       int block, int keep_blocks, int32_t* pool_out, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  return index_call(iq, w, n_q, h_i, d_i, q_seq, q_nvis, max_nvis, ik, nullptr, nullptr, seq_base, k, idx_out,
+                    block, keep_blocks, pool_out, ws, ws_bytes, stream);
+}
+
+extern "C" csa2_status csa2_index_topk_fp8(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
+                                           const int32_t* q_seq, const int32_t* q_nvis, int32_t max_nvis,
+                                           const uint8_t* ik8, const uint8_t* ik8_exp, const int64_t* seq_base,
+                                           int k, int32_t* idx_out, int block, int keep_blocks, int32_t* pool_out,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  return index_call(iq, w, n_q, h_i, d_i, q_seq, q_nvis, max_nvis, nullptr, ik8, ik8_exp, seq_base, k, idx_out,
+                    block, keep_blocks, pool_out, ws, ws_bytes, stream);
 }
 
 extern "C" csa2_status csa2_index_topk_chunk(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
@@ -2281,26 +2396,17 @@ extern "C" csa2_status csa2_reindex_topk(const uint16_t* iq, const float* w, int
                                          const int64_t* seq_base, const int32_t* pool_blocks, int block,
                                          int keep_blocks, int k, int32_t* idx_out, void* ws, size_t ws_bytes,
                                          void* stream) {
-  csa2::set_last_hip_error(0);
-  if (n_q < 0 || k < 1 || k > 2048 || keep_blocks < 1 || keep_blocks > 4096) return CSA2_E_INVAL;
-  if (!shape_ok(h_i, d_i)) return CSA2_E_UNSUPPORTED;
-  if (block != 8) return CSA2_E_UNSUPPORTED;
-  if (n_q == 0) return CSA2_OK;
-  if (!iq || !w || !q_seq || !q_nvis || !ik || !seq_base || !pool_blocks || !idx_out || !ws) return CSA2_E_INVAL;
-  if (!aligned(iq, 16) || !aligned(ik, 16) || !aligned(w, 4) || !aligned(ws, 256)) return CSA2_E_INVAL;
-  Params P{};
-  P.iq = iq; P.w = w; P.n_q = n_q; P.h_i = h_i; P.d_i = d_i;
-  P.q_seq = q_seq; P.q_nvis = q_nvis; P.ik = ik; P.seq_base = seq_base;
-  P.pool_in = pool_blocks; P.keep_in = keep_blocks; P.k = k; P.keep_blocks = 0;
-  P.idx_out = idx_out; P.pool_out = nullptr;
-  P.nprob = n_q;
-  P.reindex = 1;
-  const int64_t slots = 8LL * keep_blocks;
-  P.scan_chunk = reindex_chunk_for(n_q, slots);
-  P.stride = round_up(slots, kCmpChunk);
-  P.nchunk_cmp = (int)(P.stride / kCmpChunk);
-  const size_t need = csa2_reindex_topk_ws_bytes(n_q, h_i, d_i, k, block, keep_blocks);
-  return run_pipeline(P, slots, ws, ws_bytes, static_cast<hipStream_t>(stream), need);
+  return reindex_call(iq, w, n_q, h_i, d_i, q_seq, q_nvis, ik, nullptr, nullptr, seq_base, pool_blocks, block,
+                      keep_blocks, k, idx_out, ws, ws_bytes, stream);
+}
+
+extern "C" csa2_status csa2_reindex_topk_fp8(const uint16_t* iq, const float* w, int n_q, int h_i, int d_i,
+                                             const int32_t* q_seq, const int32_t* q_nvis, const uint8_t* ik8,
+                                             const uint8_t* ik8_exp, const int64_t* seq_base,
+                                             const int32_t* pool_blocks, int block, int keep_blocks, int k,
+                                             int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  return reindex_call(iq, w, n_q, h_i, d_i, q_seq, q_nvis, nullptr, ik8, ik8_exp, seq_base, pool_blocks, block,
+                      keep_blocks, k, idx_out, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- allocation-free Reindex

@@ -17,7 +17,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import block_keys, index_topk, index_topk_chunk, quant_append, reindex_topk, sparse_attn, Workspace
+from . import (block_keys, index_topk, index_topk_chunk, index_topk_fp8, quant_append, reindex_topk,
+               reindex_topk_fp8, sparse_attn, Workspace)
 
 FULL, REINDEX, REUSE = "full", "reindex", "reuse"
 
@@ -71,6 +72,11 @@ class DecodeState:
     max_nblk: int = 0
     seq_len: torch.Tensor | None = None   # [n_seq] int32 positions per sequence
     blk_last: torch.Tensor | None = None  # [n_seq] int32: block of each sequence's newest position
+    # FP8 indexer keys (the low-precision indexer-key variant): the Full and
+    # Reindex layers read ik8/ik8_exp (csa2_index_keys_fp8 of ik) instead of ik
+    fp8_keys: bool = False
+    ik8: torch.Tensor | None = None       # [rows, d_i] uint8 E4M3 codes
+    ik8_exp: torch.Tensor | None = None   # [rows] uint8 exponent bytes
     ws_index: Workspace = field(default_factory=Workspace)
     ws_attn: Workspace = field(default_factory=Workspace)
 
@@ -90,6 +96,8 @@ def decode_step(st: DecodeState, layers: list[LayerInputs], append_x=None, appen
         if lay.mode == FULL:
             if scan_events is not None:
                 record_scan_events(*scan_events)
+            if st.fp8_keys and (st.chunk_base is not None or st.pool_full):
+                raise ValueError("FP8 indexer keys serve the decode Full and Reindex calls only")
             if st.chunk_base is not None:
                 if st.keep_blocks:
                     raise ValueError("a chunk of one sequence's queries builds no pool")
@@ -105,6 +113,10 @@ def decode_step(st: DecodeState, layers: list[LayerInputs], append_x=None, appen
                                   k=st.keep_blocks, ws=st.ws_index)
                 idx = reindex_topk(lay.iq, lay.w, st.q_seq, st.q_nvis, st.ik, st.seq_base, pool, k=st.k,
                                    ws=st.ws_index)
+            elif st.fp8_keys:
+                r = index_topk_fp8(lay.iq, lay.w, st.q_seq, st.q_nvis, st.max_nvis, st.ik8, st.ik8_exp, st.seq_base,
+                                   k=st.k, keep_blocks=st.keep_blocks, ws=st.ws_index)
+                idx, pool = (r if st.keep_blocks else (r, None))
             else:
                 r = index_topk(lay.iq, lay.w, st.q_seq, st.q_nvis, st.max_nvis, st.ik, st.seq_base, k=st.k,
                                keep_blocks=st.keep_blocks, ws=st.ws_index)
@@ -112,8 +124,12 @@ def decode_step(st: DecodeState, layers: list[LayerInputs], append_x=None, appen
         elif lay.mode == REINDEX:
             if pool is None:
                 raise ValueError("a Reindex layer needs a preceding Full layer that built a pool")
-            idx = reindex_topk(lay.iq, lay.w, st.q_seq, st.q_nvis, st.ik, st.seq_base, pool, k=st.k,
-                               ws=st.ws_index)
+            if st.fp8_keys:
+                idx = reindex_topk_fp8(lay.iq, lay.w, st.q_seq, st.q_nvis, st.ik8, st.ik8_exp, st.seq_base, pool,
+                                       k=st.k, ws=st.ws_index)
+            else:
+                idx = reindex_topk(lay.iq, lay.w, st.q_seq, st.q_nvis, st.ik, st.seq_base, pool, k=st.k,
+                                   ws=st.ws_index)
         elif lay.mode != REUSE:
             raise ValueError(f"unknown layer mode {lay.mode}")
         if idx is None:

@@ -19,6 +19,7 @@ import torch
 
 import bench
 import csa2_inputs as gen
+import oracle
 from gpu_common import bits, device, gpu, normwise_err, note
 from oracle.step import decode_step as oracle_step
 from sparse_long_context_topk_amd.schedule import decode_step
@@ -30,15 +31,19 @@ def _host(t):
     return bits(t) if t.dtype == torch.bfloat16 else t.cpu().numpy()
 
 
-def _check_workload(name, length_div=1, sample=None, pool_full=False):
+def _check_workload(name, length_div=1, sample=None, pool_full=False, fp8_keys=False):
     """sample: query indices the oracle checks (default: every query);
     pool_full: the Full layer picks its Top-K inside its own pool (bench.py
-    --full-from-pool)."""
+    --full-from-pool); fp8_keys: the indexer keys are stored in FP8 (bench.py
+    --fp8-keys), which the oracle quantises itself from the same bf16 keys."""
     dev = device()
     wl = gen.workload(name, length_div=length_div)
     if pool_full:
         wl["pool_full"] = True
         wl["name"] += " (pool-based Full)"
+    if fp8_keys:
+        wl["fp8_keys"] = True
+        wl["name"] += " (FP8 indexer keys)"
     note(f"workload {wl['name']}: {len(wl['lengths'])} sequences, {wl['rows']} rows, layers {wl['layers']}")
     st, layers, app_x, app_rows = bench.build_state(wl, dev)
     swa0 = [bits(lay.swa) for lay in layers]   # generated window rows, before the step writes its new ones
@@ -63,7 +68,10 @@ def _check_workload(name, length_div=1, sample=None, pool_full=False):
         if lay.swa_new is not None:
             d["swa_new"], d["swa_dst"] = bits(lay.swa_new[ts]), _host(lay.swa_dst[ts])
         hl.append(d)
-    ref, rpool, secs = oracle_step(hl, bits(st.ik), np.asarray(wl["seq_base"], np.int64),
+    ik_host = bits(st.ik)
+    if fp8_keys:
+        ik_host = oracle.dequant_keys_fp8(*oracle.index_keys_fp8(ik_host))
+    ref, rpool, secs = oracle_step(hl, ik_host, np.asarray(wl["seq_base"], np.int64),
                                    np.asarray(wl["q_seq"], np.int32)[sel], np.asarray(wl["q_nvis"], np.int32)[sel],
                                    wl["k"], wl["keep_blocks"], wl["block"], raw_rows,
                                    _host(app_x) if app_x is not None else None,
@@ -126,3 +134,13 @@ def test_c5_twenty_layer_schedule_full_size_sampled():
 @gpu
 def test_c5_twenty_layer_schedule_pool_based_full():
     _check_workload("c5", length_div=16, pool_full=True)
+
+
+@gpu
+def test_c3_fp8_indexer_keys_1m_batch4():
+    _check_workload("c3", fp8_keys=True)
+
+
+@gpu
+def test_c5_twenty_layer_schedule_fp8_indexer_keys():
+    _check_workload("c5", length_div=16, fp8_keys=True)
