@@ -75,6 +75,9 @@ constexpr int kCmpChunk = 4096;
 constexpr int kCmpPerThread = kCmpChunk / kThreads;
 constexpr int kMaxChunksLds = 8192;   // compaction chunks per problem (max_nvis <= 2^25)
 constexpr int kRescoreWGs = 512;   // rescoring work-groups per launch (all queries)
+#ifndef CSA2_SCAN_NBUF_FP8
+#define CSA2_SCAN_NBUF_FP8 4
+#endif
 #ifndef CSA2_SCAN_NBUF
 #define CSA2_SCAN_NBUF 2
 #endif
@@ -483,8 +486,10 @@ __device__ uint32_t wg_coarse_bin(const Params& P, int p, const uint32_t hv[kHPe
 template <int D, int MT, bool POOL, bool INDIRECT, bool HIST, bool FP8>
 __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   constexpr int KS = D / 32;   // MFMA k-steps; also 16-byte loads per lane per key
-  constexpr int NBUF = CSA2_SCAN_NBUF;   // key groups in registers: NBUF-1 in flight, one in use (2: measured
-                                         // 4 % faster than 3 or 4 at 1M x 4; fewer registers, same occupancy)
+  // key groups in registers: NBUF-1 in flight, one in use (bf16 keys: 2, measured
+                                         // 4 % faster than 3 or 4 at 1M x 4; fewer registers, same occupancy;
+                                         // FP8 keys hold half the bytes per group, so more groups fly)
+  constexpr int NBUF = FP8 ? CSA2_SCAN_NBUF_FP8 : CSA2_SCAN_NBUF;
   __shared__ uint32_t s_hist[HIST ? kNBins : 1];
   __shared__ uint32_t s_hist_b[POOL ? kNBins : 1];
   __shared__ int32_t s_pool[INDIRECT ? 512 : 1];
@@ -524,9 +529,14 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     }
   }
 
-  // Q^T as the MFMA B operand: lane (n, g) holds head 16*mt + n, dims 32*ks + 8*g .. +7
-  // (the natural k-layout: for each k-step the four lane groups cover 64
-  // contiguous bytes of a row, so every key load instruction reads whole lines)
+  // Q^T as the MFMA B operand: lane (n, g) holds head 16*mt + n, dims dim0(ks) .. +7
+  // (bf16 keys: the natural k-layout 32 ks + 8 g, for each k-step the four
+  // lane groups cover 64 contiguous bytes of a row, so every key load
+  // instruction reads whole lines; FP8 keys: 16 g + 8 ks for ks < 2 and
+  // 64 + 16 g + 8 (ks - 2) after, so that a lane's 32 code bytes are two
+  // 16-byte loads, each instruction covering 64 contiguous bytes of a row --
+  // any k-order gives the same products, and the bound holds for any order)
+  auto dim0 = [&](int ks) { return FP8 ? (ks < 2 ? 16 * g + 8 * ks : 64 + 16 * g + 8 * (ks - 2)) : 32 * ks + 8 * g; };
   bf16x8 qb[MT][KS];
   float wr[MT];
 #pragma unroll
@@ -536,7 +546,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (head < P.h_i)
-        v = *reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + head) * D + 32 * ks + 8 * g);
+        v = *reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + head) * D + dim0(ks));
       qb[mt][ks] = __builtin_bit_cast(bf16x8, v);
     }
     wr[mt] = head < P.h_i ? P.w[(size_t)q * P.h_i + head] : 0.0f;
@@ -573,20 +583,17 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     }
     return valid ? base + pos : (int64_t)0;
   };
-  // bf16 keys: 16 bytes (dims 32 ks + 8 g .. + 7) per k-step; FP8 keys: 8
-  // code bytes per k-step in .xy and the row's exponent byte in [0].z
+  // bf16 keys: 16 bytes (dims 32 ks + 8 g .. + 7) per k-step; FP8 keys: the
+  // code bytes of dims 16 g .. + 15 in kb[0] and 64 + 16 g .. + 15 in kb[1]
+  // (k-steps 0, 1 and 2, 3: see dim0), the row's exponent byte in kb[2].x
   auto load = [&](int it, uint4* kb) {
     bool v;
     const int64_t row = key_row(min(it, my_groups - 1), v);
     if constexpr (FP8) {
-      const uint8_t* src = P.ik8 + (size_t)row * D + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint2 c = *reinterpret_cast<const uint2*>(src + 32 * ks);
-        kb[ks].x = c.x;
-        kb[ks].y = c.y;
-      }
-      kb[0].z = P.ik8e[row];
+      const uint8_t* src = P.ik8 + (size_t)row * D + 16 * g;
+      kb[0] = *reinterpret_cast<const uint4*>(src);
+      kb[1] = *reinterpret_cast<const uint4*>(src + 64);
+      kb[2].x = P.ik8e[row];
     } else {
       const uint4* src = reinterpret_cast<const uint4*>(P.ik + (size_t)row * D + 8 * g);
 #pragma unroll
@@ -603,13 +610,15 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     const uint32_t vm = valid ? 0xFFFFFFFFu : 0u;
     uint4 kb[KS];
     if constexpr (FP8) {
-      const float sc = __uint_as_float(kin[0].z << 23);
+      const float sc = __uint_as_float(kin[2].x << 23);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kin[ks].x, sc, false));
-        const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kin[ks].x, sc, true));
-        const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kin[ks].y, sc, false));
-        const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kin[ks].y, sc, true));
+        const uint4 r = kin[ks >> 1];
+        const uint32_t lo = (ks & 1) ? r.z : r.x, hi = (ks & 1) ? r.w : r.y;
+        const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false));
+        const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true));
+        const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false));
+        const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true));
         kb[ks] = make_uint4(a & vm, b & vm, c & vm, d & vm);
       }
     } else {
