@@ -18,6 +18,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=off", "-Wall", "-Wno-unused-result",
 ]
+# Per-source additions.  The indexer kernels read every MFMA result with VALU
+# code right away: accumulating in VGPRs (instead of AGPRs) saves one
+# v_accvgpr_read per result in the scan's inner loop.
+SOURCE_FLAGS = {
+    "index_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def build(verbose: bool = False) -> str:
@@ -28,7 +34,7 @@ def build(verbose: bool = False) -> str:
     procs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

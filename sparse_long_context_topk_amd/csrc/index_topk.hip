@@ -76,10 +76,10 @@ constexpr int kCmpPerThread = kCmpChunk / kThreads;
 constexpr int kMaxChunksLds = 8192;   // compaction chunks per problem (max_nvis <= 2^25)
 constexpr int kRescoreWGs = 512;   // rescoring work-groups per launch (all queries)
 #ifndef CSA2_SCAN_NBUF_FP8
-#define CSA2_SCAN_NBUF_FP8 4
+#define CSA2_SCAN_NBUF_FP8 5
 #endif
 #ifndef CSA2_SCAN_NBUF
-#define CSA2_SCAN_NBUF 2
+#define CSA2_SCAN_NBUF 3
 #endif
 #ifndef CSA2_SCAN_CHUNK
 #define CSA2_SCAN_CHUNK 8192
@@ -181,6 +181,26 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
+// max(x, 0) of an approximate (MFMA) dot as one integer max of its bits: a
+// float with the sign bit set is a negative integer, any other orders as its
+// bits.  Equals fmaxf(x, 0) for every non-NaN x (and -0 gives +0), without
+// the NaN-quieting max the compiler puts in front of a float max.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// An all-zero key row (the largest row of any supported key layout, 256
+// bytes) and exponent byte: a scan slot without a key loads it, so that its
+// products, block sums and t_k come out zero without masking the loaded
+// words.  Never written.
+static __device__ __align__(256) uint8_t g_zero_key[256];
+typedef __attribute__((address_space(1))) const uint8_t gbyte;   // global memory
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes from global memory (p 16-byte aligned)
+__device__ __forceinline__ uint4 gload16(const gbyte* p) {
+  const u32x4_t t = *(__attribute__((address_space(1))) const u32x4_t*)p;
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
 // The rounding bound's key magnitude.  For a query with heads q_h and weights
 // w_h, every per-head dot product's rounding error (exact chain or MFMA) is at
 // most a constant times sum_d |q_hd k_d|, so the score's error is at most a
@@ -243,6 +263,13 @@ __device__ __forceinline__ float sum_rows4(float v) {
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// v + the value of lane l ^ 16 (rows 0 <-> 1 and 2 <-> 3 of the wave), with
+// one VALU lane permute instead of an LDS permute.
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
 // Exclusive prefix sum over the NT-thread work-group (s_tmp: >= NT / 64
@@ -486,9 +513,9 @@ __device__ uint32_t wg_coarse_bin(const Params& P, int p, const uint32_t hv[kHPe
 template <int D, int MT, bool POOL, bool INDIRECT, bool HIST, bool FP8>
 __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   constexpr int KS = D / 32;   // MFMA k-steps; also 16-byte loads per lane per key
-  // key groups in registers: NBUF-1 in flight, one in use (bf16 keys: 2, measured
-                                         // 4 % faster than 3 or 4 at 1M x 4; fewer registers, same occupancy;
-                                         // FP8 keys hold half the bytes per group, so more groups fly)
+  // key groups in registers: one being multiplied, NBUF - 2 loaded or in
+  // flight behind it, one being loaded (FP8 keys hold half the bytes per
+  // group, so more groups fly)
   constexpr int NBUF = FP8 ? CSA2_SCAN_NBUF_FP8 : CSA2_SCAN_NBUF;
   __shared__ uint32_t s_hist[HIST ? kNBins : 1];
   __shared__ uint32_t s_hist_b[POOL ? kNBins : 1];
@@ -551,12 +578,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     }
     wr[mt] = head < P.h_i ? P.w[(size_t)q * P.h_i + head] : 0.0f;
   }
-  uint32_t up[KS][4];   // this lane's dims of u (the bound's key magnitude)
-  u_frag<MT, KS>(qb, wr, up);
-  // LDS-only barrier: orders the histogram clear and the pool ids before any
-  // wave uses them, without waiting for the query loads still in flight (the
-  // first key loads below then overlap them)
-  lds_barrier();
+  uint32_t up[KS][4];   // this lane's dims of u (the bound's key magnitude), set below
 
   float mk2 = 0.0f;   // largest key magnitude t_k of the chunk
   float* sc = P.scores + (size_t)p * P.stride;
@@ -566,10 +588,11 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   const int my_groups = ngroups > wave ? (ngroups - wave + kWaves - 1) / kWaves : 0;
 
   // Row of the key that lane (n, g) loads for local group `it` (the wave's
-  // it-th group); a slot without a key reads row 0 of the key array, so that
-  // every load is in bounds and unconditional (a pool slot's loads run even
-  // for a sequence with no visible position, whose base row may lie past the
-  // array's end); `valid` says whether the key counts.
+  // it-th group); `valid` says whether the slot holds a key.  A slot without
+  // one loads the zero row instead (a pool slot's loads run even for a
+  // sequence with no visible position, whose base row may lie past the
+  // array's end), so every load is in bounds and unconditional and the key
+  // contributes nothing.
   auto key_row = [&](int it, bool& valid) -> int64_t {
     const int cand = c0 + 16 * (wave + kWaves * it) + n;
     int pos;
@@ -581,125 +604,183 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
       pos = cand;
       valid = cand < nc;
     }
-    return valid ? base + pos : (int64_t)0;
+    return base + pos;
   };
   // bf16 keys: 16 bytes (dims 32 ks + 8 g .. + 7) per k-step; FP8 keys: the
   // code bytes of dims 16 g .. + 15 in kb[0] and 64 + 16 g .. + 15 in kb[1]
   // (k-steps 0, 1 and 2, 3: see dim0), the row's exponent byte in kb[2].x
+  // the zero row's address, taken once and held in scalar registers (the
+  // empty asm keeps the compiler from fetching it again in the loop); the
+  // loads go through global-address-space pointers, so that a select between
+  // a key row and the zero row still compiles to global loads
+  const gbyte* zrow = (const gbyte*)(g_zero_key);
+  asm volatile("" : "+s"(zrow));
   auto load = [&](int it, uint4* kb) {
     bool v;
     const int64_t row = key_row(min(it, my_groups - 1), v);
     if constexpr (FP8) {
-      const uint8_t* src = P.ik8 + (size_t)row * D + 16 * g;
-      kb[0] = *reinterpret_cast<const uint4*>(src);
-      kb[1] = *reinterpret_cast<const uint4*>(src + 64);
-      kb[2].x = P.ik8e[row];
+      const gbyte* src = (v ? (const gbyte*)(P.ik8 + (size_t)row * D) : zrow) + 16 * g;
+      kb[0] = gload16(src);
+      kb[1] = gload16(src + 64);
+      kb[2].x = *(v ? (const gbyte*)(P.ik8e + row) : zrow);
     } else {
-      const uint4* src = reinterpret_cast<const uint4*>(P.ik + (size_t)row * D + 8 * g);
+      const gbyte* src = (v ? (const gbyte*)(P.ik + (size_t)row * D) : zrow) + 16 * g;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kb[ks] = src[4 * ks];
+      for (int ks = 0; ks < KS; ++ks) kb[ks] = gload16(src + 64 * ks);
     }
   };
 
-  auto process = [&](int it, const uint4* kin) {
-    const int gi = wave + kWaves * it;
-    bool valid;
-    key_row(it, valid);
-    // zero the keys that do not count with a mask (straight-line code: a
-    // select here would become a branch and stall the load pipeline)
-    const uint32_t vm = valid ? 0xFFFFFFFFu : 0u;
-    uint4 kb[KS];
+  // k-step ks of a loaded key group as a bf16 MFMA fragment (FP8 codes
+  // decoded exactly; a slot without a key loaded the zero row, nothing to
+  // mask)
+  auto fragment = [&](const uint4* kin, int ks) -> uint4 {
     if constexpr (FP8) {
       const float sc = __uint_as_float(kin[2].x << 23);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 r = kin[ks >> 1];
-        const uint32_t lo = (ks & 1) ? r.z : r.x, hi = (ks & 1) ? r.w : r.y;
-        const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false));
-        const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true));
-        const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false));
-        const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true));
-        kb[ks] = make_uint4(a & vm, b & vm, c & vm, d & vm);
-      }
+      const uint4 r = kin[ks >> 1];
+      const uint32_t lo = (ks & 1) ? r.z : r.x, hi = (ks & 1) ? r.w : r.y;
+      const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false));
+      const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true));
+      const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false));
+      const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true));
+      return make_uint4(a, b, c, d);
     } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kb[ks] = make_uint4(kin[ks].x & vm, kin[ks].y & vm, kin[ks].z & vm, kin[ks].w & vm);
+      return kin[ks];
     }
-    // S (16 keys x 16 heads per tile) = K . Q^T ; lane (n, g) gets keys 4g+i, head 16*mt+n
-    f32x4 acc[MT];
+  };
+  // k-step ks of a group's products S (16 keys x 16 heads per tile) = K . Q^T
+  // -- lane (n, g) gets keys 4g+i, head 16*mt+n -- and of its keys'
+  // magnitudes t_k (this lane's dims; the four lane groups' parts are summed
+  // once all k-steps are in, and the final factor 1 + 2^-10 covers the
+  // roundings)
+  auto kstep = [&](const uint4& kb, int ks, f32x4 (&acc)[MT], float& t) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, kb);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int mt = 0; mt < MT; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[mt][ks], ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[mt],
+                                                        0, 0, 0);
+    const uint32_t wd[4] = {kb.x, kb.y, kb.z, kb.w};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, kb[ks]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[mt][ks], acc[mt], 0, 0, 0);
+    for (int j = 0; j < 4; ++j)
+      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[j] & 0x7FFF7FFFu),
+                                          __builtin_bit_cast(bf16x2, up[ks][j]), t, false);
+  };
+
+  // One pipeline step: the next group's products (kin -> accn, when
+  // NEXT) in KS slices, each slice's MFMAs followed by a slice of the VALU
+  // work that finishes local group `it` (the wave's it-th group) from its
+  // products accp, so that every MFMA runs on the matrix core while VALU
+  // instructions issue; then group it's scores and block scores go to LDS.
+  // What the histograms count is returned for count(), which issues the
+  // atomics.
+  struct Counted {
+    float si, bs;
+    bool cvalid, bvalid;
+  };
+  auto step = [&](auto next, int it, const f32x4 (&accp)[MT], const uint4* kin, f32x4 (&accn)[MT]) -> Counted {
+    constexpr bool NEXT = decltype(next)::value;
+    const int gi = wave + kWaves * it;
+    // block j = g/2 of the group holds keys 8j..8j+7 = rows 4g+i of lane groups g and g^1
+    const int blk = ((c0 + 16 * gi) >> 3) + (g >> 1);
+    float s[4];      // token scores of keys 4g..4g+3 (all 16 lanes of the row)
+    float pt[MT];    // block score terms, relu(mean per head)
+    float t = 0.0f;  // this lane's part of t_k of the next group's key n
+    float inv = 0.125f;
+    if constexpr (POOL) {
+      const int nb = min(max(nvis - 8 * blk, 0), 8);
+      inv = nb == 8 ? 0.125f : __builtin_amdgcn_rcpf((float)max(nb, 1));
     }
-    // token scores of keys 4g..4g+3: this lane's MT heads, then the 16 lanes of the row
-    float s[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = 0.0f;
+    for (int c = 0; c < KS; ++c) {
+      if constexpr (NEXT) {
+        kstep(fragment(kin, c), c, accn, t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) v = fmaf(wr[mt], fmaxf(acc[mt][i], 0.0f), v);
-      s[i] = sum16(v);
+      for (int i = c; i < 4; i += KS) {
+        float v = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) v = fmaf(wr[mt], relu_bits(accp[mt][i]), v);
+        s[i] = sum16(v);
+      }
+      if constexpr (POOL) {
+#pragma unroll
+        for (int mt = c; mt < MT; mt += KS)
+          pt[mt] = relu_bits(add_xor16((accp[mt][0] + accp[mt][1]) + (accp[mt][2] + accp[mt][3])) * inv);
+      }
+      if constexpr (NEXT) __builtin_amdgcn_sched_barrier(0);
     }
-    // key n's magnitude t_k for the bound: this lane's quarter of its dims,
-    // then the four lane groups' quarters (the final factor 1 + 2^-10 covers
-    // the roundings here; invalid keys were zeroed)
-    mk2 = fmaxf(mk2, sum_rows4(t_part<KS>(kb, up)));
+    if constexpr (NEXT) mk2 = fmaxf(mk2, sum_rows4(t));
     // every lane stores one score: lanes n, n+4, n+8, n+12 write the same value
+    Counted r;
     const int i0 = n & 3;
     const int cand = c0 + 16 * gi + 4 * g + i0;
-    bool cvalid;
-    {
-      const float si = i0 == 0 ? s[0] : i0 == 1 ? s[1] : i0 == 2 ? s[2] : s[3];
-      if (INDIRECT) {
-        const int b = cand < nc ? s_pool[(cand - c0) >> 3] : -1;
-        cvalid = b >= 0 && b * 8 + (cand & 7) < nvis;
-      } else {
-        cvalid = cand < nc;
-      }
-      s_sc[cand - c0] = cvalid ? si : -INFINITY;
-      if constexpr (HIST) {
-        if (n < 4 && cvalid) atomicAdd(&s_hist[sortable(si) >> kBinShift], 1u);
-      }
+    r.si = i0 == 0 ? s[0] : i0 == 1 ? s[1] : i0 == 2 ? s[2] : s[3];
+    if (INDIRECT) {
+      const int b = cand < nc ? s_pool[(cand - c0) >> 3] : -1;
+      r.cvalid = b >= 0 && b * 8 + (cand & 7) < nvis;
+    } else {
+      r.cvalid = cand < nc;
     }
+    s_sc[cand - c0] = r.cvalid ? r.si : -INFINITY;
+    r.bs = 0.0f;
+    r.bvalid = false;
     if constexpr (POOL) {
-      // block j = g/2 holds keys 8j..8j+7 = rows 4g+i of lane groups g and g^1
-      const int blk = ((c0 + 16 * gi) >> 3) + (g >> 1);
-      const int nb = min(max(nvis - 8 * blk, 0), 8);
-      const float inv = nb == 8 ? 0.125f : __builtin_amdgcn_rcpf((float)max(nb, 1));
       float v = 0.0f;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        float bsum = (acc[mt][0] + acc[mt][1]) + (acc[mt][2] + acc[mt][3]);
-        bsum += __shfl_xor(bsum, 16, kWave);
-        v = fmaf(wr[mt], fmaxf(bsum * inv, 0.0f), v);
-      }
-      const float bs = sum16(v);
+      for (int mt = 0; mt < MT; ++mt) v = fmaf(wr[mt], pt[mt], v);
+      r.bs = sum16(v);
+      r.bvalid = blk < nblk;
       // lanes of both lane groups of the block write the same value
-      s_scb[blk - (c0 >> 3)] = blk < nblk ? bs : -INFINITY;
-      if (lane == 0 || lane == 32) {
-        if (blk < nblk) atomicAdd(&s_hist_b[sortable(bs) >> kBinShift], 1u);
-      }
+      s_scb[blk - (c0 >> 3)] = r.bvalid ? r.bs : -INFINITY;
+    }
+    return r;
+  };
+  auto count = [&](const Counted& r) {
+    if constexpr (HIST) {
+      if (n < 4 && r.cvalid) atomicAdd(&s_hist[sortable(r.si) >> kBinShift], 1u);
+    }
+    if constexpr (POOL) {
+      // one lane per block (lanes 0 and 32) counts it
+      if ((lane & 31) == 0 && r.bvalid) atomicAdd(&s_hist_b[sortable(r.bs) >> kBinShift], 1u);
     }
   };
 
-  // Software pipeline over this wave's groups with NBUF-1 groups in flight.
-  // The steady state is straight-line code (every load and store issued
-  // unconditionally), so the compiler waits only for the group it is about
-  // to use; the tail has no loads left to issue.
+  // Software pipeline over this wave's groups, group g in buf[g % NBUF].
+  // Step s loads group s + NBUF - 1, issues the MFMAs of group s + 1 and
+  // finishes group s, so the matrix cores work one group ahead of the VALU
+  // code that consumes their results and NBUF - 2 loaded groups wait behind
+  // the one in use.  The steady state is straight-line code (every load and
+  // store issued unconditionally; past the wave's last group the loads and
+  // products repeat that group and are not finished), so the compiler waits
+  // only for the group it is about to use; the tail has no loads left to
+  // issue.
   uint4 buf[NBUF][KS];
-  if (my_groups > 0) {
+  f32x4 acc[MT];
+  auto first_loads = [&]() {
+    if (my_groups > 0) {
 #pragma unroll
-    for (int b = 0; b < NBUF - 1; ++b) {
-      load(b, buf[b]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int b = 0; b < NBUF - 1; ++b) {
+        load(b, buf[b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+  };
+  // a Full scan's first loads go out before the bound's setup, which waits
+  // for the query; a Reindex scan's need the pool ids in LDS first
+  if constexpr (!INDIRECT) first_loads();
+  u_frag<MT, KS>(qb, wr, up);
+  // LDS-only barrier: orders the histogram clear and the pool ids before any
+  // wave uses them, without waiting for the query and key loads in flight
+  lds_barrier();
+  if constexpr (INDIRECT) first_loads();
+  if (my_groups > 0) {
+    float t = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kstep(fragment(buf[0], ks), ks, acc, t);
+    mk2 = fmaxf(mk2, sum_rows4(t));
   }
+  using with_next = std::integral_constant<bool, true>;
+  using last = std::integral_constant<bool, false>;
   int it = 0;
   for (; it + NBUF <= my_groups; it += NBUF) {
 #pragma unroll
@@ -708,13 +789,23 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
       // keep the loads in issue order (vmcnt retires in order: a group loaded
       // later must not be scheduled ahead of the one needed next)
       __builtin_amdgcn_sched_barrier(0);
-      process(it + b, buf[b]);
+      f32x4 nxt[MT];
+      count(step(with_next{}, it + b, acc, buf[(b + 1) % NBUF], nxt));
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = nxt[mt];
     }
   }
 #pragma unroll
-  for (int b = 0; b < NBUF - 1; ++b)
-    if (it + b < my_groups) process(it + b, buf[b]);
+  for (int b = 0; b < NBUF - 1; ++b) {
+    if (it + b < my_groups) {
+      f32x4 nxt[MT] = {};
+      if (it + b + 1 < my_groups) count(step(with_next{}, it + b, acc, buf[(b + 1) % NBUF], nxt));
+      else count(step(last{}, it + b, acc, buf[(b + 1) % NBUF], nxt));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = nxt[mt];
+    }
+  }
 
   // ---- publish scores, histograms and the largest t_k
   lds_barrier();
