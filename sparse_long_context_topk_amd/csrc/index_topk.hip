@@ -860,7 +860,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
 constexpr int kChunkKeys = 4096;   // keys per chunk-scan work-group
 
 template <int D, int MT, int QB>
-__global__ __launch_bounds__(kThreads, 2) void k_scan_chunk(Params P) {   // two waves per SIMD
+__global__ __launch_bounds__(kThreads, QB <= 2 ? 2 : 1) void k_scan_chunk(Params P) {   // two waves per SIMD up to QB = 2
   static_assert(QB >= 1 && QB <= 4, "lane group g stores query g's scores");
   constexpr int KS = D / 32;
   constexpr int NBUF = 2;           // one key group in flight, one in use (registers go to the queries)
@@ -972,7 +972,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_scan_chunk(Params P) {   // two
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v = fmaf(wq[qq][mt][i], fmaxf(acc[mt][i], 0.0f), v);
+        for (int i = 0; i < 4; ++i) v = fmaf(wq[qq][mt][i], relu_bits(acc[mt][i]), v);
       sq[qq] = sum_rows4(v);   // + the other three lane groups' heads
     }
     // lane group g stores query g's score and counts it: one store and one
