@@ -162,18 +162,36 @@ def step_bytes(wl):
     return b
 
 
-def traffic_from_profile(kernel_sha):
+def traffic_from_profile(kernel_sha, key="traffic_bytes_per_launch"):
     """HBM bytes per scan launch measured with rocprofv3 counters (committed
-    summary), if it was taken on the current kernel source."""
+    summary; `key` names the bf16 or the FP8-key figure), if it was taken on
+    the current kernel source."""
     path = os.path.join(ROOT, "profiles", "index_scan_c3_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
-    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_b = re.search(r"^" + key + r":\s*([0-9.eE+]+)", text, re.M)
     if not m_sha or not m_b or m_sha.group(1) != kernel_sha:
         return None
     return float(m_b.group(1))
+
+
+def chunk_counters_from_profile(kernel_sha):
+    """Counter-based MFMA utilisation of the encoder-chunk scan (committed
+    rocprofv3 summary: MFMA-busy cycles and the MOPS rate, each a fraction of
+    the dense bf16 peak), if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "encoder_chunk_scan_c4_mfma_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_busy = re.search(r"^mfma_busy_frac:\s*([0-9.]+)", text, re.M)
+    m_mops = re.search(r"^mops_frac:\s*([0-9.]+)", text, re.M)
+    if not m_sha or not m_busy or not m_mops or m_sha.group(1) != kernel_sha:
+        return None
+    return {"mfma_busy_frac": float(m_busy.group(1)), "mops_frac": float(m_mops.group(1)),
+            "profile": "profiles/encoder_chunk_scan_c4_mfma_counters.md"}
 
 
 def _cpu_model():
@@ -445,21 +463,25 @@ def main():
         scan_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / K
         fl = chunk_flops(wl)
         achieved = fl / (scan_ms * 1e-3) / 1e12
+        sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
+        counters = chunk_counters_from_profile(sha) if a.workload == "c4" else None
         roofline = {"bound": "mfma", "kernel": "k_scan_chunk (encoder-chunk indexer scan, bf16 MFMA)",
                     "achieved": round(achieved, 1), "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
-                    "algorithmic_flops_per_launch": fl, "launch_ms": round(scan_ms, 5)}
+                    "algorithmic_flops_per_launch": fl, "launch_ms": round(scan_ms, 5),
+                    "counters": counters}
     elif has_full:
         scan_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / K
         sb = scan_bytes(wl)
         achieved = sb / (scan_ms * 1e-3) / 1e9
         sha = hashlib.sha256(open(SCAN_SRC, "rb").read()).hexdigest()
-        traffic = traffic_from_profile(sha)
+        traffic = traffic_from_profile(sha, "fp8_traffic_bytes_per_launch" if wl.get("fp8_keys")
+                                       else "traffic_bytes_per_launch")
         kname = "k_scan over block keys (pool-based Full)" if wl.get("pool_full") else "k_scan (indexer scan, Full layer)"
         if wl.get("fp8_keys"):
             kname = "k_scan over FP8 keys (indexer scan, Full layer)"
-        if wl.get("pool_full") or wl.get("fp8_keys") or a.workload != "c3":
-            traffic = None   # the committed counters cover the 1M batch-4 token scan only
+        if wl.get("pool_full") or a.workload != "c3":
+            traffic = None   # the committed counters cover the 1M batch-4 token scans (bf16 and FP8 keys) only
         roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                     "traffic": traffic, "algorithmic_bytes_per_launch": sb, "launch_ms": round(scan_ms, 5)}
