@@ -319,7 +319,10 @@ csa2_status csa2_window_append(const void* x, int x_dtype, int64_t n_rows, const
  *     lse_j = log sum exp(z)   (out = 0, lse = -inf when no key is valid)
  *   out [n_q][h][512] fp32; lse [n_q][h] fp32 or NULL.
  * Accuracy: main-KV values are decoded exactly; products run on fp16 MFMA
- * with fp32 accumulation (fp32 queries are split into two fp16 terms);
+ * with fp32 accumulation (fp32 queries are split into two fp16 terms); when a
+ * query's slots are split over several work-groups, each split's output,
+ * normalised by its own softmax sum, is kept in fp16 (relative 2^-11) until
+ * the fp32 merge;
  * bf16 queries and window rows must lie within the fp16 range (|x| < 65504).
  * Supported: d = 512, h in {16, 32, 48, 64}, 0 <= k <= 2048, 0 <= w_max <= 1024.
  * Alignment: q 16 B, swa 16 B, cache 4 B. */

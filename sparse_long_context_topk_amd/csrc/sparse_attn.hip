@@ -73,8 +73,8 @@ struct Params {
   float* out;
   float* lse;
   int nsplit, nsub;
-  float* part_o;   // [n_q][nsplit][h][512]
-  float* part_ml;  // [n_q][nsplit][h][2]
+  _Float16* part_o;   // [n_q][nsplit][h][512]: each split's output / its l
+  float* part_ml;     // [n_q][nsplit][h][2]: each split's (m, l)
 };
 
 // 8 E2M1 codes (one little-endian dword, channel 2i in the low nibble of byte
@@ -458,12 +458,15 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
     if (P.lse && g == 0)
       P.lse[(size_t)qi * P.h + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
+    // the split's output normalised by its own sum, rounded to fp16 (a convex
+    // combination of fp16 values: in range, relative error 2^-11)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = 16 * wave + 4 * g + i;
-      float* dst = P.part_o + (((size_t)qi * P.nsplit + split) * P.h + hh) * 512 + n;
+      const float inv = lrow[i] > 0.0f ? 1.0f / lrow[i] : 0.0f;
+      _Float16* dst = P.part_o + (((size_t)qi * P.nsplit + split) * P.h + hh) * 512 + n;
 #pragma unroll
-      for (int t = 0; t < 32; ++t) dst[16 * t] = o[t][i];
+      for (int t = 0; t < 32; ++t) dst[16 * t] = (_Float16)(o[t][i] * inv);
     }
     if (g == 0) {
       float* ml = P.part_ml + (((size_t)qi * P.nsplit + split) * P.h + head) * 2;
@@ -864,12 +867,15 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
     if (P.lse && g == 0)
       P.lse[(size_t)qi * P.h + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
+    // the split's output normalised by its own sum, rounded to fp16 (a convex
+    // combination of fp16 values: in range, relative error 2^-11)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = 16 * wave + 4 * g + i;
-      float* dst = P.part_o + (((size_t)qi * P.nsplit + split) * P.h + hh) * 512 + n;
+      const float inv = lrow[i] > 0.0f ? 1.0f / lrow[i] : 0.0f;
+      _Float16* dst = P.part_o + (((size_t)qi * P.nsplit + split) * P.h + hh) * 512 + n;
 #pragma unroll
-      for (int t = 0; t < 32; ++t) dst[16 * t] = o[t][i];
+      for (int t = 0; t < 32; ++t) dst[16 * t] = (_Float16)(o[t][i] * inv);
     }
     if (g == 0) {
       float* ml = P.part_ml + (((size_t)qi * P.nsplit + split) * P.h + head) * 2;
@@ -879,12 +885,13 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
   }
 }
 
-// Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One wave per (query, head), four heads per work-group: lane s holds split
-// s's (m_s, l_s) and forms its weight, then every lane sums channels 8 lane ..
-// 8 lane + 7 over the splits in ascending order (16-byte loads of each
-// split's partial row, the weights broadcast from their lanes), eight splits'
-// loads in flight at a time.
+// Merge split partials: with each split's normalised output o_s = O_s / l_s,
+// out = sum_s 2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s.  One wave per
+// (query, head), four heads per work-group: lane s holds split s's (m_s, l_s)
+// and forms its weight, then every lane sums channels 8 lane .. 8 lane + 7
+// over the splits in ascending order (one 16-byte fp16 load of each split's
+// partial row, the weights broadcast from their lanes), eight splits' loads in
+// flight at a time.
 __global__ __launch_bounds__(kThreads) void k_merge(Params P) {
   const int lane = threadIdx.x & 63;
   const int qi = blockIdx.x, hh = blockIdx.y * (kThreads / kWave) + (threadIdx.x >> 6);
@@ -898,30 +905,26 @@ __global__ __launch_bounds__(kThreads) void k_merge(Params P) {
     l = v.y;
   }
   const float M = wave_max(m);
-  const float w = (lane < ns && m != -INFINITY) ? exp2f(m - M) : 0.0f;
-  const float L = wave_sum(w * l);
-  const float4* po = reinterpret_cast<const float4*>(P.part_o + row0 * 512) + 2 * lane;
-  const size_t so4 = (size_t)P.h * 128;   // float4s between splits
+  const float w = (lane < ns && m != -INFINITY) ? exp2f(m - M) * l : 0.0f;
+  const float L = wave_sum(w);
+  const uint4* po = reinterpret_cast<const uint4*>(P.part_o + row0 * 512) + lane;
+  const size_t so = (size_t)P.h * 64;   // 16-byte pieces between splits
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   constexpr int kB = 8;
   for (int s0 = 0; s0 < ns; s0 += kB) {
-    float4 x[kB][2];
+    uint4 x[kB];
 #pragma unroll
-    for (int u = 0; u < kB; ++u) {
-      if (s0 + u < ns) {   // uniform
-        x[u][0] = po[(size_t)(s0 + u) * so4];
-        x[u][1] = po[(size_t)(s0 + u) * so4 + 1];
-      }
-    }
+    for (int u = 0; u < kB; ++u)
+      if (s0 + u < ns) x[u] = po[(size_t)(s0 + u) * so];   // uniform
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
       if (s0 + u < ns) {
         const float wu = __shfl(w, s0 + u, kWave);
-        const float xv[8] = {x[u][0].x, x[u][0].y, x[u][0].z, x[u][0].w, x[u][1].x, x[u][1].y, x[u][1].z, x[u][1].w};
+        const f16x8 xv = __builtin_bit_cast(f16x8, x[u]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wu, xv[e], acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wu, (float)xv[e], acc[e]);
       }
     }
   }
@@ -972,7 +975,7 @@ extern "C" size_t csa2_sparse_attn_ws_bytes(int n_q, int h, int k, int w_max) {
   if (n_q <= 0 || h <= 0) return 0;
   const Split s = choose_split(n_q, k, w_max);
   if (s.nsplit == 1) return 256;
-  return align256((size_t)n_q * s.nsplit * h * 512 * sizeof(float)) +
+  return align256((size_t)n_q * s.nsplit * h * 512 * sizeof(_Float16)) +
          align256((size_t)n_q * s.nsplit * h * 2 * sizeof(float));
 }
 
@@ -1007,8 +1010,8 @@ csa2_status attn_call(const void* q, int q_dtype, int n_q, int h, int d, const i
   P.out = out; P.lse = lse;
   P.nsplit = s.nsplit; P.nsub = s.nsub;
   char* w = static_cast<char*>(ws);
-  P.part_o = reinterpret_cast<float*>(w);
-  P.part_ml = reinterpret_cast<float*>(w + align256((size_t)n_q * s.nsplit * h * 512 * sizeof(float)));
+  P.part_o = reinterpret_cast<_Float16*>(w);
+  P.part_ml = reinterpret_cast<float*>(w + align256((size_t)n_q * s.nsplit * h * 512 * sizeof(_Float16)));
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(n_q, s.nsplit);
   if (q_dtype == CSA2_F32) hipLaunchKernelGGL(k_attn<true>, grid, dim3(kThreads), 0, st, P);
