@@ -239,22 +239,6 @@ __device__ __forceinline__ void u_frag(const bf16x8 (&qb)[MT][KS], const float (
   }
 }
 
-// This lane's part of t_k for the key in fragment kb (its 32 dims); the key's
-// t_k is the sum over the four lane groups (sum_rows4).
-template <int KS>
-__device__ __forceinline__ float t_part(const uint4 (&kb)[KS], const uint32_t (&up)[KS][4]) {
-  float t = 0.0f;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const uint32_t wd[4] = {kb[ks].x, kb[ks].y, kb[ks].z, kb[ks].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[j] & 0x7FFF7FFFu),
-                                          __builtin_bit_cast(bf16x2, up[ks][j]), t, false);
-  }
-  return t;
-}
-
 // Sum over the four rows of the wave (lanes l, l^16, l^32, l^48 -- the four
 // lane groups holding parts of one MFMA column), in every lane: two VALU lane
 // permutes (rows 0<->1, 2<->3, then the halves).
@@ -649,20 +633,25 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   };
   // k-step ks of a group's products S (16 keys x 16 heads per tile) = K . Q^T
   // -- lane (n, g) gets keys 4g+i, head 16*mt+n -- and of its keys'
-  // magnitudes t_k (this lane's dims; the four lane groups' parts are summed
-  // once all k-steps are in, and the final factor 1 + 2^-10 covers the
-  // roundings)
-  auto kstep = [&](const uint4& kb, int ks, f32x4 (&acc)[MT], float& t) {
+  // magnitudes t_k = |K| . u, one more MFMA whose B operand is the lane's u
+  // fragment in every column (lane (n, g) gets t of keys 4g+i; the products
+  // are exact in fp32, the sums of non-negative terms round by far less than
+  // the final factor 1 + 2^-10 covers)
+  auto kstep = [&](const uint4& kb, int ks, f32x4 (&acc)[MT], f32x4& t) {
     const bf16x8 a = __builtin_bit_cast(bf16x8, kb);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[mt][ks], ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[mt],
                                                         0, 0, 0);
-    const uint32_t wd[4] = {kb.x, kb.y, kb.z, kb.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[j] & 0x7FFF7FFFu),
-                                          __builtin_bit_cast(bf16x2, up[ks][j]), t, false);
+    const uint4 ab = make_uint4(kb.x & 0x7FFF7FFFu, kb.y & 0x7FFF7FFFu, kb.z & 0x7FFF7FFFu, kb.w & 0x7FFF7FFFu);
+    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ab),
+                                                __builtin_bit_cast(bf16x8, make_uint4(up[ks][0], up[ks][1], up[ks][2], up[ks][3])),
+                                                ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : t, 0, 0, 0);
+  };
+  // the largest of a lane's four t_k (non-negative floats order as their bits)
+  auto tmax4 = [](const f32x4& t) {
+    return __uint_as_float(max(max(__float_as_uint(t[0]), __float_as_uint(t[1])),
+                               max(__float_as_uint(t[2]), __float_as_uint(t[3]))));
   };
 
   // One pipeline step: the next group's products (kin -> accn, when
@@ -683,7 +672,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
     const int blk = ((c0 + 16 * gi) >> 3) + (g >> 1);
     float s[4];      // token scores of keys 4g..4g+3 (all 16 lanes of the row)
     float pt[MT];    // block score terms, relu(mean per head)
-    float t = 0.0f;  // this lane's part of t_k of the next group's key n
+    f32x4 t;         // t_k of the next group's keys 4g..4g+3
     float inv = 0.125f;
     if constexpr (POOL) {
       const int nb = min(max(nvis - 8 * blk, 0), 8);
@@ -709,7 +698,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
       }
       if constexpr (NEXT) __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (NEXT) mk2 = fmaxf(mk2, sum_rows4(t));
+    if constexpr (NEXT) mk2 = fmaxf(mk2, tmax4(t));
     // every lane stores one score: lanes n, n+4, n+8, n+12 write the same value
     Counted r;
     const int i0 = n & 3;
@@ -774,10 +763,10 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   lds_barrier();
   if constexpr (INDIRECT) first_loads();
   if (my_groups > 0) {
-    float t = 0.0f;
+    f32x4 t;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kstep(fragment(buf[0], ks), ks, acc, t);
-    mk2 = fmaxf(mk2, sum_rows4(t));
+    mk2 = fmaxf(mk2, tmax4(t));
   }
   using with_next = std::integral_constant<bool, true>;
   using last = std::integral_constant<bool, false>;
@@ -953,7 +942,20 @@ __global__ __launch_bounds__(kThreads, QB <= 2 ? 2 : 1) void k_scan_chunk(Params
     // no masking: a slot past the visible keys loaded the sequence's first key
     // (key_row), whose t_k belongs to the maximum anyway and whose scores are
     // not stored
-    mk2 = fmaxf(mk2, sum_rows4(t_part<KS>(kb, up)));   // as in k_scan
+    {
+      // t_k = |K| . u by one more MFMA (u, the lane's fragment, in every row
+      // of the A operand; lane (n, g) gets t of key n), as in k_scan
+      f32x4 t = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 ab = make_uint4(kb[ks].x & 0x7FFF7FFFu, kb[ks].y & 0x7FFF7FFFu, kb[ks].z & 0x7FFF7FFFu,
+                                    kb[ks].w & 0x7FFF7FFFu);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, make_uint4(up[ks][0], up[ks][1], up[ks][2], up[ks][3])),
+            __builtin_bit_cast(bf16x8, ab), t, 0, 0, 0);
+      }
+      mk2 = fmaxf(mk2, t[0]);
+    }
     const int cand = c0 + 16 * gi + n;   // this lane's key
     float sq[QB];
 #pragma unroll
