@@ -81,24 +81,18 @@ struct Params {
 // i) times an E4M3 scale byte -> 4 packed fp16 pairs.  The scale goes to fp16
 // by moving bits: (b & 0x7F) << 7 read as an fp16 is the E4M3 magnitude times
 // 2^-8 (exponent bias 15 instead of 7, E4M3 subnormals landing on fp16
-// subnormals), so the code magnitudes come from a byte table of the fp16 high
-// bytes of 2^8 x (0, .5, 1, 1.5, 2, 3, 4, 6) (the low byte is 0); the signs go
-// to bit 15, then one packed fp16 multiply.  Both factors are exact in fp16 and
-// so is their product (exact, see above).
+// subnormals); v_cvt_scalef32_pk_f16_fp4 turns a byte's two codes into fp16
+// times 2^8 (a power-of-two scale argument is applied exactly), then one
+// packed fp16 multiply.  Both factors are exact in fp16 and so is their
+// product (an E2M1 value times an E4M3 scale has at most 6 significant bits
+// and lies in [2^-10, 2688]).
 __device__ __forceinline__ void decode8(uint32_t c, uint32_t sbyte, uint32_t out[4]) {
-  const uint32_t lut_lo = 0x5E5C5800u, lut_hi = 0x66646260u;
-  uint32_t ev = __builtin_amdgcn_perm(lut_hi, lut_lo, c & 0x07070707u) | ((c << 4) & 0x80808080u);
-  uint32_t od = __builtin_amdgcn_perm(lut_hi, lut_lo, (c >> 4) & 0x07070707u) | (c & 0x80808080u);
   const uint32_t sb = ((sbyte & 0x7Fu) << 7) | ((sbyte & 0x80u) << 8);
   const f16x2 s2 = __builtin_bit_cast(f16x2, sb | (sb << 16));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // result bytes: 0, even byte i, 0, odd byte i  (selector 0x0C yields 0x00)
-    const uint32_t sel = 0x000C000Cu | ((uint32_t)i << 8) | ((uint32_t)(4 + i) << 24);
-    uint32_t pr = __builtin_amdgcn_perm(od, ev, sel);
-    f16x2 v = __builtin_bit_cast(f16x2, pr) * s2;
-    out[i] = __builtin_bit_cast(uint32_t, v);
-  }
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 256.0f, 0) * s2);
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 256.0f, 1) * s2);
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 256.0f, 2) * s2);
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 256.0f, 3) * s2);
 }
 
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
