@@ -325,7 +325,7 @@ csa2_status csa2_window_append(const void* x, int x_dtype, int64_t n_rows, const
  * the fp32 merge;
  * bf16 queries and window rows must lie within the fp16 range (|x| < 65504).
  * Supported: d = 512, h in {16, 32, 48, 64}, 0 <= k <= 2048, 0 <= w_max <= 1024.
- * Alignment: q 16 B, swa 16 B, cache 4 B. */
+ * Alignment: q 16 B, swa 16 B, out 16 B, cache 4 B. */
 csa2_status csa2_sparse_attn(const void* q, int q_dtype, int n_q, int h, int d,
                              const int32_t* q_seq, const uint8_t* cache, const int64_t* seq_base,
                              const int32_t* idx, int k,

@@ -45,7 +45,6 @@ constexpr int kThreads = 256;
 constexpr int kSub = 32;            // key slots per sub-tile
 constexpr int kKRow = 512 + 8;      // fp16 per key row in the key-major tile (16 B pad)
 constexpr int kVRow = kSub + 4;     // fp16 per channel row in the channel-major tile (8 B pad)
-constexpr int kVRow2 = kSub;       // k_attn2's channel-major rows (unpadded, chunks swizzled)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSlotsWG = 3072;   // key slots one work-group stages: k <= 2048 plus a window <= 1024
@@ -484,10 +483,39 @@ __global__ __launch_bounds__(kThreads) void k_attn(Params P) {
 // the other class's work, the FP4 scale is decoded by moving bits, and a
 // gather address is one multiply-add from a per-thread base.
 constexpr int kStages = 2;   // sub-tiles whose loads the decode waves keep in flight (3 or 4 time the same)
+// read-only kernel inputs through the constant address space (scalar loads)
+typedef __attribute__((address_space(4))) const int32_t ci32;
+typedef __attribute__((address_space(4))) const int64_t ci64;
+__device__ const int32_t kZeroI32 = 0;
+// max / sum with the value of lane l ^ 16 (rows 0 <-> 1, 2 <-> 3) or l ^ 32
+// (the wave's halves), by VALU lane swaps instead of LDS permutes
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+__device__ const int64_t kZeroI64 = 0;
+__device__ const int64_t kNoRowI64 = -1;
+constexpr int kBuf2 = 3;     // k_attn2's key-major tiles: being decoded, multiplied (Q.K), multiplied (P.V)
+constexpr int kPRow2 = kSub + 8;   // fp16 per head row of k_attn2's P tile (16-byte pad)
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
-  __shared__ __attribute__((aligned(16))) _Float16 s_k[2][kSub * kKRow];
-  __shared__ __attribute__((aligned(16))) _Float16 s_v[2][512 * kVRow2];
-  __shared__ uint32_t s_valid[2][kSub];
+  __shared__ __attribute__((aligned(16))) _Float16 s_k[kBuf2][kSub * kKRow];   // key-major tiles, a ring of three
+  __shared__ __attribute__((aligned(16))) _Float16 s_p[2][64 * kPRow2];        // P [head][key], double-buffered
+  __shared__ __attribute__((aligned(16))) float s_alpha[2][64];                 // O rescale factor per head
+  __shared__ float s_ml[64][2];                                                 // final (m, l) per head
   __shared__ int32_t s_pos[kMaxSlotsWG];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -497,68 +525,281 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
   const bool head_wave = mwave && 16 * wave < P.h;
   const int head = 16 * wave + n;
   // Key-major tile: key slot s of a sub-tile sits in row key_row(s), so that
-  // MFMA tile kt's row r holds key 8 (r >> 2) + 4 kt + (r & 3).
+  // MFMA tile kt's row r holds key 8 (r >> 2) + 4 kt + (r & 3); keys 8 g ..
+  // 8 g + 3 are rows 4 g .. 4 g + 3 and keys 8 g + 4 .. + 7 rows 16 + 4 g ..
   auto key_row = [](int s) { return 16 * ((s >> 2) & 1) + 4 * (s >> 3) + (s & 3); };
-  // Channel-major tile, unpadded 64-byte rows: 16-byte chunk ch (keys 8 ch ..
-  // 8 ch + 7) of channel row r sits at chunk ch ^ ((r >> 1) & 3) -- the reads
-  // of 8 consecutive rows and the writes of 4 chunks x 2 rows of opposite
-  // parity each cover a 128-byte LDS line once.
-  auto v_addr = [](int r, int ch) { return r * kVRow2 + 8 * (ch ^ ((r >> 1) & 3)); };
-  const int64_t cbase = P.seq_base[P.q_seq[qi]];
+  // The query's window inputs, loaded without branches (an absent array
+  // reads a constant) so that their loads are in flight together.
   const int k = P.k;
-  const int nswa = P.swa_len ? P.swa_len[qi] : 0;
-  const int64_t srow0 = nswa ? P.swa_row0[qi] : 0;
-  const int64_t wdst = P.swa_new ? P.swa_dst[qi] : -1;   // this call's new window row of the query
+  const int nswa = *(P.swa_len ? (const ci32*)(P.swa_len + qi) : (const ci32*)&kZeroI32);
+  const int64_t srow0 = *(P.swa_len ? (const ci64*)(P.swa_row0 + qi) : (const ci64*)&kZeroI64);   // used only when nswa > 0
+  const int64_t wdst = *(P.swa_new ? (const ci64*)(P.swa_dst + qi) : (const ci64*)&kNoRowI64);   // this call's new window row of the query
   auto win_src = [&](int64_t row, int cgi) -> const uint16_t* {
     return row == wdst ? P.swa_new + (size_t)qi * 512 + 8 * cgi : P.swa + (size_t)row * 512 + 8 * cgi;
   };
-  if (wdst >= 0 && wdst < P.swa_rows && split == 0 && tid < 64)
-    reinterpret_cast<uint4*>(P.swa_out + (size_t)wdst * 512)[tid] =
-        reinterpret_cast<const uint4*>(P.swa_new + (size_t)qi * 512)[tid];
   const int ns = P.nsplit;
   const int nmine = split < P.nsub ? (P.nsub - split + ns - 1) / ns : 0;
   const uint8_t* fb = static_cast<const uint8_t*>(P.q);
-  for (int i = tid; i < nmine * kSub; i += 2 * kThreads) {
-    const int slot = (split + (i / kSub) * ns) * kSub + (i % kSub);
-    if (slot < k) s_pos[i] = P.idx[(size_t)qi * k + slot];
-  }
 
-  // The two roles run separate loops (their registers are never live at the
-  // same time); both pass one barrier after the prologue and one per sub-tile.
+  // ---- state of both roles.  Every wave runs the P.V of its channel eighth
+  // (channels 64 wave .. 64 wave + 63) for all heads: O^T = V^T P^T, where
+  // row m of channel tile t is channel 64 wave + 16 (m / 4) + 4 t + m % 4, so
+  // o[mt][t] lane (head 16 mt + n, g) holds channels 64 wave + 16 g + 4 t ..
+  // + 3 of that head: the lane's sixteen are consecutive.  The P.V of sub-tile j runs in step j + 1 (after the
+  // barrier that publishes its P), reading P and the heads' rescale factors
+  // from LDS (double-buffered) and V from the key-major tile (a ring of three:
+  // the decode waves fill sub-tile j + 2 meanwhile).  Multiply waves 0-3 also
+  // run Q.K and the online softmax of heads 16 wave .. 16 wave + 15, in one
+  // block with their P.V (the MFMAs of each cover the other's LDS reads);
+  // with fewer than 64 heads the waves past them still multiply (results
+  // dropped), so no branch separates the MFMAs.
+  f32x4 o[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[mt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  // Q^T as the B operand, lane (head n, group g) holds channels 32*ks + 8*g
+  // .. +7 (rounded to fp16, as k_attn); loaded by the multiply waves
+  f16x8 qb[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) qb[ks] = f16x8{};
+
+  // One step: the P.V of sub-tile jp (tile buffer bp) when kPV, and the Q.K
+  // and softmax of sub-tile jq (tile buffer bq) when kQK; the softmax leaves P
+  // and the rescale factors of the wave's heads in LDS buffer jq & 1.
+  auto step = [&](int jp, int bp, int jq, int bq, auto pv_flag, auto qk_flag) {
+    constexpr bool kPV = decltype(pv_flag)::value, kQK = decltype(qk_flag)::value;
+    f16x8 pa[4];
+    if constexpr (kPV) {
+      // P^T (B operand): lane (head 16 mt + n, g) holds keys 8 g .. 8 g + 7;
+      // O rows of heads whose reference moved are rescaled first
+      float al[4];
+      bool moved = false;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        al[mt] = s_alpha[jp & 1][16 * mt + n];
+        pa[mt] = *reinterpret_cast<const f16x8*>(&s_p[jp & 1][(16 * mt + n) * kPRow2 + 8 * g]);
+        moved |= al[mt] != 1.0f;
+      }
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) o[mt][t] *= al[mt];
+      }
+    }
+    // S^T = K Q^T : tile kt's row r holds key 8 (r >> 2) + 4 kt + (r & 3), so
+    // lane (head n, g) gets keys 8 g + 4 kt + i: eight consecutive keys.
+    // V^T (A operand) of channel tile t: lane (row n, g) holds keys 8 g ..
+    // 8 g + 7 of its channel by two transposed reads in which source lane n
+    // reads key row 4 g + n / 4 (then 16 + 4 g + n / 4), channels 64 wave +
+    // 16 (n & 3) + 4 t .. + 3.  k-step ks carries the two Q.K MFMAs of
+    // channels 32 ks .. 32 ks + 31 and one P.V MFMA (tile ks / 4, head tile
+    // ks % 4); each k-step's fragments are read one k-step (V: one tile) ahead.
+    f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+    const _Float16* krow0 = &s_k[bq][n * kKRow + 8 * g];
+    const _Float16* krow1 = &s_k[bq][(16 + n) * kKRow + 8 * g];
+    const _Float16* v0 = &s_k[bp][(4 * g + (n >> 2)) * kKRow + 64 * wave + 16 * (n & 3)];
+    auto vread = [&](int t) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + 4 * t));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + 16 * kKRow + 4 * t));
+      const uint2 va = __builtin_bit_cast(uint2, lo), vb = __builtin_bit_cast(uint2, hi);
+      return __builtin_bit_cast(f16x8, make_uint4(va.x, va.y, vb.x, vb.y));
+    };
+    f16x8 n0{}, n1{}, bvn{}, bv{};
+    if constexpr (kQK) {
+      n0 = *reinterpret_cast<const f16x8*>(krow0);
+      n1 = *reinterpret_cast<const f16x8*>(krow1);
+    }
+    if constexpr (kPV) bvn = vread(0);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const f16x8 a0 = n0, a1 = n1;
+      if constexpr (kQK) {
+        if (ks + 1 < 16) {
+          n0 = *reinterpret_cast<const f16x8*>(krow0 + 32 * (ks + 1));
+          n1 = *reinterpret_cast<const f16x8*>(krow1 + 32 * (ks + 1));
+        }
+      }
+      if constexpr (kPV) {
+        if ((ks & 3) == 0) {
+          bv = bvn;
+          if ((ks >> 2) + 1 < 4) bvn = vread((ks >> 2) + 1);
+        }
+      }
+      if constexpr (kQK) {
+        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[ks], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[ks], sacc[1], 0, 0, 0);
+      }
+      if constexpr (kPV) {
+        const int t = ks >> 2, mt = ks & 3;
+        o[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv, pa[mt], o[mt][t], 0, 0, 0);
+      }
+    }
+    if constexpr (kQK) {
+      // validity of keys 8 g .. 8 g + 7: a selected entry with a position,
+      // or a window row the query has (the decode leaves finite values in
+      // the other slots, which P = 0 then drops)
+      const int sub0 = (split + jq * ns) * kSub;
+      const int4 pa4 = *reinterpret_cast<const int4*>(&s_pos[jq * kSub + 8 * g]);
+      const int4 pb4 = *reinterpret_cast<const int4*>(&s_pos[jq * kSub + 8 * g + 4]);
+      const int pos8[8] = {pa4.x, pa4.y, pa4.z, pa4.w, pb4.x, pb4.y, pb4.z, pb4.w};
+      bool ok[8];
+      if (sub0 + kSub <= k) {   // selected entries only (uniform)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ok[e] = pos8[e] >= 0;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int slot = sub0 + 8 * g + e;
+          ok[e] = slot < k ? pos8[e] >= 0 : slot - k < nswa;
+        }
+      }
+      float z[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * kt + i;
+          const float v = ok[e] ? sacc[kt][i] * P.scale_log2 : -INFINITY;
+          z[e] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = max_xor16(mx);
+      mx = max_xor32(mx);
+      // The running reference m_run moves only when a score exceeds it by more
+      // than 8 (base 2): otherwise P = 2^(z - m_run) <= 256, still exact to
+      // fp16's relative precision, and O and l keep their reference (the
+      // softmax, and the merge of splits by their (m, l), do not depend on
+      // which reference is used).  So the rescale of O is rare.
+      const bool bump = mx > m_run + 8.0f;   // true on the first key (m_run = -inf)
+      const float m_use = bump ? mx : m_run;
+      float alpha = 1.0f, pv[8];
+      if (m_use == -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = 0.0f;
+      } else {
+        // the hardware 2^x: results below 2^-126, flushed, are far below
+        // what the fp16 P and the fp32 sum resolve
+        if (bump && m_run != -INFINITY) alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(z[e] - m_use);
+      }
+      float ps = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ps += pv[e];
+      l_run = l_run * alpha + ps;
+      m_run = m_use;
+      // P (fp16) of head `head`, keys 8 g .. 8 g + 7, and the head's factor
+      if (head_wave) {
+        f16x8 pw;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pw[e] = (_Float16)pv[e];
+        *reinterpret_cast<f16x8*>(&s_p[jq & 1][head * kPRow2 + 8 * g]) = pw;
+        if (g == 0) s_alpha[jq & 1][head] = alpha;
+      }
+    }
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+
+  // O / l (or the split's normalised partial) of the wave's channel eighth,
+  // sixteen consecutive channels per lane (four lanes fill a head's 64), once
+  // the heads' (m, l) are in s_ml
+  auto write_out = [&]() {
+    // every value is scaled (and packed) before the first store, so no store
+    // waits for an earlier one to release its data registers
+    const int nmt = P.h >> 4;
+    float inv[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const float l = s_ml[16 * mt + n][1];   // absent heads: read, never stored
+      inv[mt] = l > 0.0f ? 1.0f / l : 0.0f;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[mt][t] *= inv[mt];
+    if (P.nsplit == 1) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        if (mt >= nmt) continue;
+        float* dst = P.out + ((size_t)qi * P.h + 16 * mt + n) * 512 + 64 * wave + 16 * g;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) *reinterpret_cast<f32x4*>(dst + 4 * t) = o[mt][t];
+      }
+    } else {
+      // the split's output normalised by its own sum, rounded to fp16 (a
+      // convex combination of fp16 values: in range, relative error 2^-11)
+      uint32_t w[4][8];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          w[mt][2 * t] = pack_f16(o[mt][t][0], o[mt][t][1]);
+          w[mt][2 * t + 1] = pack_f16(o[mt][t][2], o[mt][t][3]);
+        }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        if (mt >= nmt) continue;
+        _Float16* dst =
+            P.part_o + (((size_t)qi * P.nsplit + split) * P.h + 16 * mt + n) * 512 + 64 * wave + 16 * g;
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[mt][0], w[mt][1], w[mt][2], w[mt][3]);
+        *reinterpret_cast<uint4*>(dst + 8) = make_uint4(w[mt][4], w[mt][5], w[mt][6], w[mt][7]);
+      }
+    }
+  };
+
+  // The two roles run separate loops; both pass one barrier after the
+  // prologue, one per sub-tile and one before the output.
   if (!mwave) {
     // decode assignment as k_attn's: thread -> key slots 8*kq .. 8*kq+7,
     // channels 8*cg .. 8*cg+7
     const int dt = tid - kThreads;
     const int kq = dt & 3, cg = dt >> 2;
-    const int cpar = cg & 1;   // odd channel groups swap their rows in pairs
-    const uint32_t sel_even = cpar ? 0x07060302u : 0x05040100u, sel_odd = cpar ? 0x05040100u : 0x07060302u;
+    // The index-list loads of the first sub-tiles (when they hold selected
+    // entries only) go out before the query's row base, two dependent scalar
+    // loads, is waited for.
+    int first_pos[kStages][8];
+#pragma unroll
+    for (int x = 0; x < kStages; ++x) {
+      const int sub = split + x * ns;
+      if (x < nmine && sub_kind(sub * kSub, k) == 0) {
+        const int32_t* ip = P.idx + (size_t)qi * k + sub * kSub + 8 * kq;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) first_pos[x][jj] = ip[jj];
+      }
+    }
+    const int64_t cbase = P.seq_base[P.q_seq[qi]];
     // Global loads of a sub-tile, one loader per slot class.  Addresses of
-    // empty slots point at the fallback bytes, so no load is conditional.
+    // empty slots point at the fallback bytes, so no load is conditional (any
+    // bytes decode to finite values, and the softmax gives those slots P = 0).
     // cq: this thread's codes dword in the query's first record (fq: in the
     // fallback bytes); sdist: the distance from it to its scale dword
     const uint8_t* const cq = P.cache + (size_t)cbase * CSA2_KV_RECORD_BYTES + 4 * cg;
     const uint8_t* const fq = fb + 4 * cg;
     const int64_t sdist = 256 + 4 * (cg >> 3) - 4 * cg;
     auto load_sel_pos = [&](Stage& st, const int pos[8]) {   // all 32 slots are selected entries
-      st.valid = 0;
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const uint8_t* rc = pos[jj] >= 0 ? cq + (uint64_t)(uint32_t)pos[jj] * CSA2_KV_RECORD_BYTES : fq;
         st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rc);
         st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rc + sdist);
-        st.valid |= (pos[jj] >= 0 ? 1u : 0u) << jj;
       }
     };
-    auto load_sel = [&](Stage& st, int j) {        // local sub-tile j; positions from the LDS copy of the index list
-      const int i0 = j * kSub + 8 * kq;   // multiple of 8: two 16-byte LDS reads
+    // this thread's eight positions of local sub-tile j from the LDS copy of
+    // the index list (read ahead of their loads; j past the list reads entry 0)
+    auto staged_pos = [&](int j, int pos[8]) {
+      const int i0 = (j < nmine ? j : 0) * kSub + 8 * kq;   // multiple of 8: two 16-byte LDS reads
       const int4 pa = *reinterpret_cast<const int4*>(&s_pos[i0]);
       const int4 pb = *reinterpret_cast<const int4*>(&s_pos[i0 + 4]);
-      const int pos[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-      load_sel_pos(st, pos);
+      pos[0] = pa.x; pos[1] = pa.y; pos[2] = pa.z; pos[3] = pa.w;
+      pos[4] = pb.x; pos[5] = pb.y; pos[6] = pb.z; pos[7] = pb.w;
     };
     auto load_win = [&](Stage& st, int sub) {      // all 32 slots are window rows (or past the window)
       const int r0 = sub * kSub + 8 * kq - k;
-      st.valid = 0;
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const bool ok = r0 + jj < nswa;
@@ -566,12 +807,10 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
             ok ? win_src(srow0 + r0 + jj, cg) : reinterpret_cast<const uint16_t*>(fb) + 8 * cg;
         const uint4 v = *reinterpret_cast<const uint4*>(src);
         st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
-        st.valid |= (ok ? 1u : 0u) << jj;
       }
     };
-    auto load_mixed = [&](Stage& st, int sub) {    // the one sub-tile that straddles slot k
+    auto load_mixed = [&](Stage& st, int sub) {    // the one sub-tile that straddles slot k (empty slots: zeros)
       const int slot0 = sub * kSub + 8 * kq;
-      st.valid = 0;
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int slot = slot0 + jj;
@@ -582,38 +821,33 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
             const uint8_t* rec = P.cache + (size_t)(cbase + pos) * CSA2_KV_RECORD_BYTES;
             st.w[jj][0] = *reinterpret_cast<const uint32_t*>(rec + 4 * cg);
             st.w[jj][1] = *reinterpret_cast<const uint32_t*>(rec + 256 + 4 * (cg >> 3));
-            st.valid |= 1u << jj;
           }
         } else if (slot - k < nswa) {
           const uint4 v = *reinterpret_cast<const uint4*>(win_src(srow0 + slot - k, cg));
           st.w[jj][0] = v.x; st.w[jj][1] = v.y; st.w[jj][2] = v.z; st.w[jj][3] = v.w;
-          st.valid |= 1u << jj;
         }
       }
     };
 
-    auto load_first = [&](Stage& st, int sub) {   // positions straight from the index list
+    auto load_first = [&](Stage& st, int x) {   // local sub-tile x < kStages
+      const int sub = split + x * ns;
       const int kind = sub_kind(sub * kSub, k);
       if (kind == 0) {
-        const int32_t* ip = P.idx + (size_t)qi * k + sub * kSub + 8 * kq;
-        int pos[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) pos[jj] = ip[jj];
-        load_sel_pos(st, pos);
+        load_sel_pos(st, first_pos[x]);
       } else if (kind == 1) {
         load_win(st, sub);
       } else {
         load_mixed(st, sub);
       }
     };
-    auto load_next = [&](Stage& st, int j) {   // local sub-tile j >= 2 (staged positions readable)
+    auto load_next = [&](Stage& st, int j, const int pos[8]) {   // local sub-tile j >= kStages; pos: staged_pos(j)
       const int sub = split + j * ns;
       const int kind = sub_kind(sub * kSub, k);
-      if (kind == 0) load_sel(st, j);
+      if (kind == 0) load_sel_pos(st, pos);
       else if (kind == 1) load_win(st, sub);
       else load_mixed(st, sub);
     };
-  // Decode the loaded words to fp16 and write both LDS layouts of buffer b.
+  // Decode the loaded words to fp16 and write the key-major tile of buffer b.
     // The slot class is a compile-time argument (0: selected entries only,
     // 1: window rows only, 2: both), so a sub-tile of one class runs only its
     // own decode: the decode waves' VALU issue, which they share with the
@@ -626,7 +860,6 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const bool is_sel = slot0 + 8 * kq + jj < k;
-        const uint32_t keep = (st.valid >> jj) & 1u ? 0xFFFFFFFFu : 0u;
         uint32_t dv[4], sv[4];
         if constexpr (kCls != 1)
           decode8(st.w[jj][0], (st.w[jj][1] >> sc_shift) & 0xFFu, dv);
@@ -637,25 +870,12 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if constexpr (kCls == 0) vals[jj][j] = dv[j] & keep;
-          else if constexpr (kCls == 1) vals[jj][j] = sv[j] & keep;
-          else vals[jj][j] = (is_sel ? dv[j] : sv[j]) & keep;
+          if constexpr (kCls == 0) vals[jj][j] = dv[j];
+          else if constexpr (kCls == 1) vals[jj][j] = sv[j];
+          else vals[jj][j] = is_sel ? dv[j] : sv[j];
         }
-        if (cg == 0) s_valid[b][8 * kq + jj] = keep & 1u;
         *reinterpret_cast<uint4*>(&s_k[b][key_row(8 * kq + jj) * kKRow + 8 * cg]) =
             make_uint4(vals[jj][0], vals[jj][1], vals[jj][2], vals[jj][3]);
-      }
-      // channel-major copy: channel row 8 cg + c' gets keys 8 kq .. 8 kq + 7 as
-      // one 16-byte chunk (see v_addr); the odd channel groups write their rows
-      // in swapped pairs (c' = c ^ 1), so the two halves of a 128-byte LDS
-      // line are written by one instruction's eight lanes
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint32_t sel = (c & 1) ? sel_odd : sel_even;   // the fp16 half of channel c'
-        uint32_t pk[4];
-#pragma unroll
-        for (int jp = 0; jp < 4; ++jp) pk[jp] = __builtin_amdgcn_perm(vals[2 * jp + 1][c >> 1], vals[2 * jp][c >> 1], sel);
-        *reinterpret_cast<uint4*>(&s_v[b][v_addr(8 * cg + (c ^ cpar), kq)]) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       }
     };
 
@@ -671,10 +891,14 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
     Stage stg[kStages];
 #pragma unroll
     for (int x = 0; x < kStages; ++x)
-      if (x < nmine) load_first(stg[x], split + x * ns);
+      if (x < nmine) load_first(stg[x], x);
     if (nmine > 0) store_any(stg[0], split, 0);
     lds_barrier();   // s_pos and buffer 0
-    if (nmine > kStages) load_next(stg[0], kStages);
+    if (nmine > kStages) {
+      int pos[8];
+      staged_pos(kStages, pos);
+      load_next(stg[0], kStages, pos);
+    }
     // Local sub-tiles are in ascending slot order, so the selected-only ones
     // come first.  While the sub-tile being loaded is one of them, the loop
     // below issues only the branch-free gather loads: with no load under a
@@ -688,8 +912,11 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
       for (int u = 0; u < kStages; ++u) {
         const int j = j0 + u;
         Stage& S = stg[(u + 1) % kStages];   // sub-tile j + 1
-        store_stage(S, split + (j + 1) * ns, (j + 1) & 1, std::integral_constant<int, 0>{});
-        load_sel(S, j + 1 + kStages);
+        int pos[8];
+        staged_pos(j + 1 + kStages, pos);
+        if (j > 0) step(j - 1, (j - 1) % kBuf2, 0, 0, yes{}, no{});
+        store_stage(S, split + (j + 1) * ns, (j + 1) % kBuf2, std::integral_constant<int, 0>{});
+        load_sel_pos(S, pos);
         lds_barrier();
       }
     }
@@ -698,27 +925,46 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
       for (int u = 0; u < kStages; ++u) {
         const int j = j0 + u;
         if (j < nmine) {   // uniform
+          int pos[8];
+          staged_pos(j + 1 + kStages, pos);
+          if (j > 0) step(j - 1, (j - 1) % kBuf2, 0, 0, yes{}, no{});
           if (j + 1 < nmine) {
             Stage& S = stg[(u + 1) % kStages];   // sub-tile j + 1
-            store_any(S, split + (j + 1) * ns, (j + 1) & 1);   // its buffer was last read before the previous barrier
-            if (j + 1 + kStages < nmine) load_next(S, j + 1 + kStages);
+            store_any(S, split + (j + 1) * ns, (j + 1) % kBuf2);   // its buffer was last read before the previous barrier
+            if (j + 1 + kStages < nmine) load_next(S, j + 1 + kStages, pos);
           }
           lds_barrier();
         }
       }
     }
+    if (nmine > 0) step(nmine - 1, (nmine - 1) % kBuf2, 0, 0, yes{}, no{});
+    lds_barrier();   // the heads' (m, l)
+    write_out();
     return;
   }
 
-  // ---- multiply waves: Q^T as the B operand, lane (head n, group g) holds
-  // channels 32*ks + 8*g .. +7 (rounded to fp16, as k_attn)
-  f16x8 qb[16];
+  // ---- multiply waves.  Their prologue issues the query loads, the copy
+  // of the index list into LDS (the decode waves read their first sub-tiles'
+  // positions from global memory, so no wait of theirs is behind it) and
+  // the load of the query's new window row, which is stored at the end.
+  uint4 qraw[16];
+  if (head_wave) {
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+      qraw[ks] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(P.q) +
+                                                 ((size_t)qi * P.h + head) * 512 + 32 * ks + 8 * g);
+  }
+  const bool copy_row = wdst >= 0 && wdst < P.swa_rows && split == 0 && tid < 64;
+  uint4 new_row{};
+  if (copy_row) new_row = reinterpret_cast<const uint4*>(P.swa_new + (size_t)qi * 512)[tid];
+  for (int i = tid; i < nmine * kSub; i += kThreads) {
+    const int slot = (split + (i / kSub) * ns) * kSub + (i % kSub);
+    if (slot < k) s_pos[i] = P.idx[(size_t)qi * k + slot];
+  }
   if (head_wave) {
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
-      const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(P.q) +
-                                                      ((size_t)qi * P.h + head) * 512 + 32 * ks + 8 * g);
-      const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+      const uint32_t wd[4] = {qraw[ks].x, qraw[ks].y, qraw[ks].z, qraw[ks].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         qb[ks][2 * e] = (_Float16)__uint_as_float(wd[e] << 16);
@@ -726,155 +972,43 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
       }
     }
   }
-  f32x4 o[32];
-#pragma unroll
-  for (int t = 0; t < 32; ++t) o[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_run = 0.0f;
-  lds_barrier();   // s_pos and buffer 0
-
-  auto compute = [&](int b) {
-    if (head_wave) {
-      // ---- S^T = K Q^T : tile kt's row r holds key 8 (r >> 2) + 4 kt + (r & 3),
-      // so lane (head n, g) gets keys 8 g + 4 kt + i: eight consecutive keys
-      // the two key tiles' chains interleaved (independent accumulators); each
-      // k-step's fragments are read one k-step ahead of their MFMAs
-      f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-      const _Float16* krow0 = &s_k[b][n * kKRow + 8 * g];
-      const _Float16* krow1 = &s_k[b][(16 + n) * kKRow + 8 * g];
-      f16x8 n0 = *reinterpret_cast<const f16x8*>(krow0);
-      f16x8 n1 = *reinterpret_cast<const f16x8*>(krow1);
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const f16x8 a0 = n0, a1 = n1;
-        if (ks + 1 < 16) {
-          n0 = *reinterpret_cast<const f16x8*>(krow0 + 32 * (ks + 1));
-          n1 = *reinterpret_cast<const f16x8*>(krow1 + 32 * (ks + 1));
-        }
-        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[ks], sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[ks], sacc[1], 0, 0, 0);
-      }
-      {
-        constexpr int kM = 2;   // MFMAs per k-step
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int r = 0; r < 15; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);
-      }
-      float z[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 8 * g + 4 * kt + i;
-          const float v = s_valid[b][key] ? sacc[kt][i] * P.scale_log2 : -INFINITY;
-          z[4 * kt + i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      // The running reference m_run moves only when a score exceeds it by more
-      // than 8 (base 2): otherwise P = 2^(z - m_run) <= 256, still exact to
-      // fp16's relative precision, and O and l keep their reference (the
-      // softmax, and the merge of splits by their (m, l), do not depend on
-      // which reference is used).  So the costly rescale of O is rare.
-      const bool bump = mx > m_run + 8.0f;   // true on the first key (m_run = -inf)
-      const float m_use = bump ? mx : m_run;
-      float alpha, pv[8];
-      if (m_use == -INFINITY) {
-        alpha = 1.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = 0.0f;
-      } else {
-        alpha = bump ? exp2f(m_run - m_use) : 1.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = exp2f(z[j] - m_use);
-      }
-      float ps = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ps += pv[j];
-      l_run = l_run * alpha + ps;
-      // rescale O rows (heads 4*g + i live in this lane's accumulators); a
-      // wave whose references did not move, or whose O is still zero (no key
-      // seen yet), skips it
-      const bool rescale = bump && m_run != -INFINITY;
-      m_run = m_use;
-      if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
-        float a4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, kWave);
-#pragma unroll
-        for (int t = 0; t < 32; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[t][i] *= a4[i];
-      }
-      // P as the A operand: slot e = key 8 g + e
-      f16x8 pa;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pa[j] = (_Float16)pv[j];
-      // ---- O += P V  (each V fragment read one MFMA ahead)
-      auto vfrag = [&](int t) {   // V^T fragment: channel 16 t + n, keys 8 g .. 8 g + 7
-        return *reinterpret_cast<const f16x8*>(&s_v[b][v_addr(16 * t + n, g)]);
-      };
-      f16x8 nv = vfrag(0);
-#pragma unroll
-      for (int t = 0; t < 32; ++t) {
-        const f16x8 bv = nv;
-        if (t + 1 < 32) nv = vfrag(t + 1);
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, o[t], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int r = 0; r < 30; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-  };
-
-  for (int j = 0; j < nmine; ++j) {
-    if (head_wave) compute(j & 1);
+  for (int i = tid; i < 2 * (64 - P.h); i += kThreads) {   // absent heads: P = 0, factor 1
+    const int bi = i & 1, hh = P.h + (i >> 1);
+    *reinterpret_cast<f16x8*>(&s_p[bi][hh * kPRow2]) = f16x8{};
+    *reinterpret_cast<f16x8*>(&s_p[bi][hh * kPRow2 + 8]) = f16x8{};
+    *reinterpret_cast<f16x8*>(&s_p[bi][hh * kPRow2 + 16]) = f16x8{};
+    *reinterpret_cast<f16x8*>(&s_p[bi][hh * kPRow2 + 24]) = f16x8{};
+    s_alpha[bi][hh] = 1.0f;
+  }
+  lds_barrier();   // s_pos, buffer 0 and the absent heads' rows
+  if (nmine > 0) {
+    step(0, 0, 0, 0, no{}, yes{});
     lds_barrier();
   }
-
-  if (!head_wave) return;
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, kWave);
-  l_tot += __shfl_xor(l_tot, 32, kWave);
-  // per-row (head 4*g + i) values for this lane's accumulators
-  float lrow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l_tot, 4 * g + i, kWave);
-  if (P.nsplit == 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = 16 * wave + 4 * g + i;
-      const float inv = lrow[i] > 0.0f ? 1.0f / lrow[i] : 0.0f;
-      float* dst = P.out + ((size_t)qi * P.h + hh) * 512 + n;
-#pragma unroll
-      for (int t = 0; t < 32; ++t) dst[16 * t] = o[t][i] * inv;
-    }
-    if (P.lse && g == 0)
-      P.lse[(size_t)qi * P.h + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  } else {
-    // the split's output normalised by its own sum, rounded to fp16 (a convex
-    // combination of fp16 values: in range, relative error 2^-11)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = 16 * wave + 4 * g + i;
-      const float inv = lrow[i] > 0.0f ? 1.0f / lrow[i] : 0.0f;
-      _Float16* dst = P.part_o + (((size_t)qi * P.nsplit + split) * P.h + hh) * 512 + n;
-#pragma unroll
-      for (int t = 0; t < 32; ++t) dst[16 * t] = (_Float16)(o[t][i] * inv);
-    }
+  for (int j = 1; j < nmine; ++j) {
+    step(j - 1, (j - 1) % kBuf2, j, j % kBuf2, yes{}, yes{});
+    lds_barrier();
+  }
+  if (nmine > 0) step(nmine - 1, (nmine - 1) % kBuf2, 0, 0, yes{}, no{});
+  if (head_wave) {
+    float l_tot = l_run;
+    l_tot = add_xor32(add_xor16(l_tot));
     if (g == 0) {
-      float* ml = P.part_ml + (((size_t)qi * P.nsplit + split) * P.h + head) * 2;
-      ml[0] = m_run;
-      ml[1] = l_tot;
+      s_ml[head][0] = m_run;
+      s_ml[head][1] = l_tot;
+    }
+  }
+  lds_barrier();   // the heads' (m, l)
+  write_out();
+  if (copy_row) reinterpret_cast<uint4*>(P.swa_out + (size_t)wdst * 512)[tid] = new_row;
+  if (tid < P.h) {
+    const float m = s_ml[tid][0], l = s_ml[tid][1];
+    if (P.nsplit == 1) {
+      if (P.lse) P.lse[(size_t)qi * P.h + tid] = l > 0.0f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    } else {
+      float* ml = P.part_ml + (((size_t)qi * P.nsplit + split) * P.h + tid) * 2;
+      ml[0] = m;
+      ml[1] = l;
     }
   }
 }
@@ -989,7 +1123,8 @@ csa2_status attn_call(const void* q, int q_dtype, int n_q, int h, int d, const i
   if (k > 0 && (!idx || !cache)) return CSA2_E_INVAL;
   if (w_max > 0 && (!swa || !swa_row0 || !swa_len)) return CSA2_E_INVAL;
   if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(swa) & 15) ||
-      (reinterpret_cast<uintptr_t>(cache) & 3) || (reinterpret_cast<uintptr_t>(ws) & 255))
+      (reinterpret_cast<uintptr_t>(cache) & 3) || (reinterpret_cast<uintptr_t>(ws) & 255) ||
+      (reinterpret_cast<uintptr_t>(out) & 15))
     return CSA2_E_INVAL;
   if (swa_new && (!swa || !swa_dst || swa_rows < 0 || (reinterpret_cast<uintptr_t>(swa_new) & 15) ||
                   (reinterpret_cast<uintptr_t>(swa_dst) & 7)))
