@@ -511,6 +511,7 @@ constexpr int kBuf2 = 3;     // k_attn2's key-major tiles: being decoded, multip
 constexpr int kPRow2 = kSub + 8;   // fp16 per head row of k_attn2's P tile (16-byte pad)
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+template <int NHT>
 __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
   __shared__ __attribute__((aligned(16))) _Float16 s_k[kBuf2][kSub * kKRow];   // key-major tiles, a ring of three
   __shared__ __attribute__((aligned(16))) _Float16 s_p[2][64 * kPRow2];        // P [head][key], double-buffered
@@ -521,9 +522,13 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int qi = blockIdx.x, split = blockIdx.y;
+  // heads hbase .. hbase + 16 NHT - 1 (local rows 0 .. 16 NHT - 1)
+  const int hbase = 16 * NHT * blockIdx.z;
   const bool mwave = wave < 4;   // multiply waves; waves 4-7 decode
-  const bool head_wave = mwave && 16 * wave < P.h;
-  const int head = 16 * wave + n;
+  const bool qk_wave = wave < NHT;   // multiply waves that run Q.K and the softmax
+  const bool head_wave = qk_wave && hbase + 16 * wave < P.h;
+  const int lrow = 16 * wave + n;   // a Q.K wave's head, local row
+  const int head = hbase + lrow;
   // Key-major tile: key slot s of a sub-tile sits in row key_row(s), so that
   // MFMA tile kt's row r holds key 8 (r >> 2) + 4 kt + (r & 3); keys 8 g ..
   // 8 g + 3 are rows 4 g .. 4 g + 3 and keys 8 g + 4 .. + 7 rows 16 + 4 g ..
@@ -534,28 +539,35 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
   const int nswa = *(P.swa_len ? (const ci32*)(P.swa_len + qi) : (const ci32*)&kZeroI32);
   const int64_t srow0 = *(P.swa_len ? (const ci64*)(P.swa_row0 + qi) : (const ci64*)&kZeroI64);   // used only when nswa > 0
   const int64_t wdst = *(P.swa_new ? (const ci64*)(P.swa_dst + qi) : (const ci64*)&kNoRowI64);   // this call's new window row of the query
+  // The two window sources as values in scalar registers: a select between
+  // the kernel-argument fields themselves may be compiled into a per-lane
+  // load of the chosen field, a dependent round trip before every row load.
+  const uint16_t* swa_p = P.swa;
+  const uint16_t* swa_new_p = P.swa_new;
+  asm volatile("" : "+s"(swa_p), "+s"(swa_new_p));
   auto win_src = [&](int64_t row, int cgi) -> const uint16_t* {
-    return row == wdst ? P.swa_new + (size_t)qi * 512 + 8 * cgi : P.swa + (size_t)row * 512 + 8 * cgi;
+    return row == wdst ? swa_new_p + (size_t)qi * 512 + 8 * cgi : swa_p + (size_t)row * 512 + 8 * cgi;
   };
   const int ns = P.nsplit;
   const int nmine = split < P.nsub ? (P.nsub - split + ns - 1) / ns : 0;
   const uint8_t* fb = static_cast<const uint8_t*>(P.q);
 
   // ---- state of both roles.  Every wave runs the P.V of its channel eighth
-  // (channels 64 wave .. 64 wave + 63) for all heads: O^T = V^T P^T, where
-  // row m of channel tile t is channel 64 wave + 16 (m / 4) + 4 t + m % 4, so
-  // o[mt][t] lane (head 16 mt + n, g) holds channels 64 wave + 16 g + 4 t ..
-  // + 3 of that head: the lane's sixteen are consecutive.  The P.V of sub-tile j runs in step j + 1 (after the
-  // barrier that publishes its P), reading P and the heads' rescale factors
-  // from LDS (double-buffered) and V from the key-major tile (a ring of three:
-  // the decode waves fill sub-tile j + 2 meanwhile).  Multiply waves 0-3 also
-  // run Q.K and the online softmax of heads 16 wave .. 16 wave + 15, in one
-  // block with their P.V (the MFMAs of each cover the other's LDS reads);
-  // with fewer than 64 heads the waves past them still multiply (results
-  // dropped), so no branch separates the MFMAs.
-  f32x4 o[4][4];
+  // (channels 64 wave .. 64 wave + 63) for the work-group's heads: O^T =
+  // V^T P^T, where row m of channel tile t is channel 64 wave + 16 (m / 4) +
+  // 4 t + m % 4, so o[mt][t] lane (local head 16 mt + n, g) holds channels
+  // 64 wave + 16 g + 4 t .. + 3 of that head: the lane's sixteen are
+  // consecutive.  The P.V of sub-tile j runs in step j + 1 (after the barrier
+  // that publishes its P), reading P and the heads' rescale factors from LDS
+  // (double-buffered) and V from the key-major tile (a ring of three: the
+  // decode waves fill sub-tile j + 2 meanwhile).  Multiply waves 0 .. NHT - 1
+  // also run Q.K and the online softmax of local heads 16 wave .. 16 wave +
+  // 15, in one block with their P.V (the MFMAs of each cover the other's LDS
+  // reads); heads past h are still multiplied (results dropped), so no branch
+  // separates the MFMAs.
+  f32x4 o[NHT][4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < NHT; ++mt)
 #pragma unroll
     for (int t = 0; t < 4; ++t) o[mt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
@@ -570,21 +582,21 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
   // and the rescale factors of the wave's heads in LDS buffer jq & 1.
   auto step = [&](int jp, int bp, int jq, int bq, auto pv_flag, auto qk_flag) {
     constexpr bool kPV = decltype(pv_flag)::value, kQK = decltype(qk_flag)::value;
-    f16x8 pa[4];
+    f16x8 pa[NHT];
     if constexpr (kPV) {
-      // P^T (B operand): lane (head 16 mt + n, g) holds keys 8 g .. 8 g + 7;
-      // O rows of heads whose reference moved are rescaled first
-      float al[4];
+      // P^T (B operand): lane (local head 16 mt + n, g) holds keys 8 g .. 8 g
+      // + 7; O rows of heads whose reference moved are rescaled first
+      float al[NHT];
       bool moved = false;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < NHT; ++mt) {
         al[mt] = s_alpha[jp & 1][16 * mt + n];
         pa[mt] = *reinterpret_cast<const f16x8*>(&s_p[jp & 1][(16 * mt + n) * kPRow2 + 8 * g]);
         moved |= al[mt] != 1.0f;
       }
       if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < NHT; ++mt)
 #pragma unroll
           for (int t = 0; t < 4; ++t) o[mt][t] *= al[mt];
       }
@@ -595,8 +607,10 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
     // 8 g + 7 of its channel by two transposed reads in which source lane n
     // reads key row 4 g + n / 4 (then 16 + 4 g + n / 4), channels 64 wave +
     // 16 (n & 3) + 4 t .. + 3.  k-step ks carries the two Q.K MFMAs of
-    // channels 32 ks .. 32 ks + 31 and one P.V MFMA (tile ks / 4, head tile
-    // ks % 4); each k-step's fragments are read one k-step (V: one tile) ahead.
+    // channels 32 ks .. 32 ks + 31, and every (4 / NHT)-th k-step one of the
+    // 4 NHT P.V MFMAs (channel tile by channel tile); each k-step's fragments
+    // are read one k-step (V: one tile) ahead.
+    constexpr int kPer = 4 / NHT;
     f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
     const _Float16* krow0 = &s_k[bq][n * kKRow + 8 * g];
     const _Float16* krow1 = &s_k[bq][(16 + n) * kKRow + 8 * g];
@@ -622,10 +636,11 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
           n1 = *reinterpret_cast<const f16x8*>(krow1 + 32 * (ks + 1));
         }
       }
+      const int pvi = ks / kPer, pt = pvi / NHT, pmt = pvi % NHT;   // this k-step's P.V MFMA
       if constexpr (kPV) {
-        if ((ks & 3) == 0) {
+        if (ks % kPer == 0 && pmt == 0) {
           bv = bvn;
-          if ((ks >> 2) + 1 < 4) bvn = vread((ks >> 2) + 1);
+          if (pt + 1 < 4) bvn = vread(pt + 1);
         }
       }
       if constexpr (kQK) {
@@ -633,8 +648,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
         sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[ks], sacc[1], 0, 0, 0);
       }
       if constexpr (kPV) {
-        const int t = ks >> 2, mt = ks & 3;
-        o[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv, pa[mt], o[mt][t], 0, 0, 0);
+        if (ks % kPer == 0) o[pmt][pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv, pa[pmt], o[pmt][pt], 0, 0, 0);
       }
     }
     if constexpr (kQK) {
@@ -697,8 +711,8 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
         f16x8 pw;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pw[e] = (_Float16)pv[e];
-        *reinterpret_cast<f16x8*>(&s_p[jq & 1][head * kPRow2 + 8 * g]) = pw;
-        if (g == 0) s_alpha[jq & 1][head] = alpha;
+        *reinterpret_cast<f16x8*>(&s_p[jq & 1][lrow * kPRow2 + 8 * g]) = pw;
+        if (g == 0) s_alpha[jq & 1][lrow] = alpha;
       }
     }
   };
@@ -711,41 +725,40 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
   auto write_out = [&]() {
     // every value is scaled (and packed) before the first store, so no store
     // waits for an earlier one to release its data registers
-    const int nmt = P.h >> 4;
-    float inv[4];
+    float inv[NHT];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const float l = s_ml[16 * mt + n][1];   // absent heads: read, never stored
+    for (int mt = 0; mt < NHT; ++mt) {
+      const float l = s_ml[16 * mt + n][1];   // heads past h: read, never stored
       inv[mt] = l > 0.0f ? 1.0f / l : 0.0f;
     }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < NHT; ++mt)
 #pragma unroll
       for (int t = 0; t < 4; ++t) o[mt][t] *= inv[mt];
     if (P.nsplit == 1) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (mt >= nmt) continue;
-        float* dst = P.out + ((size_t)qi * P.h + 16 * mt + n) * 512 + 64 * wave + 16 * g;
+      for (int mt = 0; mt < NHT; ++mt) {
+        if (hbase + 16 * mt >= P.h) continue;
+        float* dst = P.out + ((size_t)qi * P.h + hbase + 16 * mt + n) * 512 + 64 * wave + 16 * g;
 #pragma unroll
         for (int t = 0; t < 4; ++t) *reinterpret_cast<f32x4*>(dst + 4 * t) = o[mt][t];
       }
     } else {
       // the split's output normalised by its own sum, rounded to fp16 (a
       // convex combination of fp16 values: in range, relative error 2^-11)
-      uint32_t w[4][8];
+      uint32_t w[NHT][8];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < NHT; ++mt)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           w[mt][2 * t] = pack_f16(o[mt][t][0], o[mt][t][1]);
           w[mt][2 * t + 1] = pack_f16(o[mt][t][2], o[mt][t][3]);
         }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (mt >= nmt) continue;
-        _Float16* dst =
-            P.part_o + (((size_t)qi * P.nsplit + split) * P.h + 16 * mt + n) * 512 + 64 * wave + 16 * g;
+      for (int mt = 0; mt < NHT; ++mt) {
+        if (hbase + 16 * mt >= P.h) continue;
+        _Float16* dst = P.part_o + (((size_t)qi * P.nsplit + split) * P.h + hbase + 16 * mt + n) * 512 +
+                        64 * wave + 16 * g;
         *reinterpret_cast<uint4*>(dst) = make_uint4(w[mt][0], w[mt][1], w[mt][2], w[mt][3]);
         *reinterpret_cast<uint4*>(dst + 8) = make_uint4(w[mt][4], w[mt][5], w[mt][6], w[mt][7]);
       }
@@ -954,7 +967,7 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
       qraw[ks] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(P.q) +
                                                  ((size_t)qi * P.h + head) * 512 + 32 * ks + 8 * g);
   }
-  const bool copy_row = wdst >= 0 && wdst < P.swa_rows && split == 0 && tid < 64;
+  const bool copy_row = wdst >= 0 && wdst < P.swa_rows && split == 0 && blockIdx.z == 0 && tid < 64;
   uint4 new_row{};
   if (copy_row) new_row = reinterpret_cast<const uint4*>(P.swa_new + (size_t)qi * 512)[tid];
   for (int i = tid; i < nmine * kSub; i += kThreads) {
@@ -972,41 +985,52 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
       }
     }
   }
-  for (int i = tid; i < 2 * (64 - P.h); i += kThreads) {   // absent heads: P = 0, factor 1
-    const int bi = i & 1, hh = P.h + (i >> 1);
-    *reinterpret_cast<f16x8*>(&s_p[bi][hh * kPRow2]) = f16x8{};
-    *reinterpret_cast<f16x8*>(&s_p[bi][hh * kPRow2 + 8]) = f16x8{};
-    *reinterpret_cast<f16x8*>(&s_p[bi][hh * kPRow2 + 16]) = f16x8{};
-    *reinterpret_cast<f16x8*>(&s_p[bi][hh * kPRow2 + 24]) = f16x8{};
-    s_alpha[bi][hh] = 1.0f;
+  for (int i = tid; i < 2 * 16 * NHT; i += kThreads) {   // local rows of heads past h: P = 0, factor 1
+    const int bi = i & 1, r = i >> 1;
+    if (hbase + r >= P.h) {
+      *reinterpret_cast<f16x8*>(&s_p[bi][r * kPRow2]) = f16x8{};
+      *reinterpret_cast<f16x8*>(&s_p[bi][r * kPRow2 + 8]) = f16x8{};
+      *reinterpret_cast<f16x8*>(&s_p[bi][r * kPRow2 + 16]) = f16x8{};
+      *reinterpret_cast<f16x8*>(&s_p[bi][r * kPRow2 + 24]) = f16x8{};
+      s_alpha[bi][r] = 1.0f;
+    }
   }
-  lds_barrier();   // s_pos, buffer 0 and the absent heads' rows
-  if (nmine > 0) {
-    step(0, 0, 0, 0, no{}, yes{});
-    lds_barrier();
-  }
-  for (int j = 1; j < nmine; ++j) {
-    step(j - 1, (j - 1) % kBuf2, j, j % kBuf2, yes{}, yes{});
-    lds_barrier();
+  lds_barrier();   // s_pos, buffer 0 and the rows of heads past h
+  if (qk_wave) {
+    if (nmine > 0) {
+      step(0, 0, 0, 0, no{}, yes{});
+      lds_barrier();
+    }
+    for (int j = 1; j < nmine; ++j) {
+      step(j - 1, (j - 1) % kBuf2, j, j % kBuf2, yes{}, yes{});
+      lds_barrier();
+    }
+  } else {   // P.V only, as the decode waves
+    if (nmine > 0) lds_barrier();
+    for (int j = 1; j < nmine; ++j) {
+      step(j - 1, (j - 1) % kBuf2, 0, 0, yes{}, no{});
+      lds_barrier();
+    }
   }
   if (nmine > 0) step(nmine - 1, (nmine - 1) % kBuf2, 0, 0, yes{}, no{});
   if (head_wave) {
     float l_tot = l_run;
     l_tot = add_xor32(add_xor16(l_tot));
     if (g == 0) {
-      s_ml[head][0] = m_run;
-      s_ml[head][1] = l_tot;
+      s_ml[lrow][0] = m_run;
+      s_ml[lrow][1] = l_tot;
     }
   }
   lds_barrier();   // the heads' (m, l)
   write_out();
   if (copy_row) reinterpret_cast<uint4*>(P.swa_out + (size_t)wdst * 512)[tid] = new_row;
-  if (tid < P.h) {
+  if (tid < 16 * NHT && hbase + tid < P.h) {
     const float m = s_ml[tid][0], l = s_ml[tid][1];
+    const int hh = hbase + tid;
     if (P.nsplit == 1) {
-      if (P.lse) P.lse[(size_t)qi * P.h + tid] = l > 0.0f ? (m + log2f(l)) * kLn2 : -INFINITY;
+      if (P.lse) P.lse[(size_t)qi * P.h + hh] = l > 0.0f ? (m + log2f(l)) * kLn2 : -INFINITY;
     } else {
-      float* ml = P.part_ml + (((size_t)qi * P.nsplit + split) * P.h + tid) * 2;
+      float* ml = P.part_ml + (((size_t)qi * P.nsplit + split) * P.h + hh) * 2;
       ml[0] = m;
       ml[1] = l;
     }
@@ -1095,16 +1119,64 @@ Split choose_split(int n_q, int k, int w_max) {
   return s;
 }
 
+// The bf16-query kernel's launch: heads per work-group (16 nht) and slot
+// splits.  Fewer heads per work-group spread one query over more CUs without
+// splitting its slots (fewer partials, less merge) but repeat the key decode
+// per head group; more splits cost the merge.  The estimate below, in
+// microseconds from MI355X measurements of each head count (a work-group's
+// fixed latency and output per 16 heads, a sub-tile's time -- MFMA-bound at
+// 64 heads, decode-bound below -- and the merge's launch and partial bytes),
+// over whole rounds of work-groups on the CUs, picks the cheapest.
+struct Plan2 {
+  int nht = 4, hgroups = 1;
+  Split s;
+};
+Plan2 plan_bf16(int n_q, int h, int k, int w_max) {
+  constexpr double kFixed = 4.6, kOutPerTile = 0.6, kMerge = 5.0, kMergePerMB = 0.12;
+  constexpr double kTsub[5] = {0.0, 1.3, 1.4, 0.0, 2.06};   // by nht
+  Plan2 best;
+  double best_cost = 1e30;
+  const int ntiles = (h + 15) / 16;
+  for (int nht : {4, 2, 1}) {
+#ifdef CSA2_ATTN_FORCE_NHT
+    if (nht != CSA2_ATTN_FORCE_NHT) continue;
+#endif
+    Plan2 c;
+    c.nht = nht;
+    c.hgroups = (ntiles + nht - 1) / nht;
+    c.s = choose_split(n_q * c.hgroups, k, w_max);
+#ifdef CSA2_ATTN_FORCE_SPLIT
+    c.s.per = (c.s.nsub + CSA2_ATTN_FORCE_SPLIT - 1) / CSA2_ATTN_FORCE_SPLIT;
+    c.s.nsplit = (c.s.nsub + c.s.per - 1) / c.s.per;
+#endif
+    const double wgs = (double)n_q * c.hgroups * c.s.nsplit;
+    const double rounds = std::ceil(wgs / CSA2_ATTN_WG_TARGET);
+    const double part_mb = c.s.nsplit > 1 ? (double)n_q * c.s.nsplit * h * 1024.0 / 1048576.0 : 0.0;
+    const double cost = rounds * (kFixed + kOutPerTile * nht + c.s.per * kTsub[nht]) +
+                        (c.s.nsplit > 1 ? kMerge + kMergePerMB * part_mb : 0.0);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = c;
+    }
+  }
+  return best;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t ws_for(int n_q, int h, int nsplit) {
+  if (nsplit == 1) return 256;
+  return align256((size_t)n_q * nsplit * h * 512 * sizeof(_Float16)) +
+         align256((size_t)n_q * nsplit * h * 2 * sizeof(float));
+}
 
 }  // namespace
 
 extern "C" size_t csa2_sparse_attn_ws_bytes(int n_q, int h, int k, int w_max) {
   if (n_q <= 0 || h <= 0) return 0;
-  const Split s = choose_split(n_q, k, w_max);
-  if (s.nsplit == 1) return 256;
-  return align256((size_t)n_q * s.nsplit * h * 512 * sizeof(_Float16)) +
-         align256((size_t)n_q * s.nsplit * h * 2 * sizeof(float));
+  // the larger of the fp32-query and bf16-query launches' needs
+  return std::max(ws_for(n_q, h, choose_split(n_q, k, w_max).nsplit),
+                  ws_for(n_q, h, plan_bf16(n_q, h, k, w_max).s.nsplit));
 }
 
 namespace {
@@ -1130,7 +1202,8 @@ csa2_status attn_call(const void* q, int q_dtype, int n_q, int h, int d, const i
                   (reinterpret_cast<uintptr_t>(swa_dst) & 7)))
     return CSA2_E_INVAL;
   if (ws_bytes < csa2_sparse_attn_ws_bytes(n_q, h, k, w_max)) return CSA2_E_WORKSPACE;
-  const Split s = choose_split(n_q, k, w_max);
+  const Plan2 plan = plan_bf16(n_q, h, k, w_max);
+  const Split s = q_dtype == CSA2_F32 ? choose_split(n_q, k, w_max) : plan.s;
   Params P{};
   P.q = q; P.n_q = n_q; P.h = h; P.q_seq = q_seq; P.cache = cache; P.seq_base = seq_base;
   P.idx = idx; P.k = k; P.swa = swa; P.swa_row0 = swa_row0; P.swa_len = w_max > 0 ? swa_len : nullptr;
@@ -1142,9 +1215,14 @@ csa2_status attn_call(const void* q, int q_dtype, int n_q, int h, int d, const i
   P.part_o = reinterpret_cast<_Float16*>(w);
   P.part_ml = reinterpret_cast<float*>(w + align256((size_t)n_q * s.nsplit * h * 512 * sizeof(_Float16)));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid(n_q, s.nsplit);
-  if (q_dtype == CSA2_F32) hipLaunchKernelGGL(k_attn<true>, grid, dim3(kThreads), 0, st, P);
-  else hipLaunchKernelGGL(k_attn2, grid, dim3(2 * kThreads), 0, st, P);
+  if (q_dtype == CSA2_F32) {
+    hipLaunchKernelGGL(k_attn<true>, dim3(n_q, s.nsplit), dim3(kThreads), 0, st, P);
+  } else {
+    const dim3 grid(n_q, s.nsplit, plan.hgroups);
+    if (plan.nht == 4) hipLaunchKernelGGL(k_attn2<4>, grid, dim3(2 * kThreads), 0, st, P);
+    else if (plan.nht == 2) hipLaunchKernelGGL(k_attn2<2>, grid, dim3(2 * kThreads), 0, st, P);
+    else hipLaunchKernelGGL(k_attn2<1>, grid, dim3(2 * kThreads), 0, st, P);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_last_hip_error((int)e);
