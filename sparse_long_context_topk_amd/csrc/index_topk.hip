@@ -1784,13 +1784,21 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
       nv_loc += ok ? 1u : 0u;
     }
   }
+  // the smallest of the threads' largest keys: at least kSmallThreads keys
+  // (one per thread) are >= it, so for K <= kSmallThreads it is <= the K-th
+  // largest key and the histogram below needs only the keys above it
+  uint32_t tmin = 0u;
+#pragma unroll
+  for (int j = 0; j < kSmallPer; ++j) tmin = max(tmin, key[j]);
   klo = wave_min_dpp(klo);
   khi = wave_max_dpp(khi);
   nv_loc = wave_sum_dpp(nv_loc);
+  tmin = wave_min_dpp(tmin);
   if (lane == 0) {
     s_tmp[wave] = klo;
     s_tmp[8 + wave] = khi;
     s_tmp[16 + wave] = nv_loc;
+    s_tmp[24 + wave] = tmin;
   }
 #pragma unroll
   for (int k = 0; k < kSmallMax / 8 / kSmallThreads; ++k)
@@ -1806,13 +1814,16 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
       s_par[0] = P.bound_tok * __uint_as_float(mk) * (1.0f + 0.0009765625f) + wa * (float)P.d_i * 7.8886e-31f;
   }
   lds_barrier();   // every wave's range and count, the pool ids, the weights
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u, nv = 0;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u, nv = 0, floor_k = 0xFFFFFFFFu;
 #pragma unroll
   for (int i = 0; i < kSmallWaves; ++i) {
     lo = min(lo, s_tmp[i]);
     hi = max(hi, s_tmp[8 + i]);
     nv += s_tmp[16 + i];
+    floor_k = min(floor_k, s_tmp[24 + i]);
   }
+  // (a thread without candidates has largest key 0, which disables the floor)
+  if (K <= kSmallThreads && floor_k != 0u && floor_k > lo) lo = floor_k;
   lds_barrier();   // publishes s_par; s_tmp is free again
   const float delta = s_par[0];
 
@@ -1835,7 +1846,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
     uint32_t* hw = s_h + wave * 256;
 #pragma unroll
     for (int j = 0; j < kSmallPer; ++j)
-      if (key[j] != 0u) atomicAdd(&hw[lbin(key[j])], 1u);
+      if (key[j] >= lo && key[j] != 0u) atomicAdd(&hw[lbin(key[j])], 1u);
     lds_barrier();
     // thread tid < 256 owns bin 255 - tid; the exclusive scan counts higher bins
     uint32_t v = 0;
@@ -2010,20 +2021,26 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(Params P) {
   // run one member per lane.  Rows h >= h_i compute a finite throwaway value.
   const bool choose = nu > 0 && need > 0 && nu > need;   // otherwise no ranking is needed
   if (choose) {
-    for (int jb = wave * kRsMembers; jb < nu; jb += kSmallWaves * kRsMembers) {
-      const int nm = min(kRsMembers, nu - jb);
-      uint32_t kw[kRsMembers];
+    // each batch's key rows are loaded while the previous batch is computed
+    uint32_t kw[kRsMembers];
+    auto load_batch = [&](int j0) {
+      const int nm = min(kRsMembers, nu - j0);
 #pragma unroll
       for (int m = 0; m < kRsMembers; ++m) {
-        const int slot = u_slot(jb + min(m, nm - 1));
+        const int slot = u_slot(j0 + min(m, nm - 1));
         const int64_t row = base + (int64_t)s_pool[slot >> 3] * 8 + (slot & 7);
         kw[m] = key_pair<D>(P, row, lane < DW ? lane : 0);
       }
+    };
+    if (wave * kRsMembers < nu) load_batch(wave * kRsMembers);
+    for (int jb = wave * kRsMembers; jb < nu; jb += kSmallWaves * kRsMembers) {
+      const int nm = min(kRsMembers, nu - jb);
 #pragma unroll
       for (int m = 0; m < kRsMembers; ++m)
         if (lane < DW)
           *reinterpret_cast<f32x2*>(&s_kf[wave][m][2 * lane]) =
               f32x2{__uint_as_float(kw[m] << 16), __uint_as_float(kw[m] & 0xFFFF0000u)};
+      if (jb + kSmallWaves * kRsMembers < nu) load_batch(jb + kSmallWaves * kRsMembers);
       // per head h = lane: fp32 fma chains over d ascending (the oracle's order)
       float acc[kRsMembers];
 #pragma unroll
