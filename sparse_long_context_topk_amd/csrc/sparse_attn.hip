@@ -1039,17 +1039,24 @@ __global__ __launch_bounds__(2 * kThreads) void k_attn2(Params P) {
 
 // Merge split partials: with each split's normalised output o_s = O_s / l_s,
 // out = sum_s 2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s.  One wave per
-// (query, head), four heads per work-group: lane s holds split s's (m_s, l_s)
-// and forms its weight, then every lane sums channels 8 lane .. 8 lane + 7
-// over the splits in ascending order (one 16-byte fp16 load of each split's
-// partial row, the weights broadcast from their lanes), eight splits' loads in
-// flight at a time.
+// (query, head), four heads per work-group: every lane sums channels 8 lane ..
+// 8 lane + 7 over the splits in ascending order (one 16-byte fp16 load of each
+// split's partial row).  The first kB splits' partial loads are issued before
+// anything else, then lane s reads split s's (m_s, l_s) and forms its weight,
+// which the lanes take by broadcast; more splits follow kB at a time.
 __global__ __launch_bounds__(kThreads) void k_merge(Params P) {
   const int lane = threadIdx.x & 63;
   const int qi = blockIdx.x, hh = blockIdx.y * (kThreads / kWave) + (threadIdx.x >> 6);
   if (hh >= P.h) return;   // whole wave
   const int ns = P.nsplit;
   const size_t row0 = (size_t)qi * ns * P.h + hh;   // row of split 0; split s adds s * h
+  const uint4* po = reinterpret_cast<const uint4*>(P.part_o + row0 * 512) + lane;
+  const size_t so = (size_t)P.h * 64;   // 16-byte pieces between splits
+  constexpr int kB = 16;
+  uint4 x[kB];
+#pragma unroll
+  for (int u = 0; u < kB; ++u)
+    if (u < ns) x[u] = po[(size_t)u * so];   // uniform
   float m = -INFINITY, l = 0.0f;
   if (lane < ns) {
     const float2 v = *reinterpret_cast<const float2*>(P.part_ml + (row0 + (size_t)lane * P.h) * 2);
@@ -1059,17 +1066,15 @@ __global__ __launch_bounds__(kThreads) void k_merge(Params P) {
   const float M = wave_max(m);
   const float w = (lane < ns && m != -INFINITY) ? exp2f(m - M) * l : 0.0f;
   const float L = wave_sum(w);
-  const uint4* po = reinterpret_cast<const uint4*>(P.part_o + row0 * 512) + lane;
-  const size_t so = (size_t)P.h * 64;   // 16-byte pieces between splits
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  constexpr int kB = 8;
   for (int s0 = 0; s0 < ns; s0 += kB) {
-    uint4 x[kB];
+    if (s0 > 0) {
 #pragma unroll
-    for (int u = 0; u < kB; ++u)
-      if (s0 + u < ns) x[u] = po[(size_t)(s0 + u) * so];   // uniform
+      for (int u = 0; u < kB; ++u)
+        if (s0 + u < ns) x[u] = po[(size_t)(s0 + u) * so];   // uniform
+    }
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
       if (s0 + u < ns) {
@@ -1082,13 +1087,8 @@ __global__ __launch_bounds__(kThreads) void k_merge(Params P) {
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   float* dst = P.out + ((size_t)qi * P.h + hh) * 512 + 8 * lane;
-  if ((reinterpret_cast<uintptr_t>(P.out) & 15) == 0) {
-    reinterpret_cast<float4*>(dst)[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-    reinterpret_cast<float4*>(dst)[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dst[e] = acc[e] * inv;
-  }
+  reinterpret_cast<float4*>(dst)[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  reinterpret_cast<float4*>(dst)[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
   if (P.lse && lane == 0) P.lse[(size_t)qi * P.h + hh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
