@@ -72,6 +72,7 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kNBins = 4096;
 constexpr int kBinShift = 20;
 constexpr int kCmpChunk = 4096;
+constexpr double kLargeSelBytes = 1024.0 * 1048576.0;   // token score bytes from which the selection runs in its large mode
 constexpr int kCmpPerThread = kCmpChunk / kThreads;
 constexpr int kMaxChunksLds = 8192;   // compaction chunks per problem (max_nvis <= 2^25)
 constexpr int kRescoreWGs = 512;   // rescoring work-groups per launch (all queries)
@@ -144,6 +145,9 @@ struct Params {
   uint32_t* chunk_unc;  // [nprob][nchunk_cmp] uncertain members per chunk
   Entry* band;          // [nprob][stride] band members, chunk c at c*kCmpChunk, in position order
   uint2* unc;           // [nprob][stride] uncertain members: {chunk-local index, candidate}
+  float* gmax;          // [n_q][stride / 256] largest score of each 256-score group of a token (or Reindex) row
+  int large_sel;        // large problems: the coarse bin and the band are computed once per problem (k_coarse,
+                        // k_band) and the selection kernels skip groups whose largest score is below them
   float* kpart;         // Reindex scan: [n_q][scan work-groups] largest key magnitude t_k of each
 };
 
@@ -403,6 +407,43 @@ __device__ __forceinline__ uint32_t key_pair(const Params& P, int64_t row, int p
   return reinterpret_cast<const uint32_t*>(P.ik + (size_t)row * D)[p];
 }
 
+// Scores of one scan chunk (n of them from LDS `src`, positions c0 .. c0 + n
+// - 1 of row `row`, c0 a multiple of 256) to global memory as whole 256-score
+// groups, one per wave at a time (each lane four consecutive scores), with the
+// largest score of each group in `gm` (its group g at gm[(c0 >> 8) + g]; a DPP
+// maximum over the scores' sortable keys, which order as the scores do); without
+// `with_max`, one score per thread and step.
+template <int NWAVES>
+__device__ __forceinline__ void store_scores(float* row, float* gm, const float* src, int c0, int n, int wave,
+                                             int lane, bool with_max) {
+  if (!with_max) {   // the plain write-out
+    for (int i = 64 * wave + lane; i < n; i += 64 * NWAVES) row[c0 + i] = src[i];
+    return;
+  }
+  const int ng = (n + 255) >> 8;
+  for (int gi = wave; gi < ng; gi += NWAVES) {
+    const int i0 = (gi << 8) + 4 * lane;
+    float m = -INFINITY;
+    if (i0 + 3 < n) {
+      const float4 v = *reinterpret_cast<const float4*>(&src[i0]);
+      *reinterpret_cast<float4*>(&row[c0 + i0]) = v;
+      m = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i0 + e < n) {
+          const float v = src[i0 + e];
+          row[c0 + i0 + e] = v;
+          m = fmaxf(m, v);
+        }
+    }
+    if (with_max) {
+      const uint32_t mk = wave_max_dpp(sortable(m));
+      if (lane == 0) gm[(c0 >> 8) + gi] = unsortable(mk);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- 1. prologue
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_prologue(Params P) {
@@ -506,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
   __shared__ int32_t s_pool[INDIRECT ? 512 : 1];
   // the chunk's scores stay in LDS until the end: the hot loop then issues
   // only loads, and the results leave as one coalesced write
-  __shared__ float s_sc[kMaxScanChunk];
+  __shared__ __attribute__((aligned(16))) float s_sc[kMaxScanChunk];
   __shared__ float s_scb[POOL ? kMaxScanChunk / 8 : 1];
   __shared__ uint32_t s_tmp[16];
 
@@ -798,7 +839,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
 
   // ---- publish scores, histograms and the largest t_k
   lds_barrier();
-  for (int i = tid; i < nslots; i += kThreads) sc[c0 + i] = s_sc[i];
+  store_scores<kWaves>(sc, P.gmax + (size_t)p * (P.stride >> 8), s_sc, c0, nslots, wave, lane, P.large_sel != 0);
   if constexpr (POOL) {
     const int nbs = min((nslots + 7) >> 3, max(nblk - (c0 >> 3), 0));
     for (int i = tid; i < nbs; i += kThreads) scb[(c0 >> 3) + i] = s_scb[i];
@@ -854,7 +895,7 @@ __global__ __launch_bounds__(kThreads, QB <= 2 ? 2 : 1) void k_scan_chunk(Params
   constexpr int KS = D / 32;
   constexpr int NBUF = 2;           // one key group in flight, one in use (registers go to the queries)
   __shared__ uint32_t s_hist[QB][kNBins];
-  __shared__ float s_sc[QB][kChunkKeys];
+  __shared__ __attribute__((aligned(16))) float s_sc[QB][kChunkKeys];
   __shared__ uint32_t s_tmp[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1022,8 +1063,8 @@ __global__ __launch_bounds__(kThreads, QB <= 2 ? 2 : 1) void k_scan_chunk(Params
     if (qq < nq) {
       const int q = q0 + qq;
       const int ns = min(kChunkKeys, max(nvis[qq] - c0, 0));
-      float* sc = P.scores + (size_t)q * P.stride + c0;
-      for (int i = tid; i < ns; i += kThreads) sc[i] = s_sc[qq][i];
+      store_scores<kWaves>(P.scores + (size_t)q * P.stride, P.gmax + (size_t)q * (P.stride >> 8), s_sc[qq], c0,
+                           ns, wave, lane, P.large_sel != 0);
       uint32_t* gh = P.hist + (size_t)q * kNBins;
       for (int i = tid; i < kNBins; i += kThreads) {
         const uint32_t c = s_hist[qq][i];
@@ -1077,14 +1118,31 @@ __global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
   const int nc = cands_of(P, kind, P.q_nvis[q]);
   if (chunk > 0 && chunk * kCmpChunk >= nc) return;
   const int my0 = chunk * kCmpChunk + tid * kCmpPerThread;
+  // with the group maxima, a thread loads its scores only once the coarse bin
+  // is known and only if its 256-score group reaches that bin
+  const bool skip = P.large_sel && kind == 0;
   float v[kCmpPerThread];
-  load16(P, p, my0, v);
+  float gm = 0.0f;
+  if (skip) gm = P.gmax[(size_t)p * (P.stride >> 8) + (my0 >> 8)];
+  else load16(P, p, my0, v);
   uint32_t hv[kHPer];
-  load_hist16(P.hist + (size_t)p * kNBins, hv);
+  if (!P.large_sel) load_hist16(P.hist + (size_t)p * kNBins, hv);
   const float maxt = __uint_as_float(P.meta[q].maxt), wabs = P.meta[p].wabs;
   for (int i = tid; i < kNBins; i += kThreads) s_h[i] = 0;
-  const uint32_t bin = wg_coarse_bin(P, p, hv, chunk == 0, maxt, wabs, s_tmp);   // its barriers order the clear
+  uint32_t bin;
+  if (P.large_sel) {
+    bin = P.meta[p].bin;   // k_coarse's
+    lds_barrier();         // orders the clear
+  } else {
+    bin = wg_coarse_bin(P, p, hv, chunk == 0, maxt, wabs, s_tmp);   // its barriers order the clear
+  }
   if (bin == kAll || chunk * kCmpChunk >= nc) return;
+  if (skip) {
+    if ((sortable(gm) >> kBinShift) >= bin) load16(P, p, my0, v);
+    else
+#pragma unroll
+      for (int j = 0; j < kCmpPerThread; ++j) v[j] = -INFINITY;
+  }
   const int m = count16(nc, my0);
 #pragma unroll
   for (int j = 0; j < kCmpPerThread; ++j) {
@@ -1157,6 +1215,27 @@ __device__ void wg_band_thresholds(const Params& P, int p, const uint32_t hv[kHP
   lds_barrier();
 }
 
+// Large problems (thousands of selection work-groups per problem): the coarse
+// bin with the bound, and then the band, once per problem in one work-group
+// each, instead of in every selection work-group from the whole histogram.
+__global__ __launch_bounds__(kThreads) void k_coarse(Params P) {
+  __shared__ uint32_t s_tmp[16];
+  const int p = blockIdx.x, q = p % P.n_q;
+  uint32_t hv[kHPer];
+  load_hist16(P.hist + (size_t)p * kNBins, hv);
+  const float maxt = __uint_as_float(P.meta[q].maxt), wabs = P.meta[p].wabs;
+  (void)wg_coarse_bin(P, p, hv, true, maxt, wabs, s_tmp);
+}
+
+__global__ __launch_bounds__(kThreads) void k_band(Params P) {
+  __shared__ uint32_t s_tmp[16];
+  const int p = blockIdx.x;
+  uint32_t hv[kHPer];
+  load_hist16(P.hist2 + (size_t)p * kNBins, hv);
+  float keep_thr, in_thr;
+  wg_band_thresholds(P, p, hv, P.meta[p].bin, P.meta[p].above, P.meta[p].delta, true, s_tmp, &keep_thr, &in_thr);
+}
+
 // ---------------------------------------------------------------- 4. compaction
 // Band members of one chunk, in position order, flagged certain or not; the
 // uncertain ones are also listed (chunk-local index) for the rescoring.
@@ -1181,15 +1260,30 @@ __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
     return;
   }
   const int my0 = c0 + tid * kCmpPerThread;
+  // with the group maxima, a thread loads its scores only once the band is
+  // known and only if its 256-score group reaches the band
+  const bool skip = P.large_sel && kind == 0;
   float v[kCmpPerThread];
-  load16(P, p, my0, v);
+  float gm = 0.0f;
+  if (skip) gm = P.gmax[(size_t)p * (P.stride >> 8) + (my0 >> 8)];
+  else load16(P, p, my0, v);
   uint32_t hv[kHPer];
-  load_hist16(P.hist2 + (size_t)p * kNBins, hv);
+  if (!P.large_sel) load_hist16(P.hist2 + (size_t)p * kNBins, hv);
   const uint32_t m_bin = P.meta[p].bin, m_above = P.meta[p].above;
   const float m_delta = P.meta[p].delta;
   float keep_thr = -INFINITY, in_thr = -INFINITY;
-  if (chunk == 0 || c0 < nc)
+  if (P.large_sel) {   // k_band's
+    keep_thr = P.meta[p].keep_thr;
+    in_thr = P.meta[p].in_thr;
+  } else if (chunk == 0 || c0 < nc) {
     wg_band_thresholds(P, p, hv, m_bin, m_above, m_delta, chunk == 0, s_tmp, &keep_thr, &in_thr);
+  }
+  if (skip) {
+    if (gm >= keep_thr) load16(P, p, my0, v);
+    else
+#pragma unroll
+      for (int j = 0; j < kCmpPerThread; ++j) v[j] = -INFINITY;
+  }
   const int m = count16(nc, my0);
   uint32_t keep = 0, cert = 0;
 #pragma unroll
@@ -2184,7 +2278,7 @@ thread_local hipEvent_t g_scan_ev_stop = nullptr;
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t scores, hist, hist2, meta, chunk_cnt, chunk_unc, band, unc, kpart, total;
+  size_t scores, hist, hist2, meta, chunk_cnt, chunk_unc, band, unc, kpart, gmax, total;
 };
 
 Layout make_layout(int nprob, int64_t stride, int nchunk_cmp) {
@@ -2207,6 +2301,8 @@ Layout make_layout(int nprob, int64_t stride, int nchunk_cmp) {
   L.unc = o;
   o = align256(o + (size_t)nprob * stride * sizeof(uint2));
   L.kpart = o;   // one float per Reindex scan work-group (256 slots each)
+  o = align256(o + (size_t)nprob * (size_t)(stride / 256) * sizeof(float));
+  L.gmax = o;    // one float per 256 scores
   o = align256(o + (size_t)nprob * (size_t)(stride / 256) * sizeof(float));
   L.total = o;
   return L;
@@ -2292,6 +2388,12 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   P.band = reinterpret_cast<Entry*>(w + L.band);
   P.unc = reinterpret_cast<uint2*>(w + L.unc);
   P.kpart = reinterpret_cast<float*>(w + L.kpart);
+  P.gmax = reinterpret_cast<float*>(w + L.gmax);
+  // the selection's large mode pays once it has thousands of work-groups per
+  // problem and reads gigabytes of scores (the encoder chunk: 4096 queries x
+  // 512 K scores, 44.97 -> 43.99 ms per step); on a 64-query decode step
+  // (256 MB) its two extra launches and round trips cost more than they save
+  P.large_sel = (double)P.n_q * (double)P.stride * sizeof(float) >= kLargeSelBytes ? 1 : 0;
   P.bound_tok = bound_constant(P.d_i, false);
   P.bound_blk = bound_constant(P.d_i, true);
 
@@ -2334,8 +2436,16 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return CSA2_E_HIP;
   // per-chunk kernels: the token (or Reindex) problem's chunks, then the block problem's
   const dim3 gchunk(P.nchunk_cmp + (pool ? (P.nchunk_cmp + 7) / 8 : 0), P.n_q);
+  if (P.large_sel) {
+    hipLaunchKernelGGL(k_coarse, dim3(P.nprob), dim3(kThreads), 0, s, P);
+    if (!launch_ok()) return CSA2_E_HIP;
+  }
   hipLaunchKernelGGL(k_finehist, gchunk, dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
+  if (P.large_sel) {
+    hipLaunchKernelGGL(k_band, dim3(P.nprob), dim3(kThreads), 0, s, P);
+    if (!launch_ok()) return CSA2_E_HIP;
+  }
   hipLaunchKernelGGL(k_compact, gchunk, dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
   // One resident round (two work-groups per CU at this kernel's register
