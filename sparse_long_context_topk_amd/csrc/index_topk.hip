@@ -72,7 +72,8 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kNBins = 4096;
 constexpr int kBinShift = 20;
 constexpr int kCmpChunk = 4096;
-constexpr double kLargeSelBytes = 1024.0 * 1048576.0;   // token score bytes from which the selection runs in its large mode
+constexpr double kLargeSelBytes = 1024.0 * 1048576.0;
+constexpr int kLargeChunks = 8;   // large mode without a block problem: chunks per fine-histogram work-group   // token score bytes from which the selection runs in its large mode
 constexpr int kCmpPerThread = kCmpChunk / kThreads;
 constexpr int kMaxChunksLds = 8192;   // compaction chunks per problem (max_nvis <= 2^25)
 constexpr int kRescoreWGs = 512;   // rescoring work-groups per launch (all queries)
@@ -266,12 +267,7 @@ template <int NT = kThreads>
 __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan_u32(v);   // DPP row shifts and broadcasts
   if (lane == 63) s_tmp[wave] = x;
   lds_barrier();
   uint32_t before = 0, all = 0;
@@ -375,6 +371,12 @@ __device__ __forceinline__ void grid_chunk(const Params& P, int* p, int* chunk) 
   const bool blk = (int)blockIdx.x >= P.nchunk_cmp;
   *p = (blk ? P.n_q : 0) + (int)blockIdx.y;
   *chunk = blk ? (int)blockIdx.x - P.nchunk_cmp : (int)blockIdx.x;
+}
+
+// Large mode without a block problem: fine-histogram work-group (x, q) takes
+// the kLargeChunks chunks from x kLargeChunks of query q's row.
+__device__ __forceinline__ bool large_multi(const Params& P) {
+  return P.large_sel && (P.reindex || P.keep_blocks == 0);
 }
 
 // Candidates of problem p (what the prologue records in Meta.nc), from the
@@ -1107,42 +1109,61 @@ __global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
   __shared__ uint32_t s_h[kNBins];
   __shared__ uint32_t s_tmp[16];
   const int tid = threadIdx.x;
+  if (P.large_sel) {
+    // Large problems: k_coarse published the bin, so each thread works alone
+    // (no barrier): a token thread whose 256-score group stays below the bin
+    // loads nothing, and the few scores inside the bin go straight to the
+    // problem's fine histogram.
+    int p, chunk0, nch = 1;
+    if (large_multi(P)) {
+      p = blockIdx.y;
+      chunk0 = blockIdx.x * kLargeChunks;
+      nch = min(kLargeChunks, P.nchunk_cmp - chunk0);
+    } else {
+      grid_chunk(P, &p, &chunk0);
+    }
+    const int q = p % P.n_q, kind = p / P.n_q;
+    const int nc = cands_of(P, kind, P.q_nvis[q]);
+    const uint32_t bin = P.meta[p].bin;
+    if (bin == kAll) return;
+    uint32_t* gh = P.hist2 + (size_t)p * kNBins;
+    for (int c = 0; c < nch; ++c) {
+      const int chunk = chunk0 + c;
+      if (chunk > 0 && chunk * kCmpChunk >= nc) return;
+      const int my0 = chunk * kCmpChunk + tid * kCmpPerThread;
+      if (kind == 0 && (sortable(P.gmax[(size_t)p * (P.stride >> 8) + (my0 >> 8)]) >> kBinShift) < bin) continue;
+      float v[kCmpPerThread];
+      load16(P, p, my0, v);
+      const int m = count16(nc, my0);
+#pragma unroll
+      for (int j = 0; j < kCmpPerThread; ++j) {
+        if (j < m && v[j] != -INFINITY) {
+          const uint32_t key = sortable(v[j]);
+          if ((key >> kBinShift) == bin) atomicAdd(&gh[(key >> 8) & (kNBins - 1)], 1u);
+        }
+      }
+    }
+    return;
+  }
   int p, chunk;
   grid_chunk(P, &p, &chunk);
   const int q = p % P.n_q, kind = p / P.n_q;
   // the visible length first: a chunk past the problem's candidates (the grid
   // spans the longest context; shorter ones leave most chunks empty) leaves
-  // before loading anything.  Then every load goes out at once: the chunk's
-  // scores (inside the problem's row), the coarse histogram and the bound's
-  // inputs
+  // before loading anything.
   const int nc = cands_of(P, kind, P.q_nvis[q]);
   if (chunk > 0 && chunk * kCmpChunk >= nc) return;
   const int my0 = chunk * kCmpChunk + tid * kCmpPerThread;
-  // with the group maxima, a thread loads its scores only once the coarse bin
-  // is known and only if its 256-score group reaches that bin
-  const bool skip = P.large_sel && kind == 0;
+  // Then every load goes out at once: the chunk's scores (inside the
+  // problem's row), the coarse histogram and the bound's inputs
   float v[kCmpPerThread];
-  float gm = 0.0f;
-  if (skip) gm = P.gmax[(size_t)p * (P.stride >> 8) + (my0 >> 8)];
-  else load16(P, p, my0, v);
+  load16(P, p, my0, v);
   uint32_t hv[kHPer];
-  if (!P.large_sel) load_hist16(P.hist + (size_t)p * kNBins, hv);
+  load_hist16(P.hist + (size_t)p * kNBins, hv);
   const float maxt = __uint_as_float(P.meta[q].maxt), wabs = P.meta[p].wabs;
   for (int i = tid; i < kNBins; i += kThreads) s_h[i] = 0;
-  uint32_t bin;
-  if (P.large_sel) {
-    bin = P.meta[p].bin;   // k_coarse's
-    lds_barrier();         // orders the clear
-  } else {
-    bin = wg_coarse_bin(P, p, hv, chunk == 0, maxt, wabs, s_tmp);   // its barriers order the clear
-  }
+  const uint32_t bin = wg_coarse_bin(P, p, hv, chunk == 0, maxt, wabs, s_tmp);   // its barriers order the clear
   if (bin == kAll || chunk * kCmpChunk >= nc) return;
-  if (skip) {
-    if ((sortable(gm) >> kBinShift) >= bin) load16(P, p, my0, v);
-    else
-#pragma unroll
-      for (int j = 0; j < kCmpPerThread; ++j) v[j] = -INFINITY;
-  }
   const int m = count16(nc, my0);
 #pragma unroll
   for (int j = 0; j < kCmpPerThread; ++j) {
@@ -1242,74 +1263,79 @@ __global__ __launch_bounds__(kThreads) void k_band(Params P) {
 __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
   __shared__ uint32_t s_tmp[16];
   const int tid = threadIdx.x;
+  auto chunk_body = [&](int p, int chunk) {
+    const int q = p % P.n_q, kind = p / P.n_q;
+    const int c0 = chunk * kCmpChunk;
+    // the visible length first: a chunk past the problem's candidates only
+    // records empty counts (the later kernels sum the counts of every chunk of
+    // the row) and loads nothing.  Then every load goes out at once: the
+    // chunk's scores, the fine histogram and the Meta fields the fine
+    // histogram kernel published
+    const int nc = cands_of(P, kind, P.q_nvis[q]);
+    if (chunk > 0 && c0 >= nc) {
+      if (tid == 0) {
+        P.chunk_cnt[(size_t)p * P.nchunk_cmp + chunk] = 0;
+        P.chunk_unc[(size_t)p * P.nchunk_cmp + chunk] = 0;
+      }
+      return;
+    }
+    const int my0 = c0 + tid * kCmpPerThread;
+    // with the group maxima, a thread loads its scores only once the band is
+    // known and only if its 256-score group reaches the band
+    const bool skip = P.large_sel && kind == 0;
+    float v[kCmpPerThread];
+    float gm = 0.0f;
+    if (skip) gm = P.gmax[(size_t)p * (P.stride >> 8) + (my0 >> 8)];
+    else load16(P, p, my0, v);
+    uint32_t hv[kHPer];
+    if (!P.large_sel) load_hist16(P.hist2 + (size_t)p * kNBins, hv);
+    const uint32_t m_bin = P.meta[p].bin, m_above = P.meta[p].above;
+    const float m_delta = P.meta[p].delta;
+    float keep_thr = -INFINITY, in_thr = -INFINITY;
+    if (P.large_sel) {   // k_band's
+      keep_thr = P.meta[p].keep_thr;
+      in_thr = P.meta[p].in_thr;
+    } else if (chunk == 0 || c0 < nc) {
+      wg_band_thresholds(P, p, hv, m_bin, m_above, m_delta, chunk == 0, s_tmp, &keep_thr, &in_thr);
+    }
+    if (skip) {
+      if (gm >= keep_thr) load16(P, p, my0, v);
+      else
+#pragma unroll
+        for (int j = 0; j < kCmpPerThread; ++j) v[j] = -INFINITY;
+    }
+    const int m = count16(nc, my0);
+    uint32_t keep = 0, cert = 0;
+#pragma unroll
+    for (int j = 0; j < kCmpPerThread; ++j) {
+      const bool k_ = j < m && v[j] != -INFINITY && v[j] >= keep_thr;
+      keep |= (k_ ? 1u : 0u) << j;
+      cert |= ((k_ && v[j] > in_thr) ? 1u : 0u) << j;
+    }
+    // one scan for both counts (each at most kCmpChunk, so the halves never carry)
+    uint32_t both;
+    const uint32_t ob = wg_exclusive_scan(__popc(keep) | ((uint32_t)__popc(keep & ~cert) << 16), s_tmp, &both);
+    uint32_t off = ob & 0xFFFFu, uoff = ob >> 16;
+    const uint32_t total = both & 0xFFFFu, utotal = both >> 16;
+    Entry* dst = P.band + (size_t)p * P.stride + c0;
+    uint2* udst = P.unc + (size_t)p * P.stride + c0;
+#pragma unroll
+    for (int j = 0; j < kCmpPerThread; ++j) {
+      if (keep & (1u << j)) {
+        const bool c_ = (cert >> j) & 1u;
+        dst[off] = Entry{(uint32_t)(my0 + j) | (c_ ? kCertain : 0u), v[j]};
+        if (!c_) udst[uoff++] = make_uint2(off, (uint32_t)(my0 + j));
+        ++off;
+      }
+    }
+    if (tid == 0) {
+      P.chunk_cnt[(size_t)p * P.nchunk_cmp + chunk] = total;
+      P.chunk_unc[(size_t)p * P.nchunk_cmp + chunk] = utotal;
+    }
+  };
   int p, chunk;
   grid_chunk(P, &p, &chunk);
-  const int q = p % P.n_q, kind = p / P.n_q;
-  const int c0 = chunk * kCmpChunk;
-  // the visible length first: a chunk past the problem's candidates only
-  // records empty counts (the later kernels sum the counts of every chunk of
-  // the row) and loads nothing.  Then every load goes out at once: the
-  // chunk's scores, the fine histogram and the Meta fields the fine
-  // histogram kernel published
-  const int nc = cands_of(P, kind, P.q_nvis[q]);
-  if (chunk > 0 && c0 >= nc) {
-    if (tid == 0) {
-      P.chunk_cnt[(size_t)p * P.nchunk_cmp + chunk] = 0;
-      P.chunk_unc[(size_t)p * P.nchunk_cmp + chunk] = 0;
-    }
-    return;
-  }
-  const int my0 = c0 + tid * kCmpPerThread;
-  // with the group maxima, a thread loads its scores only once the band is
-  // known and only if its 256-score group reaches the band
-  const bool skip = P.large_sel && kind == 0;
-  float v[kCmpPerThread];
-  float gm = 0.0f;
-  if (skip) gm = P.gmax[(size_t)p * (P.stride >> 8) + (my0 >> 8)];
-  else load16(P, p, my0, v);
-  uint32_t hv[kHPer];
-  if (!P.large_sel) load_hist16(P.hist2 + (size_t)p * kNBins, hv);
-  const uint32_t m_bin = P.meta[p].bin, m_above = P.meta[p].above;
-  const float m_delta = P.meta[p].delta;
-  float keep_thr = -INFINITY, in_thr = -INFINITY;
-  if (P.large_sel) {   // k_band's
-    keep_thr = P.meta[p].keep_thr;
-    in_thr = P.meta[p].in_thr;
-  } else if (chunk == 0 || c0 < nc) {
-    wg_band_thresholds(P, p, hv, m_bin, m_above, m_delta, chunk == 0, s_tmp, &keep_thr, &in_thr);
-  }
-  if (skip) {
-    if (gm >= keep_thr) load16(P, p, my0, v);
-    else
-#pragma unroll
-      for (int j = 0; j < kCmpPerThread; ++j) v[j] = -INFINITY;
-  }
-  const int m = count16(nc, my0);
-  uint32_t keep = 0, cert = 0;
-#pragma unroll
-  for (int j = 0; j < kCmpPerThread; ++j) {
-    const bool k_ = j < m && v[j] != -INFINITY && v[j] >= keep_thr;
-    keep |= (k_ ? 1u : 0u) << j;
-    cert |= ((k_ && v[j] > in_thr) ? 1u : 0u) << j;
-  }
-  uint32_t total, utotal;
-  uint32_t off = wg_exclusive_scan(__popc(keep), s_tmp, &total);
-  uint32_t uoff = wg_exclusive_scan(__popc(keep & ~cert), s_tmp, &utotal);
-  Entry* dst = P.band + (size_t)p * P.stride + c0;
-  uint2* udst = P.unc + (size_t)p * P.stride + c0;
-#pragma unroll
-  for (int j = 0; j < kCmpPerThread; ++j) {
-    if (keep & (1u << j)) {
-      const bool c_ = (cert >> j) & 1u;
-      dst[off] = Entry{(uint32_t)(my0 + j) | (c_ ? kCertain : 0u), v[j]};
-      if (!c_) udst[uoff++] = make_uint2(off, (uint32_t)(my0 + j));
-      ++off;
-    }
-  }
-  if (tid == 0) {
-    P.chunk_cnt[(size_t)p * P.nchunk_cmp + chunk] = total;
-    P.chunk_unc[(size_t)p * P.nchunk_cmp + chunk] = utotal;
-  }
+  chunk_body(p, chunk);
 }
 
 // Exclusive prefix of a problem's per-chunk counts into LDS (s[0..nch]).
@@ -2436,11 +2462,16 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return CSA2_E_HIP;
   // per-chunk kernels: the token (or Reindex) problem's chunks, then the block problem's
   const dim3 gchunk(P.nchunk_cmp + (pool ? (P.nchunk_cmp + 7) / 8 : 0), P.n_q);
+  // the fine histogram in large mode without a block problem: kLargeChunks
+  // chunks per work-group (its threads work alone; the compaction's chunks,
+  // each a chain of dependent steps, keep a work-group each)
+  const bool multi = P.large_sel && !pool;
+  const dim3 gfine(multi ? (P.nchunk_cmp + kLargeChunks - 1) / kLargeChunks : gchunk.x, P.n_q);
   if (P.large_sel) {
     hipLaunchKernelGGL(k_coarse, dim3(P.nprob), dim3(kThreads), 0, s, P);
     if (!launch_ok()) return CSA2_E_HIP;
   }
-  hipLaunchKernelGGL(k_finehist, gchunk, dim3(kThreads), 0, s, P);
+  hipLaunchKernelGGL(k_finehist, gfine, dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;
   if (P.large_sel) {
     hipLaunchKernelGGL(k_band, dim3(P.nprob), dim3(kThreads), 0, s, P);
