@@ -152,6 +152,30 @@ def test_many_queries_long_splits(n_q, h, k, nswa):
 
 
 @gpu
+@pytest.mark.parametrize("n_q,k,nswa,L", [(16, 512, 128, 4096), (64, 512, 128, 2048), (128, 500, 128, 640),
+                                          (300, 512, 100, 640), (8, 2048, 1024, 4096)])
+def test_partial_head_groups(n_q, k, nswa, L):
+    """48 heads (three 16-head tiles) where the bf16 kernel's work-groups take
+    two or four tiles each, so that one head group is partly past h: two-tile
+    groups with 7 and with 1 split(s) per query (16 and 128 queries), four-tile
+    groups with 4, 1 and 32 splits (64, 300 and 8 queries, the last at the
+    largest lists); padding (-1) scattered through the selections."""
+    note(f"attn h=48 n_q={n_q} k={k} nswa={nswa}")
+
+    def pad(i):
+        i = i.copy()
+        rng = np.random.default_rng(n_q + 1)
+        i[rng.random(i.shape) < 0.05] = -1
+        return i
+    c = _case(n_q, 48, L, k, nswa, torch.bfloat16, seed=90 + n_q, idx_fn=pad)
+    o, l, ro, rl = _run(c)
+    err = normwise_err(o, ro)
+    print(f"normwise err {err:.3e}")
+    assert err <= TOL
+    assert np.allclose(l, rl, rtol=1e-4, atol=1e-4)
+
+
+@gpu
 @pytest.mark.parametrize("n_q,h,qdt", [(3, 64, torch.bfloat16), (2, 16, torch.float32), (40, 64, torch.bfloat16)])
 def test_largest_selection_and_window(n_q, h, qdt):
     """The largest supported lists: k = 2048 selected entries and windows of up
