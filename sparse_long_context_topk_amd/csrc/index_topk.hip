@@ -136,6 +136,7 @@ struct Params {
   int64_t stride;          // slots per problem in scores / band arrays
   int nchunk_cmp;
   int rs_tok;              // rescoring work-groups per query given to the token problem (the rest: blocks)
+  int rs_pool;             // the block work-groups of all queries share one member list
   int64_t base0;           // chunk calls (q_seq == nullptr): every query's sequence starts at key row base0
   float bound_tok, bound_blk;
   float* scores;
@@ -146,7 +147,8 @@ struct Params {
   uint32_t* chunk_unc;  // [nprob][nchunk_cmp] uncertain members per chunk
   Entry* band;          // [nprob][stride] band members, chunk c at c*kCmpChunk, in position order
   uint2* unc;           // [nprob][stride] uncertain members: {chunk-local index, candidate}
-  float* gmax;          // [n_q][stride / 256] largest score of each 256-score group of a token (or Reindex) row
+  uint16_t* gkey;       // [n_q][stride / 16] top 16 bits of the sortable key of the largest score of each
+                        // 16-score group of a token (or Reindex) row (large mode)
   int large_sel;        // large problems: the coarse bin and the band are computed once per problem (k_coarse,
                         // k_band) and the selection kernels skip groups whose largest score is below them
   float* kpart;         // Reindex scan: [n_q][scan work-groups] largest key magnitude t_k of each
@@ -412,11 +414,13 @@ __device__ __forceinline__ uint32_t key_pair(const Params& P, int64_t row, int p
 // Scores of one scan chunk (n of them from LDS `src`, positions c0 .. c0 + n
 // - 1 of row `row`, c0 a multiple of 256) to global memory as whole 256-score
 // groups, one per wave at a time (each lane four consecutive scores), with the
-// largest score of each group in `gm` (its group g at gm[(c0 >> 8) + g]; a DPP
-// maximum over the scores' sortable keys, which order as the scores do); without
-// `with_max`, one score per thread and step.
+// top 16 bits of the sortable key of the largest score of every 16 scores in
+// `gk` (scores c0 + 16 g .. c0 + 16 g + 15 at gk[(c0 >> 4) + g]; a DPP maximum
+// over a lane quad's sortable keys, which order as the scores do): a group
+// whose value there is below a threshold key's top 16 bits holds no score at or
+// above the threshold.  Without `with_max`, one score per thread and step.
 template <int NWAVES>
-__device__ __forceinline__ void store_scores(float* row, float* gm, const float* src, int c0, int n, int wave,
+__device__ __forceinline__ void store_scores(float* row, uint16_t* gk, const float* src, int c0, int n, int wave,
                                              int lane, bool with_max) {
   if (!with_max) {   // the plain write-out
     for (int i = 64 * wave + lane; i < n; i += 64 * NWAVES) row[c0 + i] = src[i];
@@ -439,9 +443,11 @@ __device__ __forceinline__ void store_scores(float* row, float* gm, const float*
           m = fmaxf(m, v);
         }
     }
-    if (with_max) {
-      const uint32_t mk = wave_max_dpp(sortable(m));
-      if (lane == 0) gm[(c0 >> 8) + gi] = unsortable(mk);
+    if (with_max) {   // lane quad r covers the group's scores 16 r .. 16 r + 15
+      uint32_t mk = sortable(m);
+      mk = max(mk, dpp0<0xB1>(mk));   // quad_perm [1,0,3,2]
+      mk = max(mk, dpp0<0x4E>(mk));   // quad_perm [2,3,0,1]
+      if ((lane & 3) == 0) gk[(c0 >> 4) + 16 * gi + (lane >> 2)] = (uint16_t)(mk >> 16);
     }
   }
 }
@@ -841,7 +847,7 @@ __global__ __launch_bounds__(kThreads) void k_scan(Params P) {
 
   // ---- publish scores, histograms and the largest t_k
   lds_barrier();
-  store_scores<kWaves>(sc, P.gmax + (size_t)p * (P.stride >> 8), s_sc, c0, nslots, wave, lane, P.large_sel != 0);
+  store_scores<kWaves>(sc, P.gkey + (size_t)p * (P.stride >> 4), s_sc, c0, nslots, wave, lane, P.large_sel != 0);
   if constexpr (POOL) {
     const int nbs = min((nslots + 7) >> 3, max(nblk - (c0 >> 3), 0));
     for (int i = tid; i < nbs; i += kThreads) scb[(c0 >> 3) + i] = s_scb[i];
@@ -1065,7 +1071,7 @@ __global__ __launch_bounds__(kThreads, QB <= 2 ? 2 : 1) void k_scan_chunk(Params
     if (qq < nq) {
       const int q = q0 + qq;
       const int ns = min(kChunkKeys, max(nvis[qq] - c0, 0));
-      store_scores<kWaves>(P.scores + (size_t)q * P.stride, P.gmax + (size_t)q * (P.stride >> 8), s_sc[qq], c0,
+      store_scores<kWaves>(P.scores + (size_t)q * P.stride, P.gkey + (size_t)q * (P.stride >> 4), s_sc[qq], c0,
                            ns, wave, lane, P.large_sel != 0);
       uint32_t* gh = P.hist + (size_t)q * kNBins;
       for (int i = tid; i < kNBins; i += kThreads) {
@@ -1111,7 +1117,7 @@ __global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
   const int tid = threadIdx.x;
   if (P.large_sel) {
     // Large problems: k_coarse published the bin, so each thread works alone
-    // (no barrier): a token thread whose 256-score group stays below the bin
+    // (no barrier): a token thread whose 16 scores stay below the bin
     // loads nothing, and the few scores inside the bin go straight to the
     // problem's fine histogram.
     int p, chunk0, nch = 1;
@@ -1123,15 +1129,28 @@ __global__ __launch_bounds__(kThreads) void k_finehist(Params P) {
       grid_chunk(P, &p, &chunk0);
     }
     const int q = p % P.n_q, kind = p / P.n_q;
-    const int nc = cands_of(P, kind, P.q_nvis[q]);
+    // every load that does not depend on another goes out first: the visible
+    // length, the bin and the 16-bit group keys of all the thread's chunks
+    // (one 2-byte key per chunk); only the rare groups reaching the bin then
+    // load their scores
+    const int nvis = P.q_nvis[q];
     const uint32_t bin = P.meta[p].bin;
+    uint32_t gk[kLargeChunks];
+#pragma unroll
+    for (int c = 0; c < kLargeChunks; ++c) {
+      const int chunk = min(chunk0 + c, P.nchunk_cmp - 1);   // in bounds; chunks past nch are not used
+      gk[c] = kind == 0 ? P.gkey[(size_t)p * (P.stride >> 4) + ((chunk * kCmpChunk + tid * kCmpPerThread) >> 4)] : 0xFFFFu;
+    }
+    const int nc = cands_of(P, kind, nvis);
     if (bin == kAll) return;
     uint32_t* gh = P.hist2 + (size_t)p * kNBins;
-    for (int c = 0; c < nch; ++c) {
+#pragma unroll
+    for (int c = 0; c < kLargeChunks; ++c) {
+      if (c >= nch) break;
       const int chunk = chunk0 + c;
-      if (chunk > 0 && chunk * kCmpChunk >= nc) return;
+      if (chunk > 0 && chunk * kCmpChunk >= nc) break;
       const int my0 = chunk * kCmpChunk + tid * kCmpPerThread;
-      if (kind == 0 && (sortable(P.gmax[(size_t)p * (P.stride >> 8) + (my0 >> 8)]) >> kBinShift) < bin) continue;
+      if ((gk[c] >> (kBinShift - 16)) < bin) continue;
       float v[kCmpPerThread];
       load16(P, p, my0, v);
       const int m = count16(nc, my0);
@@ -1260,6 +1279,102 @@ __global__ __launch_bounds__(kThreads) void k_band(Params P) {
 // ---------------------------------------------------------------- 4. compaction
 // Band members of one chunk, in position order, flagged certain or not; the
 // uncertain ones are also listed (chunk-local index) for the rescoring.
+//
+// Large problems (k_band published the band): one wave per chunk, four
+// chunks per work-group and no barrier.  Lane l holds the chunk's scores
+// 64 l .. 64 l + 63, four groups of the scan's group maxima, and loads a
+// group only when its maximum reaches the band (a block chunk, which has no
+// maxima, always loads); a DPP scan over the lanes of the kept and uncertain
+// counts places the entries exactly where the per-work-group kernel below
+// puts them.
+constexpr int kCmpLanePer = kCmpChunk / kWave;   // scores per lane (64)
+
+__global__ __launch_bounds__(kThreads) void k_compact_large(Params P) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int pool = P.keep_blocks > 0 && !P.reindex;
+  const int nblk_ch = pool ? (P.nchunk_cmp + 7) >> 3 : 0;
+  const int f = (int)blockIdx.x * kWaves + wave;   // chunk of this wave: the token row's, then the block row's
+  if (f >= P.nchunk_cmp + nblk_ch) return;
+  const int kind = f >= P.nchunk_cmp ? 1 : 0;
+  const int chunk = kind ? f - P.nchunk_cmp : f;
+  const int q = blockIdx.y, p = kind * P.n_q + q;
+  const int c0 = chunk * kCmpChunk;
+  const int my0 = c0 + lane * kCmpLanePer;
+  // the independent loads first (visible length, band, the lane's four
+  // 16-bit group keys), then the scores that can reach the band
+  const int nvis = P.q_nvis[q];
+  const float keep_thr = P.meta[p].keep_thr, in_thr = P.meta[p].in_thr;
+  uint2 gk = make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+  if (kind == 0) gk = *reinterpret_cast<const uint2*>(P.gkey + (size_t)p * (P.stride >> 4) + (my0 >> 4));
+  const int nc = cands_of(P, kind, nvis);
+  if (chunk > 0 && c0 >= nc) {
+    if (lane == 0) {
+      P.chunk_cnt[(size_t)p * P.nchunk_cmp + chunk] = 0;
+      P.chunk_unc[(size_t)p * P.nchunk_cmp + chunk] = 0;
+    }
+    return;
+  }
+  const int m = max(0, min(kCmpLanePer, nc - my0));
+  // the lane's four 16-score groups: each is loaded only if it holds a
+  // candidate and (token rows) its largest key reaches the band's
+  uint32_t need = 0;
+  {
+    const uint32_t thr16 = sortable(keep_thr) >> 16;
+    const uint32_t k16[4] = {gk.x & 0xFFFFu, gk.x >> 16, gk.y & 0xFFFFu, gk.y >> 16};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) need |= (16 * g < m && k16[g] >= thr16 ? 1u : 0u) << g;
+  }
+  float v[kCmpLanePer];
+  const float4* s4 = reinterpret_cast<const float4*>(P.scores + (size_t)p * P.stride + my0);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    if ((need >> g) & 1u) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 t = s4[4 * g + j];
+        v[16 * g + 4 * j] = t.x;
+        v[16 * g + 4 * j + 1] = t.y;
+        v[16 * g + 4 * j + 2] = t.z;
+        v[16 * g + 4 * j + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[16 * g + j] = -INFINITY;
+    }
+  }
+  uint64_t keep = 0, cert = 0;
+#pragma unroll
+  for (int j = 0; j < kCmpLanePer; ++j) {
+    const bool k_ = j < m && v[j] != -INFINITY && v[j] >= keep_thr;
+    keep |= (k_ ? 1ull : 0ull) << j;
+    cert |= ((k_ && v[j] > in_thr) ? 1ull : 0ull) << j;
+  }
+  // both counts in one scan (each at most kCmpChunk, so the halves never carry)
+  const uint32_t mine = (uint32_t)__popcll(keep) | ((uint32_t)__popcll(keep & ~cert) << 16);
+  const uint32_t incl = wave_incl_scan_u32(mine);
+  const uint32_t both = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  uint32_t off = (incl - mine) & 0xFFFFu, uoff = (incl - mine) >> 16;
+  Entry* dst = P.band + (size_t)p * P.stride + c0;
+  uint2* udst = P.unc + (size_t)p * P.stride + c0;
+  // the few kept scores are read again (cached) rather than picked out of
+  // the registers by a run-time index, which would move them to scratch
+  const float* row = P.scores + (size_t)p * P.stride;
+  while (keep) {
+    const int j = __builtin_ctzll(keep);
+    keep &= keep - 1;
+    const bool c_ = (cert >> j) & 1ull;
+    dst[off] = Entry{(uint32_t)(my0 + j) | (c_ ? kCertain : 0u), row[my0 + j]};
+    if (!c_) udst[uoff++] = make_uint2(off, (uint32_t)(my0 + j));
+    ++off;
+  }
+  if (lane == 0) {
+    P.chunk_cnt[(size_t)p * P.nchunk_cmp + chunk] = both & 0xFFFFu;
+    P.chunk_unc[(size_t)p * P.nchunk_cmp + chunk] = both >> 16;
+  }
+}
+
+// Per-work-group mode.
 __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
   __shared__ uint32_t s_tmp[16];
   const int tid = threadIdx.x;
@@ -1280,30 +1395,14 @@ __global__ __launch_bounds__(kThreads) void k_compact(Params P) {
       return;
     }
     const int my0 = c0 + tid * kCmpPerThread;
-    // with the group maxima, a thread loads its scores only once the band is
-    // known and only if its 256-score group reaches the band
-    const bool skip = P.large_sel && kind == 0;
     float v[kCmpPerThread];
-    float gm = 0.0f;
-    if (skip) gm = P.gmax[(size_t)p * (P.stride >> 8) + (my0 >> 8)];
-    else load16(P, p, my0, v);
+    load16(P, p, my0, v);
     uint32_t hv[kHPer];
-    if (!P.large_sel) load_hist16(P.hist2 + (size_t)p * kNBins, hv);
+    load_hist16(P.hist2 + (size_t)p * kNBins, hv);
     const uint32_t m_bin = P.meta[p].bin, m_above = P.meta[p].above;
     const float m_delta = P.meta[p].delta;
     float keep_thr = -INFINITY, in_thr = -INFINITY;
-    if (P.large_sel) {   // k_band's
-      keep_thr = P.meta[p].keep_thr;
-      in_thr = P.meta[p].in_thr;
-    } else if (chunk == 0 || c0 < nc) {
-      wg_band_thresholds(P, p, hv, m_bin, m_above, m_delta, chunk == 0, s_tmp, &keep_thr, &in_thr);
-    }
-    if (skip) {
-      if (gm >= keep_thr) load16(P, p, my0, v);
-      else
-#pragma unroll
-        for (int j = 0; j < kCmpPerThread; ++j) v[j] = -INFINITY;
-    }
+    if (chunk == 0 || c0 < nc) wg_band_thresholds(P, p, hv, m_bin, m_above, m_delta, chunk == 0, s_tmp, &keep_thr, &in_thr);
     const int m = count16(nc, my0);
     uint32_t keep = 0, cert = 0;
 #pragma unroll
@@ -1373,44 +1472,104 @@ __device__ __forceinline__ int chunk_of(const uint32_t* s, int nch, uint32_t j) 
 // dimensions of all eight members loading while the current ones are used.
 // The next member's keys are loaded while the current one is scored.  A block
 // runs its eight member chains interleaved.
+//
+// Work-groups [0, rs_tok) of grid row q serve query q's token (or Reindex)
+// problem, their waves striding over its members.  The other work-groups
+// serve the block problems.  With rs_pool set, the block waves of every row
+// form one pool: each query gets waves in proportion to its undecided blocks
+// (contiguous ranges of `per` members, from a prefix over every query's chunk
+// counts), so that the long contexts of a mixed batch, which hold nearly all
+// of its block band, spread over the whole grid; without it, row q's block
+// work-groups serve query q alone.  A wave never leaves its query.
+constexpr int kPoolMaxQ = 256;   // queries of a pooled block rescoring
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
   constexpr int DW = D / 2;            // packed bf16 pairs per key row
   constexpr int KPER = 8 * DW / 64;    // key dwords of 8 members per lane
   __shared__ uint32_t s_tmp[16];
   __shared__ uint32_t s_uoff[kMaxChunksLds + 1];
+  __shared__ uint32_t s_woff[kPoolMaxQ + 1];
   __shared__ __attribute__((aligned(16))) float s_kf[kWaves][8][D];
-  __shared__ __attribute__((aligned(16))) float s_w[kWave];
+  __shared__ __attribute__((aligned(16))) float s_w[kWaves][kWave];
   __shared__ __attribute__((aligned(16))) float s_r[kWaves][kWave];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // work-groups [0, rs_tok) of a query serve its token (or Reindex) problem,
-  // the rest its block problem
-  const int q = blockIdx.y, kind = (int)blockIdx.x < P.rs_tok ? 0 : 1;
+  const int kind = (int)blockIdx.x < P.rs_tok ? 0 : 1;
+  const bool pooled = kind == 1 && P.rs_pool != 0;
+  const int nbw = (int)gridDim.x - P.rs_tok;   // block work-groups per grid row
+  // segments of the member list: one problem's chunks, or every query's block chunks
+  const int nchk = nchunks_of(P, kind);
+  const int nseg = pooled ? P.n_q * nchk : nchk;
+  const int wg = pooled ? (int)blockIdx.y * nbw + ((int)blockIdx.x - P.rs_tok)
+                        : (kind ? (int)blockIdx.x - P.rs_tok : (int)blockIdx.x);
+  const int nwg = pooled ? P.n_q * nbw : (kind ? nbw : P.rs_tok);
+  // exclusive prefix of the segments' uncertain counts into s_uoff[0 .. nseg]
+  {
+    uint32_t carry = 0;
+    for (int t0 = 0; t0 < nseg; t0 += kThreads) {
+      const int f = t0 + tid;
+      uint32_t cv = 0;
+      if (f < nseg) {
+        const int qf = pooled ? f / nchk : (int)blockIdx.y, c = pooled ? f - qf * nchk : f;
+        cv = P.chunk_unc[(size_t)(kind * P.n_q + qf) * P.nchunk_cmp + c];
+      }
+      uint32_t tt;
+      const uint32_t ex = wg_exclusive_scan(cv, s_tmp, &tt);
+      if (f < nseg) s_uoff[f] = carry + ex;
+      carry += tt;
+    }
+    if (tid == 0) s_uoff[nseg] = carry;
+    lds_barrier();
+  }
+  const int nwaves = nwg * kWaves, v = wg * kWaves + wave;
+  int q, j, j_end, stride_w;
+  if (pooled) {
+    // query qq gets ceil(n_qq / per) waves; per leaves one spare wave per
+    // query for the rounding up, so every query's members are covered
+    const int nu = (int)s_uoff[nseg];
+    const int per = max(1, (nu + nwaves - P.n_q - 1) / (nwaves - P.n_q));
+    uint32_t wc = 0;
+    if (tid < P.n_q) wc = (s_uoff[(tid + 1) * nchk] - s_uoff[tid * nchk] + per - 1) / per;
+    uint32_t wt;
+    const uint32_t wo = wg_exclusive_scan(wc, s_tmp, &wt);
+    if (tid < P.n_q) s_woff[tid] = wo;
+    if (tid == 0) s_woff[P.n_q] = wt;
+    lds_barrier();
+    if (v >= (int)wt) return;
+    q = __builtin_amdgcn_readfirstlane(chunk_of(s_woff, P.n_q, (uint32_t)v));
+    const int m0 = (int)s_uoff[q * nchk], m1 = (int)s_uoff[(q + 1) * nchk];
+    j = __builtin_amdgcn_readfirstlane(m0 + (v - (int)s_woff[q]) * per);
+    j_end = __builtin_amdgcn_readfirstlane(min(m1, j + per));
+    stride_w = 1;
+  } else {
+    q = blockIdx.y;
+    j = v;
+    j_end = (int)s_uoff[nseg];
+    stride_w = nwaves;
+  }
+  if (j >= j_end) return;
   const int p = kind * P.n_q + q;
-  const int wg = kind ? (int)blockIdx.x - P.rs_tok : (int)blockIdx.x;
-  const int nwg = kind ? (int)gridDim.x - P.rs_tok : P.rs_tok;
   const int nvis = P.q_nvis[q];
   const int64_t base = seq_base_of(P, q);
-  const int nch = nchunks_of(P, kind);
   Entry* band = P.band + (size_t)p * P.stride;
   const uint2* unc = P.unc + (size_t)p * P.stride;
+  // this problem's segments: s_uoff[seg0 .. seg0 + nchk]
+  const int seg0 = pooled ? q * nchk : 0;
 
-  if (tid < kWave) s_w[tid] = tid < P.h_i ? P.w[(size_t)q * P.h_i + tid] : 0.0f;
-  chunk_prefix(P.chunk_unc + (size_t)p * P.nchunk_cmp, nch, s_uoff, s_tmp);   // ends with a barrier
-  const int nu = (int)s_uoff[nch];
-  if (wg * kWaves >= nu) return;
+  // the head weights in the wave's own LDS row (wave-private: no barrier)
+  s_w[wave][lane] = lane < P.h_i ? P.w[(size_t)q * P.h_i + lane] : 0.0f;
   uint32_t qrow[DW];   // the lane's query row, packed bf16 pairs
   {
     const int hh = lane < P.h_i ? lane : 0;
     const uint4* src = reinterpret_cast<const uint4*>(P.iq + ((size_t)q * P.h_i + hh) * D);
 #pragma unroll
     for (int i = 0; i < DW / 4; ++i) {
-      const uint4 v = src[i];
-      qrow[4 * i] = v.x;
-      qrow[4 * i + 1] = v.y;
-      qrow[4 * i + 2] = v.z;
-      qrow[4 * i + 3] = v.w;
+      const uint4 vv = src[i];
+      qrow[4 * i] = vv.x;
+      qrow[4 * i + 1] = vv.y;
+      qrow[4 * i + 2] = vv.z;
+      qrow[4 * i + 3] = vv.w;
     }
   }
   auto qv = [&](int d) {   // query element d as fp32
@@ -1427,7 +1586,7 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
     float sc = 0.0f;
 #pragma unroll 2
     for (int h4 = 0; h4 < 16; ++h4) {   // partial unroll: few reads in flight, few VGPRs
-      const f32x4 wv = *reinterpret_cast<const f32x4*>(&s_w[4 * h4]);
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(&s_w[wave][4 * h4]);
       const f32x4 rv = *reinterpret_cast<const f32x4*>(&s_r[wave][4 * h4]);
       sc = fmaf(wv.x, rv.x, sc);
       sc = fmaf(wv.y, rv.y, sc);
@@ -1437,14 +1596,26 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
     return sc;
   };
 
-  // candidate j of this problem: its band slot, first member and member count
+  // candidate jj of this problem: its band slot, first member and member count
   struct Cand {
     uint32_t slot;
     int first, nmem;
   };
-  auto locate = [&](int j) {
-    const int c = chunk_of(s_uoff, nch, (uint32_t)j);
-    const uint2 u = unc[(size_t)c * kCmpChunk + (j - s_uoff[c])];
+  // members are visited in ascending order: a pooled wave finds its first
+  // segment by a search and walks forward from there
+  int f_cur = seg0 + (pooled ? chunk_of(s_uoff + seg0, nchk, (uint32_t)j) : 0);
+  auto locate = [&](int jj) {
+    int f;
+    if (pooled) {
+      f = f_cur;
+      while (s_uoff[f + 1] <= (uint32_t)jj) ++f;
+      f = __builtin_amdgcn_readfirstlane(f);
+      f_cur = f;
+    } else {
+      f = chunk_of(s_uoff, nseg, (uint32_t)jj);
+    }
+    const int c = f - seg0;
+    const uint2 u = unc[(size_t)c * kCmpChunk + (jj - s_uoff[f])];
     const uint32_t cand = __builtin_amdgcn_readfirstlane(u.y);
     Cand r;
     r.slot = (uint32_t)c * kCmpChunk + __builtin_amdgcn_readfirstlane(u.x);
@@ -1476,16 +1647,13 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
     }
   };
 
-  const int stride_w = nwg * kWaves;
-  int j = wg * kWaves + wave;
-  if (j >= nu) return;
   Cand cur = locate(j);
   uint32_t wv[KPER];
   load_keys(cur, wv);
   for (;;) {
     stage_keys(cur, wv);
     const int jn = j + stride_w;
-    const bool more = jn < nu;
+    const bool more = jn < j_end;
     Cand nxt = cur;
     if (more) {
       nxt = locate(jn);
@@ -2304,7 +2472,7 @@ thread_local hipEvent_t g_scan_ev_stop = nullptr;
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t scores, hist, hist2, meta, chunk_cnt, chunk_unc, band, unc, kpart, gmax, total;
+  size_t scores, hist, hist2, meta, chunk_cnt, chunk_unc, band, unc, kpart, gkey, total;
 };
 
 Layout make_layout(int nprob, int64_t stride, int nchunk_cmp) {
@@ -2328,8 +2496,8 @@ Layout make_layout(int nprob, int64_t stride, int nchunk_cmp) {
   o = align256(o + (size_t)nprob * stride * sizeof(uint2));
   L.kpart = o;   // one float per Reindex scan work-group (256 slots each)
   o = align256(o + (size_t)nprob * (size_t)(stride / 256) * sizeof(float));
-  L.gmax = o;    // one float per 256 scores
-  o = align256(o + (size_t)nprob * (size_t)(stride / 256) * sizeof(float));
+  L.gkey = o;    // 16 bits per 16 scores
+  o = align256(o + (size_t)nprob * (size_t)(stride / 16) * sizeof(uint16_t));
   L.total = o;
   return L;
 }
@@ -2414,7 +2582,7 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
   P.band = reinterpret_cast<Entry*>(w + L.band);
   P.unc = reinterpret_cast<uint2*>(w + L.unc);
   P.kpart = reinterpret_cast<float*>(w + L.kpart);
-  P.gmax = reinterpret_cast<float*>(w + L.gmax);
+  P.gkey = reinterpret_cast<uint16_t*>(w + L.gkey);
   // the selection's large mode pays once it has thousands of work-groups per
   // problem and reads gigabytes of scores (the encoder chunk: 4096 queries x
   // 512 K scores, 44.97 -> 43.99 ms per step); on a 64-query decode step
@@ -2477,15 +2645,22 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
     hipLaunchKernelGGL(k_band, dim3(P.nprob), dim3(kThreads), 0, s, P);
     if (!launch_ok()) return CSA2_E_HIP;
   }
-  hipLaunchKernelGGL(k_compact, gchunk, dim3(kThreads), 0, s, P);
+  if (P.large_sel) {
+    const dim3 gwave((unsigned)((gchunk.x + kWaves - 1) / kWaves), P.n_q);   // one wave per chunk
+    hipLaunchKernelGGL(k_compact_large, gwave, dim3(kThreads), 0, s, P);
+  } else {
+    hipLaunchKernelGGL(k_compact, gchunk, dim3(kThreads), 0, s, P);
+  }
   if (!launch_ok()) return CSA2_E_HIP;
   // One resident round (two work-groups per CU at this kernel's register
   // use): about kRescoreWGs work-groups in all, a query's share split 1:7
   // between its token and block problems (blocks have about ten times more
   // undecided members, each eight chains).  Every wave strides over its
-  // problem's members, so any split stays correct.
-  const int per_q = std::min(128, std::max(pool ? 8 : 4, kRescoreWGs / P.n_q));
+  // problem's members, so any split stays correct.  The block work-groups of
+  // all queries share one member list when its chunk counts fit in LDS.
+  const int per_q = std::min(128, std::max(pool ? 8 : 1, kRescoreWGs / P.n_q));
   P.rs_tok = pool ? std::max(1, per_q / 8) : per_q;
+  P.rs_pool = pool && P.n_q <= kPoolMaxQ && (int64_t)P.n_q * ((P.nchunk_cmp + 7) >> 3) <= kMaxChunksLds ? 1 : 0;
   if (P.d_i == 128) hipLaunchKernelGGL(k_rescore<128>, dim3(per_q, P.n_q), dim3(kThreads), 0, s, P);
   else hipLaunchKernelGGL(k_rescore<64>, dim3(per_q, P.n_q), dim3(kThreads), 0, s, P);
   if (!launch_ok()) return CSA2_E_HIP;

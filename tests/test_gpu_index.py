@@ -420,3 +420,30 @@ def test_subnormal_keys_and_queries():
     short = dict(inp)
     short["nvis"] = torch.tensor([9000, 9000, 3000], dtype=torch.int32)   # every context <= 16,384, no pool
     assert np.array_equal(_gpu_full(short, 512), _ref_full(short, 512))
+
+
+@gpu
+def test_pool_rescoring_beyond_shared_block_list():
+    """More than 256 queries with a pool: their block work-groups rescore
+    each query's own block band (the shared block list serves up to 256
+    queries).  The 300-query call must equal three 100-query calls (which
+    take the shared list), and both equal the oracle on a sample."""
+    n_q = 300
+    lengths = [17000 + (i * 7919) % 9000 for i in range(n_q)]
+    note(f"full + pool, {n_q} queries over {sum(lengths)} positions")
+    inp = index_inputs(lengths, 16, 64, seed=77)
+    got_idx, got_pool = _gpu_full(inp, 512, keep_blocks=2048)
+    for q0 in range(0, n_q, 100):
+        part = dict(inp)
+        part["iq"], part["w"] = inp["iq"][q0:q0 + 100], inp["w"][q0:q0 + 100]
+        part["q_seq"], part["nvis"] = inp["q_seq"][q0:q0 + 100], inp["nvis"][q0:q0 + 100]
+        p_idx, p_pool = _gpu_full(part, 512, keep_blocks=2048)
+        assert np.array_equal(p_idx, got_idx[q0:q0 + 100]), f"indices of queries {q0}..{q0 + 99} differ"
+        assert np.array_equal(p_pool, got_pool[q0:q0 + 100]), f"pools of queries {q0}..{q0 + 99} differ"
+    sample = [0, 1, 150, 298, 299]
+    sub = dict(inp)
+    sub["iq"], sub["w"] = inp["iq"][sample], inp["w"][sample]
+    sub["q_seq"], sub["nvis"] = inp["q_seq"][sample], inp["nvis"][sample]
+    r_idx, r_pool = _ref_full(sub, 512, keep_blocks=2048)
+    assert np.array_equal(got_idx[sample], r_idx)
+    assert np.array_equal(got_pool[sample], r_pool)

@@ -144,3 +144,37 @@ def test_c3_fp8_indexer_keys_1m_batch4():
 @gpu
 def test_c5_twenty_layer_schedule_fp8_indexer_keys():
     _check_workload("c5", length_div=16, fp8_keys=True)
+
+
+@gpu
+def test_c4_every_query_equals_decode_path_selection():
+    """All 4096 queries of the encoder-side chunk: the chunk call's Top-512
+    (8.6 GB of scores, so its selection runs in the large mode with group
+    maxima) equals the decode call's on the same queries, run in batches of
+    256 (0.5 GB of scores each, the per-work-group mode).  Both are exact
+    selections by (score desc, position asc), and the decode call is checked
+    against the oracle elsewhere, so every query of the chunk is covered at
+    its real size."""
+    from sparse_long_context_topk_amd import Workspace, index_topk, index_topk_chunk
+
+    dev = device()
+    wl = gen.workload("c4")
+    note(f"workload {wl['name']}: chunk call vs batched decode calls, every query")
+    st, layers, _, _ = bench.build_state(wl, dev)
+    full = layers[0]
+    got = index_topk_chunk(full.iq, full.w, st.q_nvis, st.max_nvis, st.ik, st.chunk_base, k=st.k,
+                           ws=st.ws_index)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    ws = Workspace()
+    n_q, nb = wl["n_q"], 256
+    for q0 in range(0, n_q, nb):
+        sl = slice(q0, min(n_q, q0 + nb))
+        nvis = st.q_nvis[sl].contiguous()
+        ref = index_topk(full.iq[sl].contiguous(), full.w[sl].contiguous(), st.q_seq[sl].contiguous(), nvis,
+                         int(nvis.max().item()), st.ik, st.seq_base, k=st.k, ws=ws)
+        torch.cuda.synchronize()
+        ref = ref.cpu().numpy()
+        bad = np.nonzero(~np.all(got[sl] == ref, axis=1))[0]
+        assert bad.size == 0, f"queries {[q0 + int(b) for b in bad[:8]]} differ between the chunk and decode calls"
+    print(f"{wl['name']}: all {n_q} queries equal", flush=True)
