@@ -76,7 +76,7 @@ constexpr double kLargeSelBytes = 1024.0 * 1048576.0;
 constexpr int kLargeChunks = 8;   // large mode without a block problem: chunks per fine-histogram work-group   // token score bytes from which the selection runs in its large mode
 constexpr int kCmpPerThread = kCmpChunk / kThreads;
 constexpr int kMaxChunksLds = 8192;   // compaction chunks per problem (max_nvis <= 2^25)
-constexpr int kRescoreWGs = 512;   // rescoring work-groups per launch (all queries)
+constexpr int kRescoreWGs = 768;   // rescoring work-groups per launch (all queries): three per CU
 #ifndef CSA2_SCAN_NBUF_FP8
 #define CSA2_SCAN_NBUF_FP8 5
 #endif
@@ -1661,6 +1661,10 @@ __global__ __launch_bounds__(kThreads) void k_rescore(Params P) {
     }
     float r;
     if (kind == 1) {
+      // the query row's fp32 values are formed per block rather than held
+      // across the loop: 64 registers fewer, three waves per SIMD
+#pragma unroll
+      for (int i = 0; i < DW; ++i) asm volatile("" : "+v"(qrow[i]));
       float a[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) a[t] = 0.0f;
@@ -2652,8 +2656,8 @@ csa2_status run_pipeline(Params P, int64_t max_slots, void* ws, size_t ws_bytes,
     hipLaunchKernelGGL(k_compact, gchunk, dim3(kThreads), 0, s, P);
   }
   if (!launch_ok()) return CSA2_E_HIP;
-  // One resident round (two work-groups per CU at this kernel's register
-  // use): about kRescoreWGs work-groups in all, a query's share split 1:7
+  // One resident round (three work-groups per CU at this kernel's register
+  // and LDS use): about kRescoreWGs work-groups in all, a query's share split 1:7
   // between its token and block problems (blocks have about ten times more
   // undecided members, each eight chains).  Every wave strides over its
   // problem's members, so any split stays correct.  The block work-groups of
