@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 import torch
 
+import csa2_inputs as gen
 import oracle
 import sparse_long_context_topk_amd as csa2
 from gpu_common import bits, device, gpu, index_inputs, note, to_dev
@@ -447,3 +448,31 @@ def test_pool_rescoring_beyond_shared_block_list():
     r_idx, r_pool = _ref_full(sub, 512, keep_blocks=2048)
     assert np.array_equal(got_idx[sample], r_idx)
     assert np.array_equal(got_pool[sample], r_pool)
+
+
+@gpu
+def test_large_mode_with_pool_equals_per_work_group_mode():
+    """A Full call with a pool whose token scores pass 1 GB (300 queries over
+    one 1M-position sequence: 1.2 GB) runs the large selection mode for both
+    of its problems (token rows with group keys, block rows loading every
+    group); three 100-query calls on the same queries (0.4 GB each) run the
+    per-work-group mode.  Both are exact, so indices and pools must agree."""
+    dev = device()
+    n_q, L, h_i, d_i = 300, 1 << 20, 16, 64
+    note(f"large mode with a pool: {n_q} queries over one {L}-position sequence")
+    ik = gen.normal((L, d_i), 91, "ik", dtype=torch.bfloat16).to(dev)
+    iq = gen.normal((n_q, h_i, d_i), 91, "iq", dtype=torch.bfloat16).to(dev)
+    w = gen.uniform((n_q, h_i), 91, "w").to(dev)
+    nvis = torch.tensor([L - 4093 * (i % 7) for i in range(n_q)], dtype=torch.int32, device=dev)
+    q_seq = torch.zeros(n_q, dtype=torch.int32, device=dev)
+    seq_base = torch.zeros(1, dtype=torch.int64, device=dev)
+    big_idx, big_pool = csa2.index_topk(iq, w, q_seq, nvis, L, ik, seq_base, k=512, keep_blocks=2048)
+    torch.cuda.synchronize()
+    big_idx, big_pool = big_idx.cpu().numpy(), big_pool.cpu().numpy()
+    for q0 in range(0, n_q, 100):
+        sl = slice(q0, q0 + 100)
+        i2, p2 = csa2.index_topk(iq[sl].contiguous(), w[sl].contiguous(), q_seq[sl].contiguous(),
+                                 nvis[sl].contiguous(), L, ik, seq_base, k=512, keep_blocks=2048)
+        torch.cuda.synchronize()
+        assert np.array_equal(i2.cpu().numpy(), big_idx[sl]), f"indices of queries {q0}..{q0 + 99} differ"
+        assert np.array_equal(p2.cpu().numpy(), big_pool[sl]), f"pools of queries {q0}..{q0 + 99} differ"
