@@ -451,28 +451,39 @@ def test_pool_rescoring_beyond_shared_block_list():
 
 
 @gpu
-def test_large_mode_with_pool_equals_per_work_group_mode():
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_large_mode_with_pool_equals_per_work_group_mode(fmt):
     """A Full call with a pool whose token scores pass 1 GB (300 queries over
     one 1M-position sequence: 1.2 GB) runs the large selection mode for both
     of its problems (token rows with group keys, block rows loading every
     group); three 100-query calls on the same queries (0.4 GB each) run the
-    per-work-group mode.  Both are exact, so indices and pools must agree."""
+    per-work-group mode.  Both are exact, so indices and pools must agree;
+    with bf16 keys and with FP8 keys."""
     dev = device()
-    n_q, L, h_i, d_i = 300, 1 << 20, 16, 64
-    note(f"large mode with a pool: {n_q} queries over one {L}-position sequence")
+    n_q, L, h_i = 300, 1 << 20, 16
+    d_i = 64 if fmt == "bf16" else 128
+    note(f"large mode with a pool ({fmt} keys): {n_q} queries over one {L}-position sequence")
     ik = gen.normal((L, d_i), 91, "ik", dtype=torch.bfloat16).to(dev)
     iq = gen.normal((n_q, h_i, d_i), 91, "iq", dtype=torch.bfloat16).to(dev)
     w = gen.uniform((n_q, h_i), 91, "w").to(dev)
     nvis = torch.tensor([L - 4093 * (i % 7) for i in range(n_q)], dtype=torch.int32, device=dev)
     q_seq = torch.zeros(n_q, dtype=torch.int32, device=dev)
     seq_base = torch.zeros(1, dtype=torch.int64, device=dev)
-    big_idx, big_pool = csa2.index_topk(iq, w, q_seq, nvis, L, ik, seq_base, k=512, keep_blocks=2048)
-    torch.cuda.synchronize()
-    big_idx, big_pool = big_idx.cpu().numpy(), big_pool.cpu().numpy()
+    if fmt == "fp8":
+        ik8, ik8e = csa2.index_keys_fp8(ik)
+
+    def call(sl):
+        args = (iq[sl].contiguous(), w[sl].contiguous(), q_seq[sl].contiguous(), nvis[sl].contiguous(), L)
+        if fmt == "fp8":
+            r = csa2.index_topk_fp8(*args, ik8, ik8e, seq_base, k=512, keep_blocks=2048)
+        else:
+            r = csa2.index_topk(*args, ik, seq_base, k=512, keep_blocks=2048)
+        torch.cuda.synchronize()
+        return r[0].cpu().numpy(), r[1].cpu().numpy()
+
+    big_idx, big_pool = call(slice(0, n_q))
     for q0 in range(0, n_q, 100):
         sl = slice(q0, q0 + 100)
-        i2, p2 = csa2.index_topk(iq[sl].contiguous(), w[sl].contiguous(), q_seq[sl].contiguous(),
-                                 nvis[sl].contiguous(), L, ik, seq_base, k=512, keep_blocks=2048)
-        torch.cuda.synchronize()
-        assert np.array_equal(i2.cpu().numpy(), big_idx[sl]), f"indices of queries {q0}..{q0 + 99} differ"
-        assert np.array_equal(p2.cpu().numpy(), big_pool[sl]), f"pools of queries {q0}..{q0 + 99} differ"
+        i2, p2 = call(sl)
+        assert np.array_equal(i2, big_idx[sl]), f"indices of queries {q0}..{q0 + 99} differ"
+        assert np.array_equal(p2, big_pool[sl]), f"pools of queries {q0}..{q0 + 99} differ"
